@@ -1,0 +1,188 @@
+/*
+ * spec.h - C ABI of the MI355X speculative-decoding verification library.
+ *
+ * The library runs the target model's verification step of lossless greedy
+ * speculative decoding on one gfx950 GPU: one forward pass scores a pending
+ * root token plus a chain or tree of draft tokens against a paged KV cache,
+ * takes the greedy argmax at every node and accepts the longest root path
+ * whose tokens equal the target's own choices.  The emitted text is then
+ * identical to plain autoregressive greedy decoding ("token forcing";
+ * zicq.com article "SpecPilot Uses Agentic Discovery to Push Speculative
+ * Decoding to 10.87x", section "Core Idea: Let Agents Discover the
+ * Bottlenecks").  Tree verification, including hybrid targets whose recurrent
+ * layers recompute their state along each root path, follows the besthub.dev
+ * article "SpecPilot: AI Agent Framework Boosts Speculative Decoding 10.87x
+ * for Qwen3.8-27B", section "(2) Best-first Tree Verification for Hybrid
+ * Architectures".  Only the exact verification may accept tokens or update
+ * the target's state (same article, "(3) Two-Level Verification"): this is
+ * why verification (spec_verify) and the state update (spec_commit) are
+ * separate calls.
+ *
+ * Conventions for every call:
+ *  - All int32_t-returning calls return SPEC_OK (0) or a negative SPEC_E_*
+ *    code; spec_last_error() then describes the failure.  On any error the
+ *    committed state (KV cache contents below each request's length,
+ *    recurrent states, lengths, pending roots) is unchanged.  After
+ *    SPEC_E_HIP the context is poisoned: every later call except
+ *    spec_last_error/spec_destroy returns SPEC_E_HIP.
+ *  - "host" pointers are ordinary CPU memory, read or written before the
+ *    call returns.  "device" pointers are GPU memory on the context's device.
+ *  - The caller owns the device workspace and the HIP stream.  The library
+ *    allocates no device memory of its own; it enqueues all GPU work on the
+ *    given stream.  A context is single-stream and not thread-safe.
+ */
+#ifndef SPEC_H
+#define SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPEC_OK = 0,
+  SPEC_E_INVAL = -1,       /* bad ids, shapes or tree (parent out of range) */
+  SPEC_E_STATE = -2,       /* call-order violation or non-root path         */
+  SPEC_E_CAPACITY = -3,    /* KV pages or max_ctx exhausted                 */
+  SPEC_E_HIP = -4,         /* a HIP runtime error; the context is poisoned  */
+  SPEC_E_UNSUPPORTED = -5  /* shape or option this build does not handle    */
+};
+
+enum { SPEC_DTYPE_FP32 = 0, SPEC_DTYPE_BF16 = 1 };
+enum { SPEC_LAYER_ATTN = 0, SPEC_LAYER_LR = 1 };
+
+#define SPEC_MAX_LAYERS 128
+
+/*
+ * Model shape and capacity.  Dense layers: RMSNorm, GQA attention with
+ * rotate-half RoPE, SwiGLU FFN.  Recurrent layers (layer_kind SPEC_LAYER_LR)
+ * replace attention with a gated diagonal linear recurrence of state width
+ * lr_state per channel: [x|a|z|B|C] = norm(h) W_in^T,
+ * H_t = sigmoid(a_t) * H_{t-1} + B_t (x) x_t, y_t = H_t C_t,
+ * h += (y_t * silu(z_t)) W_out^T.
+ */
+typedef struct spec_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  int32_t dtype;                       /* SPEC_DTYPE_*: weights and KV cache  */
+  int32_t lr_state;                    /* recurrent state width (0: none)     */
+  int32_t layer_kind[SPEC_MAX_LAYERS]; /* SPEC_LAYER_* per layer              */
+  float rms_eps, rope_theta;
+  int32_t max_requests;   /* requests alive at once                          */
+  int32_t max_ctx;        /* per request: committed tokens + one tree        */
+  int32_t max_nodes;      /* per request: rows of one verify (root + K)      */
+  int32_t max_rows;       /* rows of one verify over all its requests        */
+  int32_t prefill_chunk;  /* prompt rows per prefill pass                    */
+  int32_t page_size;      /* tokens per KV page; must be 16                  */
+} spec_config;
+
+typedef struct spec_ctx spec_ctx;
+
+/* Device bytes the caller must provide to spec_create for this config:
+ * weights in the library's tiled layout, the KV page pool (max_requests *
+ * max_ctx tokens), recurrent states and scratch.  0 if cfg is invalid. */
+size_t spec_workspace_bytes(const spec_config* cfg);
+
+/* Create a context on the current HIP device.  d_workspace: device buffer of
+ * at least spec_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the
+ * caller and used exclusively by the context until spec_destroy.
+ * hip_stream: a hipStream_t (NULL = default stream).  *out receives the
+ * context (NULL on failure). */
+int32_t spec_create(const spec_config* cfg, void* d_workspace, size_t bytes,
+                    void* hip_stream, spec_ctx** out);
+
+/* Load one weight tensor.  tensor_id follows this order: embedding [V, d];
+ * per layer, attention layers: attn_norm [d], Wq [nq*hd, d], Wk [nkv*hd, d],
+ * Wv [nkv*hd, d], Wo [d, nq*hd], ffn_norm [d], Wg [F, d], Wu [F, d],
+ * Wd [d, F]; recurrent layers: attn_norm [d], W_in [3d+2S, d], W_out [d, d],
+ * ffn_norm [d], Wg, Wu, Wd; then final_norm [d], lm_head [V, d].
+ * src: row-major [out, in] in the config's dtype (fp32, or bf16 bit
+ * patterns), `bytes` long, on the host (src_on_device = 0) or the device
+ * (src_on_device = 1).  src is only borrowed for the call; the library
+ * re-lays the tensor out once into its own tiled layout.  The call is
+ * synchronous.  Errors: SPEC_E_INVAL for a bad id or size. */
+int32_t spec_load_weights(spec_ctx* ctx, int32_t tensor_id, const void* src,
+                          size_t bytes, int32_t src_on_device);
+
+/* Start request `req` (0 <= req < max_requests, not active) with the host
+ * prompt[n] (1 <= n, n + max_nodes <= max_ctx).  Writes the prompt's KV,
+ * runs the recurrent layers over it from a zero state, and returns in
+ * *first_token (host) the greedy argmax of the last prompt row, which becomes
+ * the request's pending root.  d_logits_opt: NULL or device float[vocab]
+ * receiving that row's logits.  Synchronous.  Errors: SPEC_E_STATE if any
+ * weight is missing or req is active, SPEC_E_INVAL, SPEC_E_CAPACITY. */
+int32_t spec_prefill(spec_ctx* ctx, int32_t req, const int32_t* prompt,
+                     int32_t n, int32_t* first_token, float* d_logits_opt);
+
+/* Verify one draft tree per request, all in one forward pass.
+ * host arrays: req[n_req] (distinct active requests); n_nodes[n_req] draft
+ * counts K_r >= 0 with K_r + 1 <= max_nodes and sum(K_r + 1) <= max_rows;
+ * draft_tokens and parent_idx concatenated per request (sum K_r entries):
+ * parent_idx[i] in [-1, i-1] within its request, -1 meaning the pending
+ * root, so every parent precedes its children.  A draft node at depth j
+ * (the root has depth 0) is placed at position n_r + j.
+ * Outputs (host): path, concatenated per request with max_nodes - 1 slots
+ * each, holding the accepted draft indices in root-to-leaf order;
+ * path_len[n_req]; bonus[n_req], the target's greedy token after the
+ * accepted path.  d_logits_opt: NULL or device float[sum(K_r+1), vocab],
+ * each request's rows being its root then its drafts in order.
+ * The committed state is not modified.  Returns after the single
+ * device-to-host copy of the results. */
+int32_t spec_verify(spec_ctx* ctx, int32_t n_req, const int32_t* req,
+                    const int32_t* n_nodes, const int32_t* draft_tokens,
+                    const int32_t* parent_idx, int32_t* path,
+                    int32_t* path_len, int32_t* bonus, float* d_logits_opt);
+
+/* Commit after a spec_verify of the same requests (same order).  host
+ * arrays: path concatenated with max_nodes - 1 slots per request as returned
+ * by spec_verify; path_len[n_req]: any prefix of a root path of the verified
+ * tree may be committed; next_root[n_req] in [0, vocab) becomes the pending
+ * root (normally the bonus token; any token may be forced).  The root and
+ * the path's drafts are appended to the context, the KV of the accepted
+ * branch is moved to its final positions and the recurrent state advances
+ * along the path.  Asynchronous (stream-ordered).  Errors: SPEC_E_STATE if
+ * there is no matching verify or the path is not a root path. */
+int32_t spec_commit(spec_ctx* ctx, int32_t n_req, const int32_t* req,
+                    const int32_t* path, const int32_t* path_len,
+                    const int32_t* next_root);
+
+/* End request `req` and free its KV pages. */
+int32_t spec_release(spec_ctx* ctx, int32_t req);
+
+/* Committed length and pending root of an active request. */
+int32_t spec_request_state(const spec_ctx* ctx, int32_t req, int32_t* n_ctx,
+                           int32_t* pending_root);
+
+/* Token forcing: replace the pending root of an active request (for
+ * example with a reference token where the target's own choice was a
+ * near-tie).  Invalidates a pending verify of that request.  Host-only. */
+int32_t spec_force_root(spec_ctx* ctx, int32_t req, int32_t token);
+
+/* Fault injection for checking the token-forcing harness: adds `bias` to
+ * the logit of `token` at every row whose position is >= after_position
+ * (an analogue of the logit-bias fault of the besthub.dev article, "Phase 4:
+ * Final Validation").  token < 0 disables it (the default). */
+int32_t spec_set_fault(spec_ctx* ctx, int32_t token, float bias,
+                       int32_t after_position);
+
+/* Per-launch timing of one kernel class, for roofline measurement: while
+ * enabled, the library brackets every launch of that class with HIP events
+ * on its stream.  cls: 0 = off, 1 = FFN gate/up GEMM, 2 = FFN down GEMM,
+ * 3 = LM head GEMM, 4 = attention.  spec_timing_read synchronizes the
+ * stream, returns the summed milliseconds and launch count since the last
+ * read, and resets them. */
+int32_t spec_timing_enable(spec_ctx* ctx, int32_t cls);
+int32_t spec_timing_read(spec_ctx* ctx, double* total_ms, int64_t* launches);
+
+/* Destroy the context (the workspace stays the caller's). */
+void spec_destroy(spec_ctx* ctx);
+
+/* Message describing the last error (never NULL). */
+const char* spec_last_error(const spec_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_H */

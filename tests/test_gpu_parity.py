@@ -1,0 +1,296 @@
+"""GPU parity: the HIP verify path (through the C ABI) against the oracle.
+
+Tokens must equal the oracle's greedy output except where the oracle's
+top-1/top-2 margin is below 1e-2 (counted); logits must be within 1e-4
+(fp32 models) or 2e-2 x the row's logit std (bf16 models).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ar_greedy, top2_margin
+from parity import (NEAR_TIE, protocol_f, engine_for, oracle_for, make_drafts,
+                    logit_tol)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _setup(name):
+    if name not in _CACHE:
+        cfg = synth.model_config(name)
+        _CACHE[name] = (cfg, synth.make_weights(cfg))
+    return _CACHE[name]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _assert_ok(rep, max_tie_frac=0.2):
+    _say(rep)
+    assert rep.first_bad is None, rep
+    assert rep.max_logit_err <= 1.0, rep
+    assert rep.near_tie_mismatch <= max(1, int(max_tie_frac * rep.emitted)), rep
+
+
+# --------------------------------------------------------------- workload 0
+
+def test_tiny_chain_workload():
+    """Tiny fp32 decoder, 64-token prompt, chain K=4, alpha=0.7, 128 tokens;
+    every row's logits (rejected drafts included) against the oracle's
+    tree-masked pass."""
+    w = synth.workload("tiny_chain")
+    cfg, W = _setup("tiny")
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=w["K"] + 1)
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(cfg["vocab"], w["prompt"], w["index"])
+    rep = protocol_f(eng, cfg, orc, prompt, w["gen"], w, "chain",
+                     cfg_index=w["index"], all_rows=True)
+    _assert_ok(rep)
+    e = synth.expected_tokens_per_step(w["alpha"], w["K"])
+    _say("tokens/step", rep.emitted / rep.steps, "expected", e)
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_hybrid", "tiny_gqa_bf16",
+                                  "tiny_hybrid_bf16"])
+@pytest.mark.parametrize("kind", ["chain", "tree"])
+def test_small_models(name, kind):
+    cfg, W = _setup(name)
+    w = dict(K=8 if kind == "chain" else 20, alpha=0.8,
+             branching=(4, 3, 2, 2, 1, 1, 1, 1), max_depth=8)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=w["K"] + 1)
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(cfg["vocab"], 37, 50)
+    rep = protocol_f(eng, cfg, orc, prompt, 40, w, kind, cfg_index=50,
+                     all_rows=True)
+    _assert_ok(rep)
+
+
+def test_prefill_chunking_and_long_prompt():
+    """A prompt spanning several prefill chunks and KV pages."""
+    cfg, W = _setup("tiny_hybrid_bf16")
+    w = dict(K=6, alpha=0.7)
+    eng = engine_for(cfg, W, max_ctx=1024, max_nodes=7, prefill_chunk=96)
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(cfg["vocab"], 333, 51)
+    rep = protocol_f(eng, cfg, orc, prompt, 24, w, "chain", cfg_index=51,
+                     all_rows=True)
+    _assert_ok(rep)
+
+
+# ---------------------------------------------------------------- batched
+
+def test_batched_requests():
+    """Several requests of different lengths in one fused verify per step,
+    each checked against its own oracle greedy run."""
+    cfg, W = _setup("tiny_gqa_bf16")
+    V = cfg["vocab"]
+    n_req, K, n_gen = 5, 8, 30
+    eng = engine_for(cfg, W, max_requests=8, max_ctx=512, max_nodes=K + 1,
+                     max_rows=8 * (K + 1))
+    orc = oracle_for(cfg, W)
+    lens = [17, 40, 63, 100, 129]
+    alphas = [0.4, 0.6, 0.7, 0.8, 0.9]
+    reqs = [0, 3, 1, 7, 2]              # request ids need not be dense
+    refs, g = [], []
+    for i, r in enumerate(reqs):
+        prompt = synth.prompt_tokens(V, lens[i], 60, i)
+        S, L, M, _ = ar_greedy(orc, prompt, n_gen)
+        refs.append((S, L, M))
+        first = eng.prefill(r, prompt)
+        if first != S[0]:
+            assert M[0] < NEAR_TIE
+            eng.force_root(r, int(S[0]))
+        g.append(1)
+    step, ties = 0, 0
+    while min(g) < n_gen:
+        live = [i for i in range(n_req) if g[i] < n_gen]
+        drafts, parents = [], []
+        for i in live:
+            t, p = synth.chain_drafts(refs[i][0], g[i], K, alphas[i], V, 60, i, step)
+            drafts.append(t)
+            parents.append(p)
+        paths, bonus, lg = eng.verify([reqs[i] for i in live], drafts, parents,
+                                      logits=True)
+        lg = lg.cpu().numpy()
+        row0 = 0
+        keep_all, roots = [], []
+        for k, i in enumerate(live):
+            S, L, M = refs[i]
+            emitted = [int(drafts[k][p]) for p in paths[k]] + [bonus[k]]
+            n_ok = 0
+            for j, t in enumerate(emitted):
+                if g[i] + j >= n_gen or t != S[g[i] + j]:
+                    break
+                n_ok += 1
+            # logits of the root row and accepted rows before any mismatch
+            rows = [row0] + [row0 + p + 1 for p in paths[k]]
+            for j in range(min(n_ok + 1, len(rows))):
+                if g[i] + j < n_gen:
+                    tol = logit_tol(cfg["dtype"], L[g[i] + j])
+                    assert np.max(np.abs(lg[rows[j]] - L[g[i] + j])) <= tol
+            if n_ok < len(emitted) and g[i] + n_ok < n_gen:
+                pos = g[i] + n_ok
+                assert M[pos] < NEAR_TIE, (i, pos, emitted, S[g[i]:g[i] + 10])
+                ties += 1
+                keep = paths[k][:n_ok] if n_ok < len(paths[k]) else paths[k]
+                keep_all.append(keep)
+                roots.append(int(S[pos]))
+                g[i] += len(keep) + 1
+            else:
+                keep_all.append(paths[k])
+                roots.append(bonus[k])
+                g[i] += len(emitted)
+            row0 += len(drafts[k]) + 1
+        eng.commit([reqs[i] for i in live], keep_all, roots)
+        step += 1
+    _say("batched steps", step, "near-tie mismatches", ties)
+    assert ties <= 3
+
+
+# ------------------------------------------------- spec == GPU AR (protocol A)
+
+def test_spec_equals_gpu_autoregressive():
+    cfg, W = _setup("tiny")
+    V, n_gen = cfg["vocab"], 60
+    prompt = synth.prompt_tokens(V, 64, 0)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=5)
+    # GPU AR: K = 0 verify steps
+    S_gpu, marg = [eng.prefill(0, prompt)], []
+    for t in range(n_gen - 1):
+        paths, bonus, lg = eng.verify([0], [[]], [[]], logits=True)
+        marg.append(top2_margin(lg[0].cpu().numpy()))
+        eng.commit([0], [[]], [bonus[0]])
+        S_gpu.append(bonus[0])
+    eng.release(0)
+    orc = oracle_for(cfg, W)
+    S, _, M, _ = ar_greedy(orc, prompt, n_gen)
+    for t in range(n_gen):
+        if S_gpu[t] != S[t]:
+            assert M[t] < NEAR_TIE
+            break
+    # spec decoding with drafts from the GPU's own AR sequence
+    w = dict(K=4, alpha=0.7)
+    first = eng.prefill(0, prompt)
+    assert first == S_gpu[0]
+    g, step, mism = 1, 0, 0
+    while g < n_gen:
+        toks, par = synth.chain_drafts(np.array(S_gpu), g, 4, 0.7, V, 0, 0, step)
+        paths, bonus = eng.verify([0], [toks], [par])
+        emitted = [int(toks[p]) for p in paths[0]] + [bonus[0]]
+        n_ok = 0
+        for j, t in enumerate(emitted):
+            if g + j >= n_gen or t != S_gpu[g + j]:
+                break
+            n_ok += 1
+        if n_ok < len(emitted) and g + n_ok < n_gen:
+            mism += 1
+            assert marg[g + n_ok - 1] < NEAR_TIE
+            keep = paths[0][:n_ok] if n_ok < len(paths[0]) else paths[0]
+            eng.commit([0], [keep], [S_gpu[g + n_ok]])
+            g += len(keep) + 1
+        else:
+            eng.commit([0], paths, bonus)
+            g += len(emitted)
+        step += 1
+    _say("spec vs GPU AR mismatches:", mism)
+
+
+# ---------------------------------------------------------- fault injection
+
+def test_fault_injection_is_caught_at_first_affected_token():
+    """A logit bias switched on at a late position must make the checker
+    fail exactly at the first generated token it affects."""
+    w = synth.workload("tiny_chain")
+    cfg, W = _setup("tiny")
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=5)
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(cfg["vocab"], 64, 0)
+    S, L, M, _ = ar_greedy(orc, prompt, 96)
+    after = 64 + 70        # positions >= after are biased
+    t_star = after - 64 + 1
+    bad_tok = int((S[t_star] + 1) % cfg["vocab"])
+    eng.set_fault(bad_tok, 50.0, after)
+    rep = protocol_f(eng, cfg, orc, prompt, 96, w, "chain", cfg_index=0,
+                     oracle_ref=(S, L, M), check_logits=False)
+    _say(rep)
+    assert rep.first_bad is not None and rep.first_bad[0] == t_star
+    assert rep.first_bad[1] == bad_tok
+
+
+# -------------------------------------------------------------- error paths
+
+def test_error_paths_leave_state_unchanged():
+    from tree_verification_spec_amd import (SpecError, SPEC_E_INVAL,
+                                            SPEC_E_STATE, SPEC_E_CAPACITY)
+    cfg, W = _setup("tiny")
+    V = cfg["vocab"]
+    eng = engine_for(cfg, W, max_requests=2, max_ctx=96, max_nodes=5)
+    prompt = synth.prompt_tokens(V, 64, 0)
+    first = eng.prefill(0, prompt)
+    state0 = eng.state(0)
+
+    def code(f, *a):
+        with pytest.raises(SpecError) as ei:
+            f(*a)
+        return ei.value.code
+    assert code(eng.verify, [0], [[1, 2]], [[-1, 1]]) == SPEC_E_INVAL   # parent >= i
+    assert code(eng.verify, [0], [[1, 2]], [[-2, 0]]) == SPEC_E_INVAL
+    assert code(eng.verify, [0], [[V, 2]], [[-1, 0]]) == SPEC_E_INVAL   # token
+    assert code(eng.verify, [0], [[1] * 5], [[-1, 0, 1, 2, 3]]) == SPEC_E_INVAL  # K+1 > max_nodes
+    assert code(eng.verify, [1], [[1]], [[-1]]) == SPEC_E_STATE        # inactive
+    assert code(eng.verify, [2], [[1]], [[-1]]) == SPEC_E_INVAL        # no such id
+    assert code(eng.verify, [0, 0], [[1], [1]], [[-1], [-1]]) == SPEC_E_INVAL
+    assert code(eng.commit, [0], [[]], [1]) == SPEC_E_STATE            # no verify
+    assert eng.state(0) == state0
+    paths, bonus = eng.verify([0], [[5, 6, 7]], [[-1, -1, 0]])
+    assert code(eng.commit, [0], [[1, 2]], [1]) == SPEC_E_STATE         # not a root path
+    assert code(eng.commit, [0], [[2]], [1]) == SPEC_E_STATE            # 2's parent is 0
+    assert eng.state(0) == state0
+    eng.commit([0], [[0]], [bonus[0]])                                  # any root path
+    assert eng.state(0) == (state0[0] + 2, bonus[0])
+    # capacity: 64 + 2 committed, max_ctx 96
+    while True:
+        n, _ = eng.state(0)
+        if n + 5 > 96:
+            break
+        p, b = eng.verify([0], [[1, 2, 3, 4]], [[-1, 0, 1, 2]])
+        eng.commit([0], [[]], b)
+    st = eng.state(0)
+    assert code(eng.verify, [0], [[1, 2, 3, 4]], [[-1, 0, 1, 2]]) == SPEC_E_CAPACITY
+    assert eng.state(0) == st
+    assert code(eng.prefill, 0, prompt) == SPEC_E_STATE                # active
+    eng.release(0)
+    assert code(eng.prefill, 0, list(range(95))) == SPEC_E_CAPACITY    # too long
+
+
+def test_verify_is_deterministic():
+    cfg, W = _setup("tiny_hybrid_bf16")
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=17)
+    prompt = synth.prompt_tokens(cfg["vocab"], 50, 52)
+    eng.prefill(0, prompt)
+    toks = np.arange(16) * 7 % cfg["vocab"]
+    par = np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5, 11, 12, 8, 14])
+    a = eng.verify([0], [toks], [par], logits=True)
+    b = eng.verify([0], [toks], [par], logits=True)
+    assert a[0] == b[0] and a[1] == b[1]
+    assert np.array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
+
+
+# ------------------------------------------------ full-width model variants
+
+@pytest.mark.parametrize("name,budget", [("dense8b_l2", 64), ("hybrid27b_l4", 32)])
+def test_full_width_trees(name, budget):
+    """Real hidden size, heads, FFN and vocabulary with few layers; draft
+    trees of the workloads' node budgets; every row's logits checked."""
+    cfg, W = _setup(name)
+    w = dict(K=budget, alpha=0.8, branching=(4, 3, 2, 2, 1, 1, 1, 1), max_depth=8)
+    eng = engine_for(cfg, W, max_ctx=1024, max_nodes=budget + 1)
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(cfg["vocab"], 300, 53)
+    rep = protocol_f(eng, cfg, orc, prompt, 14, w, "tree", cfg_index=53,
+                     all_rows=True)
+    _assert_ok(rep)

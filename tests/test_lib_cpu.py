@@ -1,0 +1,58 @@
+"""Host-side checks that need no GPU: the C-ABI library loads, exports every
+symbol its header declares, and sizes its workspace from a config."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from tree_verification_spec_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libspec.so is not built (run __graft_entry__.build())")
+    return L
+
+
+def test_header_symbols_are_exported():
+    L = _lib()
+    header = open(os.path.join(ROOT, "include", "spec.h")).read()
+    declared = set(re.findall(r"\b(spec_[a-z_]+)\s*\(", header))
+    assert "spec_verify" in declared and "spec_commit" in declared
+    so = ctypes.CDLL(L.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), name
+    assert declared == set(L.EXPORTS)
+
+
+def test_workspace_bytes_and_config_validation():
+    L = _lib()
+    from tree_verification_spec_amd import make_config
+    tiny = synth.model_config("tiny")
+    n = L.spec_workspace_bytes(make_config(tiny, max_ctx=512, max_nodes=5))
+    # the weights alone
+    w = sum(int(__import__("numpy").prod(s)) for _, s, _ in synth.tensor_specs(tiny)) * 4
+    assert n > w
+    big = synth.model_config("dense8b")
+    n8 = L.spec_workspace_bytes(make_config(big, max_ctx=2600, max_nodes=17))
+    assert 16.3e9 < n8 < 20e9
+    bad = make_config(tiny, max_nodes=66)
+    assert L.spec_workspace_bytes(bad) == 0
+    odd = dict(tiny, head_dim=96)
+    assert L.spec_workspace_bytes(make_config(odd)) == 0
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The library package must not import the oracle."""
+    pkg = os.path.join(ROOT, "tree_verification_spec_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

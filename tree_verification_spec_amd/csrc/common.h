@@ -1,0 +1,110 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 storage, MFMA
+// operand fragments and wave reductions.
+//
+// Fragment convention used by every matrix kernel: a "K-step" covers 32
+// reduction indices.  For a 16-row operand tile, lane l (0..63) holds row
+// (l % 16) and the 8 consecutive reduction indices (l / 16) * 8 + e,
+// e = 0..7.  For bf16 this is exactly the operand of
+// v_mfma_f32_16x16x32_bf16; for fp32 the same 8 values feed eight
+// v_mfma_f32_16x16x4_f32 (instruction e consumes item e, so A and B see the
+// same permutation of the reduction index).  The 16x16 fp32 result is held
+// as lane l, item r -> row 4 * (l / 16) + r, column l % 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// bf16 values are stored as raw uint16_t bit patterns.
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// float -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Frag;
+
+// 8 bf16 = 16 bytes
+template <> struct Frag<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v = *reinterpret_cast<const uint4*>(p);
+  }
+};
+
+// 8 fp32 = 32 bytes
+template <> struct Frag<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void zero() {
+    lo = make_float4(0.f, 0.f, 0.f, 0.f);
+    hi = lo;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const float4*>(p);
+    hi = *reinterpret_cast<const float4*>(p + 4);
+  }
+};
+
+// acc += A(16 x 32) * B(32 x 16) for one K-step.
+__device__ __forceinline__ void mma32(floatx4_t& acc, const Frag<uint16_t>& a,
+                                      const Frag<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
+      acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma32(floatx4_t& acc, const Frag<float>& a,
+                                      const Frag<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+
+// Activations kept at fp32 precision but fed to bf16 MFMAs are stored as
+// two bf16 planes, hi = bf16(v) and lo = bf16(v - hi): hi + lo carries ~16
+// mantissa bits.  fp32 activations are stored once (lo is unused).
+__device__ __forceinline__ void store_act(uint16_t* hi, uint16_t* lo, size_t i,
+                                          float v) {
+  const uint16_t h = f2bf(v);
+  hi[i] = h;
+  lo[i] = f2bf(v - bf2f(h));
+}
+__device__ __forceinline__ void store_act(float* hi, float* /*lo*/, size_t i,
+                                          float v) {
+  hi[i] = v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

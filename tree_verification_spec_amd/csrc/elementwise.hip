@@ -1,0 +1,416 @@
+// Small kernels of the verify pass: embedding gather, RMSNorm, RoPE + KV
+// store, argmax reduction, accepted-path walk, the per-branch recurrence of
+// the hybrid layers, the commit kernels and the one-time weight re-layout.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// ---------------------------------------------------------------- embedding
+template <typename T>
+__global__ void embed_kernel(const T* emb, const RowMeta* rows, int d, float* h) {
+  const int row = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= d) return;
+  h[(size_t)row * d + c] = to_f<T>(emb[(size_t)rows[row].token * d + c]);
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// u = (h / sqrt(mean(h^2) + eps)) * w, one workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const float* w,
+                                                      int d, float eps, T* u, T* u_lo) {
+  __shared__ float part[4];
+  const int row = blockIdx.x;
+  const float* x = h + (size_t)row * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) ss += x[c] * x[c];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float denom = sqrtf(tot / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += 256)
+    store_act(u, u_lo, (size_t)row * d + c, __fmul_rn(__fdiv_rn(x[c], denom), w[c]));
+}
+
+// ------------------------------------------------------------ RoPE + KV store
+// Block = one row, one head (query, key or value head); threads cover the
+// head_dim / 2 rotation pairs (i, i + hd/2).
+template <typename T>
+__global__ void rope_kv_kernel(const float* qkv, const RowMeta* rows, int nq,
+                               int nkv, int hd, const float* cos_t,
+                               const float* sin_t, T* q_out, T* q_lo, T* kc, T* vc) {
+  const int row = blockIdx.x;
+  const int head = blockIdx.y;  // [0, nq) q, [nq, nq+nkv) k, then v
+  const int half = hd >> 1;
+  const RowMeta rm = rows[row];
+  const size_t ld = (size_t)(nq + 2 * nkv) * hd;
+  const float* x = qkv + row * ld + (size_t)head * hd;
+  const int page = rm.slot >> 4, off = rm.slot & 15;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const float x1 = x[i], x2 = x[i + half];
+    if (head < nq + nkv) {
+      const float c = cos_t[(size_t)rm.pos * half + i];
+      const float s = sin_t[(size_t)rm.pos * half + i];
+      const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
+      const float y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+      if (head < nq) {
+        const size_t base = ((size_t)row * nq + head) * hd;
+        store_act(q_out, q_lo, base + i, y1);
+        store_act(q_out, q_lo, base + i + half, y2);
+      } else {
+        const int kvh = head - nq;
+        T* dst = kc + (((size_t)page * nkv + kvh) * 16 + off) * hd;
+        dst[i] = from_f<T>(y1);
+        dst[i + half] = from_f<T>(y2);
+      }
+    } else {
+      const int kvh = head - nq - nkv;
+      T* dst = vc + ((size_t)page * nkv + kvh) * hd * 16 + off;
+      dst[(size_t)i * 16] = from_f<T>(x1);
+      dst[(size_t)(i + half) * 16] = from_f<T>(x2);
+    }
+  }
+}
+
+// ----------------------------------------------------------- argmax reduce
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* part,
+                                                            int nblocks,
+                                                            int32_t* amax) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  const int row = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int b = threadIdx.x; b < nblocks; b += 256) {
+    const float2 p = part[(size_t)row * nblocks + b];
+    const int i = __float_as_int(p.y);
+    if (better(p.x, i, bv, bi)) { bv = p.x; bi = i; }
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float v = sv[threadIdx.x + o];
+      const int i = si[threadIdx.x + o];
+      if (better(v, i, sv[threadIdx.x], si[threadIdx.x])) {
+        sv[threadIdx.x] = v;
+        si[threadIdx.x] = i;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) amax[row] = (si[0] == 0x7fffffff) ? 0 : si[0];
+}
+
+// ------------------------------------------------------------- path walk
+// ok(0) = 1; ok(i) = ok(parent) && token(i) == A(parent); best = deepest ok
+// node (lowest index among equals); path = root..best; bonus = A(best).
+__global__ void path_walk_kernel(const RowMeta* rows, const ReqMeta* reqs,
+                                 const int32_t* amax, int max_path,
+                                 int32_t* res) {
+  const int r = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const ReqMeta rm = reqs[r];
+  int32_t* out = res + (size_t)r * (2 + max_path);
+  // depth and ok of each node, kept in the result slots temporarily is not
+  // possible (sizes differ), so walk with small local arrays
+  constexpr int MAXN = 512;
+  __shared__ int8_t ok[MAXN];
+  __shared__ int16_t dep[MAXN];
+  int best = 0;
+  ok[0] = 1;
+  dep[0] = 0;
+  for (int i = 1; i < rm.nrows && i < MAXN; ++i) {
+    const RowMeta n = rows[rm.row0 + i];
+    const int p = n.parent;
+    ok[i] = ok[p] && n.token == amax[rm.row0 + p];
+    dep[i] = dep[p] + 1;
+    if (ok[i] && dep[i] > dep[best]) best = i;
+  }
+  const int plen = dep[best];
+  out[0] = plen;
+  out[1] = amax[rm.row0 + best];
+  int v = best;
+  for (int k = plen - 1; k >= 0; --k) {
+    out[2 + k] = v;
+    v = rows[rm.row0 + v].parent;
+  }
+}
+
+// ------------------------------------------------------ recurrence (verify)
+// Lanes: S consecutive lanes own one channel c (lane % S = state index s).
+// For each node in index order (parents first):
+//   H_i = sigmoid(a_i[c]) * H_parent + B_i[s] * x_i[c]   (no FMA contraction)
+//   y_i[c] = sum_s H_i[s] * C_i[s]; o_i[c] = y_i * silu(z_i[c])
+// Tree passes keep every node's state in LDS; chain passes keep one state.
+template <typename T, int S, bool TREE>
+__global__ __launch_bounds__(256) void lr_fork_kernel(
+    const float* proj, const RowMeta* rows, const ReqMeta* reqs, int d,
+    float* H, T* o, T* o_lo, bool commit_last) {
+  extern __shared__ float hs[];  // [max_rows][256] for trees
+  constexpr int CPB = 256 / S;   // channels per block
+  const int r = blockIdx.y;
+  const ReqMeta rm = reqs[r];
+  const int s = threadIdx.x % S;
+  const int c = blockIdx.x * CPB + threadIdx.x / S;
+  const bool live = c < d;
+  const int cc = live ? c : 0;
+  const int ld = 3 * d + 2 * S;
+  float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
+  const float h0 = *H0;
+  float hprev = h0;
+  for (int i = 0; i < rm.nrows; ++i) {
+    const int row = rm.row0 + i;
+    const float* pr = proj + (size_t)row * ld;
+    float hp;
+    if (TREE) {
+      const int p = rows[row].parent;
+      hp = (p < 0) ? h0 : hs[p * 256 + threadIdx.x];
+    } else {
+      hp = hprev;
+    }
+    const float a = pr[d + cc];
+    const float x = pr[cc];
+    const float sig = 1.0f / (1.0f + expf(-a));
+    const float hi = __fadd_rn(__fmul_rn(sig, hp), __fmul_rn(pr[3 * d + s], x));
+    if (TREE) hs[i * 256 + threadIdx.x] = hi;
+    hprev = hi;
+    float y = __fmul_rn(hi, pr[3 * d + S + s]);
+#pragma unroll
+    for (int off = S / 2; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
+    if (s == 0 && live) {
+      const float z = pr[2 * d + cc];
+      store_act(o, o_lo, (size_t)row * d + cc, y * (z / (1.0f + expf(-z))));
+    }
+  }
+  if (commit_last && live) *H0 = hprev;
+}
+
+// ----------------------------------------------------------- KV compaction
+// Per (request, attention layer, KV head): read every accepted node's K and V
+// first, then write them at their final positions (a node's destination may
+// be another accepted node's source).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_compact_kernel(
+    const CommitReq* cr, const int32_t* btab, int max_pages, T* kbase,
+    T* vbase, size_t layer_stride, int nkv, int hd) {
+  __shared__ T buf[2][64 * 128];
+  const int r = blockIdx.x, layer = blockIdx.y, kvh = blockIdx.z;
+  const CommitReq q = cr[r];
+  const int32_t* bt = btab + (size_t)q.table * max_pages;
+  T* kc = kbase + layer * layer_stride;
+  T* vc = vbase + layer * layer_stride;
+  const int n = q.plen * hd;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int j = e / hd, dim = e % hd;
+    const int t = q.nctx + q.nodes[j];
+    const int page = bt[t >> 4], off = t & 15;
+    buf[0][e] = kc[(((size_t)page * nkv + kvh) * 16 + off) * hd + dim];
+    buf[1][e] = vc[(((size_t)page * nkv + kvh) * hd + dim) * 16 + off];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int j = e / hd, dim = e % hd;
+    if (q.nodes[j] == j + 1) continue;  // already in place
+    const int t = q.nctx + j + 1;
+    const int page = bt[t >> 4], off = t & 15;
+    kc[(((size_t)page * nkv + kvh) * 16 + off) * hd + dim] = buf[0][e];
+    vc[(((size_t)page * nkv + kvh) * hd + dim) * 16 + off] = buf[1][e];
+  }
+}
+
+// ------------------------------------------------------ recurrence commit
+// H <- state after the root and the accepted nodes, same op order as the
+// verify pass, so the committed state equals the verified node's state.
+__global__ __launch_bounds__(256) void lr_commit_kernel(
+    const CommitReq* cr, const float* proj_all, size_t proj_layer_stride,
+    int ld, int d, int S, float* H, size_t H_layer_stride) {
+  const int r = blockIdx.z, layer = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= d * S) return;
+  const int c = e / S, s = e % S;
+  const CommitReq q = cr[r];
+  float* hp = H + layer * H_layer_stride + (size_t)q.table * d * S + e;
+  const float* proj = proj_all + layer * proj_layer_stride;
+  float h = *hp;
+  for (int k = 0; k <= q.plen; ++k) {
+    const int node = (k == 0) ? 0 : q.nodes[k - 1];
+    const float* pr = proj + (size_t)(q.row0 + node) * ld;
+    const float a = pr[d + c];
+    const float sig = 1.0f / (1.0f + expf(-a));
+    h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(pr[3 * d + s], pr[c]));
+  }
+  *hp = h;
+}
+
+// ---------------------------------------------------------- weight layout
+template <typename T>
+__global__ void relayout_kernel(const T* src, int nrows, int K, T* dst,
+                                int dst_tile0, int tile_stride) {
+  const int ksteps = K / 32;
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)(nrows / 16) * ksteps * 64;
+  if (tid >= total) return;
+  const int lane = tid & 63;
+  const size_t tile = tid >> 6;
+  const int nb = (int)(tile / ksteps), kb = (int)(tile % ksteps);
+  const int row = nb * 16 + (lane & 15);
+  const int col = kb * 32 + (lane >> 4) * 8;
+  const T* s = src + (size_t)row * K + col;
+  const size_t dtr = (size_t)dst_tile0 + (size_t)nb * tile_stride;
+  T* d = dst + ((dtr * ksteps + kb) * 64 + lane) * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d[e] = s[e];
+}
+
+template <typename T>
+__global__ void to_f32_kernel(const T* src, int n, float* dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = to_f<T>(src[i]);
+}
+
+}  // namespace
+
+hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
+                        int d, float* h, hipStream_t s) {
+  dim3 grid((d + 255) / 256, R);
+  if (bf16) embed_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)emb, rows, d, h);
+  else embed_kernel<float><<<grid, 256, 0, s>>>((const float*)emb, rows, d, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(bool bf16, const float* h, const float* w, int R,
+                          int d, float eps, void* u, void* u_lo, hipStream_t s) {
+  if (bf16)
+    rmsnorm_kernel<uint16_t><<<R, 256, 0, s>>>(h, w, d, eps, (uint16_t*)u, (uint16_t*)u_lo);
+  else rmsnorm_kernel<float><<<R, 256, 0, s>>>(h, w, d, eps, (float*)u, (float*)u_lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(bool bf16, const float* qkv, const RowMeta* rows,
+                          int R, int nq, int nkv, int hd, const float* cos_t,
+                          const float* sin_t, void* q_out, void* q_lo, void* kc,
+                          void* vc, hipStream_t s) {
+  dim3 grid(R, nq + 2 * nkv);
+  const int thr = hd / 2 < 64 ? 64 : hd / 2;
+  if (bf16)
+    rope_kv_kernel<uint16_t><<<grid, thr, 0, s>>>(qkv, rows, nq, nkv, hd, cos_t, sin_t,
+                                                  (uint16_t*)q_out, (uint16_t*)q_lo,
+                                                  (uint16_t*)kc, (uint16_t*)vc);
+  else
+    rope_kv_kernel<float><<<grid, thr, 0, s>>>(qkv, rows, nq, nkv, hd, cos_t, sin_t,
+                                               (float*)q_out, (float*)q_lo, (float*)kc,
+                                               (float*)vc);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
+                                int32_t* amax, hipStream_t s) {
+  argmax_reduce_kernel<<<R, 256, 0, s>>>(part, nblocks, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
+                            int n_req, const int32_t* amax, int max_path,
+                            int32_t* res, hipStream_t s) {
+  path_walk_kernel<<<n_req, 64, 0, s>>>(rows, reqs, amax, max_path, res);
+  return hipGetLastError();
+}
+
+template <typename T, int S>
+static hipError_t lr_fork_s(const float* proj, const RowMeta* rows,
+                            const ReqMeta* reqs, int n_req, int d, float* H,
+                            void* o, void* o_lo, bool tree, bool commit_last,
+                            int max_rows_per_req, hipStream_t s) {
+  constexpr int CPB = 256 / S;
+  dim3 grid((d + CPB - 1) / CPB, n_req);
+  if (tree) {
+    const size_t lds = (size_t)max_rows_per_req * 256 * sizeof(float);
+    hipError_t e = hipFuncSetAttribute((const void*)lr_fork_kernel<T, S, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    lr_fork_kernel<T, S, true><<<grid, 256, lds, s>>>(proj, rows, reqs, d, H, (T*)o,
+                                                      (T*)o_lo, commit_last);
+  } else {
+    lr_fork_kernel<T, S, false><<<grid, 256, 0, s>>>(proj, rows, reqs, d, H, (T*)o,
+                                                     (T*)o_lo, commit_last);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lr_fork(bool bf16, const float* proj, const RowMeta* rows,
+                          const ReqMeta* reqs, int n_req, int d, int S,
+                          float* H, void* o, void* o_lo, bool any_tree,
+                          bool commit_last, int max_rows_per_req, hipStream_t s) {
+#define LR_CASE(SV)                                                              \
+  case SV:                                                                       \
+    return bf16 ? lr_fork_s<uint16_t, SV>(proj, rows, reqs, n_req, d, H, o, o_lo,\
+                                          any_tree, commit_last,                 \
+                                          max_rows_per_req, s)                   \
+                : lr_fork_s<float, SV>(proj, rows, reqs, n_req, d, H, o, o_lo,   \
+                                       any_tree, commit_last, max_rows_per_req, s);
+  switch (S) {
+    LR_CASE(16)
+    LR_CASE(32)
+    LR_CASE(64)
+    default: return hipErrorInvalidValue;
+  }
+#undef LR_CASE
+}
+
+hipError_t launch_kv_compact(bool bf16, const CommitReq* cr, int n_req,
+                             const int32_t* btab, int max_pages, void* kbase,
+                             void* vbase, size_t layer_stride_elems,
+                             int n_attn_layers, int nkv, int hd,
+                             hipStream_t s) {
+  dim3 grid(n_req, n_attn_layers, nkv);
+  if (bf16)
+    kv_compact_kernel<uint16_t><<<grid, 256, 0, s>>>(cr, btab, max_pages, (uint16_t*)kbase,
+                                                     (uint16_t*)vbase, layer_stride_elems,
+                                                     nkv, hd);
+  else
+    kv_compact_kernel<float><<<grid, 256, 0, s>>>(cr, btab, max_pages, (float*)kbase,
+                                                  (float*)vbase, layer_stride_elems, nkv,
+                                                  hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_lr_commit(const CommitReq* cr, int n_req,
+                            const float* proj_all, size_t proj_layer_stride,
+                            int proj_ld, int n_lr, int d, int S, float* H,
+                            size_t H_layer_stride, hipStream_t s) {
+  dim3 grid((d * S + 255) / 256, n_lr, n_req);
+  lr_commit_kernel<<<grid, 256, 0, s>>>(cr, proj_all, proj_layer_stride, proj_ld,
+                                        d, S, H, H_layer_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
+                           void* dst, int dst_tile0, int tile_stride,
+                           hipStream_t s) {
+  const size_t total = (size_t)(nrows / 16) * (K / 32) * 64;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (bf16)
+    relayout_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, nrows, K,
+                                                   (uint16_t*)dst, dst_tile0, tile_stride);
+  else
+    relayout_kernel<float><<<grid, 256, 0, s>>>((const float*)src, nrows, K,
+                                                (float*)dst, dst_tile0, tile_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(bool bf16, const void* src, int n, float* dst,
+                         hipStream_t s) {
+  const int grid = (n + 255) / 256;
+  if (bf16) to_f32_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, n, dst);
+  else to_f32_kernel<float><<<grid, 256, 0, s>>>((const float*)src, n, dst);
+  return hipGetLastError();
+}

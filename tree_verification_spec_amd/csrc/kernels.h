@@ -1,0 +1,151 @@
+// Internal interface between the host runtime (spec_api.cpp) and the gfx950
+// kernels.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// One row of a forward pass (a tree node, or a prompt token in prefill).
+struct RowMeta {
+  int32_t token;
+  int32_t pos;     // RoPE position: committed length + depth
+  int32_t slot;    // physical KV slot (page * 16 + offset) written by this row
+  int32_t req;     // index of its request in this pass's ReqMeta array
+  int32_t node;    // node index inside the request (0 = root)
+  int32_t parent;  // node-local parent index, -1 for the root
+  int32_t pad0, pad1;
+};
+
+// One request of a forward pass.
+struct ReqMeta {
+  int32_t row0;       // first row of the request in the pass
+  int32_t nrows;      // rows (root + drafts)
+  int32_t nctx;       // committed tokens: keys [0, nctx) are always visible
+  int32_t table;      // request id: row of the block table
+  int32_t anc0;       // u64 offset of the request's ancestor masks
+  int32_t anc_words;  // u64 words per row
+  int32_t chain;      // rows form a chain (parent == node - 1)
+  int32_t pad;
+};
+
+// Tiled weight layout: a matrix [N, K] is stored as 16 x 32 tiles, tile
+// (nb, kb) at element offset (nb * (K / 32) + kb) * 512, lane l of the tile
+// holding W[nb * 16 + l % 16][kb * 32 + (l / 16) * 8 + e] at l * 8 + e.
+
+enum GemmEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+
+struct GemmArgs {
+  const void* W;      // tiled weights (bf16 bits or fp32)
+  const void* X;      // activations [M, K], same element type as W
+  const void* X_lo;   // bf16: low plane of the activations (hi + lo = value)
+  int32_t M, K;       // rows, reduction length
+  int32_t ntiles;     // 16-column tiles of W
+  int32_t row0;       // first row handled by this launch
+  float* Y;           // STORE: Y[M, ldy] = result; RESID: Y += result
+  int32_t ldy;
+  void* act;          // SWIGLU: act[M, ldact] (element type of X)
+  void* act_lo;       // SWIGLU, bf16: low plane of act
+  int32_t ldact;
+  float2* part;       // ARGMAX: per (row, column block) (max, index bits)
+  int32_t nblocks;    // column blocks (= ntiles / NT)
+  float* logits;      // ARGMAX: optional fp32 logits [M, ldlog]
+  int32_t ldlog;
+  const RowMeta* rows;     // ARGMAX fault injection: row positions
+  int32_t bias_tok, bias_after;
+  float bias;
+};
+
+// Launch the skinny GEMM for rows [0, M): picks the tile shape and splits
+// rows into chunks when M exceeds one launch's row capacity.
+hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, int nt_per_block,
+                       hipStream_t s);
+
+struct AttnArgs {
+  const void* q;            // [rows, nq, hd] (bf16 bits or fp32), after RoPE
+  const void* q_lo;         // bf16: low plane of q
+  const void* kc;           // K pages of this layer: [page][nkv][16][hd]
+  const void* vc;           // V pages of this layer: [page][nkv][hd][16]
+  const int32_t* btab;      // block tables [max_requests][max_pages]
+  int32_t max_pages;
+  const RowMeta* rows;
+  const ReqMeta* reqs;
+  const uint64_t* anc;      // ancestor masks (self included)
+  float* part_o;            // [split][rows * nq][hd]
+  float2* part_ml;          // [split][rows * nq] (running max, sum)
+  int32_t nq, nkv, hd;
+  int32_t split;            // keys per split (multiple of 32)
+  int32_t max_splits, max_qgroups, n_req;
+  int32_t rows_total;
+  float scale;
+};
+
+hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s);
+
+// Merge the per-split partials into o[rows, nq * hd] (element type of q;
+// bf16 also writes the low plane o_lo).
+hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o,
+                               void* o_lo, hipStream_t s);
+
+hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows,
+                        int R, int d, float* h, hipStream_t s);
+
+// u = rmsnorm(h) * w, stored in the activation type (bf16: hi/lo planes).
+hipError_t launch_rmsnorm(bool bf16, const float* h, const float* w, int R,
+                          int d, float eps, void* u, void* u_lo, hipStream_t s);
+
+// q -> RoPE -> q_out; k -> RoPE -> K cache; v -> V cache, at each row's slot.
+hipError_t launch_rope_kv(bool bf16, const float* qkv, const RowMeta* rows,
+                          int R, int nq, int nkv, int hd, const float* cos_t,
+                          const float* sin_t, void* q_out, void* q_lo, void* kc,
+                          void* vc, hipStream_t s);
+
+// Per-row argmax over the column-block partials (lowest index on ties).
+hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
+                                int32_t* amax, hipStream_t s);
+
+// Accepted-path walk per request; writes res[req][2 + max_path]:
+// {path_len, bonus, path...}.
+hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
+                            int n_req, const int32_t* amax, int max_path,
+                            int32_t* res, hipStream_t s);
+
+// Gated diagonal recurrence over the pass's nodes for one recurrent layer.
+// proj: [R, 3d + 2S] fp32 = [x | a | z | B | C]; H: committed states
+// [max_requests][d][S]; o: [R, d] activation type.  With commit_last (chain
+// passes only) the state of each request's last row is written back to H.
+hipError_t launch_lr_fork(bool bf16, const float* proj, const RowMeta* rows,
+                          const ReqMeta* reqs, int n_req, int d, int S,
+                          float* H, void* o, void* o_lo, bool any_tree,
+                          bool commit_last, int max_rows_per_req, hipStream_t s);
+
+struct CommitReq {
+  int32_t table;     // request id
+  int32_t nctx;      // committed length before the commit
+  int32_t row0;      // first row of the request in the verified pass
+  int32_t plen;      // accepted drafts
+  int32_t nodes[64]; // accepted node indices (root excluded), root-to-leaf
+};
+
+// Move the accepted branch's K/V from slot (n + node) to position
+// (n + depth) for every attention layer.
+hipError_t launch_kv_compact(bool bf16, const CommitReq* cr, int n_req,
+                             const int32_t* btab, int max_pages, void* kbase,
+                             void* vbase, size_t layer_stride_elems,
+                             int n_attn_layers, int nkv, int hd,
+                             hipStream_t s);
+
+// Advance the committed recurrent state along root + accepted nodes.
+hipError_t launch_lr_commit(const CommitReq* cr, int n_req,
+                            const float* proj_all, size_t proj_layer_stride,
+                            int proj_ld, int n_lr, int d, int S, float* H,
+                            size_t H_layer_stride, hipStream_t s);
+
+// Copy a row-major [nrows, K] slab into the tiled layout.  Source rows
+// [0, nrows) become destination tile rows dst_tile0 + t * tile_stride.
+hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
+                           void* dst, int dst_tile0, int tile_stride,
+                           hipStream_t s);
+
+// Widen a norm vector (bf16 bits or fp32) to fp32.
+hipError_t launch_to_f32(bool bf16, const void* src, int n, float* dst,
+                         hipStream_t s);

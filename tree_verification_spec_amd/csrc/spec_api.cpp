@@ -1,0 +1,1002 @@
+// Host runtime of the verification library: the C ABI declared in spec.h.
+//
+// One context = one model on one device and stream.  The caller's workspace
+// is carved into: weights (matrices in the tiled MFMA layout, embedding
+// row-major, norm vectors in fp32), the KV page pool (K pages
+// [page][kv_head][16][head_dim], V pages transposed [page][kv_head]
+// [head_dim][16], one pool per attention layer), recurrent states, RoPE
+// tables, scratch activations and the per-pass metadata.
+//
+// A verify pass is: metadata upload (one async copy), embedding, per layer
+// [RMSNorm, QKV GEMM, RoPE + KV store, tree attention + combine, O GEMM +
+// residual] or [RMSNorm, in_proj GEMM, recurrence fork, out_proj GEMM +
+// residual], then [RMSNorm, gate/up GEMM + SwiGLU, down GEMM + residual],
+// then the final RMSNorm, LM-head GEMM with argmax partials, argmax
+// reduction, path walk and the single device-to-host copy of the results.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/spec.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxSplits = 32;
+constexpr int kStagingBytes = 64 << 20;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Req {
+  bool active = false;
+  int n = 0;
+  int root = 0;
+  std::vector<int> pages;
+};
+
+struct Layer {
+  int kind = SPEC_LAYER_ATTN;
+  int idx = 0;  // index among layers of its kind
+  float* n1 = nullptr;
+  float* n2 = nullptr;
+  void* wqkv = nullptr;  // attention: [Wq; Wk; Wv] tiled
+  void* wo = nullptr;
+  void* win = nullptr;   // recurrent: W_in tiled
+  void* wout = nullptr;
+  void* wgu = nullptr;   // gate/up tiles interleaved
+  void* wd = nullptr;
+};
+
+// tensor id -> where it goes
+struct TensorSlot {
+  int kind;  // 0 embed, 1 norm, 2 matrix, 3 raw matrix part of a fused matrix
+  int layer;
+  int rows, cols;
+  void* dst;
+  int tile0, tile_stride;
+};
+
+struct Plan {
+  size_t total = 0;
+  size_t cursor = 0;
+  size_t take(size_t bytes) {
+    const size_t off = cursor;
+    cursor = align_up(cursor + bytes);
+    total = cursor;
+    return off;
+  }
+};
+
+struct LastVerify {
+  bool valid = false;
+  std::vector<int> req, row0, nrows, nctx;
+  std::vector<std::vector<int>> parent;  // node-local parents
+};
+
+}  // namespace
+
+struct spec_ctx {
+  spec_config cfg{};
+  bool bf16 = true;
+  size_t esz = 2;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  int device = 0;
+
+  int d = 0, nq = 0, nkv = 0, hd = 0, F = 0, V = 0, S = 0;
+  int n_attn = 0, n_lr = 0, qkv_n = 0, in_n = 0;
+  std::vector<Layer> layers;
+  std::vector<TensorSlot> slots;
+  std::vector<char> loaded;
+
+  void* embed = nullptr;
+  void* lm_head = nullptr;
+  float* final_norm = nullptr;
+
+  // KV pool
+  char* kpool = nullptr;
+  char* vpool = nullptr;
+  size_t kv_layer_elems = 0;
+  int n_pages = 0, max_pages = 0;
+  int32_t* d_btab = nullptr;
+  std::vector<int> free_pages;
+
+  float* H = nullptr;  // [n_lr][max_requests][d][S]
+  size_t H_layer = 0;
+  float* cos_t = nullptr;
+  float* sin_t = nullptr;
+  int max_pos = 0;
+
+  // scratch
+  int Rmax = 0;
+  float* h = nullptr;
+  void* u = nullptr;
+  void* u_lo = nullptr;
+  void* act = nullptr;
+  void* act_lo = nullptr;
+  void* attn_o = nullptr;
+  void* attn_o_lo = nullptr;
+  float* qkv = nullptr;
+  void* q = nullptr;
+  void* q_lo = nullptr;
+  float* lrproj = nullptr;
+  size_t lrproj_layer = 0;  // floats per layer slot (verify)
+  void* lr_o = nullptr;
+  void* lr_o_lo = nullptr;
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  float2* am_part = nullptr;
+  int32_t* amax = nullptr;
+  int32_t* res = nullptr;
+  void* staging = nullptr;  // aliases the scratch activations
+
+  // metadata: device and pinned host mirrors
+  RowMeta* d_rows = nullptr;
+  ReqMeta* d_reqs = nullptr;
+  uint64_t* d_anc = nullptr;
+  CommitReq* d_commit = nullptr;
+  char* h_meta = nullptr;  // pinned: rows | reqs | anc (same layout as device)
+  char* d_meta = nullptr;
+  size_t meta_bytes = 0, off_reqs = 0, off_anc = 0;
+  CommitReq* h_commit = nullptr;
+  int32_t* h_res = nullptr;
+  int32_t* h_btab_row = nullptr;
+
+  std::vector<Req> reqs;
+  LastVerify last;
+  std::string err;
+  bool poisoned = false;
+  int fault_tok = -1;
+  float fault_bias = 0.f;
+  int fault_after = 0;
+
+  int timing_cls = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t events_used = 0;
+  double timing_ms = 0.0;
+  int64_t timing_n = 0;
+};
+
+namespace {
+
+int fail(spec_ctx* c, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                        \
+  do {                                                                       \
+    hipError_t e_ = (expr);                                                  \
+    if (e_ != hipSuccess) {                                                  \
+      c->poisoned = true;                                                    \
+      return fail(c, SPEC_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+    }                                                                        \
+  } while (0)
+
+bool valid_config(const spec_config* cfg, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return false; };
+  if (!cfg) return bad("null config");
+  if (cfg->n_layers <= 0 || cfg->n_layers > SPEC_MAX_LAYERS) return bad("n_layers");
+  if (cfg->dtype != SPEC_DTYPE_FP32 && cfg->dtype != SPEC_DTYPE_BF16) return bad("dtype");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (cfg->n_kv_heads <= 0 || cfg->n_heads % cfg->n_kv_heads) return bad("heads");
+  if (cfg->d_model % 32 || cfg->ffn_dim % 32) return bad("d_model and ffn_dim must be multiples of 32");
+  if (cfg->vocab % 16 || cfg->vocab <= 0) return bad("vocab must be a multiple of 16");
+  if ((cfg->n_heads * cfg->head_dim) % 32) return bad("n_heads*head_dim");
+  if (cfg->page_size != 16) return bad("page_size must be 16");
+  if (cfg->max_requests <= 0 || cfg->max_ctx <= 0) return bad("capacity");
+  if (cfg->max_nodes < 1 || cfg->max_nodes > 65) return bad("max_nodes must be in [1, 65]");
+  if (cfg->max_rows < cfg->max_nodes) return bad("max_rows < max_nodes");
+  if (cfg->prefill_chunk < 1 || cfg->prefill_chunk > 1024) return bad("prefill_chunk");
+  if (cfg->max_ctx < cfg->max_nodes + 1) return bad("max_ctx");
+  bool any_lr = false;
+  for (int i = 0; i < cfg->n_layers; ++i) {
+    if (cfg->layer_kind[i] == SPEC_LAYER_LR) any_lr = true;
+    else if (cfg->layer_kind[i] != SPEC_LAYER_ATTN) return bad("layer_kind");
+  }
+  if (any_lr && cfg->lr_state != 16 && cfg->lr_state != 32 && cfg->lr_state != 64)
+    return bad("lr_state must be 16, 32 or 64");
+  return true;
+}
+
+// Lay out the workspace; with base == nullptr only the size is computed.
+size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
+  Plan p;
+  const size_t esz = cfg.dtype == SPEC_DTYPE_BF16 ? 2 : 4;
+  const int d = cfg.d_model, hd = cfg.head_dim, nq = cfg.n_heads, nkv = cfg.n_kv_heads;
+  const int F = cfg.ffn_dim, V = cfg.vocab, S = cfg.lr_state;
+  int n_attn = 0, n_lr = 0;
+  for (int i = 0; i < cfg.n_layers; ++i)
+    (cfg.layer_kind[i] == SPEC_LAYER_LR ? n_lr : n_attn)++;
+  const int qkv_n = (nq + 2 * nkv) * hd;
+  const int in_n = 3 * d + 2 * S;
+  auto at = [&](size_t off) -> char* { return base ? base + off : nullptr; };
+
+  // weights
+  std::vector<size_t> off_l1, off_l2, off_qkv, off_o, off_in, off_out, off_gu, off_d;
+  const size_t o_embed = p.take((size_t)V * d * esz);
+  for (int i = 0; i < cfg.n_layers; ++i) {
+    off_l1.push_back(p.take((size_t)d * 4));
+    if (cfg.layer_kind[i] == SPEC_LAYER_ATTN) {
+      off_qkv.push_back(p.take((size_t)qkv_n * d * esz));
+      off_o.push_back(p.take((size_t)d * nq * hd * esz));
+      off_in.push_back(0);
+      off_out.push_back(0);
+    } else {
+      off_qkv.push_back(0);
+      off_o.push_back(0);
+      off_in.push_back(p.take((size_t)in_n * d * esz));
+      off_out.push_back(p.take((size_t)d * d * esz));
+    }
+    off_l2.push_back(p.take((size_t)d * 4));
+    off_gu.push_back(p.take((size_t)2 * F * d * esz));
+    off_d.push_back(p.take((size_t)d * F * esz));
+  }
+  const size_t o_fnorm = p.take((size_t)d * 4);
+  const size_t o_lm = p.take((size_t)V * d * esz);
+
+  // KV pool: every request reserves max_ctx tokens
+  const int max_pages = (cfg.max_ctx + 15) / 16;
+  const int n_pages = max_pages * cfg.max_requests;
+  const size_t kv_layer_elems = (size_t)n_pages * nkv * 16 * hd;
+  const size_t o_k = p.take(kv_layer_elems * esz * std::max(n_attn, 1));
+  const size_t o_v = p.take(kv_layer_elems * esz * std::max(n_attn, 1));
+  const size_t o_btab = p.take((size_t)cfg.max_requests * max_pages * 4);
+  const size_t H_layer = (size_t)cfg.max_requests * d * std::max(S, 1);
+  const size_t o_H = p.take(H_layer * 4 * std::max(n_lr, 1));
+  const int max_pos = cfg.max_ctx + 1;
+  const size_t o_cos = p.take((size_t)max_pos * (hd / 2) * 4);
+  const size_t o_sin = p.take((size_t)max_pos * (hd / 2) * 4);
+
+  // scratch
+  const int R = std::max(cfg.max_rows, cfg.prefill_chunk);
+  const size_t scratch0 = p.cursor;
+  const size_t o_h = p.take((size_t)R * d * 4);
+  // activation buffers hold two planes (bf16: hi and lo; fp32: one used)
+  const size_t o_u = p.take((size_t)R * d * esz * 2);
+  const size_t o_act = p.take((size_t)R * F * esz * 2);
+  const size_t o_ao = p.take((size_t)R * nq * hd * esz * 2);
+  const size_t o_qkv = p.take((size_t)R * qkv_n * 4);
+  const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);
+  const size_t lr_rows = std::max((size_t)n_lr * cfg.max_rows, (size_t)cfg.prefill_chunk);
+  const size_t o_lrp = p.take(n_lr ? lr_rows * in_n * 4 : 0);
+  const size_t o_lro = p.take(n_lr ? (size_t)R * d * esz * 2 : 0);
+  const size_t o_po = p.take((size_t)kMaxSplits * R * nq * hd * 4);
+  const size_t o_pml = p.take((size_t)kMaxSplits * R * nq * 8);
+  const size_t o_amp = p.take((size_t)R * (V / 16) * 8);
+  const size_t o_amax = p.take((size_t)R * 4);
+  const size_t o_res = p.take((size_t)cfg.max_requests * (2 + 64) * 4);
+  size_t scratch_bytes = p.cursor - scratch0;
+  if (scratch_bytes < (size_t)kStagingBytes) p.take(kStagingBytes - scratch_bytes);
+
+  // metadata
+  const int anc_words = (cfg.max_nodes + 63) / 64;
+  const size_t rows_b = align_up((size_t)R * sizeof(RowMeta));
+  const size_t reqs_b = align_up((size_t)cfg.max_requests * sizeof(ReqMeta));
+  const size_t anc_b = align_up((size_t)R * anc_words * 8);
+  const size_t o_meta = p.take(rows_b + reqs_b + anc_b);
+  const size_t o_commit = p.take((size_t)cfg.max_requests * sizeof(CommitReq));
+
+  if (c && base) {
+    c->embed = at(o_embed);
+    c->final_norm = (float*)at(o_fnorm);
+    c->lm_head = at(o_lm);
+    int ia = 0, il = 0;
+    c->layers.resize(cfg.n_layers);
+    for (int i = 0; i < cfg.n_layers; ++i) {
+      Layer& L = c->layers[i];
+      L.kind = cfg.layer_kind[i];
+      L.idx = L.kind == SPEC_LAYER_ATTN ? ia++ : il++;
+      L.n1 = (float*)at(off_l1[i]);
+      L.n2 = (float*)at(off_l2[i]);
+      if (L.kind == SPEC_LAYER_ATTN) {
+        L.wqkv = at(off_qkv[i]);
+        L.wo = at(off_o[i]);
+      } else {
+        L.win = at(off_in[i]);
+        L.wout = at(off_out[i]);
+      }
+      L.wgu = at(off_gu[i]);
+      L.wd = at(off_d[i]);
+    }
+    c->kpool = at(o_k);
+    c->vpool = at(o_v);
+    c->kv_layer_elems = kv_layer_elems;
+    c->n_pages = n_pages;
+    c->max_pages = max_pages;
+    c->d_btab = (int32_t*)at(o_btab);
+    c->H = (float*)at(o_H);
+    c->H_layer = H_layer;
+    c->cos_t = (float*)at(o_cos);
+    c->sin_t = (float*)at(o_sin);
+    c->max_pos = max_pos;
+    c->Rmax = R;
+    c->h = (float*)at(o_h);
+    c->u = at(o_u);
+    c->u_lo = at(o_u + (size_t)R * d * esz);
+    c->act = at(o_act);
+    c->act_lo = at(o_act + (size_t)R * F * esz);
+    c->attn_o = at(o_ao);
+    c->attn_o_lo = at(o_ao + (size_t)R * nq * hd * esz);
+    c->qkv = (float*)at(o_qkv);
+    c->q = at(o_q);
+    c->q_lo = at(o_q + (size_t)R * nq * hd * esz);
+    c->lrproj = (float*)at(o_lrp);
+    c->lrproj_layer = (size_t)cfg.max_rows * in_n;
+    c->lr_o = at(o_lro);
+    c->lr_o_lo = n_lr ? at(o_lro + (size_t)R * d * esz) : nullptr;
+    c->part_o = (float*)at(o_po);
+    c->part_ml = (float2*)at(o_pml);
+    c->am_part = (float2*)at(o_amp);
+    c->amax = (int32_t*)at(o_amax);
+    c->res = (int32_t*)at(o_res);
+    c->staging = at(scratch0);
+    c->d_meta = at(o_meta);
+    c->meta_bytes = rows_b + reqs_b + anc_b;
+    c->off_reqs = rows_b;
+    c->off_anc = rows_b + reqs_b;
+    c->d_rows = (RowMeta*)c->d_meta;
+    c->d_reqs = (ReqMeta*)(c->d_meta + rows_b);
+    c->d_anc = (uint64_t*)(c->d_meta + rows_b + reqs_b);
+    c->d_commit = (CommitReq*)at(o_commit);
+  }
+  return p.total;
+}
+
+void build_slots(spec_ctx* c) {
+  const spec_config& cfg = c->cfg;
+  const int d = c->d, hd = c->hd;
+  c->slots.clear();
+  c->slots.push_back({0, -1, c->V, d, c->embed, 0, 1});
+  for (int i = 0; i < cfg.n_layers; ++i) {
+    Layer& L = c->layers[i];
+    c->slots.push_back({1, i, d, 1, L.n1, 0, 1});
+    if (L.kind == SPEC_LAYER_ATTN) {
+      c->slots.push_back({2, i, c->nq * hd, d, L.wqkv, 0, 1});
+      c->slots.push_back({2, i, c->nkv * hd, d, L.wqkv, c->nq * hd / 16, 1});
+      c->slots.push_back({2, i, c->nkv * hd, d, L.wqkv, (c->nq + c->nkv) * hd / 16, 1});
+      c->slots.push_back({2, i, d, c->nq * hd, L.wo, 0, 1});
+    } else {
+      c->slots.push_back({2, i, c->in_n, d, L.win, 0, 1});
+      c->slots.push_back({2, i, d, d, L.wout, 0, 1});
+    }
+    c->slots.push_back({1, i, d, 1, L.n2, 0, 1});
+    c->slots.push_back({2, i, c->F, d, L.wgu, 0, 2});   // gate -> even tiles
+    c->slots.push_back({2, i, c->F, d, L.wgu, 1, 2});   // up   -> odd tiles
+    c->slots.push_back({2, i, d, c->F, L.wd, 0, 1});
+  }
+  c->slots.push_back({1, -1, d, 1, c->final_norm, 0, 1});
+  c->slots.push_back({2, -1, c->V, d, c->lm_head, 0, 1});
+  c->loaded.assign(c->slots.size(), 0);
+}
+
+int check(spec_ctx* c) {
+  if (!c) return SPEC_E_INVAL;
+  if (c->poisoned) return fail(c, SPEC_E_HIP, "context poisoned by an earlier HIP error");
+  return SPEC_OK;
+}
+
+bool all_loaded(const spec_ctx* c) {
+  for (char x : c->loaded)
+    if (!x) return false;
+  return true;
+}
+
+// timing brackets
+void time_begin(spec_ctx* c, int cls) {
+  if (c->timing_cls != cls) return;
+  if (c->events_used == c->events.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+    c->events.push_back({a, b});
+  }
+  (void)hipEventRecord(c->events[c->events_used].first, c->stream);
+}
+
+void time_end(spec_ctx* c, int cls) {
+  if (c->timing_cls != cls || c->events_used >= c->events.size()) return;
+  (void)hipEventRecord(c->events[c->events_used].second, c->stream);
+  c->events_used++;
+}
+
+GemmArgs gemm_args(const void* W, const void* X, const void* X_lo, int M, int K,
+                   int N) {
+  GemmArgs a{};
+  a.W = W;
+  a.X = X;
+  a.X_lo = X_lo;
+  a.M = M;
+  a.K = K;
+  a.ntiles = N / 16;
+  a.bias_tok = -1;
+  return a;
+}
+
+// One forward pass over R rows already described in d_rows / d_reqs / d_anc.
+// lm_row0 / lm_rows: rows that go through the LM head (argmax into amax).
+// lr_commit_last: chain pass whose final recurrent states are committed.
+int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
+            const std::vector<int>& rows_per_req, bool any_tree, int lm_row0,
+            int lm_rows, float* d_logits, bool prefill) {
+  const spec_config& cfg = c->cfg;
+  const bool bf = c->bf16;
+  hipStream_t s = c->stream;
+  const int d = c->d, hd = c->hd, nq = c->nq, nkv = c->nkv, F = c->F;
+  const int G = nq / nkv;
+
+  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, s));
+
+  // attention split: enough workgroups for the chip, bounded partials
+  int keys_max = 0, qg_max = 0, max_rows_req = 0;
+  for (int r = 0; r < n_req; ++r) {
+    keys_max = std::max(keys_max, keys_per_req[r]);
+    const int qg = (rows_per_req[r] * G + 63) / 64;
+    qg_max = std::max(qg_max, qg);
+    max_rows_req = std::max(max_rows_req, rows_per_req[r]);
+  }
+  int split = 64;
+  while (split < 8192) {
+    const int ns = (keys_max + split - 1) / split;
+    long wgs = 0;
+    for (int r = 0; r < n_req; ++r)
+      wgs += (long)((rows_per_req[r] * G + 63) / 64) * nkv *
+             ((keys_per_req[r] + split - 1) / split);
+    if (ns <= kMaxSplits && (wgs <= 1024 || split >= 512)) break;
+    split *= 2;
+  }
+  AttnArgs aa{};
+  aa.q = c->q;
+  aa.q_lo = c->q_lo;
+  aa.btab = c->d_btab;
+  aa.max_pages = c->max_pages;
+  aa.rows = c->d_rows;
+  aa.reqs = c->d_reqs;
+  aa.anc = c->d_anc;
+  aa.part_o = c->part_o;
+  aa.part_ml = c->part_ml;
+  aa.nq = nq;
+  aa.nkv = nkv;
+  aa.hd = hd;
+  aa.split = split;
+  aa.max_splits = (keys_max + split - 1) / split;
+  aa.max_qgroups = qg_max;
+  aa.n_req = n_req;
+  aa.rows_total = R;
+  aa.scale = 1.0f / std::sqrt((float)hd);
+  if (aa.max_splits > kMaxSplits)
+    return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
+
+  for (int li = 0; li < cfg.n_layers; ++li) {
+    const Layer& L = c->layers[li];
+    HIP_TRY(launch_rmsnorm(bf, c->h, L.n1, R, d, cfg.rms_eps, c->u, c->u_lo, s));
+    if (L.kind == SPEC_LAYER_ATTN) {
+      GemmArgs g = gemm_args(L.wqkv, c->u, c->u_lo, R, d, c->qkv_n);
+      g.Y = c->qkv;
+      g.ldy = c->qkv_n;
+      HIP_TRY(launch_gemm(bf, EPI_STORE, g, 1, s));
+      char* kc = c->kpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
+      char* vc = c->vpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
+      HIP_TRY(launch_rope_kv(bf, c->qkv, c->d_rows, R, nq, nkv, hd, c->cos_t,
+                             c->sin_t, c->q, c->q_lo, kc, vc, s));
+      aa.kc = kc;
+      aa.vc = vc;
+      time_begin(c, 4);
+      HIP_TRY(launch_attention(bf, aa, s));
+      time_end(c, 4);
+      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, c->attn_o_lo, s));
+      GemmArgs o = gemm_args(L.wo, c->attn_o, c->attn_o_lo, R, nq * hd, d);
+      o.Y = c->h;
+      o.ldy = d;
+      HIP_TRY(launch_gemm(bf, EPI_RESID, o, 1, s));
+    } else {
+      float* proj = c->lrproj + (prefill ? 0 : (size_t)L.idx * c->lrproj_layer);
+      GemmArgs g = gemm_args(L.win, c->u, c->u_lo, R, d, c->in_n);
+      g.Y = proj;
+      g.ldy = c->in_n;
+      HIP_TRY(launch_gemm(bf, EPI_STORE, g, 1, s));
+      float* H = c->H + (size_t)L.idx * c->H_layer;
+      HIP_TRY(launch_lr_fork(bf, proj, c->d_rows, c->d_reqs, n_req, d, c->S, H,
+                             c->lr_o, c->lr_o_lo, any_tree, prefill, max_rows_req, s));
+      GemmArgs o = gemm_args(L.wout, c->lr_o, c->lr_o_lo, R, d, d);
+      o.Y = c->h;
+      o.ldy = d;
+      HIP_TRY(launch_gemm(bf, EPI_RESID, o, 1, s));
+    }
+    HIP_TRY(launch_rmsnorm(bf, c->h, L.n2, R, d, cfg.rms_eps, c->u, c->u_lo, s));
+    GemmArgs gu = gemm_args(L.wgu, c->u, c->u_lo, R, d, 2 * F);
+    gu.act = c->act;
+    gu.act_lo = c->act_lo;
+    gu.ldact = F;
+    time_begin(c, 1);
+    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, 2, s));
+    time_end(c, 1);
+    GemmArgs dn = gemm_args(L.wd, c->act, c->act_lo, R, F, d);
+    dn.Y = c->h;
+    dn.ldy = d;
+    time_begin(c, 2);
+    HIP_TRY(launch_gemm(bf, EPI_RESID, dn, 1, s));
+    time_end(c, 2);
+  }
+
+  // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
+  if (lm_rows == 0) return SPEC_OK;
+  HIP_TRY(launch_rmsnorm(bf, c->h + (size_t)lm_row0 * d, c->final_norm, lm_rows,
+                         d, cfg.rms_eps, c->u, c->u_lo, s));
+  GemmArgs lm = gemm_args(c->lm_head, c->u, c->u_lo, lm_rows, d, c->V);
+  lm.part = c->am_part;
+  lm.nblocks = c->V / 16;
+  lm.logits = d_logits;
+  lm.ldlog = c->V;
+  lm.rows = c->d_rows + lm_row0;
+  lm.bias_tok = c->fault_tok;
+  lm.bias = c->fault_bias;
+  lm.bias_after = c->fault_after;
+  time_begin(c, 3);
+  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, 1, s));
+  time_end(c, 3);
+  HIP_TRY(launch_argmax_reduce(c->am_part, lm_rows, c->V / 16, c->amax, s));
+  return SPEC_OK;
+}
+
+RowMeta* h_rows(spec_ctx* c) { return (RowMeta*)c->h_meta; }
+ReqMeta* h_reqs(spec_ctx* c) { return (ReqMeta*)(c->h_meta + c->off_reqs); }
+uint64_t* h_anc(spec_ctx* c) { return (uint64_t*)(c->h_meta + c->off_anc); }
+
+int slot_of(const spec_ctx* c, const Req& rq, int t) {
+  return rq.pages[t >> 4] * 16 + (t & 15);
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" size_t spec_workspace_bytes(const spec_config* cfg) {
+  if (!valid_config(cfg, nullptr)) return 0;
+  return plan_workspace(nullptr, *cfg, nullptr);
+}
+
+extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
+                               size_t bytes, void* hip_stream, spec_ctx** out) {
+  if (!out) return SPEC_E_INVAL;
+  *out = nullptr;
+  std::string why;
+  if (!valid_config(cfg, &why)) return SPEC_E_INVAL;
+  const size_t need = plan_workspace(nullptr, *cfg, nullptr);
+  if (!d_workspace || bytes < need || ((uintptr_t)d_workspace % kAlign))
+    return SPEC_E_INVAL;
+  spec_ctx* c = new spec_ctx();
+  c->cfg = *cfg;
+  c->bf16 = cfg->dtype == SPEC_DTYPE_BF16;
+  c->esz = c->bf16 ? 2 : 4;
+  c->stream = (hipStream_t)hip_stream;
+  c->ws = (char*)d_workspace;
+  c->d = cfg->d_model;
+  c->nq = cfg->n_heads;
+  c->nkv = cfg->n_kv_heads;
+  c->hd = cfg->head_dim;
+  c->F = cfg->ffn_dim;
+  c->V = cfg->vocab;
+  c->S = cfg->lr_state;
+  for (int i = 0; i < cfg->n_layers; ++i)
+    (cfg->layer_kind[i] == SPEC_LAYER_LR ? c->n_lr : c->n_attn)++;
+  c->qkv_n = (c->nq + 2 * c->nkv) * c->hd;
+  c->in_n = 3 * c->d + 2 * c->S;
+  (void)hipGetDevice(&c->device);
+  plan_workspace(c, *cfg, c->ws);
+  build_slots(c);
+  c->reqs.resize(cfg->max_requests);
+  for (int p = c->n_pages - 1; p >= 0; --p) c->free_pages.push_back(p);
+
+  auto cleanup = [&](int code) {
+    spec_destroy(c);
+    return code;
+  };
+  if (hipHostMalloc((void**)&c->h_meta, c->meta_bytes, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_commit, sizeof(CommitReq) * cfg->max_requests,
+                    hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_res, sizeof(int32_t) * cfg->max_requests * 66,
+                    hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c->h_btab_row, sizeof(int32_t) * c->max_pages,
+                    hipHostMallocDefault) != hipSuccess)
+    return cleanup(SPEC_E_HIP);
+  memset(c->h_meta, 0, c->meta_bytes);
+
+  // RoPE tables: angle = p * theta^(-2i/hd) in double, rounded once to float
+  const int half = c->hd / 2;
+  std::vector<float> ct((size_t)c->max_pos * half), st((size_t)c->max_pos * half);
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow((double)cfg->rope_theta, -2.0 * i / c->hd);
+    for (int p = 0; p < c->max_pos; ++p) {
+      ct[(size_t)p * half + i] = (float)std::cos((double)p * inv);
+      st[(size_t)p * half + i] = (float)std::sin((double)p * inv);
+    }
+  }
+  if (hipMemcpy(c->cos_t, ct.data(), ct.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->sin_t, st.data(), st.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemsetAsync(c->d_btab, 0, (size_t)cfg->max_requests * c->max_pages * 4,
+                     c->stream) != hipSuccess ||
+      (c->n_lr && hipMemsetAsync(c->H, 0, c->H_layer * 4 * c->n_lr, c->stream) != hipSuccess) ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return cleanup(SPEC_E_HIP);
+  *out = c;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
+                                     const void* src, size_t bytes,
+                                     int32_t src_on_device) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (tensor_id < 0 || tensor_id >= (int)c->slots.size() || !src)
+    return fail(c, SPEC_E_INVAL, "bad tensor id %d", tensor_id);
+  const TensorSlot& t = c->slots[tensor_id];
+  const size_t want = (size_t)t.rows * t.cols * c->esz;
+  if (bytes != want)
+    return fail(c, SPEC_E_INVAL, "tensor %d: %zu bytes given, %zu expected", tensor_id,
+                bytes, want);
+  hipStream_t s = c->stream;
+  const hipMemcpyKind kind = src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  if (t.kind == 0) {  // embedding, row-major as given
+    HIP_TRY(hipMemcpyAsync(t.dst, src, bytes, kind, s));
+  } else if (t.kind == 1) {  // norm vector -> fp32
+    const void* from = src;
+    if (!src_on_device) {
+      HIP_TRY(hipMemcpyAsync(c->staging, src, bytes, kind, s));
+      from = c->staging;
+    }
+    HIP_TRY(launch_to_f32(c->bf16, from, t.rows, (float*)t.dst, s));
+  } else {  // matrix -> tiles
+    if (t.rows % 16 || t.cols % 32)
+      return fail(c, SPEC_E_UNSUPPORTED, "tensor %d shape %dx%d not tileable", tensor_id,
+                  t.rows, t.cols);
+    const size_t row_bytes = (size_t)t.cols * c->esz;
+    int slab = src_on_device ? t.rows : (int)((size_t)kStagingBytes / row_bytes) / 16 * 16;
+    if (slab <= 0)
+      return fail(c, SPEC_E_UNSUPPORTED, "tensor %d rows too long for staging", tensor_id);
+    for (int r0 = 0; r0 < t.rows; r0 += slab) {
+      const int nr = std::min(slab, t.rows - r0);
+      const char* from = (const char*)src + (size_t)r0 * row_bytes;
+      if (!src_on_device) {
+        HIP_TRY(hipMemcpyAsync(c->staging, from, (size_t)nr * row_bytes, kind, s));
+        from = (const char*)c->staging;
+      }
+      HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst,
+                              t.tile0 + (r0 / 16) * t.tile_stride, t.tile_stride, s));
+      if (!src_on_device) HIP_TRY(hipStreamSynchronize(s));
+    }
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  c->loaded[tensor_id] = 1;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
+                                int32_t n, int32_t* first_token, float* d_logits_opt) {
+  int rc = check(c);
+  if (rc) return rc;
+  const spec_config& cfg = c->cfg;
+  if (!all_loaded(c)) return fail(c, SPEC_E_STATE, "weights not loaded");
+  if (req < 0 || req >= cfg.max_requests) return fail(c, SPEC_E_INVAL, "bad request id");
+  if (c->reqs[req].active) return fail(c, SPEC_E_STATE, "request %d is active", req);
+  if (!prompt || n < 1 || !first_token) return fail(c, SPEC_E_INVAL, "bad prompt");
+  if (n + cfg.max_nodes > cfg.max_ctx)
+    return fail(c, SPEC_E_CAPACITY, "prompt of %d tokens exceeds max_ctx", n);
+  for (int i = 0; i < n; ++i)
+    if (prompt[i] < 0 || prompt[i] >= c->V) return fail(c, SPEC_E_INVAL, "token out of range");
+  if ((int)c->free_pages.size() < c->max_pages)
+    return fail(c, SPEC_E_CAPACITY, "KV pages exhausted");
+
+  Req& rq = c->reqs[req];
+  rq.pages.assign(c->free_pages.end() - c->max_pages, c->free_pages.end());
+  std::reverse(rq.pages.begin(), rq.pages.end());
+  c->free_pages.resize(c->free_pages.size() - c->max_pages);
+  auto undo = [&](int code) {
+    for (int p : rq.pages) c->free_pages.push_back(p);
+    rq.pages.clear();
+    return code;
+  };
+  for (int i = 0; i < c->max_pages; ++i) c->h_btab_row[i] = rq.pages[i];
+  if (hipMemcpyAsync(c->d_btab + (size_t)req * c->max_pages, c->h_btab_row,
+                     (size_t)c->max_pages * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess)
+    return undo(fail(c, SPEC_E_HIP, "block table upload failed"));
+  // zero recurrent states of this request
+  for (int l = 0; l < c->n_lr; ++l)
+    if (hipMemsetAsync(c->H + l * c->H_layer + (size_t)req * c->d * c->S, 0,
+                       (size_t)c->d * c->S * 4, c->stream) != hipSuccess)
+      return undo(fail(c, SPEC_E_HIP, "state reset failed"));
+
+  int done = 0;
+  while (done < n) {
+    const int C = std::min(cfg.prefill_chunk, n - done);
+    // the previous upload from the pinned metadata buffer must have run
+    // before the buffer is rewritten
+    if (hipStreamSynchronize(c->stream) != hipSuccess) {
+      c->poisoned = true;
+      return undo(fail(c, SPEC_E_HIP, "stream synchronize failed"));
+    }
+    RowMeta* rows = h_rows(c);
+    for (int i = 0; i < C; ++i) {
+      RowMeta& r = rows[i];
+      r.token = prompt[done + i];
+      r.pos = done + i;
+      r.slot = slot_of(c, rq, done + i);
+      r.req = 0;
+      r.node = i;
+      r.parent = i - 1;
+    }
+    ReqMeta& m = h_reqs(c)[0];
+    m = ReqMeta{0, C, done, req, 0, 1, 1, 0};
+    if (hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
+                       c->stream) != hipSuccess) {
+      c->poisoned = true;
+      return undo(fail(c, SPEC_E_HIP, "metadata upload failed"));
+    }
+    const bool last = done + C == n;
+    rc = forward(c, C, 1, {done + C}, {C}, false, C - 1, last ? 1 : 0,
+                 last ? d_logits_opt : nullptr, true);
+    if (rc) return undo(rc);
+    done += C;
+  }
+  if (hipMemcpyAsync(c->h_res, c->amax, 4, hipMemcpyDeviceToHost, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess) {
+    c->poisoned = true;
+    return undo(fail(c, SPEC_E_HIP, "prefill result copy failed"));
+  }
+  rq.active = true;
+  rq.n = n;
+  rq.root = c->h_res[0];
+  *first_token = rq.root;
+  c->last.valid = false;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
+                               const int32_t* n_nodes, const int32_t* draft_tokens,
+                               const int32_t* parent_idx, int32_t* path,
+                               int32_t* path_len, int32_t* bonus, float* d_logits_opt) {
+  int rc = check(c);
+  if (rc) return rc;
+  const spec_config& cfg = c->cfg;
+  if (n_req < 1 || n_req > cfg.max_requests || !req || !n_nodes || !path || !path_len ||
+      !bonus)
+    return fail(c, SPEC_E_INVAL, "bad arguments");
+  std::vector<char> seen(cfg.max_requests, 0);
+  int R = 0, total_drafts = 0;
+  for (int r = 0; r < n_req; ++r) {
+    if (req[r] < 0 || req[r] >= cfg.max_requests) return fail(c, SPEC_E_INVAL, "bad request id");
+    if (seen[req[r]]) return fail(c, SPEC_E_INVAL, "request %d repeated", req[r]);
+    seen[req[r]] = 1;
+    if (!c->reqs[req[r]].active) return fail(c, SPEC_E_STATE, "request %d not active", req[r]);
+    if (n_nodes[r] < 0 || n_nodes[r] + 1 > cfg.max_nodes)
+      return fail(c, SPEC_E_INVAL, "request %d: %d drafts exceed max_nodes", req[r], n_nodes[r]);
+    if (c->reqs[req[r]].n + n_nodes[r] + 1 > cfg.max_ctx)
+      return fail(c, SPEC_E_CAPACITY, "request %d: context full", req[r]);
+    R += n_nodes[r] + 1;
+    total_drafts += n_nodes[r];
+  }
+  if (R > cfg.max_rows) return fail(c, SPEC_E_INVAL, "%d rows exceed max_rows", R);
+  if (total_drafts && (!draft_tokens || !parent_idx))
+    return fail(c, SPEC_E_INVAL, "missing drafts");
+  for (int i = 0, off = 0; i < n_req; off += n_nodes[i], ++i)
+    for (int j = 0; j < n_nodes[i]; ++j) {
+      const int p = parent_idx[off + j], t = draft_tokens[off + j];
+      if (p < -1 || p >= j) return fail(c, SPEC_E_INVAL, "parent_idx out of range");
+      if (t < 0 || t >= c->V) return fail(c, SPEC_E_INVAL, "draft token out of range");
+    }
+
+  const int words = (cfg.max_nodes + 63) / 64;
+  RowMeta* rows = h_rows(c);
+  ReqMeta* rm = h_reqs(c);
+  uint64_t* anc = h_anc(c);
+  LastVerify lv;
+  lv.valid = true;
+  std::vector<int> keys(n_req), nrows(n_req);
+  bool any_tree = false;
+  int row = 0, off = 0;
+  for (int r = 0; r < n_req; ++r) {
+    const Req& rq = c->reqs[req[r]];
+    const int K = n_nodes[r];
+    std::vector<int> par(K + 1), dep(K + 1);
+    bool chain = true;
+    for (int i = 0; i <= K; ++i) {
+      const int p = i == 0 ? -1 : parent_idx[off + i - 1] + 1;
+      par[i] = p;
+      dep[i] = p < 0 ? 0 : dep[p] + 1;
+      if (p != i - 1) chain = false;
+      RowMeta& m = rows[row + i];
+      m.token = i == 0 ? rq.root : draft_tokens[off + i - 1];
+      m.pos = rq.n + dep[i];
+      m.slot = slot_of(c, rq, rq.n + i);
+      m.req = r;
+      m.node = i;
+      m.parent = p;
+      uint64_t* a = anc + (size_t)(row + i) * words;
+      for (int w = 0; w < words; ++w) a[w] = p < 0 ? 0 : anc[(size_t)(row + p) * words + w];
+      a[i >> 6] |= 1ull << (i & 63);
+    }
+    if (!chain) any_tree = true;
+    rm[r] = ReqMeta{row, K + 1, rq.n, req[r], row * words, words, chain ? 1 : 0, 0};
+    keys[r] = rq.n + K + 1;
+    nrows[r] = K + 1;
+    lv.req.push_back(req[r]);
+    lv.row0.push_back(row);
+    lv.nrows.push_back(K + 1);
+    lv.nctx.push_back(rq.n);
+    lv.parent.push_back(par);
+    row += K + 1;
+    off += K;
+  }
+  HIP_TRY(hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
+                         c->stream));
+  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false);
+  if (rc) return rc;
+  const int max_path = 64;
+  HIP_TRY(launch_path_walk(c->d_rows, c->d_reqs, n_req, c->amax, max_path, c->res,
+                           c->stream));
+  HIP_TRY(hipMemcpyAsync(c->h_res, c->res, (size_t)n_req * (2 + max_path) * 4,
+                         hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  const int slots = cfg.max_nodes - 1;
+  for (int r = 0; r < n_req; ++r) {
+    const int32_t* o = c->h_res + (size_t)r * (2 + max_path);
+    path_len[r] = o[0];
+    bonus[r] = o[1];
+    for (int k = 0; k < o[0] && k < slots; ++k) path[(size_t)r * slots + k] = o[2 + k] - 1;
+  }
+  c->last = lv;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_commit(spec_ctx* c, int32_t n_req, const int32_t* req,
+                               const int32_t* path, const int32_t* path_len,
+                               const int32_t* next_root) {
+  int rc = check(c);
+  if (rc) return rc;
+  const spec_config& cfg = c->cfg;
+  if (!c->last.valid) return fail(c, SPEC_E_STATE, "commit without a matching verify");
+  if (n_req != (int)c->last.req.size() || !req || !path_len || !next_root ||
+      (!path && n_req > 0))
+    return fail(c, SPEC_E_STATE, "commit does not match the last verify");
+  const int slots = cfg.max_nodes - 1;
+  bool need_compact = false;
+  for (int r = 0; r < n_req; ++r) {
+    if (req[r] != c->last.req[r]) return fail(c, SPEC_E_STATE, "request order differs");
+    const std::vector<int>& par = c->last.parent[r];
+    const int K = (int)par.size() - 1;
+    if (path_len[r] < 0 || path_len[r] > K) return fail(c, SPEC_E_STATE, "bad path length");
+    if (next_root[r] < 0 || next_root[r] >= c->V) return fail(c, SPEC_E_INVAL, "bad next root");
+    int prev = 0;
+    for (int k = 0; k < path_len[r]; ++k) {
+      const int node = path[(size_t)r * slots + k] + 1;
+      if (node < 1 || node > K || par[node] != prev)
+        return fail(c, SPEC_E_STATE, "request %d: path is not a root path", req[r]);
+      if (node != k + 1) need_compact = true;
+      prev = node;
+    }
+  }
+  for (int r = 0; r < n_req; ++r) {
+    CommitReq& q = c->h_commit[r];
+    q.table = req[r];
+    q.nctx = c->last.nctx[r];
+    q.row0 = c->last.row0[r];
+    q.plen = path_len[r];
+    for (int k = 0; k < path_len[r]; ++k) q.nodes[k] = path[(size_t)r * slots + k] + 1;
+  }
+  if (need_compact || c->n_lr) {
+    HIP_TRY(hipMemcpyAsync(c->d_commit, c->h_commit, sizeof(CommitReq) * n_req,
+                           hipMemcpyHostToDevice, c->stream));
+    if (need_compact && c->n_attn)
+      HIP_TRY(launch_kv_compact(c->bf16, c->d_commit, n_req, c->d_btab, c->max_pages,
+                                c->kpool, c->vpool, c->kv_layer_elems, c->n_attn,
+                                c->nkv, c->hd, c->stream));
+    if (c->n_lr)
+      HIP_TRY(launch_lr_commit(c->d_commit, n_req, c->lrproj, c->lrproj_layer,
+                               c->in_n, c->n_lr, c->d, c->S, c->H, c->H_layer,
+                               c->stream));
+  }
+  for (int r = 0; r < n_req; ++r) {
+    Req& rq = c->reqs[req[r]];
+    rq.n += path_len[r] + 1;
+    rq.root = next_root[r];
+  }
+  c->last.valid = false;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_release(spec_ctx* c, int32_t req) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (req < 0 || req >= c->cfg.max_requests) return fail(c, SPEC_E_INVAL, "bad request id");
+  Req& rq = c->reqs[req];
+  if (!rq.active) return fail(c, SPEC_E_STATE, "request %d not active", req);
+  for (int p : rq.pages) c->free_pages.push_back(p);
+  rq = Req();
+  c->last.valid = false;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_request_state(const spec_ctx* c, int32_t req, int32_t* n_ctx,
+                                      int32_t* pending_root) {
+  if (!c || req < 0 || req >= c->cfg.max_requests || !c->reqs[req].active)
+    return SPEC_E_INVAL;
+  if (n_ctx) *n_ctx = c->reqs[req].n;
+  if (pending_root) *pending_root = c->reqs[req].root;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_force_root(spec_ctx* c, int32_t req, int32_t token) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (req < 0 || req >= c->cfg.max_requests || !c->reqs[req].active)
+    return fail(c, SPEC_E_INVAL, "request %d not active", req);
+  if (token < 0 || token >= c->V) return fail(c, SPEC_E_INVAL, "token out of range");
+  c->reqs[req].root = token;
+  c->last.valid = false;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_set_fault(spec_ctx* c, int32_t token, float bias,
+                                  int32_t after_position) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (token >= c->V) return fail(c, SPEC_E_INVAL, "fault token out of range");
+  c->fault_tok = token < 0 ? -1 : token;
+  c->fault_bias = bias;
+  c->fault_after = after_position;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_timing_enable(spec_ctx* c, int32_t cls) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (cls < 0 || cls > 4) return fail(c, SPEC_E_INVAL, "bad timing class");
+  c->timing_cls = cls;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_timing_read(spec_ctx* c, double* total_ms, int64_t* launches) {
+  int rc = check(c);
+  if (rc) return rc;
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  double ms = 0.0;
+  for (size_t i = 0; i < c->events_used; ++i) {
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, c->events[i].first, c->events[i].second));
+    ms += t;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = (int64_t)c->events_used;
+  c->events_used = 0;
+  return SPEC_OK;
+}
+
+extern "C" void spec_destroy(spec_ctx* c) {
+  if (!c) return;
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  for (auto& e : c->events) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  if (c->h_meta) (void)hipHostFree(c->h_meta);
+  if (c->h_commit) (void)hipHostFree(c->h_commit);
+  if (c->h_res) (void)hipHostFree(c->h_res);
+  if (c->h_btab_row) (void)hipHostFree(c->h_btab_row);
+  delete c;
+}
+
+extern "C" const char* spec_last_error(const spec_ctx* c) {
+  if (!c) return "null context";
+  return c->err.c_str();
+}

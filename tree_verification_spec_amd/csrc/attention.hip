@@ -22,12 +22,14 @@
 
 namespace {
 
+constexpr int kMaxSplitKeys = 128;  // keys of one split staged in LDS at once
+
 template <typename T, int HD>
 struct alignas(16) AttnSmem {
   static constexpr int KPAD = 16 / sizeof(T) * 1;  // one 16-byte pad per row
   static constexpr int VPAD = 8 / sizeof(T) * 2;
-  T k[32][HD + KPAD];
-  T v[HD][32 + VPAD];
+  T k[kMaxSplitKeys][HD + KPAD];
+  T v[HD][kMaxSplitKeys + VPAD];
 };
 
 template <typename T>
@@ -121,46 +123,64 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < HD / 16; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int EPC = 16 / sizeof(T);        // elements per 16-byte chunk
-  constexpr int KCH = 32 * HD / EPC;         // chunks in a K block
-  constexpr int VCH_ROW = 16 / EPC;          // chunks per (dim, half page)
-  constexpr int VCH = HD * 2 * VCH_ROW;      // chunks in a V block
+  constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
+  constexpr int KCH_ROW = HD / EPC;              // chunks per K row
+  constexpr int VCH_ROW = 16 / EPC;              // chunks per (dim, 16 keys)
+  // ---- stage the whole split (K rows and V^T) with every load in flight
+  {
+    const int nkeys = kend - kbeg;                 // <= kMaxSplitKeys
+    const int kch = ((nkeys + 31) & ~31) * KCH_ROW;
+    const int vch = HD * (((nkeys + 31) & ~31) / 16) * VCH_ROW;
+    constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / 256;  // per thread, each of K and V
+    uint4 kr[MAXCH], vr[MAXCH];
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+      const int c = threadIdx.x + j * 256;
+      kr[j] = make_uint4(0, 0, 0, 0);
+      if (c < kch) {
+        const int i = c / KCH_ROW, part = c % KCH_ROW;
+        const int t = kbeg + i;
+        if (t < kend) {
+          const int page = bt[t >> 4];
+          kr[j] = *reinterpret_cast<const uint4*>(
+              kc + (((size_t)page * a.nkv + kvh) * 16 + (t & 15)) * HD + part * EPC);
+        }
+      }
+      vr[j] = make_uint4(0, 0, 0, 0);
+      if (c < vch) {
+        const int dim = c / ((vch / HD)), rest = c % (vch / HD);
+        const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
+        const int t0 = kbeg + blk * 16 + part * EPC;
+        if (t0 < kend) {
+          const int page = bt[t0 >> 4];
+          vr[j] = *reinterpret_cast<const uint4*>(
+              vc + (((size_t)page * a.nkv + kvh) * HD + dim) * 16 + (t0 & 15));
+          T* ve = reinterpret_cast<T*>(&vr[j]);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)  // keys past the end are not written this pass
+            if (t0 + e >= kend) ve[e] = T(0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+      const int c = threadIdx.x + j * 256;
+      if (c < kch) {
+        const int i = c / KCH_ROW, part = c % KCH_ROW;
+        *reinterpret_cast<uint4*>(&sm.k[i][part * EPC]) = kr[j];
+      }
+      if (c < vch) {
+        const int dim = c / ((vch / HD)), rest = c % (vch / HD);
+        const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
+        *reinterpret_cast<uint4*>(&sm.v[dim][blk * 16 + part * EPC]) = vr[j];
+      }
+    }
+    __syncthreads();
+  }
 
   for (int kb = kbeg; kb < kend; kb += 32) {
-    __syncthreads();
-    // ---- stage K rows [kb, kb + 32) and V^T into LDS
-    for (int c = threadIdx.x; c < KCH; c += 256) {
-      const int i = c / (HD / EPC), part = c % (HD / EPC);
-      const int t = kb + i;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (t < kend) {
-        const int page = bt[t >> 4];
-        val = *reinterpret_cast<const uint4*>(
-            kc + (((size_t)page * a.nkv + kvh) * 16 + (t & 15)) * HD + part * EPC);
-      }
-      *reinterpret_cast<uint4*>(&sm.k[i][part * EPC]) = val;
-    }
-    for (int c = threadIdx.x; c < VCH; c += 256) {
-      const int dim = c / (2 * VCH_ROW);
-      const int half = (c / VCH_ROW) & 1;
-      const int part = c % VCH_ROW;
-      const int t0 = kb + half * 16 + part * EPC;  // first key of the chunk
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (t0 < kend) {
-        const int page = bt[t0 >> 4];
-        val = *reinterpret_cast<const uint4*>(
-            vc + (((size_t)page * a.nkv + kvh) * HD + dim) * 16 + (t0 & 15));
-        // zero keys past the end (their memory is not written this pass)
-        T* ve = reinterpret_cast<T*>(&val);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          if (t0 + e >= kend) ve[e] = T(0);
-      }
-      *reinterpret_cast<uint4*>(&sm.v[dim][half * 16 + part * EPC]) = val;
-    }
-    __syncthreads();
-    if (!wave_active) continue;
-
+    if (!wave_active) break;
+    const int kl = kb - kbeg;  // key offset inside the staged split
     // ---- scores: S^T tiles for keys [kb, kb+16) and [kb+16, kb+32)
     floatx4_t s[2];
 #pragma unroll
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < HD / 32; ++ks) {
         Frag<T> kf;
-        kf.load(&sm.k[kt * 16 + r16][ks * 32 + g * 8]);
+        kf.load(&sm.k[kl + kt * 16 + r16][ks * 32 + g * 8]);
         mma32(s[kt], kf, qf[ks]);
         if (kSplit) mma32(s[kt], kf, qfl[ks]);
       }
@@ -227,7 +247,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) {
       Frag<T> vf;
-      load_vfrag<T>(vf, &sm.v[dt * 16 + r16][4 * g], &sm.v[dt * 16 + r16][16 + 4 * g]);
+      load_vfrag<T>(vf, &sm.v[dt * 16 + r16][kl + 4 * g], &sm.v[dt * 16 + r16][kl + 16 + 4 * g]);
       mma32(o[dt], vf, pf);
       if (kSplitP) mma32(o[dt], vf, pf_lo);
     }
@@ -245,43 +265,53 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }
 
 // One wave per (row, query head): merge the splits of the row's request.
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out,
-                                                           T* out_lo) {
+// Lane s reads split s's (max, sum); the wave forms the weights, then every
+// lane accumulates its dims over the splits in split order.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, float* out) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= a.rows_total * a.nq) return;
   const int grow = wid / a.nq, qhead = wid % a.nq;
   const ReqMeta rm = a.reqs[a.rows[grow].req];
-  const int nsplit = (rm.nctx + rm.nrows + a.split - 1) / a.split;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s)
-    M = fmaxf(M, a.part_ml[(size_t)s * a.rows_total * a.nq + wid].x);
-  float L = 0.f;
-  float acc[HD / 64 > 0 ? HD / 64 : 1] = {};
-  constexpr int PER = HD / 64 > 0 ? HD / 64 : 1;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t slot = (size_t)s * a.rows_total * a.nq + wid;
-    const float2 ml = a.part_ml[slot];
-    if (ml.x == -INFINITY) continue;
-    const float w = expf(ml.x - M);
-    L += ml.y * w;
+  const int nsplit = (rm.nctx + rm.nrows + a.split - 1) / a.split;  // <= 64
+  const size_t sstride = (size_t)a.rows_total * a.nq;
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (lane < nsplit) ml = a.part_ml[(size_t)lane * sstride + wid];
+  const float M = wave_max(ml.x);
+  const float wgt = (ml.x == -INFINITY) ? 0.f : expf(ml.x - M);
+  const float L = wave_sum(ml.y * wgt);
+  constexpr int PER = HD / 64;
+  float acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int dim = lane + 64 * j;
-      if (dim < HD) acc[j] += a.part_o[slot * HD + dim] * w;
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  const float* po = a.part_o + (size_t)wid * HD + lane * PER;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float v[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = s0 + u < nsplit ? s0 + u : nsplit - 1;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = po[(size_t)sp * sstride * HD + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = __shfl(wgt, s0 + u, 64);
+      if (s0 + u < nsplit) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += v[u][j] * wu;
+      }
     }
   }
   const float inv = 1.0f / L;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int dim = lane + 64 * j;
-    if (dim < HD) store_act(out, out_lo, ((size_t)grow * a.nq + qhead) * HD + dim, acc[j] * inv);
-  }
+  for (int j = 0; j < PER; ++j)
+    out[((size_t)grow * a.nq + qhead) * HD + lane * PER + j] = acc[j] * inv;
 }
 
 template <typename T>
 hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
+  if (a.split > kMaxSplitKeys || a.split % 32) return hipErrorInvalidValue;
   dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
   if (a.hd == 128) attn_kernel<T, 128><<<grid, 256, 0, s>>>(a);
   else if (a.hd == 64) attn_kernel<T, 64><<<grid, 256, 0, s>>>(a);
@@ -289,12 +319,12 @@ hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t combine_typed(const AttnArgs& a, void* o, void* o_lo, hipStream_t s) {
+hipError_t combine_any(const AttnArgs& a, float* o, hipStream_t s) {
+  if (a.max_splits > 64) return hipErrorInvalidValue;
   const int waves = a.rows_total * a.nq;
   dim3 grid((waves + 3) / 4);
-  if (a.hd == 128) attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a, (T*)o, (T*)o_lo);
-  else if (a.hd == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a, (T*)o, (T*)o_lo);
+  if (a.hd == 128) attn_combine_kernel<128><<<grid, 256, 0, s>>>(a, o);
+  else if (a.hd == 64) attn_combine_kernel<64><<<grid, 256, 0, s>>>(a, o);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -305,8 +335,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s) {
   return bf16 ? attn_typed<uint16_t>(a, s) : attn_typed<float>(a, s);
 }
 
-hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o,
-                               void* o_lo, hipStream_t s) {
-  return bf16 ? combine_typed<uint16_t>(a, o, o_lo, s)
-              : combine_typed<float>(a, o, o_lo, s);
+hipError_t launch_attn_combine(bool /*bf16*/, const AttnArgs& a, float* o,
+                               hipStream_t s) {
+  return combine_any(a, o, s);
 }

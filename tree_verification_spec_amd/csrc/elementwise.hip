@@ -1,5 +1,4 @@
-// Small kernels of the verify pass: embedding gather, RMSNorm, RoPE + KV
-// store, argmax reduction, accepted-path walk, the per-branch recurrence of
+// Small kernels of the verify pass: embedding gather, RoPE + KV store, argmax reduction, accepted-path walk, the per-branch recurrence of
 // the hybrid layers, the commit kernels and the one-time weight re-layout.
 #include "common.h"
 #include "kernels.h"
@@ -7,49 +6,53 @@
 namespace {
 
 // ---------------------------------------------------------------- embedding
+// One workgroup per row: h = float(E[token]) and the row's sum of squares
+// (the input of the first RMSNorm, one column block).
 template <typename T>
-__global__ void embed_kernel(const T* emb, const RowMeta* rows, int d, float* h) {
-  const int row = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= d) return;
-  h[(size_t)row * d + c] = to_f<T>(emb[(size_t)rows[row].token * d + c]);
-}
-
-// ------------------------------------------------------------------ RMSNorm
-// u = (h / sqrt(mean(h^2) + eps)) * w, one workgroup per row.
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const float* w,
-                                                      int d, float eps, T* u, T* u_lo) {
+__global__ __launch_bounds__(256) void embed_kernel(const T* emb, const RowMeta* rows,
+                                                    int d, float* h, float* ss) {
   __shared__ float part[4];
   const int row = blockIdx.x;
-  const float* x = h + (size_t)row * d;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) ss += x[c] * x[c];
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  const T* e = emb + (size_t)rows[row].token * d;
+  float acc = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = to_f<T>(e[c]);
+    h[(size_t)row * d + c] = v;
+    acc += v * v;
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float denom = sqrtf(tot / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += 256)
-    store_act(u, u_lo, (size_t)row * d + c, __fmul_rn(__fdiv_rn(x[c], denom), w[c]));
+  if (threadIdx.x == 0) ss[row] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // ------------------------------------------------------------ RoPE + KV store
 // Block = one row, one head (query, key or value head); threads cover the
 // head_dim / 2 rotation pairs (i, i + hd/2).
-template <typename T>
-__global__ void rope_kv_kernel(const float* qkv, const RowMeta* rows, int nq,
-                               int nkv, int hd, const float* cos_t,
-                               const float* sin_t, T* q_out, T* q_lo, T* kc, T* vc) {
+template <typename T, int S>
+__global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t sstride,
+                               const RowMeta* rows, int nq, int nkv, int hd,
+                               const float* cos_t, const float* sin_t, T* q_out,
+                               T* q_lo, T* kc, T* vc, int ld) {
   const int row = blockIdx.x;
   const int head = blockIdx.y;  // [0, nq) q, [nq, nq+nkv) k, then v
   const int half = hd >> 1;
   const RowMeta rm = rows[row];
-  const size_t ld = (size_t)(nq + 2 * nkv) * hd;
-  const float* x = qkv + row * ld + (size_t)head * hd;
+  const float* x = qkv + (size_t)row * ld + (size_t)head * hd;
   const int page = rm.slot >> 4, off = rm.slot & 15;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const float x1 = x[i], x2 = x[i + half];
+    float p1[S], p2[S];  // GEMM split partials, loaded together
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      p1[k] = x[k * sstride + i];
+      p2[k] = x[k * sstride + i + half];
+    }
+    float x1 = 0.f, x2 = 0.f;  // added in split order
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      x1 += p1[k];
+      x2 += p2[k];
+    }
     if (head < nq + nkv) {
       const float c = cos_t[(size_t)rm.pos * half + i];
       const float s = sin_t[(size_t)rm.pos * half + i];
@@ -72,6 +75,70 @@ __global__ void rope_kv_kernel(const float* qkv, const RowMeta* rows, int nq,
       dst[(size_t)(i + half) * 16] = from_f<T>(x2);
     }
   }
+}
+
+// ------------------------------------------------------- residual reduce
+// h[r] += (sum of the S split partials of the GEMM output, in split order),
+// then the row's sum of squares for the next RMSNorm.  One workgroup of 1024
+// threads per row; all S partial loads of a thread are in flight together.
+template <int S>
+__global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size_t sstride,
+                                                            int ldp, int d, float* h,
+                                                            float* ss) {
+  __shared__ float part[16];
+  const int row = blockIdx.x;
+  float acc = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024 * 4) {
+    float4 pv[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      pv[k] = *reinterpret_cast<const float4*>(P + k * sstride + (size_t)row * ldp + c);
+    float4 v = *reinterpret_cast<const float4*>(h + (size_t)row * d + c);
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      v.x += pv[k].x;
+      v.y += pv[k].y;
+      v.z += pv[k].z;
+      v.w += pv[k].w;
+    }
+    *reinterpret_cast<float4*>(h + (size_t)row * d + c) = v;
+    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += part[w];
+    ss[row] = t;
+  }
+}
+
+// --------------------------------------------------------- SwiGLU reduce
+// act[r][j] = silu(g) * u with g, u the sums of the gate/up GEMM's split
+// partials; gate and up columns are interleaved per 16: output j reads
+// column (j / 16) * 32 + j % 16 (gate) and that + 16 (up).
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* P, int S,
+                                                            size_t sstride, int ldp,
+                                                            int F, float* act) {
+  const int row = blockIdx.y;
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (j >= F) return;
+  const int col = (j >> 4) * 32 + (j & 15);
+  const float* p = P + (size_t)row * ldp + col;
+  float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+  for (int k = 0; k < S; ++k) {
+    const float4 gv = *reinterpret_cast<const float4*>(p + k * sstride);
+    const float4 uv = *reinterpret_cast<const float4*>(p + k * sstride + 16);
+    gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
+    us.x += uv.x; us.y += uv.y; us.z += uv.z; us.w += uv.w;
+  }
+  float4 o;
+  o.x = gs.x / (1.0f + expf(-gs.x)) * us.x;
+  o.y = gs.y / (1.0f + expf(-gs.y)) * us.y;
+  o.z = gs.z / (1.0f + expf(-gs.z)) * us.z;
+  o.w = gs.w / (1.0f + expf(-gs.w)) * us.w;
+  *reinterpret_cast<float4*>(act + (size_t)row * F + j) = o;
 }
 
 // ----------------------------------------------------------- argmax reduce
@@ -150,10 +217,10 @@ __global__ void path_walk_kernel(const RowMeta* rows, const ReqMeta* reqs,
 //   H_i = sigmoid(a_i[c]) * H_parent + B_i[s] * x_i[c]   (no FMA contraction)
 //   y_i[c] = sum_s H_i[s] * C_i[s]; o_i[c] = y_i * silu(z_i[c])
 // Tree passes keep every node's state in LDS; chain passes keep one state.
-template <typename T, int S, bool TREE>
+template <int S, bool TREE, int NS>
 __global__ __launch_bounds__(256) void lr_fork_kernel(
-    const float* proj, const RowMeta* rows, const ReqMeta* reqs, int d,
-    float* H, T* o, T* o_lo, bool commit_last) {
+    const float* proj, size_t sstride, int ld, const RowMeta* rows,
+    const ReqMeta* reqs, int d, float* H, float* o, float* save, bool commit_last) {
   extern __shared__ float hs[];  // [max_rows][256] for trees
   constexpr int CPB = 256 / S;   // channels per block
   const int r = blockIdx.y;
@@ -162,13 +229,22 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
   const int c = blockIdx.x * CPB + threadIdx.x / S;
   const bool live = c < d;
   const int cc = live ? c : 0;
-  const int ld = 3 * d + 2 * S;
+  // in_proj output of a row (sum of the GEMM's split partials, in order)
+  auto pv = [&](int row, int col) {
+    const float* p = proj + (size_t)row * ld + col;
+    float t[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) t[k] = p[k * sstride];
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) v += t[k];
+    return v;
+  };
   float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
   const float h0 = *H0;
   float hprev = h0;
   for (int i = 0; i < rm.nrows; ++i) {
     const int row = rm.row0 + i;
-    const float* pr = proj + (size_t)row * ld;
     float hp;
     if (TREE) {
       const int p = rows[row].parent;
@@ -176,19 +252,27 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     } else {
       hp = hprev;
     }
-    const float a = pr[d + cc];
-    const float x = pr[cc];
+    const float a = pv(row, d + cc);
+    const float x = pv(row, cc);
+    const float Bs = pv(row, 3 * d + s);
+    const float Cs = pv(row, 3 * d + S + s);
     const float sig = 1.0f / (1.0f + expf(-a));
-    const float hi = __fadd_rn(__fmul_rn(sig, hp), __fmul_rn(pr[3 * d + s], x));
+    const float hi = __fadd_rn(__fmul_rn(sig, hp), __fmul_rn(Bs, x));
     if (TREE) hs[i * 256 + threadIdx.x] = hi;
     hprev = hi;
-    float y = __fmul_rn(hi, pr[3 * d + S + s]);
+    float y = __fmul_rn(hi, Cs);
 #pragma unroll
     for (int off = S / 2; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
     if (s == 0 && live) {
-      const float z = pr[2 * d + cc];
-      store_act(o, o_lo, (size_t)row * d + cc, y * (z / (1.0f + expf(-z))));
+      const float z = pv(row, 2 * d + cc);
+      o[(size_t)row * d + cc] = y * (z / (1.0f + expf(-z)));
+      if (save) {
+        save[(size_t)row * (2 * d + S) + cc] = x;
+        save[(size_t)row * (2 * d + S) + d + cc] = a;
+      }
     }
+    if (save && blockIdx.x == 0 && threadIdx.x < S)
+      save[(size_t)row * (2 * d + S) + 2 * d + s] = Bs;
   }
   if (commit_last && live) *H0 = hprev;
 }
@@ -242,10 +326,10 @@ __global__ __launch_bounds__(256) void lr_commit_kernel(
   float h = *hp;
   for (int k = 0; k <= q.plen; ++k) {
     const int node = (k == 0) ? 0 : q.nodes[k - 1];
-    const float* pr = proj + (size_t)(q.row0 + node) * ld;
+    const float* pr = proj + (size_t)(q.row0 + node) * ld;  // [x | a | B]
     const float a = pr[d + c];
     const float sig = 1.0f / (1.0f + expf(-a));
-    h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(pr[3 * d + s], pr[c]));
+    h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(pr[2 * d + s], pr[c]));
   }
   *hp = h;
 }
@@ -279,35 +363,62 @@ __global__ void to_f32_kernel(const T* src, int n, float* dst) {
 }  // namespace
 
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
-                        int d, float* h, hipStream_t s) {
-  dim3 grid((d + 255) / 256, R);
-  if (bf16) embed_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)emb, rows, d, h);
-  else embed_kernel<float><<<grid, 256, 0, s>>>((const float*)emb, rows, d, h);
+                        int d, float* h, float* ss, hipStream_t s) {
+  if (bf16) embed_kernel<uint16_t><<<R, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, ss);
+  else embed_kernel<float><<<R, 256, 0, s>>>((const float*)emb, rows, d, h, ss);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(bool bf16, const float* h, const float* w, int R,
-                          int d, float eps, void* u, void* u_lo, hipStream_t s) {
-  if (bf16)
-    rmsnorm_kernel<uint16_t><<<R, 256, 0, s>>>(h, w, d, eps, (uint16_t*)u, (uint16_t*)u_lo);
-  else rmsnorm_kernel<float><<<R, 256, 0, s>>>(h, w, d, eps, (float*)u, (float*)u_lo);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_kv(bool bf16, const float* qkv, const RowMeta* rows,
-                          int R, int nq, int nkv, int hd, const float* cos_t,
-                          const float* sin_t, void* q_out, void* q_lo, void* kc,
-                          void* vc, hipStream_t s) {
+template <typename T>
+static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta* rows,
+                         int R, int nq, int nkv, int hd, const float* cos_t,
+                         const float* sin_t, T* q_out, T* q_lo, T* kc, T* vc, int ld,
+                         hipStream_t s) {
   dim3 grid(R, nq + 2 * nkv);
-  const int thr = hd / 2 < 64 ? 64 : hd / 2;
+  const int thr = 64;  // loops over hd / 2 rotation pairs
+  switch (S) {
+#define RO_CASE(SV)                                                                    \
+  case SV:                                                                             \
+    rope_kv_kernel<T, SV><<<grid, thr, 0, s>>>(qkv, sstride, rows, nq, nkv, hd, cos_t, \
+                                               sin_t, q_out, q_lo, kc, vc, ld);        \
+    break;
+    RO_CASE(1) RO_CASE(2) RO_CASE(4) RO_CASE(8) RO_CASE(16) RO_CASE(32)
+#undef RO_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
+                          const RowMeta* rows, int R, int nq, int nkv, int hd,
+                          const float* cos_t, const float* sin_t, void* q_out,
+                          void* q_lo, void* kc, void* vc, int ld_qkv, hipStream_t s) {
   if (bf16)
-    rope_kv_kernel<uint16_t><<<grid, thr, 0, s>>>(qkv, rows, nq, nkv, hd, cos_t, sin_t,
-                                                  (uint16_t*)q_out, (uint16_t*)q_lo,
-                                                  (uint16_t*)kc, (uint16_t*)vc);
-  else
-    rope_kv_kernel<float><<<grid, thr, 0, s>>>(qkv, rows, nq, nkv, hd, cos_t, sin_t,
-                                               (float*)q_out, (float*)q_lo, (float*)kc,
-                                               (float*)vc);
+    return rope_t<uint16_t>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
+                            (uint16_t*)q_out, (uint16_t*)q_lo, (uint16_t*)kc,
+                            (uint16_t*)vc, ld_qkv, s);
+  return rope_t<float>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
+                       (float*)q_out, (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, s);
+}
+
+hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int ld_p,
+                               int R, int d, float* h, float* ss, hipStream_t s) {
+  if (d % 4) return hipErrorInvalidValue;
+  switch (S) {
+#define RR_CASE(SV) \
+  case SV: resid_reduce_kernel<SV><<<R, 1024, 0, s>>>(P, split_stride, ld_p, d, h, ss); break;
+    RR_CASE(1) RR_CASE(2) RR_CASE(4) RR_CASE(8) RR_CASE(16) RR_CASE(32)
+#undef RR_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_reduce(const float* P, int S, size_t split_stride, int ld_p,
+                                int R, int F, float* act, hipStream_t s) {
+  if (F % 64) return hipErrorInvalidValue;
+  dim3 grid((F / 4 + 255) / 256, R);
+  swiglu_reduce_kernel<<<grid, 256, 0, s>>>(P, S, split_stride, ld_p, F, act);
   return hipGetLastError();
 }
 
@@ -324,46 +435,59 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
   return hipGetLastError();
 }
 
-template <typename T, int S>
-static hipError_t lr_fork_s(const float* proj, const RowMeta* rows,
-                            const ReqMeta* reqs, int n_req, int d, float* H,
-                            void* o, void* o_lo, bool tree, bool commit_last,
-                            int max_rows_per_req, hipStream_t s) {
+template <int S, int NS>
+static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
+                            const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
+                            float* H, float* o, float* save, bool tree,
+                            bool commit_last, int max_rows_per_req, hipStream_t s) {
   constexpr int CPB = 256 / S;
   dim3 grid((d + CPB - 1) / CPB, n_req);
   if (tree) {
     const size_t lds = (size_t)max_rows_per_req * 256 * sizeof(float);
-    hipError_t e = hipFuncSetAttribute((const void*)lr_fork_kernel<T, S, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)lr_fork_kernel<S, true, NS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
-    lr_fork_kernel<T, S, true><<<grid, 256, lds, s>>>(proj, rows, reqs, d, H, (T*)o,
-                                                      (T*)o_lo, commit_last);
+    lr_fork_kernel<S, true, NS><<<grid, 256, lds, s>>>(proj, sstride, ld, rows, reqs, d,
+                                                       H, o, save, commit_last);
   } else {
-    lr_fork_kernel<T, S, false><<<grid, 256, 0, s>>>(proj, rows, reqs, d, H, (T*)o,
-                                                     (T*)o_lo, commit_last);
+    lr_fork_kernel<S, false, NS><<<grid, 256, 0, s>>>(proj, sstride, ld, rows, reqs, d,
+                                                      H, o, save, commit_last);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_lr_fork(bool bf16, const float* proj, const RowMeta* rows,
-                          const ReqMeta* reqs, int n_req, int d, int S,
-                          float* H, void* o, void* o_lo, bool any_tree,
+template <int S>
+static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
+                             const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
+                             float* H, float* o, float* save, bool tree,
+                             bool commit_last, int max_rows_per_req, hipStream_t s) {
+  switch (NS) {
+#define NS_CASE(NV)                                                                   \
+  case NV:                                                                            \
+    return lr_fork_s<S, NV>(proj, sstride, ld, rows, reqs, n_req, d, H, o, save, tree, \
+                            commit_last, max_rows_per_req, s);
+    NS_CASE(1) NS_CASE(2) NS_CASE(4) NS_CASE(8) NS_CASE(16) NS_CASE(32)
+#undef NS_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_lr_fork(const float* proj, int NS, size_t split_stride, int ld,
+                          const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
+                          int S, float* H, float* o, float* save, bool any_tree,
                           bool commit_last, int max_rows_per_req, hipStream_t s) {
-#define LR_CASE(SV)                                                              \
-  case SV:                                                                       \
-    return bf16 ? lr_fork_s<uint16_t, SV>(proj, rows, reqs, n_req, d, H, o, o_lo,\
-                                          any_tree, commit_last,                 \
-                                          max_rows_per_req, s)                   \
-                : lr_fork_s<float, SV>(proj, rows, reqs, n_req, d, H, o, o_lo,   \
-                                       any_tree, commit_last, max_rows_per_req, s);
   switch (S) {
+#define LR_CASE(SV)                                                                   \
+  case SV:                                                                            \
+    return lr_fork_ns<SV>(NS, proj, split_stride, ld, rows, reqs, n_req, d, H, o,     \
+                          save, any_tree, commit_last, max_rows_per_req, s);
     LR_CASE(16)
     LR_CASE(32)
     LR_CASE(64)
+#undef LR_CASE
     default: return hipErrorInvalidValue;
   }
-#undef LR_CASE
 }
 
 hipError_t launch_kv_compact(bool bf16, const CommitReq* cr, int n_req,

@@ -2,229 +2,355 @@
 // (rows of the pass) small and W streamed once from HBM.
 //
 // Design for gfx950:
-//  - W is pre-tiled (see kernels.h) so that one wavefront reads one 16 x 32
-//    tile as a single contiguous 1 KB (bf16) load, 16 bytes per lane, which
-//    is exactly that lane's MFMA operand.  A workgroup owns NT adjacent
-//    16-column tiles and streams them over the whole K range.
-//  - The K range is split across the WAVES wavefronts of the workgroup;
-//    each wave keeps a block of U K-steps of W loads in flight
-//    (double-buffered) while it multiplies the previous block.
-//  - X (a few hundred KB at most) is read through L2; rows beyond M read
-//    zeros, so the per-element result does not depend on M.  bf16 weights
-//    meet activations held as hi + lo bf16 planes: two MFMAs per product,
-//    which keeps the activations at ~16 mantissa bits while W is streamed
-//    once (the kernel is HBM-bound, so the extra MFMA work is hidden).
-//  - Partial sums of the waves are reduced in LDS in a fixed order, so the
-//    result of a row is bitwise independent of how many rows the pass has
-//    and of the launch's row chunking.
-//  - Epilogues: plain store, residual add, SwiGLU (gate and up tiles are
-//    interleaved so one workgroup owns both halves of 16 outputs), and the
-//    LM-head argmax partial (per-row max over the workgroup's columns,
-//    lowest index on ties).
+//  - W is pre-tiled (see kernels.h): one wavefront reads one 16 x 32 tile as
+//    a single contiguous 1 KB (bf16) load, 16 bytes per lane, which is
+//    exactly that lane's MFMA operand.  Each wave owns NTW adjacent tiles
+//    and streams them over the workgroup's K range, keeping the next block
+//    of U K-steps in flight while it multiplies the current one.
+//  - The activations of the workgroup's K range are staged once per chunk
+//    in LDS, shared by all waves, so the vector-memory path carries weights
+//    only.  Activations are fp32 in HBM; for bf16 weights they are staged as
+//    hi + lo bf16 pairs (two MFMAs per product, ~16 mantissa bits) and the
+//    optional RMSNorm of the input (per-row scale from partial sums of
+//    squares written by the producer of h, times the norm weight) is applied
+//    while staging.  Rows beyond M stage zeros.
+//  - The K range can be split over S workgroups.  Split GEMMs (EPI_PART)
+//    write fp32 partials with plain stores and the consumer kernel adds the S
+//    partials in split order (so no workgroup of this kernel waits for or
+//    fences against another: on gfx950 a device-scope fence writes back and
+//    invalidates the whole L2 of the XCD).
+//  - Epilogues: partial store, SwiGLU (gate and up tiles are interleaved so a
+//    wave owns both halves of 16 outputs; S = 1), and the LM-head argmax
+//    partial (per-row max over the workgroup's columns, lowest index on ties;
+//    S = 1).
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kD = 8;  // minimum K-steps of W loads in flight per wave (rolling window)
 
-template <typename T, int MT, int NT, int EPI>
-__global__ __launch_bounds__(kWaves * 64) void gemm_kernel(GemmArgs a) {
-  constexpr int U = (sizeof(T) == 2) ? 8 : 4;  // K-steps per load block
+// Staged chunk width (K elements) per row-tile count: two LDS buffers of
+// MT*16 rows x (KC + pad) x 4 bytes stay near 64 KB.
+template <int MT> struct ChunkK {
+  static constexpr int value = MT <= 1 ? 256 : MT <= 2 ? 256 : MT <= 3 ? 160
+                             : MT <= 4 ? 128 : MT <= 5 ? 96 : 64;
+};
+
+template <typename T, int MT, int NTW, int WAVES, int EPI, int XM>
+__global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr bool kBf = sizeof(T) == 2;
   constexpr int TROWS = MT * 16;
-  constexpr int TCOLS = NT * 16;
-  constexpr int LDT = TCOLS + 1;
-  __shared__ float red[kWaves * TROWS * LDT];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int COLS = WAVES * NTW * 16;  // output columns of the workgroup
+  constexpr int NTHR = WAVES * 64;
+  constexpr int KC = ChunkK<MT>::value;
+  constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
+  constexpr int QUADS = KC / 4;                      // float4 per staged row
+  constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // float4 per thread
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int nb = blockIdx.x;
+  const int nblk = a.ntiles / (WAVES * NTW);
+  const int nb = blockIdx.x % nblk;
+  const int sk = blockIdx.x / nblk;
+  const int kbeg = sk * a.KR;
+  const int kend = min(a.K, kbeg + a.KR);
   const int ksteps = a.K >> 5;
-  const int s0 = (wave * ksteps) / kWaves;
-  const int s1 = ((wave + 1) * ksteps) / kWaves;
+
+  // two staging buffers; each holds a bf16 hi plane then a lo plane, or fp32
+  constexpr int BUF_ELEMS = TROWS * LDS_ROW * (kBf ? 2 : 1);
+  T* xbuf = reinterpret_cast<T*>(smem);
 
   const Frag<T>* Wt = reinterpret_cast<const Frag<T>*>(a.W);
-  const T* X = reinterpret_cast<const T*>(a.X);
-
-  constexpr bool kSplit = sizeof(T) == 2;
-  const T* Xlo = reinterpret_cast<const T*>(a.X_lo);
-  size_t xoff[MT];
-  bool xok[MT];
+  const Frag<T>* wbase[NTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = a.row0 + mt * 16 + r16;
-    xok[mt] = row < a.M;
-    xoff[mt] = (size_t)(xok[mt] ? row : 0) * a.K + g * 8;
+  for (int t = 0; t < NTW; ++t)
+    wbase[t] = Wt + ((size_t)((nb * WAVES + wave) * NTW + t) * ksteps) * 64 + lane;
+
+  floatx4_t acc[NTW][MT];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // per-row RMSNorm scale (XM_NORM)
+  __shared__ float rscale[TROWS];
+  if (XM == XM_NORM) {
+    for (int r = threadIdx.x; r < TROWS; r += NTHR) {
+      const int m = a.row0 + r;
+      float sc = 0.f;
+      if (m < a.M) {
+        float ss = 0.f;
+        for (int b = 0; b < a.ss_nb; ++b) ss += a.ss[(size_t)b * a.ss_ld + m];
+        sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+      }
+      rscale[r] = sc;
+    }
+    __syncthreads();
   }
 
-  floatx4_t acc[NT][MT];
+  // ---- activation chunk prefetch (registers) and store (LDS)
+  float4 xr[XQ];
+  float4 wr[XM == XM_NORM ? XQ : 1];
+  auto fetch = [&](int kc0, int kcl) {
+    // columns kc0 .. kc0 + min(kcl, KC) of the real K range; the rest zero.
+    // (The norm weights are fetched here too, so that every load the LDS
+    // store waits for was issued before the next window of W loads.)
+    const int quads = kcl <= 0 ? 0 : (kcl >= KC ? QUADS : kcl >> 2);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  const Frag<T>* wbase[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-    wbase[nt] = Wt + ((size_t)(nb * NT + nt) * ksteps) * 64 + lane;
-
-  auto load_block = [&](Frag<T> (&w)[U][NT], int sb) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = sb + u;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (kb < s1) w[u][nt] = wbase[nt][(size_t)kb * 64];
-        else w[u][nt].zero();
+    for (int q = 0; q < XQ; ++q) {
+      const int e = threadIdx.x + q * NTHR;
+      const int r = e / QUADS, c = (e % QUADS) * 4;
+      const int m = a.row0 + r;
+      xr[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
+      if (in) xr[q] = *reinterpret_cast<const float4*>(a.X + (size_t)m * a.ldx + kc0 + c);
+      if constexpr (XM == XM_NORM) {
+        wr[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (in) wr[q] = *reinterpret_cast<const float4*>(a.nw + kc0 + c);
       }
     }
   };
-  auto mul_block = [&](const Frag<T> (&w)[U][NT], int sb) {
+  auto store = [&](int buf, int kc0, int kcl) {
+    // all KC columns are written (fetch zeroed those past the real range)
+    (void)kc0;
+    (void)kcl;
+    T* hi = xbuf + buf * BUF_ELEMS;
+    T* lo = hi + TROWS * LDS_ROW;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = sb + u;
-      if (kb < s1) {
+    for (int q = 0; q < XQ; ++q) {
+      const int e = threadIdx.x + q * NTHR;
+      const int r = e / QUADS, c = (e % QUADS) * 4;
+      if (r >= TROWS) continue;
+      float4 v = xr[q];
+      if constexpr (XM == XM_NORM) {
+        const float sc = rscale[r];
+        const float4 w = wr[q];  // zero outside the real range
+        v.x = (v.x * sc) * w.x;
+        v.y = (v.y * sc) * w.y;
+        v.z = (v.z * sc) * w.z;
+        v.w = (v.w * sc) * w.w;
+      }
+      if constexpr (kBf) {
+        const uint16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+        const uint16_t l0 = f2bf(v.x - bf2f(h0)), l1 = f2bf(v.y - bf2f(h1));
+        const uint16_t l2 = f2bf(v.z - bf2f(h2)), l3 = f2bf(v.w - bf2f(h3));
+        *reinterpret_cast<uint2*>(&hi[r * LDS_ROW + c]) =
+            make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16));
+        *reinterpret_cast<uint2*>(&lo[r * LDS_ROW + c]) =
+            make_uint2(l0 | ((uint32_t)l1 << 16), l2 | ((uint32_t)l3 << 16));
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(hi) + r * LDS_ROW + c) = v;
+      }
+    }
+  };
+
+  const int kb_beg = kbeg >> 5, kb_end = kend >> 5;
+  constexpr int CSTEPS = KC / 32;              // K-steps per staged chunk
+  constexpr int CPW = (kD + CSTEPS - 1) / CSTEPS;  // chunks per window
+  constexpr int WIN = CPW * CSTEPS;            // K-steps of W loads in flight
+  // Rolling window: slot u holds the W tiles of K-step (window start + u);
+  // right after a slot is consumed it is reloaded with the step WIN ahead.
+  // Slot indices are compile-time constants (the window is a whole number of
+  // chunks) and the loop body has no branches around loads: loads past the
+  // end are clamped to the last tile (an L2 hit) and staged activations past
+  // the end are zero, so padded steps add nothing.  This keeps the
+  // compiler's in-order load counters exact (no drain at chunk boundaries).
+  Frag<T> w[WIN][NTW];
+  auto load_step = [&](Frag<T> (&dst)[NTW], int kb) {
+    const int k = kb < kb_end ? kb : kb_end - 1;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) dst[t] = wbase[t][(size_t)k * 64];
+  };
+  // the first chunk is fetched now (before the W window, as in the steady
+  // state); each chunk is stored into LDS at its start and the next one is
+  // fetched into registers right after
+  fetch(kbeg, kend - kbeg);
+#pragma unroll
+  for (int u = 0; u < WIN; ++u) load_step(w[u], kb_beg + u);
+
+  int buf = 0;
+  for (int kw = kb_beg; kw < kb_end; kw += WIN) {
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int k0 = (kw + cc * CSTEPS) * 32;  // first K index of this chunk
+      store(buf, k0, kend - k0);
+      fetch(k0 + KC, kend - k0 - KC);
+      __syncthreads();
+      const T* hi = xbuf + buf * BUF_ELEMS;
+      buf ^= 1;
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j) {
+        const int u = cc * CSTEPS + j;
+        const int kk = j * 32 + g * 8;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          Frag<T> x, xl;
-          if (xok[mt]) {
-            x.load(X + xoff[mt] + kb * 32);
-            if (kSplit) xl.load(Xlo + xoff[mt] + kb * 32);
-          } else {
-            x.zero();
-            xl.zero();
-          }
+          const int r = mt * 16 + r16;
+          Frag<T> x;
+          if constexpr (kBf) {
+            Frag<T> xl;
+            x.load(&hi[r * LDS_ROW + kk]);
+            xl.load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            mma32(acc[nt][mt], w[u][nt], x);
-            if (kSplit) mma32(acc[nt][mt], w[u][nt], xl);
+            for (int t = 0; t < NTW; ++t) {
+              mma32(acc[t][mt], w[u][t], x);
+              mma32(acc[t][mt], w[u][t], xl);
+            }
+          } else {
+            x.load(reinterpret_cast<const float*>(hi) + r * LDS_ROW + kk);
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) mma32(acc[t][mt], w[u][t], x);
           }
         }
+        load_step(w[u], kw + u + WIN);
       }
     }
-  };
-
-  Frag<T> wa[U][NT], wb[U][NT];
-  int sb = s0;
-  if (sb < s1) load_block(wa, sb);
-  while (sb < s1) {
-    if (sb + U < s1) load_block(wb, sb + U);
-    mul_block(wa, sb);
-    sb += U;
-    if (sb >= s1) break;
-    if (sb + U < s1) load_block(wa, sb + U);
-    mul_block(wb, sb);
-    sb += U;
   }
 
-  // wave partials -> LDS, lane/item -> (row, col) as in common.h
+  // ---- results
+  const int col0 = nb * COLS;
+  const int N = a.ntiles * 16;
+  if (EPI == EPI_PART) {
+    float* P = a.P + (size_t)sk * a.P_ld * N;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = a.row0 + mt * 16 + r16;
+        if (m < a.M) {
+          float* pp = P + (size_t)m * N + col0 + (wave * NTW + t) * 16 + 4 * g;
+          *reinterpret_cast<float4*>(pp) =
+              make_float4(acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
+        }
+      }
+    return;
+  }
+  // S == 1: tile [TROWS][COLS] in LDS (reusing the staging area)
+  constexpr int LDT = COLS + 1;
+  float* tile = reinterpret_cast<float*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        red[(wave * TROWS + mt * 16 + r16) * LDT + nt * 16 + 4 * g + r] =
-            acc[nt][mt][r];
+        tile[(mt * 16 + r16) * LDT + (wave * NTW + t) * 16 + 4 * g + r] = acc[t][mt][r];
   __syncthreads();
 
-  const int col0 = nb * TCOLS;
   if (EPI == EPI_SWIGLU) {
-    // columns [0,16) gate, [16,32) up of the same 16 outputs
-    for (int e = threadIdx.x; e < TROWS * 16; e += kWaves * 64) {
-      const int row = e >> 4, col = e & 15;
+    // tile pair p: columns [p*32, p*32+16) gate, [p*32+16, p*32+32) up
+    constexpr int OUTS = COLS / 2;
+    for (int e = threadIdx.x; e < TROWS * OUTS; e += NTHR) {
+      const int row = e / OUTS, j = e % OUTS;
       const int m = a.row0 + row;
       if (m >= a.M) continue;
-      float gv = 0.f, uv = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        gv += red[(w * TROWS + row) * LDT + col];
-        uv += red[(w * TROWS + row) * LDT + col + 16];
-      }
-      const float act = gv / (1.0f + expf(-gv)) * uv;
-      store_act(reinterpret_cast<T*>(a.act), reinterpret_cast<T*>(a.act_lo),
-                (size_t)m * a.ldact + nb * 16 + col, act);
+      const int p = j >> 4, c = j & 15;
+      const float gv = tile[row * LDT + p * 32 + c];
+      const float uv = tile[row * LDT + p * 32 + 16 + c];
+      a.Y[(size_t)m * a.ldy + nb * OUTS + j] = gv / (1.0f + expf(-gv)) * uv;
     }
     return;
   }
-
-  for (int e = threadIdx.x; e < TROWS * TCOLS; e += kWaves * 64) {
-    const int row = e / TCOLS, col = e % TCOLS;
+  // EPI_ARGMAX
+  for (int e = threadIdx.x; e < TROWS * COLS; e += NTHR) {
+    const int row = e / COLS, col = e % COLS;
     const int m = a.row0 + row;
     if (m >= a.M) continue;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * TROWS + row) * LDT + col];
     const int n = col0 + col;
-    if (EPI == EPI_STORE) {
-      a.Y[(size_t)m * a.ldy + n] = v;
-    } else if (EPI == EPI_RESID) {
-      a.Y[(size_t)m * a.ldy + n] += v;
-    } else {  // EPI_ARGMAX
-      if (n == a.bias_tok && a.rows[m].pos >= a.bias_after) v += a.bias;
-      if (a.logits) a.logits[(size_t)m * a.ldlog + n] = v;
-      red[row * LDT + col] = v;
-    }
+    float v = tile[row * LDT + col];
+    if (n >= a.ncols) v = -INFINITY;
+    if (n == a.bias_tok && a.rows[m].pos >= a.bias_after) v += a.bias;
+    if (a.logits && n < a.ncols) a.logits[(size_t)m * a.ldlog + n] = v;
+    tile[row * LDT + col] = v;
   }
-  if (EPI == EPI_ARGMAX) {
-    __syncthreads();
-    for (int row = threadIdx.x; row < TROWS; row += kWaves * 64) {
-      const int m = a.row0 + row;
-      if (m >= a.M) continue;
-      float best = -INFINITY;
-      int bi = col0;
-      for (int col = 0; col < TCOLS; ++col) {
-        const float v = red[row * LDT + col];
-        if (v > best) { best = v; bi = col0 + col; }  // NaN never wins
-      }
-      a.part[(size_t)m * a.nblocks + nb] = make_float2(best, __int_as_float(bi));
+  __syncthreads();
+  for (int row = threadIdx.x; row < TROWS; row += NTHR) {
+    const int m = a.row0 + row;
+    if (m >= a.M) continue;
+    float best = -INFINITY;
+    int bi = col0;
+    for (int col = 0; col < COLS; ++col) {
+      const float v = tile[row * LDT + col];
+      if (v > best) { best = v; bi = col0 + col; }  // NaN never wins
     }
+    a.part[(size_t)m * a.nblocks + nb] = make_float2(best, __int_as_float(bi));
   }
 }
 
-template <typename T, int EPI, int NT>
-hipError_t launch_mt(int mt, const GemmArgs& a, int grid, hipStream_t s) {
-  dim3 blk(kWaves * 64);
-  switch (mt) {
-    case 1: gemm_kernel<T, 1, NT, EPI><<<grid, blk, 0, s>>>(a); break;
-    case 2: gemm_kernel<T, 2, NT, EPI><<<grid, blk, 0, s>>>(a); break;
-    case 3: gemm_kernel<T, 3, NT, EPI><<<grid, blk, 0, s>>>(a); break;
-    case 4: gemm_kernel<T, 4, NT, EPI><<<grid, blk, 0, s>>>(a); break;
-    case 5: gemm_kernel<T, 5, NT, EPI><<<grid, blk, 0, s>>>(a); break;
-    default: gemm_kernel<T, 8, NT, EPI><<<grid, blk, 0, s>>>(a); break;
+template <typename T, int MT, int NTW, int WAVES, int EPI, int XM>
+hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
+  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, XM>;
+  constexpr int KC = ChunkK<MT>::value;
+  const size_t stage_b = 2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * 4;
+  const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
+  const size_t lds = stage_b > tile_b ? stage_b : tile_b;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)k,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
   }
+  const int nblk = a.ntiles / (WAVES * NTW);
+  k<<<nblk * a.S, WAVES * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
+constexpr int kWaves = 8;  // waves per workgroup, one 16-column tile each
+constexpr int kNtw = 1;
+
+template <typename T, int EPI, int XM>
+hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_one<T, 1, kNtw, kWaves, EPI, XM>(a, s);
+    case 2: return launch_one<T, 2, kNtw, kWaves, EPI, XM>(a, s);
+    case 3: return launch_one<T, 3, kNtw, kWaves, EPI, XM>(a, s);
+    case 4: return launch_one<T, 4, kNtw, kWaves, EPI, XM>(a, s);
+    case 5: return launch_one<T, 5, kNtw, kWaves, EPI, XM>(a, s);
+    default: return launch_one<T, 8, kNtw, kWaves, EPI, XM>(a, s);
+  }
+}
+
 template <typename T>
-hipError_t launch_typed(int epi, const GemmArgs& a0, hipStream_t s) {
+hipError_t launch_typed(int epi, int xm, const GemmArgs& a, int mt, hipStream_t s) {
+#define GEMM_CASE(E, X)                                                    \
+  if (epi == E && xm == X) return launch_mt<T, E, X>(mt, a, s);
+  GEMM_CASE(EPI_PART, XM_F32)
+  GEMM_CASE(EPI_PART, XM_NORM)
+  GEMM_CASE(EPI_SWIGLU, XM_NORM)
+  GEMM_CASE(EPI_ARGMAX, XM_NORM)
+#undef GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int gemm_cols_per_block() { return kWaves * kNtw * 16; }
+
+int gemm_splits(int K, int N, int M) {
+  // about one workgroup per CU (measured best for the 8B/27B shapes at
+  // 1..65 rows) and at least 256 reduction indices per split
+  (void)M;
+  const int nblk = N / gemm_cols_per_block();
+  int S = 1;
+  while (S * nblk < 256 && K / (S * 2) >= 256 && (K / (S * 2)) % 32 == 0) S *= 2;
+  return S;
+}
+
+hipError_t launch_gemm(bool bf16, int epi, int xm, const GemmArgs& a0, hipStream_t s) {
+  if (a0.M <= 0) return hipSuccess;
   GemmArgs a = a0;
-  const int NT = (epi == EPI_SWIGLU) ? 2 : 1;
-  const int grid = a.ntiles / NT;
-  // rows per launch: up to 8 tiles of 16; smaller passes use the smallest
-  // tile count that covers them
+  if (a.S < 1 || (epi != EPI_PART && a.S != 1) || a.K % a.S || (a.K / a.S) % 32)
+    return hipErrorInvalidValue;
+  a.KR = a.K / a.S;
   for (int r0 = 0; r0 < a.M; r0 += 128) {
     const int rows = (a.M - r0 < 128) ? a.M - r0 : 128;
     const int need = (rows + 15) / 16;
     const int mt = need <= 5 ? need : 8;
     a.row0 = r0;
-    hipError_t e;
-    switch (epi) {
-      case EPI_STORE: e = launch_mt<T, EPI_STORE, 1>(mt, a, grid, s); break;
-      case EPI_RESID: e = launch_mt<T, EPI_RESID, 1>(mt, a, grid, s); break;
-      case EPI_SWIGLU: e = launch_mt<T, EPI_SWIGLU, 2>(mt, a, grid, s); break;
-      default: e = launch_mt<T, EPI_ARGMAX, 1>(mt, a, grid, s); break;
-    }
+    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, xm, a, mt, s)
+                        : launch_typed<float>(epi, xm, a, mt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-}  // namespace
-
-hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, int /*nt*/,
-                       hipStream_t s) {
-  if (a.M <= 0) return hipSuccess;
-  return bf16 ? launch_typed<uint16_t>(epi, a, s) : launch_typed<float>(epi, a, s);
 }

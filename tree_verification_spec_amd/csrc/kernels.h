@@ -32,32 +32,48 @@ struct ReqMeta {
 // (nb, kb) at element offset (nb * (K / 32) + kb) * 512, lane l of the tile
 // holding W[nb * 16 + l % 16][kb * 32 + (l / 16) * 8 + e] at l * 8 + e.
 
-enum GemmEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+// EPI_PART: fp32 partial sums of split s at P[s][row][col] (any S); the
+// consumer adds the S partials in order.  EPI_SWIGLU / EPI_ARGMAX need S = 1.
+enum GemmEpi { EPI_PART = 0, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+enum GemmXMode { XM_F32 = 0, XM_NORM = 1 };
 
 struct GemmArgs {
-  const void* W;      // tiled weights (bf16 bits or fp32)
-  const void* X;      // activations [M, K], same element type as W
-  const void* X_lo;   // bf16: low plane of the activations (hi + lo = value)
-  int32_t M, K;       // rows, reduction length
-  int32_t ntiles;     // 16-column tiles of W
-  int32_t row0;       // first row handled by this launch
-  float* Y;           // STORE: Y[M, ldy] = result; RESID: Y += result
+  const void* W;        // tiled weights (bf16 bits or fp32), ntiles x 16 rows
+  const float* X;       // fp32 activations [M, ldx] (XM_NORM: the residual h)
+  int32_t ldx;
+  // XM_NORM: RMSNorm of X applied while staging: scale of row m is
+  // 1 / sqrt(sum_b ss[b * ss_ld + m] / K + eps), then times nw[k]
+  const float* ss;
+  int32_t ss_nb, ss_ld;
+  const float* nw;
+  float eps;
+  int32_t M, K;         // rows, reduction length
+  int32_t ntiles;       // 16-column tiles of W (a multiple of 8)
+  int32_t ncols;        // real output columns (<= ntiles * 16)
+  int32_t row0;         // first row handled by this launch (set by launch_gemm)
+  int32_t S;            // K splits (EPI_PART only; see gemm_splits)
+  int32_t KR;           // K per split (set by launch_gemm)
+  float* P;             // EPI_PART: partials [S][P_ld][ntiles * 16]
+  int32_t P_ld;
+  float* Y;             // SWIGLU: act (fp32) [M, ldy]
   int32_t ldy;
-  void* act;          // SWIGLU: act[M, ldact] (element type of X)
-  void* act_lo;       // SWIGLU, bf16: low plane of act
-  int32_t ldact;
-  float2* part;       // ARGMAX: per (row, column block) (max, index bits)
-  int32_t nblocks;    // column blocks (= ntiles / NT)
-  float* logits;      // ARGMAX: optional fp32 logits [M, ldlog]
+  float2* part;         // ARGMAX: per (row, column block) (max, index bits)
+  int32_t nblocks;      // ARGMAX: column blocks per row
+  float* logits;        // ARGMAX: optional fp32 logits [M, ldlog]
   int32_t ldlog;
-  const RowMeta* rows;     // ARGMAX fault injection: row positions
+  const RowMeta* rows;  // ARGMAX fault injection: row positions
   int32_t bias_tok, bias_after;
   float bias;
 };
 
+// Output columns of one GEMM workgroup (ARGMAX partial blocks and RESID sums
+// of squares come per such block); K-split count of a matrix shape.
+int gemm_cols_per_block();
+int gemm_splits(int K, int N, int M);
+
 // Launch the skinny GEMM for rows [0, M): picks the tile shape and splits
 // rows into chunks when M exceeds one launch's row capacity.
-hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, int nt_per_block,
+hipError_t launch_gemm(bool bf16, int epi, int xm, const GemmArgs& a,
                        hipStream_t s);
 
 struct AttnArgs {
@@ -81,23 +97,31 @@ struct AttnArgs {
 
 hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s);
 
-// Merge the per-split partials into o[rows, nq * hd] (element type of q;
-// bf16 also writes the low plane o_lo).
-hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o,
-                               void* o_lo, hipStream_t s);
+// Merge the per-split partials into the fp32 attention output o[rows, nq*hd].
+hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, float* o,
+                               hipStream_t s);
 
+// h[r] = E[token_r] in fp32, and ss[r] = sum(h[r]^2) (one column block).
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows,
-                        int R, int d, float* h, hipStream_t s);
-
-// u = rmsnorm(h) * w, stored in the activation type (bf16: hi/lo planes).
-hipError_t launch_rmsnorm(bool bf16, const float* h, const float* w, int R,
-                          int d, float eps, void* u, void* u_lo, hipStream_t s);
+                        int R, int d, float* h, float* ss, hipStream_t s);
 
 // q -> RoPE -> q_out; k -> RoPE -> K cache; v -> V cache, at each row's slot.
-hipError_t launch_rope_kv(bool bf16, const float* qkv, const RowMeta* rows,
-                          int R, int nq, int nkv, int hd, const float* cos_t,
-                          const float* sin_t, void* q_out, void* q_lo, void* kc,
-                          void* vc, hipStream_t s);
+// qkv = sum of the S GEMM partials qkv[s * split_stride + row * ld_qkv + c].
+hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
+                          const RowMeta* rows, int R, int nq, int nkv, int hd,
+                          const float* cos_t, const float* sin_t, void* q_out,
+                          void* q_lo, void* kc, void* vc, int ld_qkv, hipStream_t s);
+
+// h[r] += sum_s P[s * split_stride + r * ld_p + c] (c < d), then
+// ss[r] = sum(h[r]^2): the residual add of a split GEMM and the input of the
+// next RMSNorm.  One workgroup per row.
+hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int ld_p,
+                               int R, int d, float* h, float* ss, hipStream_t s);
+
+// act = silu(gate) * up from the gate/up GEMM's split partials (gate and up
+// tiles interleaved per 16 columns).  F % 64 == 0.
+hipError_t launch_swiglu_reduce(const float* P, int S, size_t split_stride, int ld_p,
+                                int R, int F, float* act, hipStream_t s);
 
 // Per-row argmax over the column-block partials (lowest index on ties).
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
@@ -110,12 +134,14 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
                             int32_t* res, hipStream_t s);
 
 // Gated diagonal recurrence over the pass's nodes for one recurrent layer.
-// proj: [R, 3d + 2S] fp32 = [x | a | z | B | C]; H: committed states
-// [max_requests][d][S]; o: [R, d] activation type.  With commit_last (chain
-// passes only) the state of each request's last row is written back to H.
-hipError_t launch_lr_fork(bool bf16, const float* proj, const RowMeta* rows,
-                          const ReqMeta* reqs, int n_req, int d, int S,
-                          float* H, void* o, void* o_lo, bool any_tree,
+// proj: in_proj output as S split partials (stride split_stride floats), each
+// [R, ld] = [x | a | z | B | C | pad]; H: committed states
+// [max_requests][d][S]; o: [R, d] fp32.  save (or NULL): per row [x | a | B]
+// ([R, 2d + S]) for the commit.  With commit_last (chain passes only) the
+// state of each request's last row is written back to H.
+hipError_t launch_lr_fork(const float* proj, int NS, size_t split_stride, int ld,
+                          const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
+                          int S, float* H, float* o, float* save, bool any_tree,
                           bool commit_last, int max_rows_per_req, hipStream_t s);
 
 struct CommitReq {
@@ -134,7 +160,8 @@ hipError_t launch_kv_compact(bool bf16, const CommitReq* cr, int n_req,
                              int n_attn_layers, int nkv, int hd,
                              hipStream_t s);
 
-// Advance the committed recurrent state along root + accepted nodes.
+// Advance the committed recurrent state along root + accepted nodes (proj_all
+// holds the summed in_proj outputs that the verify pass saved per layer).
 hipError_t launch_lr_commit(const CommitReq* cr, int n_req,
                             const float* proj_all, size_t proj_layer_stride,
                             int proj_ld, int n_lr, int d, int S, float* H,

@@ -29,7 +29,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxSplits = 32;
+constexpr int kMaxSplits = 64;  // attention key splits (one combine lane each)
 constexpr int kStagingBytes = 64 << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -117,19 +117,16 @@ struct spec_ctx {
   // scratch
   int Rmax = 0;
   float* h = nullptr;
-  void* u = nullptr;
-  void* u_lo = nullptr;
-  void* act = nullptr;
-  void* act_lo = nullptr;
-  void* attn_o = nullptr;
-  void* attn_o_lo = nullptr;
-  float* qkv = nullptr;
+  float* ss = nullptr;       // per row sum of squares of h (RMSNorm input)
+  float* act = nullptr;
+  float* attn_o = nullptr;
   void* q = nullptr;
   void* q_lo = nullptr;
-  float* lrproj = nullptr;
-  size_t lrproj_layer = 0;  // floats per layer slot (verify)
-  void* lr_o = nullptr;
-  void* lr_o_lo = nullptr;
+  float* P = nullptr;        // GEMM split partials [S][Rmax][N]
+  float* lrsave = nullptr;   // per recurrent layer [max_rows][x | a | B]
+  size_t lrsave_layer = 0;
+  size_t weights_end = 0;
+  float* lr_o = nullptr;
   float* part_o = nullptr;
   float2* part_ml = nullptr;
   float2* am_part = nullptr;
@@ -192,7 +189,8 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->dtype != SPEC_DTYPE_FP32 && cfg->dtype != SPEC_DTYPE_BF16) return bad("dtype");
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (cfg->n_kv_heads <= 0 || cfg->n_heads % cfg->n_kv_heads) return bad("heads");
-  if (cfg->d_model % 32 || cfg->ffn_dim % 32) return bad("d_model and ffn_dim must be multiples of 32");
+  if (cfg->d_model % 32) return bad("d_model must be a multiple of 32");
+  if (cfg->ffn_dim % 64) return bad("ffn_dim must be a multiple of 64");
   if (cfg->vocab % 16 || cfg->vocab <= 0) return bad("vocab must be a multiple of 16");
   if ((cfg->n_heads * cfg->head_dim) % 32) return bad("n_heads*head_dim");
   if (cfg->page_size != 16) return bad("page_size must be 16");
@@ -223,6 +221,9 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const int qkv_n = (nq + 2 * nkv) * hd;
   const int in_n = 3 * d + 2 * S;
   auto at = [&](size_t off) -> char* { return base ? base + off : nullptr; };
+  // GEMM output rows are padded to whole workgroup column blocks
+  const int cb = gemm_cols_per_block();
+  auto npad = [&](int n) { return (n + cb - 1) / cb * cb; };
 
   // weights
   std::vector<size_t> off_l1, off_l2, off_qkv, off_o, off_in, off_out, off_gu, off_d;
@@ -230,22 +231,23 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   for (int i = 0; i < cfg.n_layers; ++i) {
     off_l1.push_back(p.take((size_t)d * 4));
     if (cfg.layer_kind[i] == SPEC_LAYER_ATTN) {
-      off_qkv.push_back(p.take((size_t)qkv_n * d * esz));
-      off_o.push_back(p.take((size_t)d * nq * hd * esz));
+      off_qkv.push_back(p.take((size_t)npad(qkv_n) * d * esz));
+      off_o.push_back(p.take((size_t)npad(d) * nq * hd * esz));
       off_in.push_back(0);
       off_out.push_back(0);
     } else {
       off_qkv.push_back(0);
       off_o.push_back(0);
-      off_in.push_back(p.take((size_t)in_n * d * esz));
-      off_out.push_back(p.take((size_t)d * d * esz));
+      off_in.push_back(p.take((size_t)npad(in_n) * d * esz));
+      off_out.push_back(p.take((size_t)npad(d) * d * esz));
     }
     off_l2.push_back(p.take((size_t)d * 4));
     off_gu.push_back(p.take((size_t)2 * F * d * esz));
-    off_d.push_back(p.take((size_t)d * F * esz));
+    off_d.push_back(p.take((size_t)npad(d) * F * esz));
   }
   const size_t o_fnorm = p.take((size_t)d * 4);
-  const size_t o_lm = p.take((size_t)V * d * esz);
+  const size_t o_lm = p.take((size_t)npad(V) * d * esz);
+  const size_t weights_end = p.cursor;
 
   // KV pool: every request reserves max_ctx tokens
   const int max_pages = (cfg.max_ctx + 15) / 16;
@@ -264,20 +266,33 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const int R = std::max(cfg.max_rows, cfg.prefill_chunk);
   const size_t scratch0 = p.cursor;
   const size_t o_h = p.take((size_t)R * d * 4);
-  // activation buffers hold two planes (bf16: hi and lo; fp32: one used)
-  const size_t o_u = p.take((size_t)R * d * esz * 2);
-  const size_t o_act = p.take((size_t)R * F * esz * 2);
-  const size_t o_ao = p.take((size_t)R * nq * hd * esz * 2);
-  const size_t o_qkv = p.take((size_t)R * qkv_n * 4);
-  const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);
-  const size_t lr_rows = std::max((size_t)n_lr * cfg.max_rows, (size_t)cfg.prefill_chunk);
-  const size_t o_lrp = p.take(n_lr ? lr_rows * in_n * 4 : 0);
-  const size_t o_lro = p.take(n_lr ? (size_t)R * d * esz * 2 : 0);
+  const size_t o_ss = p.take((size_t)R * 4);
+  const size_t o_act = p.take((size_t)R * F * 4);
+  const size_t o_ao = p.take((size_t)R * nq * hd * 4);
+  const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);  // bf16: hi and lo planes
+  const size_t o_lrs = p.take(n_lr ? (size_t)n_lr * cfg.max_rows * (2 * d + S) * 4 : 0);
+  const size_t o_lro = p.take(n_lr ? (size_t)R * d * 4 : 0);
   const size_t o_po = p.take((size_t)kMaxSplits * R * nq * hd * 4);
   const size_t o_pml = p.take((size_t)kMaxSplits * R * nq * 8);
-  const size_t o_amp = p.take((size_t)R * (V / 16) * 8);
+  const size_t o_amp = p.take((size_t)R * (npad(V) / cb) * 8);
   const size_t o_amax = p.take((size_t)R * 4);
   const size_t o_res = p.take((size_t)cfg.max_requests * (2 + 64) * 4);
+  // GEMM split partials: the largest S x N over the model's matrices, for
+  // any row count up to R (the split count depends on the rows of a launch)
+  size_t psz = 0;
+  auto need_p = [&](int K, int N) {
+    for (int m = 1; m <= std::min(R, 128); ++m)
+      psz = std::max(psz, (size_t)gemm_splits(K, npad(N), m) * npad(N));
+  };
+  need_p(d, qkv_n);
+  need_p(nq * hd, d);
+  need_p(d, 2 * F);
+  need_p(F, d);
+  if (n_lr) {
+    need_p(d, in_n);
+    need_p(d, d);
+  }
+  const size_t o_P = p.take(psz * R * 4);
   size_t scratch_bytes = p.cursor - scratch0;
   if (scratch_bytes < (size_t)kStagingBytes) p.take(kStagingBytes - scratch_bytes);
 
@@ -324,19 +339,16 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     c->max_pos = max_pos;
     c->Rmax = R;
     c->h = (float*)at(o_h);
-    c->u = at(o_u);
-    c->u_lo = at(o_u + (size_t)R * d * esz);
-    c->act = at(o_act);
-    c->act_lo = at(o_act + (size_t)R * F * esz);
-    c->attn_o = at(o_ao);
-    c->attn_o_lo = at(o_ao + (size_t)R * nq * hd * esz);
-    c->qkv = (float*)at(o_qkv);
+    c->ss = (float*)at(o_ss);
+    c->act = (float*)at(o_act);
+    c->attn_o = (float*)at(o_ao);
     c->q = at(o_q);
     c->q_lo = at(o_q + (size_t)R * nq * hd * esz);
-    c->lrproj = (float*)at(o_lrp);
-    c->lrproj_layer = (size_t)cfg.max_rows * in_n;
-    c->lr_o = at(o_lro);
-    c->lr_o_lo = n_lr ? at(o_lro + (size_t)R * d * esz) : nullptr;
+    c->lrsave = (float*)at(o_lrs);
+    c->lrsave_layer = (size_t)cfg.max_rows * (2 * d + S);
+    c->lr_o = (float*)at(o_lro);
+    c->P = (float*)at(o_P);
+    c->weights_end = weights_end;
     c->part_o = (float*)at(o_po);
     c->part_ml = (float2*)at(o_pml);
     c->am_part = (float2*)at(o_amp);
@@ -411,22 +423,37 @@ void time_end(spec_ctx* c, int cls) {
   c->events_used++;
 }
 
-GemmArgs gemm_args(const void* W, const void* X, const void* X_lo, int M, int K,
-                   int N) {
+GemmArgs gemm_args(const spec_ctx* c, const void* W, const float* X, int ldx,
+                   int M, int K, int N) {
   GemmArgs a{};
   a.W = W;
   a.X = X;
-  a.X_lo = X_lo;
+  a.ldx = ldx;
   a.M = M;
   a.K = K;
-  a.ntiles = N / 16;
+  const int cb = gemm_cols_per_block();
+  a.ntiles = (N + cb - 1) / cb * cb / 16;
+  a.ncols = N;
+  a.S = 1;
+  a.P = c->P;
+  a.P_ld = c->Rmax;
   a.bias_tok = -1;
+  a.eps = c->cfg.rms_eps;
+  a.ss_nb = 1;
+  a.ss_ld = c->Rmax;
   return a;
+}
+
+// Split GEMM into the partial buffer; returns the split count used.
+int gemm_part(spec_ctx* c, GemmArgs& g, int xm, hipError_t* err) {
+  g.S = gemm_splits(g.K, g.ntiles * 16, g.M);
+  *err = launch_gemm(c->bf16, EPI_PART, xm, g, c->stream);
+  return g.S;
 }
 
 // One forward pass over R rows already described in d_rows / d_reqs / d_anc.
 // lm_row0 / lm_rows: rows that go through the LM head (argmax into amax).
-// lr_commit_last: chain pass whose final recurrent states are committed.
+// prefill: chain pass whose final recurrent states are committed.
 int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
             const std::vector<int>& rows_per_req, bool any_tree, int lm_row0,
             int lm_rows, float* d_logits, bool prefill) {
@@ -435,26 +462,25 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   hipStream_t s = c->stream;
   const int d = c->d, hd = c->hd, nq = c->nq, nkv = c->nkv, F = c->F;
   const int G = nq / nkv;
+  hipError_t e = hipSuccess;
 
-  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, s));
+  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->ss, s));
 
   // attention split: enough workgroups for the chip, bounded partials
   int keys_max = 0, qg_max = 0, max_rows_req = 0;
   for (int r = 0; r < n_req; ++r) {
     keys_max = std::max(keys_max, keys_per_req[r]);
-    const int qg = (rows_per_req[r] * G + 63) / 64;
-    qg_max = std::max(qg_max, qg);
+    qg_max = std::max(qg_max, (rows_per_req[r] * G + 63) / 64);
     max_rows_req = std::max(max_rows_req, rows_per_req[r]);
   }
+  // attention key split: 64 keys when that keeps the split table and the
+  // grid moderate, else 128 (the most one workgroup stages in LDS)
   int split = 64;
-  while (split < 8192) {
-    const int ns = (keys_max + split - 1) / split;
+  {
     long wgs = 0;
     for (int r = 0; r < n_req; ++r)
-      wgs += (long)((rows_per_req[r] * G + 63) / 64) * nkv *
-             ((keys_per_req[r] + split - 1) / split);
-    if (ns <= kMaxSplits && (wgs <= 1024 || split >= 512)) break;
-    split *= 2;
+      wgs += (long)((rows_per_req[r] * G + 63) / 64) * nkv * ((keys_per_req[r] + 63) / 64);
+    if ((keys_max + 63) / 64 > kMaxSplits || wgs > 4096) split = 128;
   }
   AttnArgs aa{};
   aa.q = c->q;
@@ -478,65 +504,73 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   if (aa.max_splits > kMaxSplits)
     return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
 
+  auto normed = [&](GemmArgs& g, const float* w) {
+    g.ss = c->ss;
+    g.nw = w;
+  };
   for (int li = 0; li < cfg.n_layers; ++li) {
     const Layer& L = c->layers[li];
-    HIP_TRY(launch_rmsnorm(bf, c->h, L.n1, R, d, cfg.rms_eps, c->u, c->u_lo, s));
     if (L.kind == SPEC_LAYER_ATTN) {
-      GemmArgs g = gemm_args(L.wqkv, c->u, c->u_lo, R, d, c->qkv_n);
-      g.Y = c->qkv;
-      g.ldy = c->qkv_n;
-      HIP_TRY(launch_gemm(bf, EPI_STORE, g, 1, s));
+      GemmArgs g = gemm_args(c, L.wqkv, c->h, d, R, d, c->qkv_n);
+      normed(g, L.n1);
+      const int S = gemm_part(c, g, XM_NORM, &e);
+      HIP_TRY(e);
       char* kc = c->kpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
       char* vc = c->vpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
-      HIP_TRY(launch_rope_kv(bf, c->qkv, c->d_rows, R, nq, nkv, hd, c->cos_t,
-                             c->sin_t, c->q, c->q_lo, kc, vc, s));
+      const int ld = g.ntiles * 16;
+      HIP_TRY(launch_rope_kv(bf, c->P, S, (size_t)c->Rmax * ld, c->d_rows, R, nq, nkv, hd,
+                             c->cos_t, c->sin_t, c->q, c->q_lo, kc, vc, ld, s));
       aa.kc = kc;
       aa.vc = vc;
       time_begin(c, 4);
       HIP_TRY(launch_attention(bf, aa, s));
       time_end(c, 4);
-      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, c->attn_o_lo, s));
-      GemmArgs o = gemm_args(L.wo, c->attn_o, c->attn_o_lo, R, nq * hd, d);
-      o.Y = c->h;
-      o.ldy = d;
-      HIP_TRY(launch_gemm(bf, EPI_RESID, o, 1, s));
+      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, s));
+      GemmArgs o = gemm_args(c, L.wo, c->attn_o, nq * hd, R, nq * hd, d);
+      const int So = gemm_part(c, o, XM_F32, &e);
+      HIP_TRY(e);
+      const int ldo = o.ntiles * 16;
+      HIP_TRY(launch_resid_reduce(c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h, c->ss, s));
     } else {
-      float* proj = c->lrproj + (prefill ? 0 : (size_t)L.idx * c->lrproj_layer);
-      GemmArgs g = gemm_args(L.win, c->u, c->u_lo, R, d, c->in_n);
-      g.Y = proj;
-      g.ldy = c->in_n;
-      HIP_TRY(launch_gemm(bf, EPI_STORE, g, 1, s));
+      GemmArgs g = gemm_args(c, L.win, c->h, d, R, d, c->in_n);
+      normed(g, L.n1);
+      const int S = gemm_part(c, g, XM_NORM, &e);
+      HIP_TRY(e);
+      const int ld = g.ntiles * 16;
       float* H = c->H + (size_t)L.idx * c->H_layer;
-      HIP_TRY(launch_lr_fork(bf, proj, c->d_rows, c->d_reqs, n_req, d, c->S, H,
-                             c->lr_o, c->lr_o_lo, any_tree, prefill, max_rows_req, s));
-      GemmArgs o = gemm_args(L.wout, c->lr_o, c->lr_o_lo, R, d, d);
-      o.Y = c->h;
-      o.ldy = d;
-      HIP_TRY(launch_gemm(bf, EPI_RESID, o, 1, s));
+      float* save = prefill ? nullptr : c->lrsave + (size_t)L.idx * c->lrsave_layer;
+      HIP_TRY(launch_lr_fork(c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
+                             n_req, d, c->S, H, c->lr_o, save, any_tree, prefill,
+                             max_rows_req, s));
+      GemmArgs o = gemm_args(c, L.wout, c->lr_o, d, R, d, d);
+      const int So = gemm_part(c, o, XM_F32, &e);
+      HIP_TRY(e);
+      const int ldo = o.ntiles * 16;
+      HIP_TRY(launch_resid_reduce(c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h, c->ss, s));
     }
-    HIP_TRY(launch_rmsnorm(bf, c->h, L.n2, R, d, cfg.rms_eps, c->u, c->u_lo, s));
-    GemmArgs gu = gemm_args(L.wgu, c->u, c->u_lo, R, d, 2 * F);
-    gu.act = c->act;
-    gu.act_lo = c->act_lo;
-    gu.ldact = F;
+    GemmArgs gu = gemm_args(c, L.wgu, c->h, d, R, d, 2 * F);
+    normed(gu, L.n2);
+    gu.Y = c->act;
+    gu.ldy = F;
     time_begin(c, 1);
-    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, 2, s));
+    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, XM_NORM, gu, s));
     time_end(c, 1);
-    GemmArgs dn = gemm_args(L.wd, c->act, c->act_lo, R, F, d);
-    dn.Y = c->h;
-    dn.ldy = d;
+    GemmArgs dn = gemm_args(c, L.wd, c->act, F, R, F, d);
     time_begin(c, 2);
-    HIP_TRY(launch_gemm(bf, EPI_RESID, dn, 1, s));
+    const int Sd = gemm_part(c, dn, XM_F32, &e);
+    HIP_TRY(e);
     time_end(c, 2);
+    const int ldd = dn.ntiles * 16;
+    HIP_TRY(launch_resid_reduce(c->P, Sd, (size_t)c->Rmax * ldd, ldd, R, d, c->h, c->ss, s));
   }
 
   // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
   if (lm_rows == 0) return SPEC_OK;
-  HIP_TRY(launch_rmsnorm(bf, c->h + (size_t)lm_row0 * d, c->final_norm, lm_rows,
-                         d, cfg.rms_eps, c->u, c->u_lo, s));
-  GemmArgs lm = gemm_args(c->lm_head, c->u, c->u_lo, lm_rows, d, c->V);
+  GemmArgs lm = gemm_args(c, c->lm_head, c->h + (size_t)lm_row0 * d, d, lm_rows, d, c->V);
+  lm.ss = c->ss + lm_row0;
+  lm.nw = c->final_norm;
   lm.part = c->am_part;
-  lm.nblocks = c->V / 16;
+  lm.nblocks = lm.ntiles * 16 / gemm_cols_per_block();
   lm.logits = d_logits;
   lm.ldlog = c->V;
   lm.rows = c->d_rows + lm_row0;
@@ -544,9 +578,9 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   lm.bias = c->fault_bias;
   lm.bias_after = c->fault_after;
   time_begin(c, 3);
-  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, 1, s));
+  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, XM_NORM, lm, s));
   time_end(c, 3);
-  HIP_TRY(launch_argmax_reduce(c->am_part, lm_rows, c->V / 16, c->amax, s));
+  HIP_TRY(launch_argmax_reduce(c->am_part, lm_rows, lm.nblocks, c->amax, s));
   return SPEC_OK;
 }
 
@@ -627,6 +661,7 @@ extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
       hipMemcpy(c->sin_t, st.data(), st.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemsetAsync(c->d_btab, 0, (size_t)cfg->max_requests * c->max_pages * 4,
                      c->stream) != hipSuccess ||
+      hipMemsetAsync(c->ws, 0, c->weights_end, c->stream) != hipSuccess ||
       (c->n_lr && hipMemsetAsync(c->H, 0, c->H_layer * 4 * c->n_lr, c->stream) != hipSuccess) ||
       hipStreamSynchronize(c->stream) != hipSuccess)
     return cleanup(SPEC_E_HIP);
@@ -902,8 +937,8 @@ extern "C" int32_t spec_commit(spec_ctx* c, int32_t n_req, const int32_t* req,
                                 c->kpool, c->vpool, c->kv_layer_elems, c->n_attn,
                                 c->nkv, c->hd, c->stream));
     if (c->n_lr)
-      HIP_TRY(launch_lr_commit(c->d_commit, n_req, c->lrproj, c->lrproj_layer,
-                               c->in_n, c->n_lr, c->d, c->S, c->H, c->H_layer,
+      HIP_TRY(launch_lr_commit(c->d_commit, n_req, c->lrsave, c->lrsave_layer,
+                               2 * c->d + c->S, c->n_lr, c->d, c->S, c->H, c->H_layer,
                                c->stream));
   }
   for (int r = 0; r < n_req; ++r) {

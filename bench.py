@@ -54,9 +54,12 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.7)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--ref-len", type=int, default=0,
                     help="tokens of the GPU AR reference run (0: enough for the steps)")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="first run one elementwise copy (dst = -src) of this many "
+                         "bytes (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is "
@@ -67,6 +70,16 @@ def main():
     import torch
     import synth
     from tree_verification_spec_amd import Engine
+
+    if args.copy_probe_bytes:
+        n = args.copy_probe_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)        # an elementwise kernel: reads n*4, writes n*4
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {4 * n} bytes")
 
     w = synth.workload("dense8b_chain")
     cfg = synth.model_config(w["model"])
@@ -152,7 +165,9 @@ def main():
         eng.release(1)
         return dict(tps=toks / tot, ms=1e3 * tot / steps, toks=toks,
                     tok_per_step=toks / steps, mism=mism,
-                    dev_ms=float(np.median(dev_ms)), lb_ms=1e3 * float(np.mean(lbs)),
+                    dev_ms=float(np.median(dev_ms)),
+                    dev_pct=[float(x) for x in np.percentile(dev_ms, [10, 50, 90])],
+                    lb_ms=1e3 * float(np.mean(lbs)),
                     bytes=float(np.mean(lbs_b)), ktime=kt)
 
     res = run(args.alpha, args.steps, args.warmup, timing_cls=1)
@@ -203,6 +218,7 @@ def main():
             "byte_lower_bound_ms": round(res["lb_ms"], 4),
             "lb_frac": round(res["lb_ms"] / res["dev_ms"], 4),
             "algorithmic_GBps": round(res["bytes"] / (res["dev_ms"] / 1e3) / 1e9, 1),
+            "device_ms_p10_p50_p90": [round(x, 4) for x in res["dev_pct"]],
             "tokens_per_step": round(res["tok_per_step"], 3),
             "forced_mismatches": res["mism"],
         },
@@ -212,13 +228,45 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "kernel": "FFN gate/up GEMM + SwiGLU (201.3 MB of weights per launch)",
                      "launches": k_n, "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
     }
     eng.close()
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_swiglu_dense8b_chain_k16_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "tree_verification_spec_amd", "csrc", f)
+                   for f in ("gemm.hip", "common.h", "kernels.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
+    None when the kernel sources changed since the counters were taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].strip().split(": ", 1)
+                    kv[k.strip("`")] = v.strip().strip("`")
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, W, n_tok):

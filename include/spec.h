@@ -70,7 +70,8 @@ typedef struct spec_config {
   int32_t layer_kind[SPEC_MAX_LAYERS]; /* SPEC_LAYER_* per layer              */
   float rms_eps, rope_theta;
   int32_t max_requests;   /* requests alive at once                          */
-  int32_t max_ctx;        /* per request: committed tokens + one tree        */
+  int32_t max_ctx;        /* per request: committed tokens + one tree;
+                             at most 8192                                    */
   int32_t max_nodes;      /* per request: rows of one verify (root + K)      */
   int32_t max_rows;       /* rows of one verify over all its requests        */
   int32_t prefill_chunk;  /* prompt rows per prefill pass                    */

@@ -18,8 +18,9 @@ linear recurrence per channel c and state index s::
     y_t[c] = sum_s H_t[c, s] C_t[s] ;  h += (y_t * silu(z_t)) W_out^T
 
 For a draft tree the state of a node comes from running the recurrence along
-its own root path ("recomputes state along each root path"; besthub.dev
-article, "(2) Best-first Tree Verification for Hybrid Architectures").
+its own root path, from the committed state, so that sibling branches never
+see each other's updates (besthub.dev article, section "(2) Best-first Tree
+Verification for Hybrid Architectures").
 
 Precision: fp32 models are fp32 throughout.  bf16 models hold bf16 weight
 values and a bf16 KV cache: k (after RoPE) and v are rounded to bf16

@@ -45,6 +45,9 @@ def test_workspace_bytes_and_config_validation():
     assert L.spec_workspace_bytes(bad) == 0
     odd = dict(tiny, head_dim=96)
     assert L.spec_workspace_bytes(make_config(odd)) == 0
+    # the attention split table covers 64 splits of 128 keys
+    assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8192)) > 0
+    assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8193)) == 0
 
 
 def test_product_path_has_no_oracle_dependency():

@@ -114,33 +114,6 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
   }
 }
 
-// --------------------------------------------------------- SwiGLU reduce
-// act[r][j] = silu(g) * u with g, u the sums of the gate/up GEMM's split
-// partials; gate and up columns are interleaved per 16: output j reads
-// column (j / 16) * 32 + j % 16 (gate) and that + 16 (up).
-__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* P, int S,
-                                                            size_t sstride, int ldp,
-                                                            int F, float* act) {
-  const int row = blockIdx.y;
-  const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (j >= F) return;
-  const int col = (j >> 4) * 32 + (j & 15);
-  const float* p = P + (size_t)row * ldp + col;
-  float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
-  for (int k = 0; k < S; ++k) {
-    const float4 gv = *reinterpret_cast<const float4*>(p + k * sstride);
-    const float4 uv = *reinterpret_cast<const float4*>(p + k * sstride + 16);
-    gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
-    us.x += uv.x; us.y += uv.y; us.z += uv.z; us.w += uv.w;
-  }
-  float4 o;
-  o.x = gs.x / (1.0f + expf(-gs.x)) * us.x;
-  o.y = gs.y / (1.0f + expf(-gs.y)) * us.y;
-  o.z = gs.z / (1.0f + expf(-gs.z)) * us.z;
-  o.w = gs.w / (1.0f + expf(-gs.w)) * us.w;
-  *reinterpret_cast<float4*>(act + (size_t)row * F + j) = o;
-}
-
 // ----------------------------------------------------------- argmax reduce
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -411,14 +384,6 @@ hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int l
 #undef RR_CASE
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_reduce(const float* P, int S, size_t split_stride, int ld_p,
-                                int R, int F, float* act, hipStream_t s) {
-  if (F % 64) return hipErrorInvalidValue;
-  dim3 grid((F / 4 + 255) / 256, R);
-  swiglu_reduce_kernel<<<grid, 256, 0, s>>>(P, S, split_stride, ld_p, F, act);
   return hipGetLastError();
 }
 

@@ -118,11 +118,6 @@ hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_strid
 hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int ld_p,
                                int R, int d, float* h, float* ss, hipStream_t s);
 
-// act = silu(gate) * up from the gate/up GEMM's split partials (gate and up
-// tiles interleaved per 16 columns).  F % 64 == 0.
-hipError_t launch_swiglu_reduce(const float* P, int S, size_t split_stride, int ld_p,
-                                int R, int F, float* act, hipStream_t s);
-
 // Per-row argmax over the column-block partials (lowest index on ties).
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
                                 int32_t* amax, hipStream_t s);

@@ -199,6 +199,7 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->max_rows < cfg->max_nodes) return bad("max_rows < max_nodes");
   if (cfg->prefill_chunk < 1 || cfg->prefill_chunk > 1024) return bad("prefill_chunk");
   if (cfg->max_ctx < cfg->max_nodes + 1) return bad("max_ctx");
+  if (cfg->max_ctx > kMaxSplits * 128) return bad("max_ctx must be <= 8192");
   bool any_lr = false;
   for (int i = 0; i < cfg->n_layers; ++i) {
     if (cfg->layer_kind[i] == SPEC_LAYER_LR) any_lr = true;

@@ -4,19 +4,20 @@
 // node of request r attends to the request's committed keys [0, n_r) and,
 // among the pass's own keys (written at slots n_r + node), to itself and its
 // ancestors.  GQA: the G = n_heads / n_kv_heads query heads that share a KV
-// head are processed together, so each K/V tile staged in LDS serves
+// head are processed together, so each K/V split staged in LDS serves
 // (rows * G) query rows.
 //
-// Workgroup = 4 wavefronts = one (request, KV head, query group of 64 query
-// rows, key split).  Each wave owns one 16-row query tile and keeps the
-// transposed flash-attention state in registers: S^T = K Q^T (so a lane holds
-// one query row's scores), an online softmax in fp32, and O^T += V^T P^T.
-// With a bf16 cache, the fp32 operands q and P enter the MFMAs as bf16
-// hi + lo pairs, so only the stored K and V are rounded.  Keys are consumed in blocks of 32
-// (two 16-token pages) staged in LDS; V pages are stored transposed
-// ([dim][16 tokens]) in the cache so that the V^T operand is read directly.
-// Each split writes un-normalised partials (O, running max, running sum),
-// merged in split order by attn_combine.
+// Workgroup = 4 wavefronts = one (request, KV head, key split, group of up
+// to 8 query tiles of 16 query rows).  The split's keys (at most 128) are
+// staged in LDS once, with every load in flight; then each wave takes query
+// tiles of the group in turn and keeps the transposed flash-attention state
+// in registers: S^T = K Q^T (so a lane holds one query row's scores), an
+// online softmax in fp32, and O^T += V^T P^T.  With a bf16 cache, the fp32
+// operands q and P enter the MFMAs as bf16 hi + lo pairs, so only the stored
+// K and V are rounded.  V pages are stored transposed ([dim][16 tokens]) in
+// the cache so that the V^T operand is read directly.  Each split writes
+// un-normalised partials (O, running max, running sum), merged in split
+// order by attn_combine.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,12 +25,16 @@ namespace {
 
 constexpr int kMaxSplitKeys = 128;  // keys of one split staged in LDS at once
 
+// LDS layout of one staged split of `split` keys: K rows [split][HD + KPAD],
+// then V^T [HD][split + VPAD] (pads keep 16-byte alignment and spread banks).
 template <typename T, int HD>
-struct alignas(16) AttnSmem {
-  static constexpr int KPAD = 16 / sizeof(T) * 1;  // one 16-byte pad per row
-  static constexpr int VPAD = 8 / sizeof(T) * 2;
-  T k[kMaxSplitKeys][HD + KPAD];
-  T v[HD][kMaxSplitKeys + VPAD];
+struct SplitLds {
+  static constexpr int KPAD = 16 / sizeof(T);
+  static constexpr int VPAD = 16 / sizeof(T);
+  static constexpr int KS = HD + KPAD;
+  __host__ __device__ static size_t bytes(int split) {
+    return ((size_t)split * KS + (size_t)HD * (split + VPAD)) * sizeof(T);
+  }
 };
 
 template <typename T>
@@ -70,67 +75,69 @@ __device__ __forceinline__ float op_round(float x, float) { return x; }
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  __shared__ AttnSmem<T, HD> sm;
+  extern __shared__ __align__(16) unsigned char attn_smem[];
+  using L = SplitLds<T, HD>;
+  T* sk = reinterpret_cast<T*>(attn_smem);      // [split][KS]
+  T* sv = sk + (size_t)a.split * L::KS;          // [HD][VS]
+  const int VS = a.split + L::VPAD;
+
   const int split = blockIdx.x, qg = blockIdx.y;
   const int req = blockIdx.z / a.nkv, kvh = blockIdx.z % a.nkv;
   const ReqMeta rm = a.reqs[req];
   const int G = a.nq / a.nkv;
   const int qrows = rm.nrows * G;
+  const int qtiles = (qrows + 15) / 16;
+  const int t_beg = qg * a.qtiles_per_wg;
+  const int t_end = min(qtiles, t_beg + a.qtiles_per_wg);
   const int total_keys = rm.nctx + rm.nrows;
   const int kbeg = split * a.split;
-  if (kbeg >= total_keys || qg * 64 >= qrows) return;  // uniform per block
+  if (kbeg >= total_keys || t_beg >= qtiles) return;  // uniform per block
   const int kend = min(total_keys, kbeg + a.split);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;
-  const int qtile = qg * 4 + wave;
-  const bool wave_active = qtile * 16 < qrows;
-  const int qr = qtile * 16 + r16;
-  const bool qvalid = wave_active && qr < qrows;
-  const int node = qvalid ? qr / G : 0;
-  const int qhead = kvh * G + (qvalid ? qr % G : 0);
-  const int grow = rm.row0 + node;
-
-  // q enters the score MFMA as hi + lo bf16 planes (bf16 KV) or as fp32
-  constexpr bool kSplit = sizeof(T) == 2;
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* qlo = reinterpret_cast<const T*>(a.q_lo);
-  Frag<T> qf[HD / 32], qfl[HD / 32];
-#pragma unroll
-  for (int ks = 0; ks < HD / 32; ++ks) {
-    const size_t off = ((size_t)grow * a.nq + qhead) * HD + ks * 32 + g * 8;
-    if (qvalid) {
-      qf[ks].load(q + off);
-      if (kSplit) qfl[ks].load(qlo + off);
-    } else {
-      qf[ks].zero();
-      qfl[ks].zero();
-    }
-  }
-  uint64_t anc_lo = 0, anc_hi = 0;
-  if (qvalid && !rm.chain) {
-    const uint64_t* am = a.anc + rm.anc0 + (size_t)node * rm.anc_words;
-    anc_lo = am[0];
-    if (rm.anc_words > 1) anc_hi = am[1];
-  }
 
   const T* kc = reinterpret_cast<const T*>(a.kc);
   const T* vc = reinterpret_cast<const T*>(a.vc);
   const int32_t* bt = a.btab + (size_t)rm.table * a.max_pages;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  floatx4_t o[HD / 16];
+  constexpr bool kSplit = sizeof(T) == 2;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* qlo = reinterpret_cast<const T*>(a.q_lo);
+  // q fragments of one query tile: hi + lo bf16 planes (bf16 KV) or fp32
+  auto load_q = [&](int qtile, Frag<T> (&qf)[HD / 32], Frag<T> (&qfl)[HD / 32]) {
+    const int qr = qtile * 16 + r16;
+    const bool qvalid = qtile < t_end && qr < qrows;
+    const int node = qvalid ? qr / G : 0;
+    const int qhead = kvh * G + (qvalid ? qr % G : 0);
+    const int grow = rm.row0 + node;
 #pragma unroll
-  for (int dt = 0; dt < HD / 16; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < HD / 32; ++ks) {
+      const size_t off = ((size_t)grow * a.nq + qhead) * HD + ks * 32 + g * 8;
+      if (qvalid) {
+        qf[ks].load(q + off);
+        if (kSplit) qfl[ks].load(qlo + off);
+      } else {
+        qf[ks].zero();
+        qfl[ks].zero();
+      }
+    }
+  };
+  // the wave's first tile is fetched before the K/V staging (its latency
+  // overlaps the staging's); each later tile is fetched during the previous
+  Frag<T> qf[HD / 32], qfl[HD / 32];
+  load_q(t_beg + wave, qf, qfl);
 
   constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
   constexpr int KCH_ROW = HD / EPC;              // chunks per K row
   constexpr int VCH_ROW = 16 / EPC;              // chunks per (dim, 16 keys)
-  // ---- stage the whole split (K rows and V^T) with every load in flight
+  // ---- stage the whole split (K rows and V^T) with every load in flight;
+  // keys are padded with zeros to a multiple of 32
   {
-    const int nkeys = kend - kbeg;                 // <= kMaxSplitKeys
+    const int nkeys = kend - kbeg;                 // <= a.split <= kMaxSplitKeys
     const int kch = ((nkeys + 31) & ~31) * KCH_ROW;
-    const int vch = HD * (((nkeys + 31) & ~31) / 16) * VCH_ROW;
+    const int vblk = ((nkeys + 31) & ~31) / 16;    // 16-key blocks per dim
+    const int vch = HD * vblk * VCH_ROW;
     constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / 256;  // per thread, each of K and V
     uint4 kr[MAXCH], vr[MAXCH];
 #pragma unroll
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
       vr[j] = make_uint4(0, 0, 0, 0);
       if (c < vch) {
-        const int dim = c / ((vch / HD)), rest = c % (vch / HD);
+        const int dim = c / (vblk * VCH_ROW), rest = c % (vblk * VCH_ROW);
         const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
         const int t0 = kbeg + blk * 16 + part * EPC;
         if (t0 < kend) {
@@ -167,108 +174,137 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const int c = threadIdx.x + j * 256;
       if (c < kch) {
         const int i = c / KCH_ROW, part = c % KCH_ROW;
-        *reinterpret_cast<uint4*>(&sm.k[i][part * EPC]) = kr[j];
+        *reinterpret_cast<uint4*>(&sk[(size_t)i * L::KS + part * EPC]) = kr[j];
       }
       if (c < vch) {
-        const int dim = c / ((vch / HD)), rest = c % (vch / HD);
+        const int dim = c / (vblk * VCH_ROW), rest = c % (vblk * VCH_ROW);
         const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
-        *reinterpret_cast<uint4*>(&sm.v[dim][blk * 16 + part * EPC]) = vr[j];
+        *reinterpret_cast<uint4*>(&sv[(size_t)dim * VS + blk * 16 + part * EPC]) = vr[j];
       }
     }
     __syncthreads();
   }
 
-  for (int kb = kbeg; kb < kend; kb += 32) {
-    if (!wave_active) break;
-    const int kl = kb - kbeg;  // key offset inside the staged split
-    // ---- scores: S^T tiles for keys [kb, kb+16) and [kb+16, kb+32)
-    floatx4_t s[2];
+  // each wave takes the group's query tiles in turn (no barriers below)
+  for (int qtile = t_beg + wave; qtile < t_end; qtile += 4) {
+    const int qr = qtile * 16 + r16;
+    const bool qvalid = qr < qrows;
+    const int node = qvalid ? qr / G : 0;
+    const int qhead = kvh * G + (qvalid ? qr % G : 0);
+    const int grow = rm.row0 + node;
+    Frag<T> qn[HD / 32], qnl[HD / 32];
+    const bool more = qtile + 4 < t_end;
+    if (more) load_q(qtile + 4, qn, qnl);
+    uint64_t anc_lo = 0, anc_hi = 0;
+    if (qvalid && !rm.chain) {
+      const uint64_t* am = a.anc + rm.anc0 + (size_t)node * rm.anc_words;
+      anc_lo = am[0];
+      if (rm.anc_words > 1) anc_hi = am[1];
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    floatx4_t o[HD / 16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < HD / 16; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = kbeg; kb < kend; kb += 32) {
+      const int kl = kb - kbeg;  // key offset inside the staged split
+      // ---- scores: S^T tiles for keys [kb, kb+16) and [kb+16, kb+32)
+      floatx4_t s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          Frag<T> kf;
+          kf.load(&sk[(size_t)(kl + kt * 16 + r16) * L::KS + ks * 32 + g * 8]);
+          mma32(s[kt], kf, qf[ks]);
+          if (kSplit) mma32(s[kt], kf, qfl[ks]);
+        }
+      }
+      // lane holds row r16, keys kb + kt*16 + 4g + r
+      float p[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = kb + kt * 16 + 4 * g + r;
+          bool ok = qvalid && t < kend;
+          if (ok && t >= rm.nctx) {
+            const int tn = t - rm.nctx;  // tree node of this key
+            if (rm.chain) ok = tn <= node;
+            else ok = (tn < 64 ? (anc_lo >> tn) : (anc_hi >> (tn - 64))) & 1ull;
+          }
+          const float v = ok ? s[kt][r] * a.scale : -INFINITY;
+          p[kt * 4 + r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // No lane may skip the MFMAs below (they read operands of all lanes),
+      // so a row with nothing visible yet uses a finite stand-in maximum:
+      // every weight is then 0 and the state stays (-inf, 0, O = 0).
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = expf(m_run - m_use);  // exp(-inf) = 0 on first block
+      float lsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = (p[e] == -INFINITY) ? 0.f : expf(p[e] - m_use);
+        lsum += p[e];
+      }
+      lsum += __shfl_xor(lsum, 16, 64);
+      lsum += __shfl_xor(lsum, 32, 64);
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) o[dt] *= alpha;
+
+      // P as an operand of the KV type; for bf16 it is carried as a hi + lo
+      // pair (two MFMAs), which keeps ~16 mantissa bits of the weights
+      Frag<T> pf, pf_lo;
+      if (kSplit) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = p[e] - op_round(p[e], T(0));
+        pack_p(pf_lo, lo);
+      }
+      pack_p(pf, p);
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        Frag<T> vf;
+        const T* vrow = sv + (size_t)(dt * 16 + r16) * VS + kl;
+        load_vfrag<T>(vf, vrow + 4 * g, vrow + 16 + 4 * g);
+        mma32(o[dt], vf, pf);
+        if (kSplit) mma32(o[dt], vf, pf_lo);
+      }
+    }
+
+    if (qvalid) {
+      const size_t slot = (size_t)split * a.rows_total * a.nq + (size_t)grow * a.nq + qhead;
+      float* po = a.part_o + slot * HD;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
+            make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
+    }
+    if (more) {
 #pragma unroll
       for (int ks = 0; ks < HD / 32; ++ks) {
-        Frag<T> kf;
-        kf.load(&sm.k[kl + kt * 16 + r16][ks * 32 + g * 8]);
-        mma32(s[kt], kf, qf[ks]);
-        if (kSplit) mma32(s[kt], kf, qfl[ks]);
+        qf[ks] = qn[ks];
+        qfl[ks] = qnl[ks];
       }
     }
-    // lane holds row r16, keys kb + kt*16 + 4g + r
-    float p[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = kb + kt * 16 + 4 * g + r;
-        bool ok = qvalid && t < kend;
-        if (ok && t >= rm.nctx) {
-          const int tn = t - rm.nctx;  // tree node of this key
-          if (rm.chain) ok = tn <= node;
-          else ok = (tn < 64 ? (anc_lo >> tn) : (anc_hi >> (tn - 64))) & 1ull;
-        }
-        const float v = ok ? s[kt][r] * a.scale : -INFINITY;
-        p[kt * 4 + r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // No lane may skip the MFMAs below (they read operands of all lanes), so
-    // a row with nothing visible yet uses a finite stand-in maximum: every
-    // weight is then 0 and the state stays (max = -inf, sum = 0, O = 0).
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = expf(m_run - m_use);  // exp(-inf) = 0 on first block
-    float lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = (p[e] == -INFINITY) ? 0.f : expf(p[e] - m_use);
-      lsum += p[e];
-    }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) o[dt] *= alpha;
-
-    // P as an operand of the KV type; for bf16 it is carried as a hi + lo
-    // pair (two MFMAs), which keeps ~16 mantissa bits of the weights
-    Frag<T> pf, pf_lo;
-    constexpr bool kSplitP = kSplit;
-    if (kSplitP) {
-      float lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lo[e] = p[e] - op_round(p[e], T(0));
-      pack_p(pf_lo, lo);
-    }
-    pack_p(pf, p);
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) {
-      Frag<T> vf;
-      load_vfrag<T>(vf, &sm.v[dt * 16 + r16][kl + 4 * g], &sm.v[dt * 16 + r16][kl + 16 + 4 * g]);
-      mma32(o[dt], vf, pf);
-      if (kSplitP) mma32(o[dt], vf, pf_lo);
-    }
-  }
-
-  if (qvalid) {
-    const size_t slot = (size_t)split * a.rows_total * a.nq + (size_t)grow * a.nq + qhead;
-    float* po = a.part_o + slot * HD;
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt)
-      *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
-          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
   }
 }
 
 // One wave per (row, query head): merge the splits of the row's request.
 // Lane s reads split s's (max, sum); the wave forms the weights, then every
 // lane accumulates its dims over the splits in split order.
-template <int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, float* out) {
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, size_t olo) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= a.rows_total * a.nq) return;
@@ -306,25 +342,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, float* ou
   const float inv = 1.0f / L;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
-    out[((size_t)grow * a.nq + qhead) * HD + lane * PER + j] = acc[j] * inv;
+    store_act(out, out + olo, ((size_t)grow * a.nq + qhead) * HD + lane * PER + j,
+              acc[j] * inv);
+}
+
+template <typename T, int HD>
+hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
+  auto k = attn_kernel<T, HD>;
+  const size_t lds = SplitLds<T, HD>::bytes(a.split);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)k,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
+  k<<<grid, 256, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
-  if (a.split > kMaxSplitKeys || a.split % 32) return hipErrorInvalidValue;
-  dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
-  if (a.hd == 128) attn_kernel<T, 128><<<grid, 256, 0, s>>>(a);
-  else if (a.hd == 64) attn_kernel<T, 64><<<grid, 256, 0, s>>>(a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.split > kMaxSplitKeys || a.split < 32 || a.split % 32 || a.qtiles_per_wg < 1)
+    return hipErrorInvalidValue;
+  if (a.hd == 128) return attn_launch<T, 128>(a, s);
+  if (a.hd == 64) return attn_launch<T, 64>(a, s);
+  return hipErrorInvalidValue;
 }
 
-hipError_t combine_any(const AttnArgs& a, float* o, hipStream_t s) {
+template <typename T>
+hipError_t combine_t(const AttnArgs& a, T* o, size_t olo, hipStream_t s) {
   if (a.max_splits > 64) return hipErrorInvalidValue;
   const int waves = a.rows_total * a.nq;
   dim3 grid((waves + 3) / 4);
-  if (a.hd == 128) attn_combine_kernel<128><<<grid, 256, 0, s>>>(a, o);
-  else if (a.hd == 64) attn_combine_kernel<64><<<grid, 256, 0, s>>>(a, o);
+  if (a.hd == 128) attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a, o, olo);
+  else if (a.hd == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a, o, olo);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -335,7 +386,8 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s) {
   return bf16 ? attn_typed<uint16_t>(a, s) : attn_typed<float>(a, s);
 }
 
-hipError_t launch_attn_combine(bool /*bf16*/, const AttnArgs& a, float* o,
+hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o, size_t o_lo,
                                hipStream_t s) {
-  return combine_any(a, o, s);
+  return bf16 ? combine_t<uint16_t>(a, (uint16_t*)o, o_lo, s)
+              : combine_t<float>(a, (float*)o, o_lo, s);
 }

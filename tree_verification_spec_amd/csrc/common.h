@@ -22,11 +22,9 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// float -> bf16, round to nearest even (inputs are finite).
+// float -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename T> struct Frag;

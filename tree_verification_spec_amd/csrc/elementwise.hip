@@ -5,25 +5,43 @@
 
 namespace {
 
+// -------------------------------------------------------------- RMSNorm
+// Block-wide sum over blockDim.x threads (a multiple of 64, <= 1024).
+__device__ __forceinline__ float block_sum(float v, float* part) {
+  v = wave_sum(v);
+  const int nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < nw; ++w) t += part[w];  // same order in every thread
+  return t;
+}
+
+// The per-row RMSNorm scale 1 / sqrt(mean(h^2) + eps).
+__device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+
 // ---------------------------------------------------------------- embedding
-// One workgroup per row: h = float(E[token]) and the row's sum of squares
-// (the input of the first RMSNorm, one column block).
+// One workgroup per row: h = float(E[token]), then u = RMSNorm(h) * nw as
+// activation planes for the first layer's input GEMM.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* emb, const RowMeta* rows,
-                                                    int d, float* h, float* ss) {
+                                                    int d, float* h, const float* nw,
+                                                    float eps, T* u, size_t ulo) {
   __shared__ float part[4];
   const int row = blockIdx.x;
   const T* e = emb + (size_t)rows[row].token * d;
+  float* hr = h + (size_t)row * d;
   float acc = 0.f;
   for (int c = threadIdx.x; c < d; c += 256) {
     const float v = to_f<T>(e[c]);
-    h[(size_t)row * d + c] = v;
+    hr[c] = v;
     acc += v * v;
   }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) ss[row] = (part[0] + part[1]) + (part[2] + part[3]);
+  const float sc = rms_scale(block_sum(acc, part), d, eps);
+  for (int c = threadIdx.x; c < d; c += 256)  // this thread's own writes
+    store_act(u, u + ulo, (size_t)row * d + c, (hr[c] * sc) * nw[c]);
 }
 
 // ------------------------------------------------------------ RoPE + KV store
@@ -79,16 +97,23 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
 
 // ------------------------------------------------------- residual reduce
 // h[r] += (sum of the S split partials of the GEMM output, in split order),
-// then the row's sum of squares for the next RMSNorm.  One workgroup of 1024
-// threads per row; all S partial loads of a thread are in flight together.
-template <int S>
+// then u = RMSNorm(h[r]) * nw as activation planes for the next GEMM.  One
+// workgroup of 1024 threads per row; all S partial loads of a thread are in
+// flight together; the row stays in registers between the two passes.
+template <int S, typename T>
 __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size_t sstride,
                                                             int ldp, int d, float* h,
-                                                            float* ss) {
+                                                            const float* nw, float eps,
+                                                            T* u, size_t ulo) {
   __shared__ float part[16];
+  constexpr int MAXQ = 4;  // float4 per thread: d <= 16384
   const int row = blockIdx.x;
+  float4 keep[MAXQ];
   float acc = 0.f;
-  for (int c = threadIdx.x * 4; c < d; c += 1024 * 4) {
+#pragma unroll
+  for (int j = 0; j < MAXQ; ++j) {
+    const int c = (threadIdx.x + j * 1024) * 4;
+    if (c >= d) break;
     float4 pv[S];
 #pragma unroll
     for (int k = 0; k < S; ++k)
@@ -103,14 +128,19 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
     }
     *reinterpret_cast<float4*>(h + (size_t)row * d + c) = v;
     acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    keep[j] = v;
   }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.f;
-    for (int w = 0; w < 16; ++w) t += part[w];
-    ss[row] = t;
+  const float sc = rms_scale(block_sum(acc, part), d, eps);
+#pragma unroll
+  for (int j = 0; j < MAXQ; ++j) {
+    const int c = (threadIdx.x + j * 1024) * 4;
+    if (c >= d) break;
+    const float4 w = *reinterpret_cast<const float4*>(nw + c);
+    const size_t i = (size_t)row * d + c;
+    store_act(u, u + ulo, i + 0, (keep[j].x * sc) * w.x);
+    store_act(u, u + ulo, i + 1, (keep[j].y * sc) * w.y);
+    store_act(u, u + ulo, i + 2, (keep[j].z * sc) * w.z);
+    store_act(u, u + ulo, i + 3, (keep[j].w * sc) * w.w);
   }
 }
 
@@ -193,7 +223,8 @@ __global__ void path_walk_kernel(const RowMeta* rows, const ReqMeta* reqs,
 template <int S, bool TREE, int NS>
 __global__ __launch_bounds__(256) void lr_fork_kernel(
     const float* proj, size_t sstride, int ld, const RowMeta* rows,
-    const ReqMeta* reqs, int d, float* H, float* o, float* save, bool commit_last) {
+    const ReqMeta* reqs, int d, float* H, void* o, size_t olo, bool obf,
+    float* save, bool commit_last) {
   extern __shared__ float hs[];  // [max_rows][256] for trees
   constexpr int CPB = 256 / S;   // channels per block
   const int r = blockIdx.y;
@@ -238,7 +269,10 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     for (int off = S / 2; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
     if (s == 0 && live) {
       const float z = pv(row, 2 * d + cc);
-      o[(size_t)row * d + cc] = y * (z / (1.0f + expf(-z)));
+      const float ov = y * (z / (1.0f + expf(-z)));
+      const size_t oi = (size_t)row * d + cc;
+      if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
+      else store_act((float*)o, (float*)o + olo, oi, ov);
       if (save) {
         save[(size_t)row * (2 * d + S) + cc] = x;
         save[(size_t)row * (2 * d + S) + d + cc] = a;
@@ -260,7 +294,7 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(
     T* vbase, size_t layer_stride, int nkv, int hd) {
   __shared__ T buf[2][64 * 128];
   const int r = blockIdx.x, layer = blockIdx.y, kvh = blockIdx.z;
-  const CommitReq q = cr[r];
+  const CommitReq& q = cr[r];  // read in place (nodes[] is indexed dynamically)
   const int32_t* bt = btab + (size_t)q.table * max_pages;
   T* kc = kbase + layer * layer_stride;
   T* vc = vbase + layer * layer_stride;
@@ -293,7 +327,7 @@ __global__ __launch_bounds__(256) void lr_commit_kernel(
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= d * S) return;
   const int c = e / S, s = e % S;
-  const CommitReq q = cr[r];
+  const CommitReq& q = cr[r];  // read in place (nodes[] is indexed dynamically)
   float* hp = H + layer * H_layer_stride + (size_t)q.table * d * S + e;
   const float* proj = proj_all + layer * proj_layer_stride;
   float h = *hp;
@@ -310,7 +344,7 @@ __global__ __launch_bounds__(256) void lr_commit_kernel(
 // ---------------------------------------------------------- weight layout
 template <typename T>
 __global__ void relayout_kernel(const T* src, int nrows, int K, T* dst,
-                                int dst_tile0, int tile_stride) {
+                                int dst_tile0, int tile_stride, int wsn, int wsk) {
   const int ksteps = K / 32;
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)(nrows / 16) * ksteps * 64;
@@ -322,7 +356,7 @@ __global__ void relayout_kernel(const T* src, int nrows, int K, T* dst,
   const int col = kb * 32 + (lane >> 4) * 8;
   const T* s = src + (size_t)row * K + col;
   const size_t dtr = (size_t)dst_tile0 + (size_t)nb * tile_stride;
-  T* d = dst + ((dtr * ksteps + kb) * 64 + lane) * 8;
+  T* d = dst + ((dtr * wsn + (size_t)kb * wsk) * 64 + lane) * 8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) d[e] = s[e];
 }
@@ -336,9 +370,14 @@ __global__ void to_f32_kernel(const T* src, int n, float* dst) {
 }  // namespace
 
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
-                        int d, float* h, float* ss, hipStream_t s) {
-  if (bf16) embed_kernel<uint16_t><<<R, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, ss);
-  else embed_kernel<float><<<R, 256, 0, s>>>((const float*)emb, rows, d, h, ss);
+                        int d, float* h, const float* nw, float eps, void* u, size_t u_lo,
+                        hipStream_t s) {
+  if (bf16)
+    embed_kernel<uint16_t><<<R, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, nw, eps,
+                                             (uint16_t*)u, u_lo);
+  else
+    embed_kernel<float><<<R, 256, 0, s>>>((const float*)emb, rows, d, h, nw, eps,
+                                          (float*)u, u_lo);
   return hipGetLastError();
 }
 
@@ -374,17 +413,31 @@ hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_strid
                        (float*)q_out, (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, s);
 }
 
-hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int ld_p,
-                               int R, int d, float* h, float* ss, hipStream_t s) {
-  if (d % 4) return hipErrorInvalidValue;
+template <typename T>
+static hipError_t resid_t(const float* P, int S, size_t split_stride, int ld_p, int R,
+                          int d, float* h, const float* nw, float eps, T* u, size_t u_lo,
+                          hipStream_t s) {
   switch (S) {
-#define RR_CASE(SV) \
-  case SV: resid_reduce_kernel<SV><<<R, 1024, 0, s>>>(P, split_stride, ld_p, d, h, ss); break;
+#define RR_CASE(SV)                                                                \
+  case SV:                                                                         \
+    resid_reduce_kernel<SV, T><<<R, 1024, 0, s>>>(P, split_stride, ld_p, d, h, nw, eps, \
+                                                  u, u_lo);                        \
+    break;
     RR_CASE(1) RR_CASE(2) RR_CASE(4) RR_CASE(8) RR_CASE(16) RR_CASE(32)
 #undef RR_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_resid_reduce(bool bf16, const float* P, int S, size_t split_stride,
+                               int ld_p, int R, int d, float* h, const float* nw,
+                               float eps, void* u, size_t u_lo, hipStream_t s) {
+  if (d % 4 || d > 16384) return hipErrorInvalidValue;
+  if (bf16)
+    return resid_t<uint16_t>(P, S, split_stride, ld_p, R, d, h, nw, eps, (uint16_t*)u,
+                             u_lo, s);
+  return resid_t<float>(P, S, split_stride, ld_p, R, d, h, nw, eps, (float*)u, u_lo, s);
 }
 
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
@@ -403,7 +456,7 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
 template <int S, int NS>
 static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                             const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                            float* H, float* o, float* save, bool tree,
+                            float* H, void* o, size_t olo, bool obf, float* save, bool tree,
                             bool commit_last, int max_rows_per_req, hipStream_t s) {
   constexpr int CPB = 256 / S;
   dim3 grid((d + CPB - 1) / CPB, n_req);
@@ -414,10 +467,10 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                                        (int)lds);
     if (e != hipSuccess) return e;
     lr_fork_kernel<S, true, NS><<<grid, 256, lds, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                       H, o, save, commit_last);
+                                                       H, o, olo, obf, save, commit_last);
   } else {
     lr_fork_kernel<S, false, NS><<<grid, 256, 0, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                      H, o, save, commit_last);
+                                                      H, o, olo, obf, save, commit_last);
   }
   return hipGetLastError();
 }
@@ -425,28 +478,29 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
 template <int S>
 static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
                              const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                             float* H, float* o, float* save, bool tree,
+                             float* H, void* o, size_t olo, bool obf, float* save, bool tree,
                              bool commit_last, int max_rows_per_req, hipStream_t s) {
   switch (NS) {
-#define NS_CASE(NV)                                                                   \
-  case NV:                                                                            \
-    return lr_fork_s<S, NV>(proj, sstride, ld, rows, reqs, n_req, d, H, o, save, tree, \
-                            commit_last, max_rows_per_req, s);
+#define NS_CASE(NV)                                                                    \
+  case NV:                                                                             \
+    return lr_fork_s<S, NV>(proj, sstride, ld, rows, reqs, n_req, d, H, o, olo, obf,    \
+                            save, tree, commit_last, max_rows_per_req, s);
     NS_CASE(1) NS_CASE(2) NS_CASE(4) NS_CASE(8) NS_CASE(16) NS_CASE(32)
 #undef NS_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_lr_fork(const float* proj, int NS, size_t split_stride, int ld,
-                          const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                          int S, float* H, float* o, float* save, bool any_tree,
-                          bool commit_last, int max_rows_per_req, hipStream_t s) {
+hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_stride,
+                          int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
+                          int d, int S, float* H, void* o, size_t o_lo, float* save,
+                          bool any_tree, bool commit_last, int max_rows_per_req,
+                          hipStream_t s) {
   switch (S) {
-#define LR_CASE(SV)                                                                   \
-  case SV:                                                                            \
-    return lr_fork_ns<SV>(NS, proj, split_stride, ld, rows, reqs, n_req, d, H, o,     \
-                          save, any_tree, commit_last, max_rows_per_req, s);
+#define LR_CASE(SV)                                                                    \
+  case SV:                                                                             \
+    return lr_fork_ns<SV>(NS, proj, split_stride, ld, rows, reqs, n_req, d, H, o, o_lo, \
+                          bf16, save, any_tree, commit_last, max_rows_per_req, s);
     LR_CASE(16)
     LR_CASE(32)
     LR_CASE(64)
@@ -483,16 +537,18 @@ hipError_t launch_lr_commit(const CommitReq* cr, int n_req,
 }
 
 hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
-                           void* dst, int dst_tile0, int tile_stride,
+                           void* dst, int dst_tile0, int tile_stride, int wsn, int wsk,
                            hipStream_t s) {
   const size_t total = (size_t)(nrows / 16) * (K / 32) * 64;
   const unsigned grid = (unsigned)((total + 255) / 256);
   if (bf16)
     relayout_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, nrows, K,
-                                                   (uint16_t*)dst, dst_tile0, tile_stride);
+                                                   (uint16_t*)dst, dst_tile0, tile_stride,
+                                                   wsn, wsk);
   else
     relayout_kernel<float><<<grid, 256, 0, s>>>((const float*)src, nrows, K,
-                                                (float*)dst, dst_tile0, tile_stride);
+                                                (float*)dst, dst_tile0, tile_stride,
+                                                wsn, wsk);
   return hipGetLastError();
 }
 

@@ -9,11 +9,10 @@
 //    of U K-steps in flight while it multiplies the current one.
 //  - The activations of the workgroup's K range are staged once per chunk
 //    in LDS, shared by all waves, so the vector-memory path carries weights
-//    only.  Activations are fp32 in HBM; for bf16 weights they are staged as
-//    hi + lo bf16 pairs (two MFMAs per product, ~16 mantissa bits) and the
-//    optional RMSNorm of the input (per-row scale from partial sums of
-//    squares written by the producer of h, times the norm weight) is applied
-//    while staging.  Rows beyond M stage zeros.
+//    only.  Activations arrive as planes of the weight type written once by
+//    their producer (for bf16 weights hi + lo bf16 planes: two MFMAs per
+//    product, ~16 mantissa bits; any RMSNorm already applied), so staging is
+//    a plain copy.  Rows beyond M stage zeros.
 //  - The K range can be split over S workgroups.  Split GEMMs (EPI_PART)
 //    write fp32 partials with plain stores and the consumer kernel adds the S
 //    partials in split order (so no workgroup of this kernel waits for or
@@ -23,6 +22,8 @@
 //    wave owns both halves of 16 outputs; S = 1), and the LM-head argmax
 //    partial (per-row max over the workgroup's columns, lowest index on ties;
 //    S = 1).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,7 +38,7 @@ template <int MT> struct ChunkK {
                              : MT <= 4 ? 128 : MT <= 5 ? 96 : 64;
 };
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int XM>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr bool kBf = sizeof(T) == 2;
@@ -55,7 +56,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   const int sk = blockIdx.x / nblk;
   const int kbeg = sk * a.KR;
   const int kend = min(a.K, kbeg + a.KR);
-  const int ksteps = a.K >> 5;
 
   // two staging buffers; each holds a bf16 hi plane then a lo plane, or fp32
   constexpr int BUF_ELEMS = TROWS * LDS_ROW * (kBf ? 2 : 1);
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   const Frag<T>* wbase[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
-    wbase[t] = Wt + ((size_t)((nb * WAVES + wave) * NTW + t) * ksteps) * 64 + lane;
+    wbase[t] = Wt + (size_t)((nb * WAVES + wave) * NTW + t) * a.wsn * 64 + lane;
+  const size_t wk = (size_t)a.wsk * 64;  // Frag stride between K-steps
 
   floatx4_t acc[NTW][MT];
 #pragma unroll
@@ -73,48 +74,34 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // per-row RMSNorm scale (XM_NORM)
-  __shared__ float rscale[TROWS];
-  if (XM == XM_NORM) {
-    for (int r = threadIdx.x; r < TROWS; r += NTHR) {
-      const int m = a.row0 + r;
-      float sc = 0.f;
-      if (m < a.M) {
-        float ss = 0.f;
-        for (int b = 0; b < a.ss_nb; ++b) ss += a.ss[(size_t)b * a.ss_ld + m];
-        sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-      }
-      rscale[r] = sc;
-    }
-    __syncthreads();
-  }
-
   // ---- activation chunk prefetch (registers) and store (LDS)
-  float4 xr[XQ];
-  float4 wr[XM == XM_NORM ? XQ : 1];
+  // one unit = 4 consecutive K values of one row: 8 bytes of each bf16
+  // plane, or 16 bytes of fp32
+  using Unit = typename std::conditional<kBf, uint2, float4>::type;
+  const T* Xh = reinterpret_cast<const T*>(a.X);
+  const T* Xl = Xh + a.xlo;
+  Unit xr[XQ], xl[kBf ? XQ : 1];
   auto fetch = [&](int kc0, int kcl) {
-    // columns kc0 .. kc0 + min(kcl, KC) of the real K range; the rest zero.
-    // (The norm weights are fetched here too, so that every load the LDS
-    // store waits for was issued before the next window of W loads.)
+    // columns kc0 .. kc0 + min(kcl, KC) of the real K range; the rest zero
     const int quads = kcl <= 0 ? 0 : (kcl >= KC ? QUADS : kcl >> 2);
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const int e = threadIdx.x + q * NTHR;
       const int r = e / QUADS, c = (e % QUADS) * 4;
       const int m = a.row0 + r;
-      xr[q] = make_float4(0.f, 0.f, 0.f, 0.f);
       const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
-      if (in) xr[q] = *reinterpret_cast<const float4*>(a.X + (size_t)m * a.ldx + kc0 + c);
-      if constexpr (XM == XM_NORM) {
-        wr[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (in) wr[q] = *reinterpret_cast<const float4*>(a.nw + kc0 + c);
+      const size_t off = (size_t)m * a.ldx + kc0 + c;
+      if constexpr (kBf) {
+        xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
+        xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+      } else {
+        xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
-  auto store = [&](int buf, int kc0, int kcl) {
+  auto store = [&](int buf) {
     // all KC columns are written (fetch zeroed those past the real range)
-    (void)kc0;
-    (void)kcl;
     T* hi = xbuf + buf * BUF_ELEMS;
     T* lo = hi + TROWS * LDS_ROW;
 #pragma unroll
@@ -122,32 +109,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       const int e = threadIdx.x + q * NTHR;
       const int r = e / QUADS, c = (e % QUADS) * 4;
       if (r >= TROWS) continue;
-      float4 v = xr[q];
-      if constexpr (XM == XM_NORM) {
-        const float sc = rscale[r];
-        const float4 w = wr[q];  // zero outside the real range
-        v.x = (v.x * sc) * w.x;
-        v.y = (v.y * sc) * w.y;
-        v.z = (v.z * sc) * w.z;
-        v.w = (v.w * sc) * w.w;
-      }
-      if constexpr (kBf) {
-        const uint16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
-        const uint16_t l0 = f2bf(v.x - bf2f(h0)), l1 = f2bf(v.y - bf2f(h1));
-        const uint16_t l2 = f2bf(v.z - bf2f(h2)), l3 = f2bf(v.w - bf2f(h3));
-        *reinterpret_cast<uint2*>(&hi[r * LDS_ROW + c]) =
-            make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16));
-        *reinterpret_cast<uint2*>(&lo[r * LDS_ROW + c]) =
-            make_uint2(l0 | ((uint32_t)l1 << 16), l2 | ((uint32_t)l3 << 16));
-      } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(hi) + r * LDS_ROW + c) = v;
-      }
+      *reinterpret_cast<Unit*>(&hi[r * LDS_ROW + c]) = xr[q];
+      if constexpr (kBf) *reinterpret_cast<Unit*>(&lo[r * LDS_ROW + c]) = xl[q];
     }
   };
 
   const int kb_beg = kbeg >> 5, kb_end = kend >> 5;
   constexpr int CSTEPS = KC / 32;              // K-steps per staged chunk
-  constexpr int CPW = (kD + CSTEPS - 1) / CSTEPS;  // chunks per window
+  constexpr int CPW = (D + CSTEPS - 1) / CSTEPS;  // chunks per window
   constexpr int WIN = CPW * CSTEPS;            // K-steps of W loads in flight
   // Rolling window: slot u holds the W tiles of K-step (window start + u);
   // right after a slot is consumed it is reloaded with the step WIN ahead.
@@ -160,7 +129,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   auto load_step = [&](Frag<T> (&dst)[NTW], int kb) {
     const int k = kb < kb_end ? kb : kb_end - 1;
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) dst[t] = wbase[t][(size_t)k * 64];
+    for (int t = 0; t < NTW; ++t) dst[t] = wbase[t][(size_t)k * wk];
   };
   // the first chunk is fetched now (before the W window, as in the steady
   // state); each chunk is stored into LDS at its start and the next one is
@@ -174,7 +143,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
       const int k0 = (kw + cc * CSTEPS) * 32;  // first K index of this chunk
-      store(buf, k0, kend - k0);
+      store(buf);
       fetch(k0 + KC, kend - k0 - KC);
       __syncthreads();
       const T* hi = xbuf + buf * BUF_ELEMS;
@@ -248,7 +217,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       const int p = j >> 4, c = j & 15;
       const float gv = tile[row * LDT + p * 32 + c];
       const float uv = tile[row * LDT + p * 32 + 16 + c];
-      a.Y[(size_t)m * a.ldy + nb * OUTS + j] = gv / (1.0f + expf(-gv)) * uv;
+      T* Yh = reinterpret_cast<T*>(a.Y);
+      store_act(Yh, Yh + a.ylo, (size_t)m * a.ldy + nb * OUTS + j,
+                gv / (1.0f + expf(-gv)) * uv);
     }
     return;
   }
@@ -278,9 +249,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int XM>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, XM>;
+  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D>;
   constexpr int KC = ChunkK<MT>::value;
   const size_t stage_b = 2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * 4;
   const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
@@ -299,27 +270,23 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
 constexpr int kWaves = 8;  // waves per workgroup, one 16-column tile each
 constexpr int kNtw = 1;
 
-template <typename T, int EPI, int XM>
+template <typename T, int EPI>
 hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_one<T, 1, kNtw, kWaves, EPI, XM>(a, s);
-    case 2: return launch_one<T, 2, kNtw, kWaves, EPI, XM>(a, s);
-    case 3: return launch_one<T, 3, kNtw, kWaves, EPI, XM>(a, s);
-    case 4: return launch_one<T, 4, kNtw, kWaves, EPI, XM>(a, s);
-    case 5: return launch_one<T, 5, kNtw, kWaves, EPI, XM>(a, s);
-    default: return launch_one<T, 8, kNtw, kWaves, EPI, XM>(a, s);
+    case 1: return launch_one<T, 1, kNtw, kWaves, EPI>(a, s);
+    case 2: return launch_one<T, 2, kNtw, kWaves, EPI>(a, s);
+    case 3: return launch_one<T, 3, kNtw, kWaves, EPI>(a, s);
+    case 4: return launch_one<T, 4, kNtw, kWaves, EPI>(a, s);
+    case 5: return launch_one<T, 5, kNtw, kWaves, EPI>(a, s);
+    default: return launch_one<T, 8, kNtw, kWaves, EPI>(a, s);
   }
 }
 
 template <typename T>
-hipError_t launch_typed(int epi, int xm, const GemmArgs& a, int mt, hipStream_t s) {
-#define GEMM_CASE(E, X)                                                    \
-  if (epi == E && xm == X) return launch_mt<T, E, X>(mt, a, s);
-  GEMM_CASE(EPI_PART, XM_F32)
-  GEMM_CASE(EPI_PART, XM_NORM)
-  GEMM_CASE(EPI_SWIGLU, XM_NORM)
-  GEMM_CASE(EPI_ARGMAX, XM_NORM)
-#undef GEMM_CASE
+hipError_t launch_typed(int epi, const GemmArgs& a, int mt, hipStream_t s) {
+  if (epi == EPI_PART) return launch_mt<T, EPI_PART>(mt, a, s);
+  if (epi == EPI_SWIGLU) return launch_mt<T, EPI_SWIGLU>(mt, a, s);
+  if (epi == EPI_ARGMAX) return launch_mt<T, EPI_ARGMAX>(mt, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -337,19 +304,20 @@ int gemm_splits(int K, int N, int M) {
   return S;
 }
 
-hipError_t launch_gemm(bool bf16, int epi, int xm, const GemmArgs& a0, hipStream_t s) {
+hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
   if (a0.M <= 0) return hipSuccess;
   GemmArgs a = a0;
   if (a.S < 1 || (epi != EPI_PART && a.S != 1) || a.K % a.S || (a.K / a.S) % 32)
     return hipErrorInvalidValue;
   a.KR = a.K / a.S;
+  if (a.wsn <= 0 || a.wsk <= 0) return hipErrorInvalidValue;
   for (int r0 = 0; r0 < a.M; r0 += 128) {
     const int rows = (a.M - r0 < 128) ? a.M - r0 : 128;
     const int need = (rows + 15) / 16;
     const int mt = need <= 5 ? need : 8;
     a.row0 = r0;
-    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, xm, a, mt, s)
-                        : launch_typed<float>(epi, xm, a, mt, s);
+    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, a, mt, s)
+                        : launch_typed<float>(epi, a, mt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

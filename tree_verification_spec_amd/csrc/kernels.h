@@ -29,24 +29,26 @@ struct ReqMeta {
 };
 
 // Tiled weight layout: a matrix [N, K] is stored as 16 x 32 tiles, tile
-// (nb, kb) at element offset (nb * (K / 32) + kb) * 512, lane l of the tile
-// holding W[nb * 16 + l % 16][kb * 32 + (l / 16) * 8 + e] at l * 8 + e.
+// (nb, kb) at element offset (nb * wsn + kb * wsk) * 512 (wsn, wsk: the
+// matrix's tile strides, N-major or K-major), lane l of the tile holding
+// W[nb * 16 + l % 16][kb * 32 + (l / 16) * 8 + e] at l * 8 + e.
+
+// Activations that feed a GEMM are stored once, by the kernel that produces
+// them, as "activation planes" of the weight type: for bf16 weights two bf16
+// planes hi = bf16(v) and lo = bf16(v - hi) (lo at a fixed element offset
+// from hi), so a bf16 MFMA pair sees ~16 mantissa bits of the fp32 value;
+// for fp32 weights one fp32 plane.  RMSNorm is applied by the producer.
 
 // EPI_PART: fp32 partial sums of split s at P[s][row][col] (any S); the
 // consumer adds the S partials in order.  EPI_SWIGLU / EPI_ARGMAX need S = 1.
 enum GemmEpi { EPI_PART = 0, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
-enum GemmXMode { XM_F32 = 0, XM_NORM = 1 };
 
 struct GemmArgs {
   const void* W;        // tiled weights (bf16 bits or fp32), ntiles x 16 rows
-  const float* X;       // fp32 activations [M, ldx] (XM_NORM: the residual h)
+  int32_t wsn, wsk;     // tile strides of W between tile rows and between K-steps
+  const void* X;        // activation planes [M, ldx] (hi; lo at X + xlo)
   int32_t ldx;
-  // XM_NORM: RMSNorm of X applied while staging: scale of row m is
-  // 1 / sqrt(sum_b ss[b * ss_ld + m] / K + eps), then times nw[k]
-  const float* ss;
-  int32_t ss_nb, ss_ld;
-  const float* nw;
-  float eps;
+  int64_t xlo;
   int32_t M, K;         // rows, reduction length
   int32_t ntiles;       // 16-column tiles of W (a multiple of 8)
   int32_t ncols;        // real output columns (<= ntiles * 16)
@@ -55,8 +57,9 @@ struct GemmArgs {
   int32_t KR;           // K per split (set by launch_gemm)
   float* P;             // EPI_PART: partials [S][P_ld][ntiles * 16]
   int32_t P_ld;
-  float* Y;             // SWIGLU: act (fp32) [M, ldy]
+  void* Y;              // SWIGLU: activation planes [M, ldy] (lo at Y + ylo)
   int32_t ldy;
+  int64_t ylo;
   float2* part;         // ARGMAX: per (row, column block) (max, index bits)
   int32_t nblocks;      // ARGMAX: column blocks per row
   float* logits;        // ARGMAX: optional fp32 logits [M, ldlog]
@@ -73,8 +76,7 @@ int gemm_splits(int K, int N, int M);
 
 // Launch the skinny GEMM for rows [0, M): picks the tile shape and splits
 // rows into chunks when M exceeds one launch's row capacity.
-hipError_t launch_gemm(bool bf16, int epi, int xm, const GemmArgs& a,
-                       hipStream_t s);
+hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const void* q;            // [rows, nq, hd] (bf16 bits or fp32), after RoPE
@@ -89,7 +91,8 @@ struct AttnArgs {
   float* part_o;            // [split][rows * nq][hd]
   float2* part_ml;          // [split][rows * nq] (running max, sum)
   int32_t nq, nkv, hd;
-  int32_t split;            // keys per split (multiple of 32)
+  int32_t split;            // keys per split (multiple of 32, <= 128)
+  int32_t qtiles_per_wg;    // 16-row query tiles per workgroup (a query group)
   int32_t max_splits, max_qgroups, n_req;
   int32_t rows_total;
   float scale;
@@ -97,13 +100,16 @@ struct AttnArgs {
 
 hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s);
 
-// Merge the per-split partials into the fp32 attention output o[rows, nq*hd].
-hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, float* o,
+// Merge the per-split partials into the attention output, written as
+// activation planes o[rows, nq*hd] (lo plane at o + o_lo elements).
+hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o, size_t o_lo,
                                hipStream_t s);
 
-// h[r] = E[token_r] in fp32, and ss[r] = sum(h[r]^2) (one column block).
+// h[r] = E[token_r] in fp32, and u[r] = RMSNorm(h[r]) * nw as activation
+// planes (lo plane at u + u_lo elements).
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows,
-                        int R, int d, float* h, float* ss, hipStream_t s);
+                        int R, int d, float* h, const float* nw, float eps,
+                        void* u, size_t u_lo, hipStream_t s);
 
 // q -> RoPE -> q_out; k -> RoPE -> K cache; v -> V cache, at each row's slot.
 // qkv = sum of the S GEMM partials qkv[s * split_stride + row * ld_qkv + c].
@@ -113,10 +119,11 @@ hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_strid
                           void* q_lo, void* kc, void* vc, int ld_qkv, hipStream_t s);
 
 // h[r] += sum_s P[s * split_stride + r * ld_p + c] (c < d), then
-// ss[r] = sum(h[r]^2): the residual add of a split GEMM and the input of the
-// next RMSNorm.  One workgroup per row.
-hipError_t launch_resid_reduce(const float* P, int S, size_t split_stride, int ld_p,
-                               int R, int d, float* h, float* ss, hipStream_t s);
+// u[r] = RMSNorm(h[r]) * nw as activation planes: the residual add of a split
+// GEMM and the input of the next GEMM.  One workgroup per row.
+hipError_t launch_resid_reduce(bool bf16, const float* P, int S, size_t split_stride,
+                               int ld_p, int R, int d, float* h, const float* nw,
+                               float eps, void* u, size_t u_lo, hipStream_t s);
 
 // Per-row argmax over the column-block partials (lowest index on ties).
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
@@ -131,13 +138,15 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
 // Gated diagonal recurrence over the pass's nodes for one recurrent layer.
 // proj: in_proj output as S split partials (stride split_stride floats), each
 // [R, ld] = [x | a | z | B | C | pad]; H: committed states
-// [max_requests][d][S]; o: [R, d] fp32.  save (or NULL): per row [x | a | B]
-// ([R, 2d + S]) for the commit.  With commit_last (chain passes only) the
-// state of each request's last row is written back to H.
-hipError_t launch_lr_fork(const float* proj, int NS, size_t split_stride, int ld,
-                          const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                          int S, float* H, float* o, float* save, bool any_tree,
-                          bool commit_last, int max_rows_per_req, hipStream_t s);
+// [max_requests][d][S]; o: [R, d] activation planes (lo at o + o_lo).
+// save (or NULL): per row [x | a | B] ([R, 2d + S]) for the commit.  With
+// commit_last (chain passes only) the state of each request's last row is
+// written back to H.
+hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_stride,
+                          int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
+                          int d, int S, float* H, void* o, size_t o_lo, float* save,
+                          bool any_tree, bool commit_last, int max_rows_per_req,
+                          hipStream_t s);
 
 struct CommitReq {
   int32_t table;     // request id
@@ -163,9 +172,11 @@ hipError_t launch_lr_commit(const CommitReq* cr, int n_req,
                             size_t H_layer_stride, hipStream_t s);
 
 // Copy a row-major [nrows, K] slab into the tiled layout.  Source rows
-// [0, nrows) become destination tile rows dst_tile0 + t * tile_stride.
+// [0, nrows) become destination tile rows dst_tile0 + t * tile_stride; tile
+// (row tr, K-step kb) of the destination starts at tile index
+// tr * wsn + kb * wsk.
 hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
-                           void* dst, int dst_tile0, int tile_stride,
+                           void* dst, int dst_tile0, int tile_stride, int wsn, int wsk,
                            hipStream_t s);
 
 // Widen a norm vector (bf16 bits or fp32) to fp32.

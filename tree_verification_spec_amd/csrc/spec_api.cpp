@@ -30,6 +30,11 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxSplits = 64;  // attention key splits (one combine lane each)
+// tile order of the input projections (QKV, in_proj) and of the matrices
+// whose output is added to the residual (O, out_proj, down); gate/up and the
+// LM head are always K-major
+constexpr bool kKmajorQkv = true;
+constexpr bool kKmajorOut = false;
 constexpr int kStagingBytes = 64 << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -61,7 +66,22 @@ struct TensorSlot {
   int rows, cols;
   void* dst;
   int tile0, tile_stride;
+  int wsn = 0, wsk = 0;  // matrices: tile strides of the destination layout
 };
+
+// Tile order of a weight matrix [N, K] (N padded to whole workgroup column
+// blocks).  K-major (the tiles of one K-step of every tile row adjacent):
+// all workgroups of an unsplit GEMM sweep one contiguous region together,
+// which streams best; used for the matrices whose GEMM runs with few or no
+// K splits.  N-major (a tile row's K-steps adjacent) for the rest.
+struct TileOrder {
+  int wsn, wsk;
+};
+TileOrder tile_order(int N, int K, bool kmajor) {
+  const int cb = gemm_cols_per_block();
+  const int nt = (N + cb - 1) / cb * cb / 16;
+  return kmajor ? TileOrder{1, nt} : TileOrder{K / 32, 1};
+}
 
 struct Plan {
   size_t total = 0;
@@ -117,16 +137,18 @@ struct spec_ctx {
   // scratch
   int Rmax = 0;
   float* h = nullptr;
-  float* ss = nullptr;       // per row sum of squares of h (RMSNorm input)
-  float* act = nullptr;
-  float* attn_o = nullptr;
+  // activation planes [Rmax, width] feeding the GEMMs (bf16: hi plane then
+  // lo plane, lo at + Rmax * width elements; fp32: one plane)
+  void* u = nullptr;         // RMSNorm output (QKV / in_proj / gate-up / LM head input)
+  void* act = nullptr;       // SwiGLU output (down input)
+  void* attn_o = nullptr;    // attention output (O input)
   void* q = nullptr;
   void* q_lo = nullptr;
   float* P = nullptr;        // GEMM split partials [S][Rmax][N]
   float* lrsave = nullptr;   // per recurrent layer [max_rows][x | a | B]
   size_t lrsave_layer = 0;
   size_t weights_end = 0;
-  float* lr_o = nullptr;
+  void* lr_o = nullptr;      // recurrent mixer output (out_proj input)
   float* part_o = nullptr;
   float2* part_ml = nullptr;
   float2* am_part = nullptr;
@@ -267,7 +289,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const int R = std::max(cfg.max_rows, cfg.prefill_chunk);
   const size_t scratch0 = p.cursor;
   const size_t o_h = p.take((size_t)R * d * 4);
-  const size_t o_ss = p.take((size_t)R * 4);
+  const size_t o_u = p.take((size_t)R * d * 4);
   const size_t o_act = p.take((size_t)R * F * 4);
   const size_t o_ao = p.take((size_t)R * nq * hd * 4);
   const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);  // bf16: hi and lo planes
@@ -340,14 +362,14 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     c->max_pos = max_pos;
     c->Rmax = R;
     c->h = (float*)at(o_h);
-    c->ss = (float*)at(o_ss);
-    c->act = (float*)at(o_act);
-    c->attn_o = (float*)at(o_ao);
+    c->u = at(o_u);
+    c->act = at(o_act);
+    c->attn_o = at(o_ao);
     c->q = at(o_q);
     c->q_lo = at(o_q + (size_t)R * nq * hd * esz);
     c->lrsave = (float*)at(o_lrs);
     c->lrsave_layer = (size_t)cfg.max_rows * (2 * d + S);
-    c->lr_o = (float*)at(o_lro);
+    c->lr_o = at(o_lro);
     c->P = (float*)at(o_P);
     c->weights_end = weights_end;
     c->part_o = (float*)at(o_po);
@@ -370,28 +392,36 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
 
 void build_slots(spec_ctx* c) {
   const spec_config& cfg = c->cfg;
-  const int d = c->d, hd = c->hd;
+  const int d = c->d, hd = c->hd, F = c->F;
   c->slots.clear();
+  auto mat = [&](int layer, int rows, int cols, void* dst, int tile0, int tstride, int N,
+                 bool kmajor) {
+    const TileOrder o = tile_order(N, cols, kmajor);
+    TensorSlot t{2, layer, rows, cols, dst, tile0, tstride};
+    t.wsn = o.wsn;
+    t.wsk = o.wsk;
+    c->slots.push_back(t);
+  };
   c->slots.push_back({0, -1, c->V, d, c->embed, 0, 1});
   for (int i = 0; i < cfg.n_layers; ++i) {
     Layer& L = c->layers[i];
     c->slots.push_back({1, i, d, 1, L.n1, 0, 1});
     if (L.kind == SPEC_LAYER_ATTN) {
-      c->slots.push_back({2, i, c->nq * hd, d, L.wqkv, 0, 1});
-      c->slots.push_back({2, i, c->nkv * hd, d, L.wqkv, c->nq * hd / 16, 1});
-      c->slots.push_back({2, i, c->nkv * hd, d, L.wqkv, (c->nq + c->nkv) * hd / 16, 1});
-      c->slots.push_back({2, i, d, c->nq * hd, L.wo, 0, 1});
+      mat(i, c->nq * hd, d, L.wqkv, 0, 1, c->qkv_n, kKmajorQkv);
+      mat(i, c->nkv * hd, d, L.wqkv, c->nq * hd / 16, 1, c->qkv_n, kKmajorQkv);
+      mat(i, c->nkv * hd, d, L.wqkv, (c->nq + c->nkv) * hd / 16, 1, c->qkv_n, kKmajorQkv);
+      mat(i, d, c->nq * hd, L.wo, 0, 1, d, kKmajorOut);
     } else {
-      c->slots.push_back({2, i, c->in_n, d, L.win, 0, 1});
-      c->slots.push_back({2, i, d, d, L.wout, 0, 1});
+      mat(i, c->in_n, d, L.win, 0, 1, c->in_n, kKmajorQkv);
+      mat(i, d, d, L.wout, 0, 1, d, kKmajorOut);
     }
     c->slots.push_back({1, i, d, 1, L.n2, 0, 1});
-    c->slots.push_back({2, i, c->F, d, L.wgu, 0, 2});   // gate -> even tiles
-    c->slots.push_back({2, i, c->F, d, L.wgu, 1, 2});   // up   -> odd tiles
-    c->slots.push_back({2, i, d, c->F, L.wd, 0, 1});
+    mat(i, F, d, L.wgu, 0, 2, 2 * F, true);   // gate -> even tiles
+    mat(i, F, d, L.wgu, 1, 2, 2 * F, true);   // up   -> odd tiles
+    mat(i, d, F, L.wd, 0, 1, d, kKmajorOut);
   }
   c->slots.push_back({1, -1, d, 1, c->final_norm, 0, 1});
-  c->slots.push_back({2, -1, c->V, d, c->lm_head, 0, 1});
+  mat(-1, c->V, d, c->lm_head, 0, 1, c->V, true);
   c->loaded.assign(c->slots.size(), 0);
 }
 
@@ -424,12 +454,21 @@ void time_end(spec_ctx* c, int cls) {
   c->events_used++;
 }
 
-GemmArgs gemm_args(const spec_ctx* c, const void* W, const float* X, int ldx,
-                   int M, int K, int N) {
+// Element offset of the lo plane of an activation buffer of `width` columns.
+size_t lo_off(const spec_ctx* c, int width) {
+  return c->bf16 ? (size_t)c->Rmax * width : 0;
+}
+
+GemmArgs gemm_args(const spec_ctx* c, const void* W, bool kmajor, const void* X,
+                   int ldx, int M, int K, int N) {
   GemmArgs a{};
   a.W = W;
+  const TileOrder o = tile_order(N, K, kmajor);
+  a.wsn = o.wsn;
+  a.wsk = o.wsk;
   a.X = X;
   a.ldx = ldx;
+  a.xlo = (int64_t)lo_off(c, ldx);
   a.M = M;
   a.K = K;
   const int cb = gemm_cols_per_block();
@@ -439,16 +478,13 @@ GemmArgs gemm_args(const spec_ctx* c, const void* W, const float* X, int ldx,
   a.P = c->P;
   a.P_ld = c->Rmax;
   a.bias_tok = -1;
-  a.eps = c->cfg.rms_eps;
-  a.ss_nb = 1;
-  a.ss_ld = c->Rmax;
   return a;
 }
 
 // Split GEMM into the partial buffer; returns the split count used.
-int gemm_part(spec_ctx* c, GemmArgs& g, int xm, hipError_t* err) {
+int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err) {
   g.S = gemm_splits(g.K, g.ntiles * 16, g.M);
-  *err = launch_gemm(c->bf16, EPI_PART, xm, g, c->stream);
+  *err = launch_gemm(c->bf16, EPI_PART, g, c->stream);
   return g.S;
 }
 
@@ -465,22 +501,29 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   const int G = nq / nkv;
   hipError_t e = hipSuccess;
 
-  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->ss, s));
+  const float eps = cfg.rms_eps;
+  const size_t u_lo = lo_off(c, d);
+  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, eps, c->u,
+                       u_lo, s));
 
-  // attention split: enough workgroups for the chip, bounded partials
-  int keys_max = 0, qg_max = 0, max_rows_req = 0;
+  // attention launch shape: a workgroup stages one key split of one
+  // (request, KV head) and serves a group of up to 8 query tiles (16 query
+  // rows each) of it; splits of 64 keys when that keeps the split table and
+  // the grid moderate, else 128 (the most one workgroup stages in LDS)
+  int keys_max = 0, qt_max = 0, max_rows_req = 0;
   for (int r = 0; r < n_req; ++r) {
     keys_max = std::max(keys_max, keys_per_req[r]);
-    qg_max = std::max(qg_max, (rows_per_req[r] * G + 63) / 64);
+    qt_max = std::max(qt_max, (rows_per_req[r] * G + 15) / 16);
     max_rows_req = std::max(max_rows_req, rows_per_req[r]);
   }
-  // attention key split: 64 keys when that keeps the split table and the
-  // grid moderate, else 128 (the most one workgroup stages in LDS)
+  const int q_groups = (qt_max + 7) / 8;
+  const int tpw = (qt_max + q_groups - 1) / q_groups;
   int split = 64;
   {
     long wgs = 0;
     for (int r = 0; r < n_req; ++r)
-      wgs += (long)((rows_per_req[r] * G + 63) / 64) * nkv * ((keys_per_req[r] + 63) / 64);
+      wgs += (long)(((rows_per_req[r] * G + 15) / 16 + tpw - 1) / tpw) * nkv *
+             ((keys_per_req[r] + 63) / 64);
     if ((keys_max + 63) / 64 > kMaxSplits || wgs > 4096) split = 128;
   }
   AttnArgs aa{};
@@ -498,23 +541,22 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   aa.hd = hd;
   aa.split = split;
   aa.max_splits = (keys_max + split - 1) / split;
-  aa.max_qgroups = qg_max;
+  aa.qtiles_per_wg = tpw;
+  aa.max_qgroups = (qt_max + tpw - 1) / tpw;
   aa.n_req = n_req;
   aa.rows_total = R;
   aa.scale = 1.0f / std::sqrt((float)hd);
   if (aa.max_splits > kMaxSplits)
     return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
 
-  auto normed = [&](GemmArgs& g, const float* w) {
-    g.ss = c->ss;
-    g.nw = w;
-  };
   for (int li = 0; li < cfg.n_layers; ++li) {
     const Layer& L = c->layers[li];
+    // the norm applied after this layer's down GEMM: the next layer's input
+    // norm, or the final norm in front of the LM head
+    const float* next_norm = li + 1 < cfg.n_layers ? c->layers[li + 1].n1 : c->final_norm;
     if (L.kind == SPEC_LAYER_ATTN) {
-      GemmArgs g = gemm_args(c, L.wqkv, c->h, d, R, d, c->qkv_n);
-      normed(g, L.n1);
-      const int S = gemm_part(c, g, XM_NORM, &e);
+      GemmArgs g = gemm_args(c, L.wqkv, kKmajorQkv, c->u, d, R, d, c->qkv_n);
+      const int S = gemm_part(c, g, &e);
       HIP_TRY(e);
       char* kc = c->kpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
       char* vc = c->vpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
@@ -526,50 +568,52 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
       time_begin(c, 4);
       HIP_TRY(launch_attention(bf, aa, s));
       time_end(c, 4);
-      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, s));
-      GemmArgs o = gemm_args(c, L.wo, c->attn_o, nq * hd, R, nq * hd, d);
-      const int So = gemm_part(c, o, XM_F32, &e);
+      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, lo_off(c, nq * hd), s));
+      GemmArgs o = gemm_args(c, L.wo, kKmajorOut, c->attn_o, nq * hd, R, nq * hd, d);
+      const int So = gemm_part(c, o, &e);
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
-      HIP_TRY(launch_resid_reduce(c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h, c->ss, s));
+      HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
+                                  L.n2, eps, c->u, u_lo, s));
     } else {
-      GemmArgs g = gemm_args(c, L.win, c->h, d, R, d, c->in_n);
-      normed(g, L.n1);
-      const int S = gemm_part(c, g, XM_NORM, &e);
+      GemmArgs g = gemm_args(c, L.win, kKmajorQkv, c->u, d, R, d, c->in_n);
+      const int S = gemm_part(c, g, &e);
       HIP_TRY(e);
       const int ld = g.ntiles * 16;
       float* H = c->H + (size_t)L.idx * c->H_layer;
       float* save = prefill ? nullptr : c->lrsave + (size_t)L.idx * c->lrsave_layer;
-      HIP_TRY(launch_lr_fork(c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
-                             n_req, d, c->S, H, c->lr_o, save, any_tree, prefill,
-                             max_rows_req, s));
-      GemmArgs o = gemm_args(c, L.wout, c->lr_o, d, R, d, d);
-      const int So = gemm_part(c, o, XM_F32, &e);
+      HIP_TRY(launch_lr_fork(bf, c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
+                             n_req, d, c->S, H, c->lr_o, lo_off(c, d), save, any_tree,
+                             prefill, max_rows_req, s));
+      GemmArgs o = gemm_args(c, L.wout, kKmajorOut, c->lr_o, d, R, d, d);
+      const int So = gemm_part(c, o, &e);
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
-      HIP_TRY(launch_resid_reduce(c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h, c->ss, s));
+      HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
+                                  L.n2, eps, c->u, u_lo, s));
     }
-    GemmArgs gu = gemm_args(c, L.wgu, c->h, d, R, d, 2 * F);
-    normed(gu, L.n2);
+    GemmArgs gu = gemm_args(c, L.wgu, true, c->u, d, R, d, 2 * F);
     gu.Y = c->act;
     gu.ldy = F;
+    gu.ylo = (int64_t)lo_off(c, F);
     time_begin(c, 1);
-    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, XM_NORM, gu, s));
+    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, s));
     time_end(c, 1);
-    GemmArgs dn = gemm_args(c, L.wd, c->act, F, R, F, d);
+    GemmArgs dn = gemm_args(c, L.wd, kKmajorOut, c->act, F, R, F, d);
     time_begin(c, 2);
-    const int Sd = gemm_part(c, dn, XM_F32, &e);
+    const int Sd = gemm_part(c, dn, &e);
     HIP_TRY(e);
     time_end(c, 2);
     const int ldd = dn.ntiles * 16;
-    HIP_TRY(launch_resid_reduce(c->P, Sd, (size_t)c->Rmax * ldd, ldd, R, d, c->h, c->ss, s));
+    HIP_TRY(launch_resid_reduce(bf, c->P, Sd, (size_t)c->Rmax * ldd, ldd, R, d, c->h,
+                                next_norm, eps, c->u, u_lo, s));
   }
 
   // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
   if (lm_rows == 0) return SPEC_OK;
-  GemmArgs lm = gemm_args(c, c->lm_head, c->h + (size_t)lm_row0 * d, d, lm_rows, d, c->V);
-  lm.ss = c->ss + lm_row0;
-  lm.nw = c->final_norm;
+  GemmArgs lm = gemm_args(c, c->lm_head, true,
+                          (const char*)c->u + (size_t)lm_row0 * d * c->esz, d, lm_rows, d,
+                          c->V);
   lm.part = c->am_part;
   lm.nblocks = lm.ntiles * 16 / gemm_cols_per_block();
   lm.logits = d_logits;
@@ -579,7 +623,7 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   lm.bias = c->fault_bias;
   lm.bias_after = c->fault_after;
   time_begin(c, 3);
-  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, XM_NORM, lm, s));
+  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s));
   time_end(c, 3);
   HIP_TRY(launch_argmax_reduce(c->am_part, lm_rows, lm.nblocks, c->amax, s));
   return SPEC_OK;
@@ -709,7 +753,8 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
         from = (const char*)c->staging;
       }
       HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst,
-                              t.tile0 + (r0 / 16) * t.tile_stride, t.tile_stride, s));
+                              t.tile0 + (r0 / 16) * t.tile_stride, t.tile_stride, t.wsn,
+                              t.wsk, s));
       if (!src_on_device) HIP_TRY(hipStreamSynchronize(s));
     }
   }

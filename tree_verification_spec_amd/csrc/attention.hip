@@ -7,10 +7,11 @@
 // head are processed together, so each K/V split staged in LDS serves
 // (rows * G) query rows.
 //
-// Workgroup = 4 wavefronts = one (request, KV head, key split, group of up
-// to 8 query tiles of 16 query rows).  The split's keys (at most 128) are
-// staged in LDS once, with every load in flight; then each wave takes query
-// tiles of the group in turn and keeps the transposed flash-attention state
+// Workgroup = 8 wavefronts = one (request, KV head, key split, group of
+// query tiles of 16 query rows; all of a verify pass's tiles of that KV
+// head).  The split's keys (at most 128) are staged in LDS once, with every
+// load in flight; then the waves take the group's query tiles in turn and
+// keep the transposed flash-attention state
 // in registers: S^T = K Q^T (so a lane holds one query row's scores), an
 // online softmax in fp32, and O^T += V^T P^T.  With a bf16 cache, the fp32
 // operands q and P enter the MFMAs as bf16 hi + lo pairs, so only the stored
@@ -73,8 +74,11 @@ __device__ __forceinline__ void pack_p(Frag<float>& f, const float* p) {
 __device__ __forceinline__ float op_round(float x, uint16_t) { return bf2f(f2bf(x)); }
 __device__ __forceinline__ float op_round(float x, float) { return x; }
 
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = kAttnWaves * 64;
+
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char attn_smem[];
   using L = SplitLds<T, HD>;
   T* sk = reinterpret_cast<T*>(attn_smem);      // [split][KS]
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   };
   // the wave's first tile is fetched before the K/V staging (its latency
-  // overlaps the staging's); each later tile is fetched during the previous
+  // overlaps the staging's)
   Frag<T> qf[HD / 32], qfl[HD / 32];
   load_q(t_beg + wave, qf, qfl);
 
@@ -136,13 +140,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   {
     const int nkeys = kend - kbeg;                 // <= a.split <= kMaxSplitKeys
     const int kch = ((nkeys + 31) & ~31) * KCH_ROW;
-    const int vblk = ((nkeys + 31) & ~31) / 16;    // 16-key blocks per dim
-    const int vch = HD * vblk * VCH_ROW;
-    constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / 256;  // per thread, each of K and V
+    const int vblk = ((nkeys + 31) & ~31) / 16;    // 16-key pages of the split
+    const int vch = vblk * HD * VCH_ROW;
+    // chunk c of V: page blk = c / (HD * VCH_ROW), then (dim, part) in the
+    // page's [dim][16 keys] order, so a wave reads contiguous memory
+    constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / kAttnThreads;  // per thread, each of K, V
     uint4 kr[MAXCH], vr[MAXCH];
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
-      const int c = threadIdx.x + j * 256;
+      const int c = threadIdx.x + j * kAttnThreads;
       kr[j] = make_uint4(0, 0, 0, 0);
       if (c < kch) {
         const int i = c / KCH_ROW, part = c % KCH_ROW;
@@ -155,8 +161,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
       vr[j] = make_uint4(0, 0, 0, 0);
       if (c < vch) {
-        const int dim = c / (vblk * VCH_ROW), rest = c % (vblk * VCH_ROW);
-        const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
+        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+        const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
         const int t0 = kbeg + blk * 16 + part * EPC;
         if (t0 < kend) {
           const int page = bt[t0 >> 4];
@@ -171,14 +177,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
-      const int c = threadIdx.x + j * 256;
+      const int c = threadIdx.x + j * kAttnThreads;
       if (c < kch) {
         const int i = c / KCH_ROW, part = c % KCH_ROW;
         *reinterpret_cast<uint4*>(&sk[(size_t)i * L::KS + part * EPC]) = kr[j];
       }
       if (c < vch) {
-        const int dim = c / (vblk * VCH_ROW), rest = c % (vblk * VCH_ROW);
-        const int blk = rest / VCH_ROW, part = rest % VCH_ROW;
+        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+        const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
         *reinterpret_cast<uint4*>(&sv[(size_t)dim * VS + blk * 16 + part * EPC]) = vr[j];
       }
     }
@@ -186,15 +192,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 
   // each wave takes the group's query tiles in turn (no barriers below)
-  for (int qtile = t_beg + wave; qtile < t_end; qtile += 4) {
+  for (int qtile = t_beg + wave; qtile < t_end; qtile += kAttnWaves) {
     const int qr = qtile * 16 + r16;
     const bool qvalid = qr < qrows;
     const int node = qvalid ? qr / G : 0;
     const int qhead = kvh * G + (qvalid ? qr % G : 0);
     const int grow = rm.row0 + node;
-    Frag<T> qn[HD / 32], qnl[HD / 32];
-    const bool more = qtile + 4 < t_end;
-    if (more) load_q(qtile + 4, qn, qnl);
+    if (qtile != t_beg + wave) load_q(qtile, qf, qfl);  // the first was prefetched
     uint64_t anc_lo = 0, anc_hi = 0;
     if (qvalid && !rm.chain) {
       const uint64_t* am = a.anc + rm.anc0 + (size_t)node * rm.anc_words;
@@ -290,33 +294,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
       if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
     }
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < HD / 32; ++ks) {
-        qf[ks] = qn[ks];
-        qfl[ks] = qnl[ks];
-      }
-    }
   }
 }
 
 // One wave per (row, query head): merge the splits of the row's request.
-// Lane s reads split s's (max, sum); the wave forms the weights, then every
-// lane accumulates its dims over the splits in split order.
+// Lane l reads the (max, sum) of splits l and l + 64; the wave forms the
+// weights, then every lane accumulates its dims over the splits in split
+// order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, size_t olo) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= a.rows_total * a.nq) return;
   const int grow = wid / a.nq, qhead = wid % a.nq;
-  const ReqMeta rm = a.reqs[a.rows[grow].req];
-  const int nsplit = (rm.nctx + rm.nrows + a.split - 1) / a.split;  // <= 64
+  const int nsplit = (a.rows[grow].keys + a.split - 1) / a.split;  // <= 128
   const size_t sstride = (size_t)a.rows_total * a.nq;
-  float2 ml = make_float2(-INFINITY, 0.f);
-  if (lane < nsplit) ml = a.part_ml[(size_t)lane * sstride + wid];
-  const float M = wave_max(ml.x);
-  const float wgt = (ml.x == -INFINITY) ? 0.f : expf(ml.x - M);
-  const float L = wave_sum(ml.y * wgt);
+  float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = ml0;
+  if (lane < nsplit) ml0 = a.part_ml[(size_t)lane * sstride + wid];
+  if (lane + 64 < nsplit) ml1 = a.part_ml[(size_t)(lane + 64) * sstride + wid];
+  const float M = wave_max(fmaxf(ml0.x, ml1.x));
+  const float w0 = (ml0.x == -INFINITY) ? 0.f : expf(ml0.x - M);
+  const float w1 = (ml1.x == -INFINITY) ? 0.f : expf(ml1.x - M);
+  const float L = wave_sum(ml0.y * w0 + ml1.y * w1);
   constexpr int PER = HD / 64;
   float acc[PER];
 #pragma unroll
@@ -330,9 +329,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
 #pragma unroll
       for (int j = 0; j < PER; ++j) v[u][j] = po[(size_t)sp * sstride * HD + j];
     }
+    const float wsel = s0 < 64 ? w0 : w1;  // s0 is a multiple of 8
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float wu = __shfl(wgt, s0 + u, 64);
+      const float wu = __shfl(wsel, (s0 + u) & 63, 64);
       if (s0 + u < nsplit) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) acc[j] += v[u][j] * wu;
@@ -356,7 +356,7 @@ hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
-  k<<<grid, 256, lds, s>>>(a);
+  k<<<grid, kAttnThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -371,7 +371,7 @@ hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
 
 template <typename T>
 hipError_t combine_t(const AttnArgs& a, T* o, size_t olo, hipStream_t s) {
-  if (a.max_splits > 64) return hipErrorInvalidValue;
+  if (a.max_splits > 128) return hipErrorInvalidValue;
   const int waves = a.rows_total * a.nq;
   dim3 grid((waves + 3) / 4);
   if (a.hd == 128) attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a, o, olo);

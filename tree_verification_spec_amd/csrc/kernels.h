@@ -13,7 +13,8 @@ struct RowMeta {
   int32_t req;     // index of its request in this pass's ReqMeta array
   int32_t node;    // node index inside the request (0 = root)
   int32_t parent;  // node-local parent index, -1 for the root
-  int32_t pad0, pad1;
+  int32_t keys;    // keys of its request in this pass (committed + pass rows)
+  int32_t pad;
 };
 
 // One request of a forward pass.

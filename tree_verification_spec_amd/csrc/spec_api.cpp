@@ -29,7 +29,9 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxSplits = 64;  // attention key splits (one combine lane each)
+constexpr int kMaxSplits = 128;  // attention key splits per request (verify passes)
+constexpr int kMaxSplitsPrefill = 64;  // prefill chunks: splits of 128 keys up to 8192
+constexpr int kAttnSlots = 512;  // attention workgroups resident at once (2 per CU)
 // tile order of the input projections (QKV, in_proj) and of the matrices
 // whose output is added to the residual (O, out_proj, down); gate/up and the
 // LM head are always K-major
@@ -145,6 +147,7 @@ struct spec_ctx {
   void* q = nullptr;
   void* q_lo = nullptr;
   float* P = nullptr;        // GEMM split partials [S][Rmax][N]
+  size_t split_rows = 0;     // capacity of the attention split table (splits x rows)
   float* lrsave = nullptr;   // per recurrent layer [max_rows][x | a | B]
   size_t lrsave_layer = 0;
   size_t weights_end = 0;
@@ -221,7 +224,7 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->max_rows < cfg->max_nodes) return bad("max_rows < max_nodes");
   if (cfg->prefill_chunk < 1 || cfg->prefill_chunk > 1024) return bad("prefill_chunk");
   if (cfg->max_ctx < cfg->max_nodes + 1) return bad("max_ctx");
-  if (cfg->max_ctx > kMaxSplits * 128) return bad("max_ctx must be <= 8192");
+  if (cfg->max_ctx > kMaxSplitsPrefill * 128) return bad("max_ctx must be <= 8192");
   bool any_lr = false;
   for (int i = 0; i < cfg->n_layers; ++i) {
     if (cfg->layer_kind[i] == SPEC_LAYER_LR) any_lr = true;
@@ -295,8 +298,11 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);  // bf16: hi and lo planes
   const size_t o_lrs = p.take(n_lr ? (size_t)n_lr * cfg.max_rows * (2 * d + S) * 4 : 0);
   const size_t o_lro = p.take(n_lr ? (size_t)R * d * 4 : 0);
-  const size_t o_po = p.take((size_t)kMaxSplits * R * nq * hd * 4);
-  const size_t o_pml = p.take((size_t)kMaxSplits * R * nq * 8);
+  // attention split partials: (splits x rows) of one pass
+  const size_t split_rows = std::max((size_t)kMaxSplits * cfg.max_rows,
+                                     (size_t)kMaxSplitsPrefill * R);
+  const size_t o_po = p.take(split_rows * nq * hd * 4);
+  const size_t o_pml = p.take(split_rows * nq * 8);
   const size_t o_amp = p.take((size_t)R * (npad(V) / cb) * 8);
   const size_t o_amax = p.take((size_t)R * 4);
   const size_t o_res = p.take((size_t)cfg.max_requests * (2 + 64) * 4);
@@ -374,6 +380,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     c->weights_end = weights_end;
     c->part_o = (float*)at(o_po);
     c->part_ml = (float2*)at(o_pml);
+    c->split_rows = split_rows;
     c->am_part = (float2*)at(o_amp);
     c->amax = (int32_t*)at(o_amax);
     c->res = (int32_t*)at(o_res);
@@ -507,24 +514,34 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
                        u_lo, s));
 
   // attention launch shape: a workgroup stages one key split of one
-  // (request, KV head) and serves a group of up to 8 query tiles (16 query
-  // rows each) of it; splits of 64 keys when that keeps the split table and
-  // the grid moderate, else 128 (the most one workgroup stages in LDS)
+  // (request, KV head) and serves a group of up to 32 query tiles (16 query
+  // rows each; all of a verify pass's) of it.  The split is the smallest of
+  // 32, 64, 96, 128 keys whose grid fits the resident workgroup slots (one
+  // round, most parallelism), else 128 keys; the split table bounds it.
   int keys_max = 0, qt_max = 0, max_rows_req = 0;
   for (int r = 0; r < n_req; ++r) {
     keys_max = std::max(keys_max, keys_per_req[r]);
     qt_max = std::max(qt_max, (rows_per_req[r] * G + 15) / 16);
     max_rows_req = std::max(max_rows_req, rows_per_req[r]);
   }
-  const int q_groups = (qt_max + 7) / 8;
+  const int q_groups = (qt_max + 31) / 32;
   const int tpw = (qt_max + q_groups - 1) / q_groups;
-  int split = 64;
-  {
-    long wgs = 0;
+  auto wgs_for = [&](int sp) {
+    long w = 0;
     for (int r = 0; r < n_req; ++r)
-      wgs += (long)(((rows_per_req[r] * G + 15) / 16 + tpw - 1) / tpw) * nkv *
-             ((keys_per_req[r] + 63) / 64);
-    if ((keys_max + 63) / 64 > kMaxSplits || wgs > 4096) split = 128;
+      w += (long)(((rows_per_req[r] * G + 15) / 16 + tpw - 1) / tpw) * nkv *
+           ((keys_per_req[r] + sp - 1) / sp);
+    return w;
+  };
+  const int split_cap = R <= cfg.max_rows ? kMaxSplits : kMaxSplitsPrefill;
+  int split = 128;
+  for (int sp : {32, 64, 96, 128}) {
+    const int ns = (keys_max + sp - 1) / sp;
+    if (ns > split_cap || (size_t)ns * R > c->split_rows) continue;
+    if (wgs_for(sp) <= kAttnSlots) {
+      split = sp;
+      break;
+    }
   }
   AttnArgs aa{};
   aa.q = c->q;
@@ -546,7 +563,7 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   aa.n_req = n_req;
   aa.rows_total = R;
   aa.scale = 1.0f / std::sqrt((float)hd);
-  if (aa.max_splits > kMaxSplits)
+  if (aa.max_splits > split_cap || (size_t)aa.max_splits * R > c->split_rows)
     return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
 
   for (int li = 0; li < cfg.n_layers; ++li) {
@@ -816,6 +833,7 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
       r.req = 0;
       r.node = i;
       r.parent = i - 1;
+      r.keys = done + C;
     }
     ReqMeta& m = h_reqs(c)[0];
     m = ReqMeta{0, C, done, req, 0, 1, 1, 0};
@@ -903,6 +921,7 @@ extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
       m.req = r;
       m.node = i;
       m.parent = p;
+      m.keys = rq.n + K + 1;
       uint64_t* a = anc + (size_t)(row + i) * words;
       for (int w = 0; w < words; ++w) a[w] = p < 0 ? 0 : anc[(size_t)(row + p) * words + w];
       a[i >> 6] |= 1ull << (i & 63);

@@ -167,6 +167,17 @@ int32_t spec_force_root(spec_ctx* ctx, int32_t req, int32_t token);
 int32_t spec_set_fault(spec_ctx* ctx, int32_t token, float bias,
                        int32_t after_position);
 
+/* Verify passes replay a captured HIP graph of their kernel sequence when a
+ * pass with the same launch parameters (rows, requests, tree or chain,
+ * attention split shape, logits buffer, fault setting) ran before; the
+ * first such pass captures it (up to 8 are kept per context, least recently
+ * used dropped).  Results are identical either way.  enable = 0 launches
+ * every kernel individually.  The default is 1 unless the context was
+ * created on the null stream (which cannot be captured; enabling graphs
+ * there returns SPEC_E_UNSUPPORTED).  Kernel timing (below) also launches
+ * individually while enabled.  Host-only. */
+int32_t spec_use_graphs(spec_ctx* ctx, int32_t enable);
+
 /* Per-launch timing of one kernel class, for roofline measurement: while
  * enabled, the library brackets every launch of that class with HIP events
  * on its stream.  cls: 0 = off, 1 = FFN gate/up GEMM, 2 = FFN down GEMM,

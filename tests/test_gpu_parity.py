@@ -275,9 +275,45 @@ def test_verify_is_deterministic():
     toks = np.arange(16) * 7 % cfg["vocab"]
     par = np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5, 11, 12, 8, 14])
     a = eng.verify([0], [toks], [par], logits=True)
+    la = a[2].cpu().numpy()  # the logits view is reused by the next verify
     b = eng.verify([0], [toks], [par], logits=True)
     assert a[0] == b[0] and a[1] == b[1]
-    assert np.array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
+    assert np.array_equal(la, b[2].cpu().numpy())
+
+
+def test_graph_replay_equals_individual_launches():
+    """Verify passes replayed from captured graphs (the default) give the
+    same paths, bonus tokens and logits as individually launched kernels:
+    several replays of each captured pass (chain, tree, with and without
+    logits), with eager commits and host synchronisation between them."""
+    cfg, W = _setup("tiny_hybrid_bf16")
+    V = cfg["vocab"]
+    prompt = synth.prompt_tokens(V, 70, 54)
+    rng = np.random.default_rng(54)
+    tree_par = np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5])
+    steps = []
+    for k in range(12):
+        if k % 2:
+            steps.append((rng.integers(0, V, 12), tree_par, k % 4 == 1))
+        else:
+            steps.append((rng.integers(0, V, 8), np.arange(-1, 7), k % 4 == 0))
+    runs = []
+    for graphs in (True, False):
+        eng = engine_for(cfg, W, max_ctx=512, max_nodes=17)
+        eng.use_graphs(graphs)
+        eng.prefill(0, prompt)
+        out = []
+        for toks, par, want_logits in steps:
+            r = eng.verify([0], [toks], [par], logits=want_logits)
+            lg = r[2].cpu().numpy().copy() if want_logits else None
+            out.append((r[0], r[1], lg))
+            eng.commit([0], r[0], r[1])
+        runs.append(out)
+        eng.close()
+    for (pa, ba, la), (pb, bb, lb) in zip(*runs):
+        assert pa == pb and ba == bb
+        if la is not None:
+            assert np.array_equal(la, lb)
 
 
 # ------------------------------------------------ full-width model variants

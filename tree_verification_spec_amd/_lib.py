@@ -25,7 +25,8 @@ SPEC_MAX_LAYERS = 128
 EXPORTS = [
     "spec_workspace_bytes", "spec_create", "spec_load_weights", "spec_prefill",
     "spec_verify", "spec_commit", "spec_release", "spec_request_state",
-    "spec_force_root", "spec_set_fault", "spec_timing_enable", "spec_timing_read",
+    "spec_force_root", "spec_set_fault", "spec_use_graphs", "spec_timing_enable",
+    "spec_timing_read",
     "spec_destroy", "spec_last_error",
 ]
 
@@ -76,6 +77,7 @@ def lib():
         "spec_request_state": (c_int32, [c_void_p, c_int32, i32p, i32p]),
         "spec_force_root": (c_int32, [c_void_p, c_int32, c_int32]),
         "spec_set_fault": (c_int32, [c_void_p, c_int32, c_float, c_int32]),
+        "spec_use_graphs": (c_int32, [c_void_p, c_int32]),
         "spec_timing_enable": (c_int32, [c_void_p, c_int32]),
         "spec_timing_read": (c_int32, [c_void_p, P(c_double), P(c_int64)]),
         "spec_destroy": (None, [c_void_p]),
@@ -174,6 +176,10 @@ def spec_force_root(ctx, req, token):
 
 def spec_set_fault(ctx, token, bias, after_position):
     return _check(ctx, lib().spec_set_fault(ctx, token, bias, after_position))
+
+
+def spec_use_graphs(ctx, enable):
+    return _check(ctx, lib().spec_use_graphs(ctx, 1 if enable else 0))
 
 
 def spec_timing_enable(ctx, cls):

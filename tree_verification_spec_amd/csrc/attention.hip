@@ -297,15 +297,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   }
 }
 
-// One wave per (row, query head): merge the splits of the row's request.
-// Lane l reads the (max, sum) of splits l and l + 64; the wave forms the
-// weights, then every lane accumulates its dims over the splits in split
-// order.
+// One workgroup of 4 waves per (row, query head): merge the splits of the
+// row's request.  Every wave reads the (max, sum) of all splits (lane l:
+// splits l and l + 64) and forms the same weights; wave w then accumulates
+// splits w, w + 4, ... for its lanes' dims (all loads of a wave in flight
+// together), and the four sums are added in wave order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, size_t olo) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wid >= a.rows_total * a.nq) return;
+  __shared__ float red[4][HD];
+  const int wid = blockIdx.x;  // row * nq + head
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grow = wid / a.nq, qhead = wid % a.nq;
   const int nsplit = (a.rows[grow].keys + a.split - 1) / a.split;  // <= 128
   const size_t sstride = (size_t)a.rows_total * a.nq;
@@ -317,33 +318,37 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   const float w1 = (ml1.x == -INFINITY) ? 0.f : expf(ml1.x - M);
   const float L = wave_sum(ml0.y * w0 + ml1.y * w1);
   constexpr int PER = HD / 64;
+  constexpr int U = 8;  // splits per wave loaded together
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   const float* po = a.part_o + (size_t)wid * HD + lane * PER;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    float v[8][PER];
+  for (int s0 = wave; s0 < nsplit; s0 += 4 * U) {
+    float v[U][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sp = s0 + u < nsplit ? s0 + u : nsplit - 1;
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + 4 * u, nsplit - 1);
 #pragma unroll
       for (int j = 0; j < PER; ++j) v[u][j] = po[(size_t)sp * sstride * HD + j];
     }
-    const float wsel = s0 < 64 ? w0 : w1;  // s0 is a multiple of 8
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wu = __shfl(wsel, (s0 + u) & 63, 64);
-      if (s0 + u < nsplit) {
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + 4 * u;
+      const float wu = __shfl(sp < 64 ? w0 : w1, sp & 63, 64);
+      if (sp < nsplit) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) acc[j] += v[u][j] * wu;
       }
     }
   }
-  const float inv = 1.0f / L;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    store_act(out, out + olo, ((size_t)grow * a.nq + qhead) * HD + lane * PER + j,
-              acc[j] * inv);
+  for (int j = 0; j < PER; ++j) red[wave][lane * PER + j] = acc[j];
+  __syncthreads();
+  const float inv = 1.0f / L;
+  for (int dim = threadIdx.x; dim < HD; dim += 256) {
+    const float t = ((red[0][dim] + red[1][dim]) + red[2][dim]) + red[3][dim];
+    store_act(out, out + olo, ((size_t)grow * a.nq + qhead) * HD + dim, t * inv);
+  }
 }
 
 template <typename T, int HD>
@@ -372,8 +377,7 @@ hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
 template <typename T>
 hipError_t combine_t(const AttnArgs& a, T* o, size_t olo, hipStream_t s) {
   if (a.max_splits > 128) return hipErrorInvalidValue;
-  const int waves = a.rows_total * a.nq;
-  dim3 grid((waves + 3) / 4);
+  dim3 grid(a.rows_total * a.nq);
   if (a.hd == 128) attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a, o, olo);
   else if (a.hd == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a, o, olo);
   else return hipErrorInvalidValue;

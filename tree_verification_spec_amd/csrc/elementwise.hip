@@ -108,12 +108,13 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
   __shared__ float part[16];
   constexpr int MAXQ = 4;  // float4 per thread: d <= 16384
   const int row = blockIdx.x;
-  float4 keep[MAXQ];
+  float4 keep[MAXQ], wn[MAXQ];
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXQ; ++j) {
     const int c = (threadIdx.x + j * 1024) * 4;
     if (c >= d) break;
+    wn[j] = *reinterpret_cast<const float4*>(nw + c);  // needed after the reduction
     float4 pv[S];
 #pragma unroll
     for (int k = 0; k < S; ++k)
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
   for (int j = 0; j < MAXQ; ++j) {
     const int c = (threadIdx.x + j * 1024) * 4;
     if (c >= d) break;
-    const float4 w = *reinterpret_cast<const float4*>(nw + c);
+    const float4 w = wn[j];
     const size_t i = (size_t)row * d + c;
     store_act(u, u + ulo, i + 0, (keep[j].x * sc) * w.x);
     store_act(u, u + ulo, i + 1, (keep[j].y * sc) * w.y);

@@ -32,6 +32,8 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxSplits = 128;  // attention key splits per request (verify passes)
 constexpr int kMaxSplitsPrefill = 64;  // prefill chunks: splits of 128 keys up to 8192
 constexpr int kAttnSlots = 512;  // attention workgroups resident at once (2 per CU)
+constexpr int kMaxPath = 64;     // accepted-path slots per request in the walk result
+constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 // tile order of the input projections (QKV, in_proj) and of the matrices
 // whose output is added to the residual (O, out_proj, down); gate/up and the
 // LM head are always K-major
@@ -84,6 +86,12 @@ TileOrder tile_order(int N, int K, bool kmajor) {
   const int nt = (N + cb - 1) / cb * cb / 16;
   return kmajor ? TileOrder{1, nt} : TileOrder{K / 32, 1};
 }
+
+struct GraphEntry {
+  std::vector<int64_t> key;
+  hipGraphExec_t exec;
+  uint64_t used;
+};
 
 struct Plan {
   size_t total = 0;
@@ -148,6 +156,10 @@ struct spec_ctx {
   void* q_lo = nullptr;
   float* P = nullptr;        // GEMM split partials [S][Rmax][N]
   size_t split_rows = 0;     // capacity of the attention split table (splits x rows)
+  // captured verify passes (see run_pass)
+  bool use_graphs = true;
+  std::vector<GraphEntry> graphs;
+  uint64_t graph_tick = 0;
   float* lrsave = nullptr;   // per recurrent layer [max_rows][x | a | B]
   size_t lrsave_layer = 0;
   size_t weights_end = 0;
@@ -305,7 +317,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const size_t o_pml = p.take(split_rows * nq * 8);
   const size_t o_amp = p.take((size_t)R * (npad(V) / cb) * 8);
   const size_t o_amax = p.take((size_t)R * 4);
-  const size_t o_res = p.take((size_t)cfg.max_requests * (2 + 64) * 4);
+  const size_t o_res = p.take((size_t)cfg.max_requests * (2 + kMaxPath) * 4);
   // GEMM split partials: the largest S x N over the model's matrices, for
   // any row count up to R (the split count depends on the rows of a launch)
   size_t psz = 0;
@@ -495,32 +507,46 @@ int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err) {
   return g.S;
 }
 
-// One forward pass over R rows already described in d_rows / d_reqs / d_anc.
-// lm_row0 / lm_rows: rows that go through the LM head (argmax into amax).
-// prefill: chain pass whose final recurrent states are committed.
-int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
-            const std::vector<int>& rows_per_req, bool any_tree, int lm_row0,
-            int lm_rows, float* d_logits, bool prefill) {
+// Launch parameters of one forward pass: everything the kernel sequence
+// depends on besides the device-side metadata (rows, requests, masks), so
+// that two passes with equal parameters can replay one captured graph.
+struct Pass {
+  int R = 0, n_req = 0;
+  bool any_tree = false, prefill = false;
+  int lm_row0 = 0, lm_rows = 0;
+  float* d_logits = nullptr;
+  int split = 0, max_splits = 0, tpw = 0, max_qgroups = 0, max_rows_req = 0;
+  bool walk = false;  // append the accepted-path walk (verify passes)
+  std::vector<int64_t> key(const spec_ctx* c) const;
+};
+
+// Plan a forward pass over R rows already described in d_rows / d_reqs /
+// d_anc.  lm_row0 / lm_rows: rows that go through the LM head (argmax into
+// amax).  prefill: chain pass whose final recurrent states are committed.
+int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& keys_per_req,
+              const std::vector<int>& rows_per_req, bool any_tree, int lm_row0, int lm_rows,
+              float* d_logits, bool prefill) {
   const spec_config& cfg = c->cfg;
-  const bool bf = c->bf16;
-  hipStream_t s = c->stream;
-  const int d = c->d, hd = c->hd, nq = c->nq, nkv = c->nkv, F = c->F;
+  const int nq = c->nq, nkv = c->nkv;
   const int G = nq / nkv;
-  hipError_t e = hipSuccess;
-
-  const float eps = cfg.rms_eps;
-  const size_t u_lo = lo_off(c, d);
-  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, eps, c->u,
-                       u_lo, s));
-
+  P.R = R;
+  P.n_req = n_req;
+  P.any_tree = any_tree;
+  P.prefill = prefill;
+  P.lm_row0 = lm_row0;
+  P.lm_rows = lm_rows;
+  P.d_logits = d_logits;
   // attention launch shape: a workgroup stages one key split of one
   // (request, KV head) and serves a group of up to 32 query tiles (16 query
   // rows each; all of a verify pass's) of it.  The split is the smallest of
   // 32, 64, 96, 128 keys whose grid fits the resident workgroup slots (one
-  // round, most parallelism), else 128 keys; the split table bounds it.
+  // round, most parallelism), else 128 keys; the split table bounds it.  Key
+  // counts are rounded up to 256 so that the launch shape (and a captured
+  // graph) stays the same while a request grows; surplus splits exit early.
+  auto keys_up = [&](int k) { return std::min((k + 255) / 256 * 256, cfg.max_ctx); };
   int keys_max = 0, qt_max = 0, max_rows_req = 0;
   for (int r = 0; r < n_req; ++r) {
-    keys_max = std::max(keys_max, keys_per_req[r]);
+    keys_max = std::max(keys_max, keys_up(keys_per_req[r]));
     qt_max = std::max(qt_max, (rows_per_req[r] * G + 15) / 16);
     max_rows_req = std::max(max_rows_req, rows_per_req[r]);
   }
@@ -530,7 +556,7 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
     long w = 0;
     for (int r = 0; r < n_req; ++r)
       w += (long)(((rows_per_req[r] * G + 15) / 16 + tpw - 1) / tpw) * nkv *
-           ((keys_per_req[r] + sp - 1) / sp);
+           ((keys_up(keys_per_req[r]) + sp - 1) / sp);
     return w;
   };
   const int split_cap = R <= cfg.max_rows ? kMaxSplits : kMaxSplitsPrefill;
@@ -543,6 +569,37 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
       break;
     }
   }
+  P.split = split;
+  P.max_splits = (keys_max + split - 1) / split;
+  P.tpw = tpw;
+  P.max_qgroups = (qt_max + tpw - 1) / tpw;
+  P.max_rows_req = max_rows_req;
+  if (P.max_splits > split_cap || (size_t)P.max_splits * R > c->split_rows)
+    return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
+  return SPEC_OK;
+}
+
+std::vector<int64_t> Pass::key(const spec_ctx* c) const {
+  return {R, n_req, any_tree, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
+          split, max_splits, tpw, max_qgroups, max_rows_req, walk, c->fault_tok,
+          (int64_t)__builtin_bit_cast(uint32_t, c->fault_bias), c->fault_after};
+}
+
+// Enqueue the kernels of a planned pass on the context's stream.
+int launch_pass(spec_ctx* c, const Pass& P) {
+  const spec_config& cfg = c->cfg;
+  const bool bf = c->bf16;
+  hipStream_t s = c->stream;
+  const int d = c->d, hd = c->hd, nq = c->nq, nkv = c->nkv, F = c->F;
+  const int R = P.R, n_req = P.n_req, max_rows_req = P.max_rows_req;
+  const bool any_tree = P.any_tree, prefill = P.prefill;
+  hipError_t e = hipSuccess;
+
+  const float eps = cfg.rms_eps;
+  const size_t u_lo = lo_off(c, d);
+  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, eps, c->u,
+                       u_lo, s));
+
   AttnArgs aa{};
   aa.q = c->q;
   aa.q_lo = c->q_lo;
@@ -556,15 +613,13 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   aa.nq = nq;
   aa.nkv = nkv;
   aa.hd = hd;
-  aa.split = split;
-  aa.max_splits = (keys_max + split - 1) / split;
-  aa.qtiles_per_wg = tpw;
-  aa.max_qgroups = (qt_max + tpw - 1) / tpw;
+  aa.split = P.split;
+  aa.max_splits = P.max_splits;
+  aa.qtiles_per_wg = P.tpw;
+  aa.max_qgroups = P.max_qgroups;
   aa.n_req = n_req;
   aa.rows_total = R;
   aa.scale = 1.0f / std::sqrt((float)hd);
-  if (aa.max_splits > split_cap || (size_t)aa.max_splits * R > c->split_rows)
-    return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
 
   for (int li = 0; li < cfg.n_layers; ++li) {
     const Layer& L = c->layers[li];
@@ -627,23 +682,77 @@ int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
   }
 
   // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
-  if (lm_rows == 0) return SPEC_OK;
-  GemmArgs lm = gemm_args(c, c->lm_head, true,
-                          (const char*)c->u + (size_t)lm_row0 * d * c->esz, d, lm_rows, d,
-                          c->V);
-  lm.part = c->am_part;
-  lm.nblocks = lm.ntiles * 16 / gemm_cols_per_block();
-  lm.logits = d_logits;
-  lm.ldlog = c->V;
-  lm.rows = c->d_rows + lm_row0;
-  lm.bias_tok = c->fault_tok;
-  lm.bias = c->fault_bias;
-  lm.bias_after = c->fault_after;
-  time_begin(c, 3);
-  HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s));
-  time_end(c, 3);
-  HIP_TRY(launch_argmax_reduce(c->am_part, lm_rows, lm.nblocks, c->amax, s));
+  if (P.lm_rows > 0) {
+    GemmArgs lm = gemm_args(c, c->lm_head, true,
+                            (const char*)c->u + (size_t)P.lm_row0 * d * c->esz, d, P.lm_rows,
+                            d, c->V);
+    lm.part = c->am_part;
+    lm.nblocks = lm.ntiles * 16 / gemm_cols_per_block();
+    lm.logits = P.d_logits;
+    lm.ldlog = c->V;
+    lm.rows = c->d_rows + P.lm_row0;
+    lm.bias_tok = c->fault_tok;
+    lm.bias = c->fault_bias;
+    lm.bias_after = c->fault_after;
+    time_begin(c, 3);
+    HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s));
+    time_end(c, 3);
+    HIP_TRY(launch_argmax_reduce(c->am_part, P.lm_rows, lm.nblocks, c->amax, s));
+  }
+  if (P.walk)
+    HIP_TRY(launch_path_walk(c->d_rows, c->d_reqs, n_req, c->amax, kMaxPath, c->res, s));
   return SPEC_OK;
+}
+
+// Run a planned pass: replay a captured graph of its kernels when one with
+// the same launch parameters exists (capturing it on first use), else
+// launch eagerly.  Graphs are off while kernel timing is enabled.
+int run_pass(spec_ctx* c, const Pass& P) {
+  if (!c->use_graphs || c->timing_cls != 0) return launch_pass(c, P);
+  const std::vector<int64_t> key = P.key(c);
+  GraphEntry* hit = nullptr;
+  for (auto& g : c->graphs)
+    if (g.key == key) hit = &g;
+  if (!hit) {
+    hipGraph_t graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed));
+    const int rc = launch_pass(c, P);
+    const hipError_t ee = hipStreamEndCapture(c->stream, &graph);
+    if (rc) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    HIP_TRY(ee);
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    HIP_TRY(ie);
+    if (c->graphs.size() >= kMaxGraphs) {  // drop the least recently used
+      auto lru = std::min_element(c->graphs.begin(), c->graphs.end(),
+                                  [](const GraphEntry& a, const GraphEntry& b) {
+                                    return a.used < b.used;
+                                  });
+      (void)hipGraphExecDestroy(lru->exec);
+      c->graphs.erase(lru);
+    }
+    c->graphs.push_back(GraphEntry{key, exec, 0});
+    hit = &c->graphs.back();
+  }
+  hit->used = ++c->graph_tick;
+  HIP_TRY(hipGraphLaunch(hit->exec, c->stream));
+  return SPEC_OK;
+}
+
+int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
+            const std::vector<int>& rows_per_req, bool any_tree, int lm_row0, int lm_rows,
+            float* d_logits, bool prefill, bool walk) {
+  Pass P;
+  const int rc = plan_pass(c, P, R, n_req, keys_per_req, rows_per_req, any_tree, lm_row0,
+                           lm_rows, d_logits, prefill);
+  if (rc) return rc;
+  P.walk = walk;
+  // prefill chunks run eagerly (their shapes vary); verify passes replay graphs
+  return prefill ? launch_pass(c, P) : run_pass(c, P);
 }
 
 RowMeta* h_rows(spec_ctx* c) { return (RowMeta*)c->h_meta; }
@@ -677,6 +786,7 @@ extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
   c->bf16 = cfg->dtype == SPEC_DTYPE_BF16;
   c->esz = c->bf16 ? 2 : 4;
   c->stream = (hipStream_t)hip_stream;
+  c->use_graphs = hip_stream != nullptr;  // the null stream cannot be captured
   c->ws = (char*)d_workspace;
   c->d = cfg->d_model;
   c->nq = cfg->n_heads;
@@ -702,7 +812,7 @@ extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
   if (hipHostMalloc((void**)&c->h_meta, c->meta_bytes, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_commit, sizeof(CommitReq) * cfg->max_requests,
                     hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_res, sizeof(int32_t) * cfg->max_requests * 66,
+      hipHostMalloc((void**)&c->h_res, sizeof(int32_t) * cfg->max_requests * (2 + kMaxPath),
                     hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_btab_row, sizeof(int32_t) * c->max_pages,
                     hipHostMallocDefault) != hipSuccess)
@@ -844,7 +954,7 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
     }
     const bool last = done + C == n;
     rc = forward(c, C, 1, {done + C}, {C}, false, C - 1, last ? 1 : 0,
-                 last ? d_logits_opt : nullptr, true);
+                 last ? d_logits_opt : nullptr, true, false);
     if (rc) return undo(rc);
     done += C;
   }
@@ -940,11 +1050,9 @@ extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
   }
   HIP_TRY(hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
                          c->stream));
-  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false);
+  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false, true);
   if (rc) return rc;
-  const int max_path = 64;
-  HIP_TRY(launch_path_walk(c->d_rows, c->d_reqs, n_req, c->amax, max_path, c->res,
-                           c->stream));
+  const int max_path = kMaxPath;
   HIP_TRY(hipMemcpyAsync(c->h_res, c->res, (size_t)n_req * (2 + max_path) * 4,
                          hipMemcpyDeviceToHost, c->stream));
   HIP_TRY(hipStreamSynchronize(c->stream));
@@ -1058,6 +1166,15 @@ extern "C" int32_t spec_set_fault(spec_ctx* c, int32_t token, float bias,
   return SPEC_OK;
 }
 
+extern "C" int32_t spec_use_graphs(spec_ctx* c, int32_t enable) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (enable && !c->stream)
+    return fail(c, SPEC_E_UNSUPPORTED, "graphs need a stream other than the null stream");
+  c->use_graphs = enable != 0;
+  return SPEC_OK;
+}
+
 extern "C" int32_t spec_timing_enable(spec_ctx* c, int32_t cls) {
   int rc = check(c);
   if (rc) return rc;
@@ -1085,6 +1202,8 @@ extern "C" int32_t spec_timing_read(spec_ctx* c, double* total_ms, int64_t* laun
 extern "C" void spec_destroy(spec_ctx* c) {
   if (!c) return;
   if (c->stream) (void)hipStreamSynchronize(c->stream);
+  for (auto& g : c->graphs) (void)hipGraphExecDestroy(g.exec);
+  c->graphs.clear();
   for (auto& e : c->events) {
     (void)hipEventDestroy(e.first);
     (void)hipEventDestroy(e.second);

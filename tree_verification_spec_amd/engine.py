@@ -32,8 +32,11 @@ def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
 
 
 class Engine:
-    """Owns a device workspace (a torch uint8 tensor) and a libspec context
-    bound to torch's current stream on `device`."""
+    """Owns a device workspace (a torch uint8 tensor), a HIP stream of its
+    own (default priority; the library captures graphs on it) and a libspec
+    context bound to that stream on `device`.  Every library call that hands
+    results back synchronizes the stream first, so tensors it wrote may be
+    read on torch's current stream afterwards."""
 
     def __init__(self, model, device=0, **caps):
         import torch
@@ -48,7 +51,8 @@ class Engine:
             raise ValueError("invalid spec_config")
         with torch.cuda.device(self.device):
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-            self.stream = torch.cuda.current_stream(self.device)
+            self.stream = torch.cuda.Stream(device=self.device)
+            torch.cuda.synchronize(self.device)
             self.ctx = L.spec_create(self.cfg, self.workspace.data_ptr(), nbytes,
                                      self.stream.cuda_stream)
         self.workspace_bytes = nbytes
@@ -78,15 +82,20 @@ class Engine:
 
     def verify(self, reqs, drafts, parents, logits=False):
         """drafts/parents: one array per request.  Returns (paths, bonus
-        [, logits tensor [rows, vocab]])."""
+        [, logits tensor [rows, vocab]]).  The logits tensor is a view of one
+        buffer owned by the engine (so repeated passes keep one launch
+        shape): it is valid until the next verify."""
         n_nodes = [len(d) for d in drafts]
         flat_d = [int(t) for d in drafts for t in d]
         flat_p = [int(p) for ps in parents for p in ps]
         out = None
         if logits:
             rows = sum(n + 1 for n in n_nodes)
-            out = self.torch.empty((rows, self.model["vocab"]),
-                                   dtype=self.torch.float32, device=self.device)
+            if getattr(self, "_logits", None) is None:
+                self._logits = self.torch.empty((self.cfg.max_rows, self.model["vocab"]),
+                                                dtype=self.torch.float32,
+                                                device=self.device)
+            out = self._logits[:rows]
         paths, bonus = L.spec_verify(self.ctx, list(reqs), n_nodes, flat_d, flat_p,
                                      self.max_nodes,
                                      out.data_ptr() if out is not None else None)
@@ -107,6 +116,9 @@ class Engine:
 
     def set_fault(self, token, bias, after_position):
         return L.spec_set_fault(self.ctx, token, bias, after_position)
+
+    def use_graphs(self, enable):
+        L.spec_use_graphs(self.ctx, enable)
 
     def timing(self, cls):
         L.spec_timing_enable(self.ctx, cls)

@@ -1,18 +1,23 @@
 """Benchmark of the speculative-decoding verify step on one MI355X.
 
-Workload: 8B-shaped dense decoder (36 layers, d=4096, 32/8 GQA heads, FFN
-12288, vocab 151936, bf16 weights, random init), 2048-token random prompt,
-batch 1, chain drafts of K=16 tokens synthesised from the target's own
-greedy continuation with per-position match probability alpha (0.7 headline;
-0.5 and 0.9 reported too).  A step is one spec_verify + spec_commit.
+Default workload (the headline): 8B-shaped dense decoder (36 layers,
+d=4096, 32/8 GQA heads, FFN 12288, vocab 151936, bf16 weights, random init),
+2048-token random prompt, batch 1, chain drafts of K=16 tokens synthesised
+from the target's own greedy continuation with per-position match
+probability alpha (0.7 headline; 0.5 and 0.9 reported too).  A step is one
+spec_verify + spec_commit.  --workload selects the other measured
+workloads: a 64-node best-first tree at a 4096-token prompt, 32 batched
+requests (contexts 512..4096, K=8, alpha 0.4..0.9 per request) verified in
+one fused pass per step, and the 27B-shaped hybrid with 32-node trees.
 
-Reported: accepted tokens/s (emitted tokens over the summed step times; host
-draft synthesis excluded), the byte lower bound of a step
-(max(FLOPs at 60% of 2.5 PFLOP/s, bytes at 90% of 8 TB/s)) and the fraction
-of it reached, the GPU autoregressive rate (K=0, same library) and, for the
-dominant kernel (the FFN gate/up GEMM), algorithmic GB/s from per-launch HIP
-events against the 8 TB/s HBM peak.  The CPU oracle's AR decode rate on the
-same model is timed on a bounded sample as a reported baseline.
+Reported: accepted tokens/s (emitted tokens over the summed wall time of
+the verify + commit calls, inputs resident in HBM; host draft synthesis
+excluded), the byte lower bound of a step (max(FLOPs at 60% of 2.5 PFLOP/s,
+bytes at 90% of 8 TB/s)) and the fraction of it reached, the GPU
+autoregressive rate (K=0, same library) and, for the dominant kernel (the
+FFN gate/up GEMM), algorithmic GB/s from per-launch HIP events against the
+8 TB/s HBM peak.  The CPU oracle's AR decode rate on the same model is
+timed on a bounded sample as a reported baseline.
 """
 
 import argparse
@@ -27,21 +32,36 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, FLOP/s
 
+WORKLOADS = ("dense8b_chain", "dense8b_tree", "dense8b_batched", "hybrid27b_tree")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bounds(cfg, rows, ctx):
-    """Algorithmic bytes and FLOPs of one verify step of `rows` rows at
-    committed context `ctx` (weights once, committed KV once, new KV)."""
-    d, F, V = cfg["d_model"], cfg["ffn_dim"], cfg["vocab"]
-    nq, nkv, hd, L = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["n_layers"]
-    layer_params = d * (nq + 2 * nkv) * hd + nq * hd * d + 3 * F * d
-    params = L * layer_params + V * d
-    kv_pos = L * nkv * hd * 2 * 2
-    nbytes = params * 2 + ctx * kv_pos + rows * kv_pos
-    flops = 2 * params * rows + 4 * nq * hd * L * rows * (ctx + rows)
+def model_bytes(cfg):
+    """Weight elements read by a verify pass (every matrix but the
+    embedding, which is gathered) and the bytes of one cached position."""
+    import numpy as np
+    import synth
+    mats = sum(int(np.prod(shape)) for name, shape, kind in synth.tensor_specs(cfg)
+               if kind == "mat" and name != "embed")
+    n_attn = cfg["layer_kinds"].count("A")
+    kv_pos = n_attn * cfg["n_kv_heads"] * cfg["head_dim"] * 2 * 2
+    return mats, n_attn, kv_pos
+
+
+def step_bounds(cfg, req_rows, req_ctx):
+    """Algorithmic bytes, FLOPs and lower-bound seconds of one verify step:
+    weights once, every request's committed KV once, the pass's new KV, the
+    recurrent states read once and committed once."""
+    mats, n_attn, kv_pos = model_bytes(cfg)
+    n_lr = cfg["layer_kinds"].count("L")
+    R = sum(req_rows)
+    state = 2 * n_lr * cfg["d_model"] * cfg["lr_state"] * 4 * len(req_rows)
+    nbytes = mats * 2 + sum(req_ctx) * kv_pos + R * kv_pos + state
+    attn = sum(r * (c + r) for r, c in zip(req_rows, req_ctx))
+    flops = 2 * mats * R + 4 * cfg["n_heads"] * cfg["head_dim"] * n_attn * attn
     lb = max(flops / (0.6 * PEAK_BF16), nbytes / (0.9 * PEAK_HBM))
     return nbytes, flops, lb
 
@@ -51,7 +71,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--alpha", type=float, default=0.7)
+    ap.add_argument("--workload", default="dense8b_chain", choices=WORKLOADS)
+    ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -81,88 +102,128 @@ def main():
         del src, dst
         log(f"copy probe: {4 * n} bytes")
 
-    w = synth.workload("dense8b_chain")
+    w = synth.workload(args.workload)
     cfg = synth.model_config(w["model"])
-    K, P = w["K"], w["prompt"]
-    V = cfg["vocab"]
+    V, K, idx = cfg["vocab"], w["K"], w["index"]
+    batched = args.workload == "dense8b_batched"
+    tree = w["draft"] == "tree"
+    if batched:
+        B = w["batch"]
+        ctx0, alphas = synth.batched_mix(B, w["ctx_lo"], w["ctx_hi"], w["alpha_lo"],
+                                         w["alpha_hi"])
+        prompts = [synth.prompt_tokens(V, int(ctx0[r]), idx, r) for r in range(B)]
+        alpha_main = None
+    else:
+        B = 1
+        alphas = None
+        prompts = [synth.prompt_tokens(V, w["prompt"], idx)]
+        alpha_main = args.alpha if args.alpha is not None else w["alpha"]
+    sweep_alphas = [] if (args.no_sweep or batched or tree) else \
+        [a for a in w.get("alphas", ()) if abs(a - alpha_main) > 1e-9]
+    # reference length: enough tokens for every run's expected acceptance
+    depth = w.get("max_depth", 8) if tree else K
+    runs = [(alpha_main if not batched else 0.9, args.warmup + args.steps),
+            (alpha_main if not batched else 0.9, max(10, args.steps // 3) + 2)]
+    runs += [(a, max(20, args.steps // 2) + 4) for a in sweep_alphas]
+    need = max(synth.expected_tokens_per_step(a, depth) * n for a, n in runs)
+    ref_len = args.ref_len or min(int(need * 1.5) + 64, (depth + 1) *
+                                  max(n for _, n in runs) + 8)
+
     t0 = time.time()
     W = synth.make_weights(cfg)
     log(f"weights generated in {time.time() - t0:.1f}s")
-    ref_len = args.ref_len or (max(w["gen"], int((args.warmup + args.steps) * 3.5)) + K + 2)
-    eng = Engine(cfg, device=0, max_requests=2, max_ctx=P + ref_len + 2 * (K + 1),
-                 max_nodes=K + 1, prefill_chunk=512)
+    max_ctx = max(len(p) for p in prompts) + ref_len + 2 * (K + 1)
+    eng = Engine(cfg, device=0, max_requests=B, max_ctx=max_ctx, max_nodes=K + 1,
+                 max_rows=B * (K + 1), prefill_chunk=512)
     t0 = time.time()
     eng.load_weights([W[n] for n, _, _ in synth.tensor_specs(cfg)])
     log(f"weights loaded in {time.time() - t0:.1f}s")
-    prompt = synth.prompt_tokens(V, P, w["index"])
 
-    # ---- GPU autoregressive reference (K = 0): continuation + AR rate
+    # ---- GPU autoregressive reference (K = 0): continuations + AR rate
     sync = torch.cuda.synchronize
-    first = eng.prefill(0, prompt)
-    S = [first]
+    t0 = time.time()
+    S = [[eng.prefill(r, prompts[r])] for r in range(B)]
     sync()
+    log(f"prefill of {sum(len(p) for p in prompts)} tokens in {time.time() - t0:.1f}s")
     t_ar = 0.0
     for t in range(ref_len - 1):
         a = time.perf_counter()
-        paths, bonus = eng.verify([0], [[]], [[]])
-        eng.commit([0], [[]], bonus)
+        paths, bonus = eng.verify(list(range(B)), [[]] * B, [[]] * B)
+        eng.commit(list(range(B)), [[]] * B, bonus)
         sync()
         t_ar += time.perf_counter() - a
-        S.append(bonus[0])
-    eng.release(0)
-    S = np.array(S, np.int32)
-    ar_tps = (ref_len - 1) / t_ar
-    log(f"GPU AR: {ref_len - 1} tokens, {ar_tps:.1f} tok/s")
+        for r in range(B):
+            S[r].append(bonus[r])
+    for r in range(B):
+        eng.release(r)
+    S = [np.array(s, np.int32) for s in S]
+    ar_tps = B * (ref_len - 1) / t_ar
+    log(f"GPU AR: {ref_len - 1} tokens x {B} requests, {ar_tps:.1f} tok/s")
+
+    def drafts_for(r, g, step, alpha):
+        if tree:
+            return synth.tree_drafts(S[r], g, K, w["branching"], w["max_depth"], alpha, V,
+                                     idx, r, step)
+        return synth.chain_drafts(S[r], g, K, alpha, V, idx, r, step)
 
     def run(alpha, steps, warmup, timing_cls=0):
-        eng.prefill(1, prompt)
-        g, step = 1, 0
+        slots = list(range(B))  # the reference run released them
+        for r in range(B):
+            eng.prefill(slots[r], prompts[r])
+        g = [1] * B
         tot, toks, mism, lbs, lbs_b, dev_ms = 0.0, 0, 0, [], [], []
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
+        al = [float(a) for a in alphas] if batched else [alpha] * B
         for it in range(warmup + steps):
             timed = it >= warmup
             if timed and it == warmup and timing_cls:
                 eng.timing(timing_cls)
                 eng.timing_read()
-            d_t, d_p = synth.chain_drafts(S, g, K, alpha, V, w["index"], 0, step)
-            n_ctx, _ = eng.state(1)
+            dr = [drafts_for(r, g[r], it, al[r]) for r in range(B)]
+            ctx = [eng.state(slots[r])[0] for r in range(B)]
             sync()
             a = time.perf_counter()
             ev0.record(eng.stream)
-            paths, bonus = eng.verify([1], [d_t], [d_p])
-            emitted = [int(d_t[p]) for p in paths[0]] + [bonus[0]]
-            n_ok = 0
-            for j, tk in enumerate(emitted):
-                if g + j >= len(S) or tk != S[g + j]:
-                    break
-                n_ok += 1
-            if n_ok < len(emitted) and g + n_ok < len(S):
-                # token forcing: keep the run aligned with the reference
-                keep = paths[0][:n_ok] if n_ok < len(paths[0]) else paths[0]
-                eng.commit([1], [keep], [int(S[g + n_ok])])
-                n_new = len(keep) + 1
-                mism += 1
-            else:
-                eng.commit([1], paths, bonus)
-                n_new = len(emitted)
+            paths, bonus = eng.verify(slots, [d[0] for d in dr], [d[1] for d in dr])
+            keep, roots, n_new = [], [], []
+            for r in range(B):
+                emitted = [int(dr[r][0][p]) for p in paths[r]] + [bonus[r]]
+                n_ok = 0
+                for j, tk in enumerate(emitted):
+                    if g[r] + j >= len(S[r]) or tk != S[r][g[r] + j]:
+                        break
+                    n_ok += 1
+                if n_ok < len(emitted) and g[r] + n_ok < len(S[r]):
+                    # token forcing: keep the run aligned with the reference
+                    kp = paths[r][:n_ok] if n_ok < len(paths[r]) else paths[r]
+                    keep.append(kp)
+                    roots.append(int(S[r][g[r] + n_ok]))
+                    n_new.append(len(kp) + 1)
+                    mism += 1
+                else:
+                    keep.append(paths[r])
+                    roots.append(bonus[r])
+                    n_new.append(len(emitted))
+            eng.commit(slots, keep, roots)
             ev1.record(eng.stream)
             sync()
             dt = time.perf_counter() - a
             if timed:
                 tot += dt
-                toks += n_new
+                toks += sum(n_new)
                 dev_ms.append(ev0.elapsed_time(ev1))
-                nb, fl, lb = step_bounds(cfg, K + 1, n_ctx)
+                nb, fl, lb = step_bounds(cfg, [K + 1] * B, ctx)
                 lbs.append(lb)
                 lbs_b.append(nb)
-            g += n_new
-            step += 1
+            for r in range(B):
+                g[r] += n_new[r]
         kt = None
         if timing_cls:
             kt = eng.timing_read()
             eng.timing(0)
-        eng.release(1)
+        for r in range(B):
+            eng.release(slots[r])
         return dict(tps=toks / tot, ms=1e3 * tot / steps, toks=toks,
                     tok_per_step=toks / steps, mism=mism,
                     dev_ms=float(np.median(dev_ms)),
@@ -170,27 +231,26 @@ def main():
                     lb_ms=1e3 * float(np.mean(lbs)),
                     bytes=float(np.mean(lbs_b)), ktime=kt)
 
-    res = run(args.alpha, args.steps, args.warmup)
-    log(f"alpha={args.alpha}: {res}")
+    res = run(alpha_main, args.steps, args.warmup)
+    log(f"{args.workload} alpha={alpha_main}: {res}")
     # the dominant kernel's launch times, from HIP events the library records
     # around each gate/up launch (kernels launched one by one for this run)
-    rl = run(args.alpha, max(10, args.steps // 3), 2, timing_cls=1)
-    log(f"alpha={args.alpha} (timed launches): {rl}")
+    rl = run(alpha_main, max(10, args.steps // 3), 2, timing_cls=1)
+    log(f"timed launches: {rl}")
     sweep = {}
-    if not args.no_sweep:
-        for al in w["alphas"]:
-            if abs(al - args.alpha) < 1e-9:
-                continue
-            r = run(al, max(20, args.steps // 2), 4)
-            sweep[str(al)] = dict(tokens_per_s=round(r["tps"], 1),
-                                  tokens_per_step=round(r["tok_per_step"], 3),
-                                  lb_frac=round(r["lb_ms"] / r["dev_ms"], 4))
-            log(f"alpha={al}: {r}")
-    sweep[str(args.alpha)] = dict(tokens_per_s=round(res["tps"], 1),
-                                  tokens_per_step=round(res["tok_per_step"], 3),
-                                  lb_frac=round(res["lb_ms"] / res["dev_ms"], 4))
+    for al in sweep_alphas:
+        r = run(al, max(20, args.steps // 2), 4)
+        sweep[str(al)] = dict(tokens_per_s=round(r["tps"], 1),
+                              tokens_per_step=round(r["tok_per_step"], 3),
+                              lb_frac=round(r["lb_ms"] / r["dev_ms"], 4))
+        log(f"alpha={al}: {r}")
+    if not batched:
+        sweep[str(alpha_main)] = dict(tokens_per_s=round(res["tps"], 1),
+                                      tokens_per_step=round(res["tok_per_step"], 3),
+                                      lb_frac=round(res["lb_ms"] / res["dev_ms"], 4))
 
     # roofline of the dominant kernel: FFN gate/up GEMM, weights streamed once
+    # per launch (passes of more than 128 rows launch it once per 128 rows)
     gu_bytes = 2 * cfg["ffn_dim"] * cfg["d_model"] * 2
     k_ms, k_n = rl["ktime"]
     k_avg_s = k_ms / 1e3 / max(1, k_n)
@@ -200,6 +260,19 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, W, args.cpu_tokens)
 
+    if batched:
+        desc = ("8B-shaped dense decoder, 32 requests (contexts 512..4096 in 16-token "
+                "pages), chain drafts K=8, alpha 0.4..0.9 per request, one fused "
+                "verify per step")
+    elif tree:
+        model = ("8B-shaped dense decoder" if w["model"] == "dense8b" else
+                 "27B-shaped hybrid (48 recurrent + 16 attention layers)")
+        desc = (f"{model}, {w['prompt']}-token prompt, best-first draft tree of {K} "
+                f"nodes (depth <= {w['max_depth']}), alpha={alpha_main} on the main "
+                f"path, batch 1")
+    else:
+        desc = ("8B-shaped dense decoder, 2048-token prompt, chain draft K=16, "
+                "alpha=%.1f, batch 1" % alpha_main)
     out = {
         "metric": "accepted tokens/s at batch 1 + verify-step HBM GB/s vs byte lower bound",
         "value": round(res["tps"], 2),
@@ -214,9 +287,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (random-init weights N(0,0.02), uniform random prompt, "
                 "drafts from the target's greedy continuation)",
-        "config": {"workload": "8B-shaped dense decoder, 2048-token prompt, chain "
-                               "draft K=16, alpha=%.1f, batch 1" % args.alpha,
-                   "batch": 1, "draft_K": K, "alpha": args.alpha, "prompt": P},
+        "config": {"workload": desc, "name": args.workload, "batch": B, "draft_K": K,
+                   "alpha": alpha_main, "prompt": None if batched else w["prompt"]},
         "verify_step": {
             "device_ms_median": round(res["dev_ms"], 4),
             "byte_lower_bound_ms": round(res["lb_ms"], 4),
@@ -232,8 +304,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "FFN gate/up GEMM + SwiGLU (201.3 MB of weights per launch)",
+                     "traffic": (measured_traffic() if args.workload == "dense8b_chain"
+                                 else None),
+                     "kernel": "FFN gate/up GEMM + SwiGLU (%.1f MB of weights per launch)"
+                               % (gu_bytes / 1e6),
                      "launches": k_n, "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
     }
@@ -274,9 +348,9 @@ def measured_traffic():
 
 
 def cpu_baseline(cfg, W, n_tok):
-    """The oracle's AR decode rate on the same 8B model (fp32 numpy on the
-    host cores), after a short prompt; weight widening is done before the
-    timed tokens."""
+    """The oracle's AR decode rate on the same model (fp32 numpy on the host
+    cores), after a short prompt; weight widening is done before the timed
+    tokens."""
     import numpy as np
     import synth
     from oracle import Model
@@ -294,7 +368,7 @@ def cpu_baseline(cfg, W, n_tok):
     log(f"cpu oracle: {n_tok} tokens in {dt:.1f}s")
     return {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"AR greedy decode of {n_tok} tokens on the full 8B-shaped "
+            "sample": f"AR greedy decode of {n_tok} tokens on the full {cfg['name']} "
                       f"model after a 32-token prompt (context ~{32 + n_tok}), fp32 "
                       f"numpy with {cores} BLAS threads; weights widened to fp32 "
                       f"before timing"}

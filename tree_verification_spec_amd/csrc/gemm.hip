@@ -32,7 +32,8 @@ namespace {
 constexpr int kD = 8;  // minimum K-steps of W loads in flight per wave (rolling window)
 
 // Staged chunk width (K elements) per row-tile count: two LDS buffers of
-// MT*16 rows x (KC + pad) x 4 bytes stay near 64 KB.
+// MT*16 rows x (KC + pad) x 4 bytes stay near 64 KB (two workgroups per CU;
+// measured faster than larger chunks at every row count).
 template <int MT> struct ChunkK {
   static constexpr int value = MT <= 1 ? 256 : MT <= 2 ? 256 : MT <= 3 ? 160
                              : MT <= 4 ? 128 : MT <= 5 ? 96 : 64;
@@ -148,30 +149,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       __syncthreads();
       const T* hi = xbuf + buf * BUF_ELEMS;
       buf ^= 1;
-#pragma unroll
-      for (int j = 0; j < CSTEPS; ++j) {
-        const int u = cc * CSTEPS + j;
+      // activation fragments of K-step j + 1 are read from LDS while the
+      // MFMAs of step j run (software pipelining hides the LDS latency)
+      constexpr int XF = kBf ? 2 : 1;  // hi (+ lo) planes
+      Frag<T> xc[MT][XF], xn[MT][XF];
+      auto load_x = [&](Frag<T> (&x)[MT][XF], int j) {
         const int kk = j * 32 + g * 8;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int r = mt * 16 + r16;
-          Frag<T> x;
-          if constexpr (kBf) {
-            Frag<T> xl;
-            x.load(&hi[r * LDS_ROW + kk]);
-            xl.load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) {
-              mma32(acc[t][mt], w[u][t], x);
-              mma32(acc[t][mt], w[u][t], xl);
-            }
-          } else {
-            x.load(reinterpret_cast<const float*>(hi) + r * LDS_ROW + kk);
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) mma32(acc[t][mt], w[u][t], x);
-          }
+          x[mt][0].load(&hi[r * LDS_ROW + kk]);
+          if constexpr (kBf) x[mt][1].load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
         }
+      };
+      load_x(xc, 0);
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j) {
+        const int u = cc * CSTEPS + j;
+        if (j + 1 < CSTEPS) load_x(xn, j + 1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int p = 0; p < XF; ++p) mma32(acc[t][mt], w[u][t], xc[mt][p]);
         load_step(w[u], kw + u + WIN);
+        if (j + 1 < CSTEPS) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int p = 0; p < XF; ++p) xc[mt][p] = xn[mt][p];
+        }
       }
     }
   }
@@ -267,40 +275,68 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int kWaves = 8;  // waves per workgroup, one 16-column tile each
-constexpr int kNtw = 1;
+// Workgroup shapes: (tiles per wave, waves).  128 columns with one tile per
+// wave stream best when the rows are few; 256 columns with two tiles per
+// wave halve the LDS reads per MFMA and fill the CUs evenly when a
+// 128-column grid would leave a small second round; two tiles per wave on
+// 4 waves keep 128 columns for narrow matrices at more rows.
+struct Variant {
+  int ntw, waves;
+};
 
-template <typename T, int EPI>
+Variant gemm_variant(bool bf16, int N, int M) {
+  if (!bf16) return {1, 8};
+  const int b128 = N / 128, b256 = N / 256;
+  if (M <= 32) return (b128 > 256 && b128 < 512) ? Variant{2, 8} : Variant{1, 8};
+  return b256 >= 128 ? Variant{2, 8} : Variant{2, 4};
+}
+
+template <typename T, int EPI, int NTW, int WAVES, int D>
 hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_one<T, 1, kNtw, kWaves, EPI>(a, s);
-    case 2: return launch_one<T, 2, kNtw, kWaves, EPI>(a, s);
-    case 3: return launch_one<T, 3, kNtw, kWaves, EPI>(a, s);
-    case 4: return launch_one<T, 4, kNtw, kWaves, EPI>(a, s);
-    case 5: return launch_one<T, 5, kNtw, kWaves, EPI>(a, s);
-    default: return launch_one<T, 8, kNtw, kWaves, EPI>(a, s);
+    case 1: return launch_one<T, 1, NTW, WAVES, EPI, D>(a, s);
+    case 2: return launch_one<T, 2, NTW, WAVES, EPI, D>(a, s);
+    case 3: return launch_one<T, 3, NTW, WAVES, EPI, D>(a, s);
+    case 4: return launch_one<T, 4, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
+    case 5: return launch_one<T, 5, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
+    default: return launch_one<T, 8, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
   }
 }
 
+template <typename T, int EPI>
+hipError_t launch_var(Variant v, int mt, const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD>(mt, a, s);
+    if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD>(mt, a, s);
+  }
+  if (v.ntw == 1 && v.waves == 8) return launch_mt<T, EPI, 1, 8, kD>(mt, a, s);
+  return hipErrorInvalidValue;
+}
+
 template <typename T>
-hipError_t launch_typed(int epi, const GemmArgs& a, int mt, hipStream_t s) {
-  if (epi == EPI_PART) return launch_mt<T, EPI_PART>(mt, a, s);
-  if (epi == EPI_SWIGLU) return launch_mt<T, EPI_SWIGLU>(mt, a, s);
-  if (epi == EPI_ARGMAX) return launch_mt<T, EPI_ARGMAX>(mt, a, s);
+hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
+  if (epi == EPI_PART) return launch_var<T, EPI_PART>(v, mt, a, s);
+  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU>(v, mt, a, s);
+  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX>(v, mt, a, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int gemm_cols_per_block() { return kWaves * kNtw * 16; }
+int gemm_pad_cols() { return 256; }
 
-int gemm_splits(int K, int N, int M) {
-  // about one workgroup per CU (measured best for the 8B/27B shapes at
-  // 1..65 rows) and at least 256 reduction indices per split
-  (void)M;
-  const int nblk = N / gemm_cols_per_block();
+int gemm_argmax_blocks(bool bf16, int N, int M) {
+  const Variant v = gemm_variant(bf16, N, M);
+  return N / (v.ntw * v.waves * 16);
+}
+
+int gemm_splits(bool bf16, int K, int N, int M) {
+  // at most one workgroup per CU (the largest power-of-two split whose grid
+  // fits the 256 CUs) and at least 256 reduction indices per split
+  const Variant v = gemm_variant(bf16, N, M);
+  const int nblk = N / (v.ntw * v.waves * 16);
   int S = 1;
-  while (S * nblk < 256 && K / (S * 2) >= 256 && (K / (S * 2)) % 32 == 0) S *= 2;
+  while (2 * S * nblk <= 256 && K / (S * 2) >= 256 && (K / (S * 2)) % 32 == 0) S *= 2;
   return S;
 }
 
@@ -311,13 +347,18 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
     return hipErrorInvalidValue;
   a.KR = a.K / a.S;
   if (a.wsn <= 0 || a.wsk <= 0) return hipErrorInvalidValue;
+  // one workgroup shape for all row chunks (the ARGMAX block layout and the
+  // partial sums must not depend on the chunk)
+  const Variant v = gemm_variant(bf16, a.ntiles * 16, a.M);
+  if (a.ntiles % (v.ntw * v.waves)) return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX) a.nblocks = a.ntiles / (v.ntw * v.waves);
   for (int r0 = 0; r0 < a.M; r0 += 128) {
     const int rows = (a.M - r0 < 128) ? a.M - r0 : 128;
     const int need = (rows + 15) / 16;
     const int mt = need <= 5 ? need : 8;
     a.row0 = r0;
-    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, a, mt, s)
-                        : launch_typed<float>(epi, a, mt, s);
+    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, v, a, mt, s)
+                        : launch_typed<float>(epi, v, a, mt, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -70,13 +70,16 @@ struct GemmArgs {
   float bias;
 };
 
-// Output columns of one GEMM workgroup (ARGMAX partial blocks and RESID sums
-// of squares come per such block); K-split count of a matrix shape.
-int gemm_cols_per_block();
-int gemm_splits(int K, int N, int M);
+// Weight matrices have their output rows padded to a multiple of
+// gemm_pad_cols().  gemm_splits: the K split count launch_gemm expects for a
+// matrix shape at M rows (EPI_PART); gemm_argmax_blocks: the per-row column
+// blocks of the ARGMAX partials at M rows.
+int gemm_pad_cols();
+int gemm_splits(bool bf16, int K, int N, int M);
+int gemm_argmax_blocks(bool bf16, int N, int M);
 
-// Launch the skinny GEMM for rows [0, M): picks the tile shape and splits
-// rows into chunks when M exceeds one launch's row capacity.
+// Launch the skinny GEMM for rows [0, M): picks the workgroup shape and the
+// row-tile count, and splits rows into chunks of 128.
 hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, hipStream_t s);
 
 struct AttnArgs {

@@ -82,7 +82,7 @@ struct TileOrder {
   int wsn, wsk;
 };
 TileOrder tile_order(int N, int K, bool kmajor) {
-  const int cb = gemm_cols_per_block();
+  const int cb = gemm_pad_cols();
   const int nt = (N + cb - 1) / cb * cb / 16;
   return kmajor ? TileOrder{1, nt} : TileOrder{K / 32, 1};
 }
@@ -260,7 +260,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const int in_n = 3 * d + 2 * S;
   auto at = [&](size_t off) -> char* { return base ? base + off : nullptr; };
   // GEMM output rows are padded to whole workgroup column blocks
-  const int cb = gemm_cols_per_block();
+  const int cb = gemm_pad_cols();
   auto npad = [&](int n) { return (n + cb - 1) / cb * cb; };
 
   // weights
@@ -315,15 +315,15 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
                                      (size_t)kMaxSplitsPrefill * R);
   const size_t o_po = p.take(split_rows * nq * hd * 4);
   const size_t o_pml = p.take(split_rows * nq * 8);
-  const size_t o_amp = p.take((size_t)R * (npad(V) / cb) * 8);
+  const size_t o_amp = p.take((size_t)R * (npad(V) / 128) * 8);  // <= 128-column blocks
   const size_t o_amax = p.take((size_t)R * 4);
   const size_t o_res = p.take((size_t)cfg.max_requests * (2 + kMaxPath) * 4);
   // GEMM split partials: the largest S x N over the model's matrices, for
   // any row count up to R (the split count depends on the rows of a launch)
   size_t psz = 0;
   auto need_p = [&](int K, int N) {
-    for (int m = 1; m <= std::min(R, 128); ++m)
-      psz = std::max(psz, (size_t)gemm_splits(K, npad(N), m) * npad(N));
+    for (int m = 1; m <= R; ++m)
+      psz = std::max(psz, (size_t)gemm_splits(esz == 2, K, npad(N), m) * npad(N));
   };
   need_p(d, qkv_n);
   need_p(nq * hd, d);
@@ -490,7 +490,7 @@ GemmArgs gemm_args(const spec_ctx* c, const void* W, bool kmajor, const void* X,
   a.xlo = (int64_t)lo_off(c, ldx);
   a.M = M;
   a.K = K;
-  const int cb = gemm_cols_per_block();
+  const int cb = gemm_pad_cols();
   a.ntiles = (N + cb - 1) / cb * cb / 16;
   a.ncols = N;
   a.S = 1;
@@ -502,7 +502,7 @@ GemmArgs gemm_args(const spec_ctx* c, const void* W, bool kmajor, const void* X,
 
 // Split GEMM into the partial buffer; returns the split count used.
 int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err) {
-  g.S = gemm_splits(g.K, g.ntiles * 16, g.M);
+  g.S = gemm_splits(c->bf16, g.K, g.ntiles * 16, g.M);
   *err = launch_gemm(c->bf16, EPI_PART, g, c->stream);
   return g.S;
 }
@@ -687,7 +687,7 @@ int launch_pass(spec_ctx* c, const Pass& P) {
                             (const char*)c->u + (size_t)P.lm_row0 * d * c->esz, d, P.lm_rows,
                             d, c->V);
     lm.part = c->am_part;
-    lm.nblocks = lm.ntiles * 16 / gemm_cols_per_block();
+    lm.nblocks = gemm_argmax_blocks(c->bf16, lm.ntiles * 16, P.lm_rows);
     lm.logits = P.d_logits;
     lm.ldlog = c->V;
     lm.rows = c->d_rows + P.lm_row0;

@@ -17,8 +17,8 @@
 // operands q and P enter the MFMAs as bf16 hi + lo pairs, so only the stored
 // K and V are rounded.  V pages are stored transposed ([dim][16 tokens]) in
 // the cache so that the V^T operand is read directly.  Each split writes
-// un-normalised partials (O, running max, running sum), merged in split
-// order by attn_combine.
+// un-normalised partials (O, running max of the scores scaled by log2 e,
+// running sum), merged in split order by attn_combine.
 #include "common.h"
 #include "kernels.h"
 
@@ -78,7 +78,7 @@ constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = kAttnWaves * 64;
 
 template <typename T, int HD>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char attn_smem[];
   using L = SplitLds<T, HD>;
   T* sk = reinterpret_cast<T*>(attn_smem);      // [split][KS]
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   // overlaps the staging's)
   Frag<T> qf[HD / 32], qfl[HD / 32];
   load_q(t_beg + wave, qf, qfl);
+  asm volatile("" ::: "memory");  // keep these loads ahead of the staging
 
   constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
   constexpr int KCH_ROW = HD / EPC;              // chunks per K row
@@ -206,6 +207,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
       if (rm.anc_words > 1) anc_hi = am[1];
     }
 
+    const float scale2 = a.scale * 1.44269504088896340736f;  // log2(e)
     float m_run = -INFINITY, l_run = 0.f;
     floatx4_t o[HD / 16];
 #pragma unroll
@@ -214,52 +216,89 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     for (int kb = kbeg; kb < kend; kb += 32) {
       const int kl = kb - kbeg;  // key offset inside the staged split
       // ---- scores: S^T tiles for keys [kb, kb+16) and [kb+16, kb+32)
-      floatx4_t s[2];
+      // all K fragments of the block are read from LDS first, then the two
+      // independent score chains are interleaved (no exposed LDS latency,
+      // no back-to-back dependent MFMAs)
+      // (hi and lo halves of q accumulate separately: four chains of
+      // HD / 32 dependent MFMAs instead of two of twice that length)
+      floatx4_t s[2], sl[2];
+      Frag<T> kf[2][HD / 32];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ks = 0; ks < HD / 32; ++ks) {
-          Frag<T> kf;
-          kf.load(&sk[(size_t)(kl + kt * 16 + r16) * L::KS + ks * 32 + g * 8]);
-          mma32(s[kt], kf, qf[ks]);
-          if (kSplit) mma32(s[kt], kf, qfl[ks]);
+        for (int ks = 0; ks < HD / 32; ++ks)
+          kf[kt][ks].load(&sk[(size_t)(kl + kt * 16 + r16) * L::KS + ks * 32 + g * 8]);
+      s[0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      s[1] = s[0];
+      sl[0] = s[0];
+      sl[1] = s[0];
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        mma32(s[0], kf[0][ks], qf[ks]);
+        mma32(s[1], kf[1][ks], qf[ks]);
+        if (kSplit) {
+          mma32(sl[0], kf[0][ks], qfl[ks]);
+          mma32(sl[1], kf[1][ks], qfl[ks]);
         }
       }
-      // lane holds row r16, keys kb + kt*16 + 4g + r
+      if (kSplit) {
+        s[0] += sl[0];
+        s[1] += sl[1];
+      }
+      // visibility of the block's 32 keys for this lane's row, as a bit mask
+      // (bit i: key kb + i): keys past the split end are out; committed keys
+      // are in; a pass key (tree node tn = key - nctx) is in along a chain up
+      // to the row's own node, in a tree when tn is an ancestor or itself
+      uint32_t vis = 0;
+      if (qvalid) {
+        auto low_bits = [](int n) -> uint32_t {
+          return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : ((1u << n) - 1u);
+        };
+        const int c = rm.nctx - kb;  // committed keys in the block: [0, c)
+        uint32_t pass;
+        if (rm.chain) {
+          pass = low_bits(c + node + 1);
+        } else {
+          // block bit i <-> tree node i - c: the ancestor mask shifted by c
+          const int sh = -c;  // node of block bit 0 (may be negative)
+          uint64_t w;
+          if (sh >= 0) {
+            w = sh >= 128 ? 0 : sh >= 64 ? (anc_hi >> (sh - 64))
+                          : sh == 0 ? anc_lo : ((anc_lo >> sh) | (anc_hi << (64 - sh)));
+          } else {
+            w = -sh >= 64 ? 0 : (anc_lo << (-sh));
+          }
+          pass = (uint32_t)w;
+        }
+        vis = (low_bits(c) | pass) & low_bits(kend - kb);
+      }
+      // lane holds row r16, keys kb + kt*16 + 4g + r; scores in the base-2
+      // domain (scaled by log2 e) so that every weight is one v_exp_f32
       float p[8];
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = kb + kt * 16 + 4 * g + r;
-          bool ok = qvalid && t < kend;
-          if (ok && t >= rm.nctx) {
-            const int tn = t - rm.nctx;  // tree node of this key
-            if (rm.chain) ok = tn <= node;
-            else ok = (tn < 64 ? (anc_lo >> tn) : (anc_hi >> (tn - 64))) & 1ull;
-          }
-          const float v = ok ? s[kt][r] * a.scale : -INFINITY;
+          const bool ok = (vis >> (kt * 16 + 4 * g + r)) & 1u;
+          const float v = ok ? s[kt][r] * scale2 : -INFINITY;
           p[kt * 4 + r] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = quad_max(mx);
       // No lane may skip the MFMAs below (they read operands of all lanes),
       // so a row with nothing visible yet uses a finite stand-in maximum:
       // every weight is then 0 and the state stays (-inf, 0, O = 0).
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = expf(m_run - m_use);  // exp(-inf) = 0 on first block
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 2^-inf = 0
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = (p[e] == -INFINITY) ? 0.f : expf(p[e] - m_use);
+        p[e] = (p[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_use);
         lsum += p[e];
       }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
+      lsum = quad_sum(lsum);
       l_run = l_run * alpha + lsum;
       m_run = m_new;
 #pragma unroll
@@ -275,13 +314,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         pack_p(pf_lo, lo);
       }
       pack_p(pf, p);
+      // V fragments in groups of four dim tiles, read before their MFMAs
 #pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt) {
-        Frag<T> vf;
-        const T* vrow = sv + (size_t)(dt * 16 + r16) * VS + kl;
-        load_vfrag<T>(vf, vrow + 4 * g, vrow + 16 + 4 * g);
-        mma32(o[dt], vf, pf);
-        if (kSplit) mma32(o[dt], vf, pf_lo);
+      for (int d0 = 0; d0 < HD / 16; d0 += 4) {
+        Frag<T> vf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const T* vrow = sv + (size_t)((d0 + u) * 16 + r16) * VS + kl;
+          load_vfrag<T>(vf[u], vrow + 4 * g, vrow + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf);
+        if (kSplit) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf_lo);
+        }
       }
     }
 
@@ -314,8 +361,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   if (lane < nsplit) ml0 = a.part_ml[(size_t)lane * sstride + wid];
   if (lane + 64 < nsplit) ml1 = a.part_ml[(size_t)(lane + 64) * sstride + wid];
   const float M = wave_max(fmaxf(ml0.x, ml1.x));
-  const float w0 = (ml0.x == -INFINITY) ? 0.f : expf(ml0.x - M);
-  const float w1 = (ml1.x == -INFINITY) ? 0.f : expf(ml1.x - M);
+  // the running maxima are in the base-2 domain of the split kernel
+  const float w0 = (ml0.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml0.x - M);
+  const float w1 = (ml1.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml1.x - M);
   const float L = wave_sum(ml0.y * w0 + ml1.y * w1);
   constexpr int PER = HD / 64;
   constexpr int U = 8;  // splits per wave loaded together

@@ -93,6 +93,24 @@ __device__ __forceinline__ void store_act(float* hi, float* /*lo*/, size_t i,
   hi[i] = v;
 }
 
+// Reductions over the four lanes {l, l^16, l^32, l^48} (one MFMA output
+// column's four row groups) with the gfx950 row-swap instructions: after a
+// swap of a register with itself, the two results hold, in every lane, the
+// lane's own value and its partner's (in the same order in both lanes of a
+// pair, so the reduction is bitwise symmetric).
+__device__ __forceinline__ float quad_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -73,6 +73,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense8b_chain", choices=WORKLOADS)
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--weights", default="native", choices=("w12", "native"),
+                    help="weight storage: W12 (lossless 12-bit, bitwise-identical "
+                         "results) or the model's bf16")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -134,7 +137,7 @@ def main():
     log(f"weights generated in {time.time() - t0:.1f}s")
     max_ctx = max(len(p) for p in prompts) + ref_len + 2 * (K + 1)
     eng = Engine(cfg, device=0, max_requests=B, max_ctx=max_ctx, max_nodes=K + 1,
-                 max_rows=B * (K + 1), prefill_chunk=512)
+                 max_rows=B * (K + 1), prefill_chunk=512, weight_format=args.weights)
     t0 = time.time()
     eng.load_weights([W[n] for n, _, _ in synth.tensor_specs(cfg)])
     log(f"weights loaded in {time.time() - t0:.1f}s")
@@ -288,7 +291,8 @@ def main():
         "data": "synthetic (random-init weights N(0,0.02), uniform random prompt, "
                 "drafts from the target's greedy continuation)",
         "config": {"workload": desc, "name": args.workload, "batch": B, "draft_K": K,
-                   "alpha": alpha_main, "prompt": None if batched else w["prompt"]},
+                   "alpha": alpha_main, "prompt": None if batched else w["prompt"],
+                   "weights": args.weights},
         "verify_step": {
             "device_ms_median": round(res["dev_ms"], 4),
             "byte_lower_bound_ms": round(res["lb_ms"], 4),

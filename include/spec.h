@@ -51,6 +51,13 @@ enum {
 };
 
 enum { SPEC_DTYPE_FP32 = 0, SPEC_DTYPE_BF16 = 1 };
+/* Weight storage: the weights' own type, or W12 for bf16 models: each
+ * weight in 12 bits (sign, 4-bit exponent offset from its output row's
+ * base exponent, 7-bit mantissa) plus per-tile lists of the exceptions,
+ * restored exactly in registers by the GEMMs, so every result is bitwise
+ * the same as with bf16 storage while the weights move in ~0.78x the bytes
+ * (besthub.dev article, section "(1) W12: Lossless 12-bit Weight Format"). */
+enum { SPEC_WEIGHTS_NATIVE = 0, SPEC_WEIGHTS_W12 = 1 };
 enum { SPEC_LAYER_ATTN = 0, SPEC_LAYER_LR = 1 };
 
 #define SPEC_MAX_LAYERS 128
@@ -76,6 +83,7 @@ typedef struct spec_config {
   int32_t max_rows;       /* rows of one verify over all its requests        */
   int32_t prefill_chunk;  /* prompt rows per prefill pass                    */
   int32_t page_size;      /* tokens per KV page; must be 16                  */
+  int32_t weight_format;  /* SPEC_WEIGHTS_*; W12 needs SPEC_DTYPE_BF16        */
 } spec_config;
 
 typedef struct spec_ctx spec_ctx;

@@ -330,3 +330,104 @@ def test_full_width_trees(name, budget):
     rep = protocol_f(eng, cfg, orc, prompt, 14, w, "tree", cfg_index=53,
                      all_rows=True)
     _assert_ok(rep)
+
+
+# ------------------------------------------------- W12 weight storage
+
+def _run_steps(eng, cfg, prompt, steps, seed):
+    """Prefill, then verify + commit steps alternating chains and trees;
+    returns every pass's paths, bonus tokens and logits."""
+    V = cfg["vocab"]
+    rng = np.random.default_rng(seed)
+    tree_par = np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5])
+    first, lg = eng.prefill(0, prompt, logits=True)
+    out = [(first, lg.cpu().numpy().copy())]
+    for k in range(steps):
+        if k % 2:
+            toks, par = rng.integers(0, V, 12), tree_par
+        else:
+            toks, par = rng.integers(0, V, 8), np.arange(-1, 7)
+        paths, bonus, lg = eng.verify([0], [toks], [par], logits=True)
+        out.append((paths, bonus, lg.cpu().numpy().copy()))
+        eng.commit([0], paths, bonus)
+    return out
+
+
+def _assert_same(a, b):
+    assert a[0][0] == b[0][0] and np.array_equal(a[0][1], b[0][1])
+    for (pa, ba, la), (pb, bb, lb) in zip(a[1:], b[1:]):
+        assert pa == pb and ba == bb
+        assert np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa_bf16", "tiny_hybrid_bf16", "dense8b_l2"])
+def test_w12_weights_give_bitwise_identical_results(name):
+    """W12 storage restores every bf16 weight exactly, so logits, paths and
+    bonus tokens equal those of bf16 storage bit for bit."""
+    cfg, W = _setup(name)
+    prompt = synth.prompt_tokens(cfg["vocab"], 90, 55)
+    runs = []
+    for fmt in ("native", "w12"):
+        eng = engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format=fmt)
+        runs.append(_run_steps(eng, cfg, prompt, 6, 55))
+        eng.close()
+    _assert_same(*runs)
+
+
+def test_w12_exceptions():
+    """Weights the 12-bit code cannot hold: exact zeros, negative zeros,
+    bf16 subnormals and values far below their row's largest (a row with one
+    large weight), at most 7 in any tile.  Results must still equal bf16
+    storage bit for bit."""
+    cfg, W0 = _setup("tiny_gqa_bf16")
+    W = dict(W0)
+    names = [n for n, _, k in synth.tensor_specs(cfg) if k == "mat" and n != "embed"]
+    rng = np.random.default_rng(56)
+    for i, n in enumerate(names):
+        w = W[n].copy()                      # bf16 bit patterns (uint16)
+        r, c = w.shape
+        # one tile with exactly 7 exceptions (tile row t0 // 16, K-step 1)
+        t0 = ((i * 16) % r) // 16 * 16
+        full = (t0 // 16) * (c // 32) + 1
+        sel = rng.choice(512, 7, replace=False)
+        w[t0 + sel // 32, 32 + sel % 32] = 0
+        # scattered exact zeros, negative zeros and subnormals, one per tile
+        tiles = rng.choice((r // 16) * (c // 32), size=max(12, r * c // 4000),
+                           replace=False)
+        tiles = tiles[tiles != full]
+        rr = (tiles // (c // 32)) * 16 + rng.integers(0, 16, tiles.size)
+        cc = (tiles % (c // 32)) * 32 + rng.integers(0, 32, tiles.size)
+        vals = np.where(np.arange(tiles.size) % 3 == 0, 0x0000,
+                        np.where(np.arange(tiles.size) % 3 == 1, 0x8000,
+                                 rng.integers(1, 0x7F, tiles.size)))
+        w[rr, cc] = vals.astype(np.uint16)
+        # one row (outside that tile) with a large weight: its small weights
+        # leave the row's exponent window
+        w[(t0 + 16 + 3 * i % 16) % r, 5] = 0x3F80   # 1.0
+        W[n] = w
+    prompt = synth.prompt_tokens(cfg["vocab"], 60, 56)
+    runs = []
+    for fmt in ("native", "w12"):
+        eng = engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format=fmt)
+        runs.append(_run_steps(eng, cfg, prompt, 4, 56))
+        eng.close()
+    assert np.all(np.isfinite(runs[0][0][1]))
+    _assert_same(*runs)
+
+
+def test_w12_tile_over_capacity_is_rejected():
+    """A tile with more than 7 weights outside its rows' exponent windows
+    does not fit W12: the load fails with SPEC_E_UNSUPPORTED and the same
+    weights load in native format."""
+    from tree_verification_spec_amd import SpecError, SPEC_E_UNSUPPORTED
+    cfg, W0 = _setup("tiny_gqa_bf16")
+    W = dict(W0)
+    n = [n for n, _, k in synth.tensor_specs(cfg) if k == "mat" and n != "embed"][1]
+    w = W[n].copy()
+    sel = np.random.default_rng(3).choice(512, 8, replace=False)
+    w[16 + sel // 32, 64 + sel % 32] = 0
+    W[n] = w
+    with pytest.raises(SpecError) as ei:
+        engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="w12")
+    assert ei.value.code == SPEC_E_UNSUPPORTED
+    engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="native").close()

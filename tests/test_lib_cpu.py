@@ -45,6 +45,10 @@ def test_workspace_bytes_and_config_validation():
     assert L.spec_workspace_bytes(bad) == 0
     odd = dict(tiny, head_dim=96)
     assert L.spec_workspace_bytes(make_config(odd)) == 0
+    # W12 weight storage: bf16 models only
+    assert L.spec_workspace_bytes(make_config(tiny, weight_format="w12")) == 0
+    b16 = synth.model_config("tiny_gqa_bf16")
+    assert L.spec_workspace_bytes(make_config(b16, weight_format="w12")) > 0
     # the attention split table covers 64 splits of 128 keys
     assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8192)) > 0
     assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8193)) == 0

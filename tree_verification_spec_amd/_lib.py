@@ -20,6 +20,8 @@ SPEC_DTYPE_FP32 = 0
 SPEC_DTYPE_BF16 = 1
 SPEC_LAYER_ATTN = 0
 SPEC_LAYER_LR = 1
+SPEC_WEIGHTS_NATIVE = 0
+SPEC_WEIGHTS_W12 = 1
 SPEC_MAX_LAYERS = 128
 
 EXPORTS = [
@@ -40,6 +42,7 @@ class spec_config(ctypes.Structure):
         ("rms_eps", c_float), ("rope_theta", c_float),
         ("max_requests", c_int32), ("max_ctx", c_int32), ("max_nodes", c_int32),
         ("max_rows", c_int32), ("prefill_chunk", c_int32), ("page_size", c_int32),
+        ("weight_format", c_int32),
     ]
 
 

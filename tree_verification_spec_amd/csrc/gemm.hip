@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "w12.h"
 
 namespace {
 
@@ -39,7 +40,7 @@ template <int MT> struct ChunkK {
                              : MT <= 4 ? 128 : MT <= 5 ? 96 : 64;
 };
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D, bool W12>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr bool kBf = sizeof(T) == 2;
@@ -62,12 +63,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   constexpr int BUF_ELEMS = TROWS * LDS_ROW * (kBf ? 2 : 1);
   T* xbuf = reinterpret_cast<T*>(smem);
 
-  const Frag<T>* Wt = reinterpret_cast<const Frag<T>*>(a.W);
+  // weights: bf16 / fp32 tiles (a Frag per lane), or W12 tiles (12 bytes
+  // per lane plus one exception-slot word, decoded to a Frag before use)
+  static_assert(!W12 || sizeof(T) == 2, "W12 holds bf16 weights");
+  using WReg = typename std::conditional<W12, W12Raw, Frag<T>>::type;
   const Frag<T>* wbase[NTW];
+  const uint8_t* w12base[NTW];
+  uint32_t eb2[NTW];
 #pragma unroll
-  for (int t = 0; t < NTW; ++t)
-    wbase[t] = Wt + (size_t)((nb * WAVES + wave) * NTW + t) * a.wsn * 64 + lane;
-  const size_t wk = (size_t)a.wsk * 64;  // Frag stride between K-steps
+  for (int t = 0; t < NTW; ++t) {
+    const size_t tr = (size_t)((nb * WAVES + wave) * NTW + t);  // tile row
+    if constexpr (W12) {
+      w12base[t] = reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * kW12TileBytes;
+      const uint32_t e = a.eb[tr * 16 + r16];
+      eb2[t] = e | (e << 16);
+    } else {
+      wbase[t] = reinterpret_cast<const Frag<T>*>(a.W) + tr * a.wsn * 64 + lane;
+      eb2[t] = 0;
+    }
+  }
+  const size_t wk = (size_t)a.wsk * (W12 ? kW12TileBytes : 64);  // stride between K-steps
 
   floatx4_t acc[NTW][MT];
 #pragma unroll
@@ -126,11 +141,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // end are clamped to the last tile (an L2 hit) and staged activations past
   // the end are zero, so padded steps add nothing.  This keeps the
   // compiler's in-order load counters exact (no drain at chunk boundaries).
-  Frag<T> w[WIN][NTW];
-  auto load_step = [&](Frag<T> (&dst)[NTW], int kb) {
+  WReg w[WIN][NTW];
+  auto load_step = [&](WReg (&dst)[NTW], int kb) {
     const int k = kb < kb_end ? kb : kb_end - 1;
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) dst[t] = wbase[t][(size_t)k * wk];
+    for (int t = 0; t < NTW; ++t) {
+      if constexpr (W12) {
+        const uint8_t* p = w12base[t] + (size_t)k * wk;
+        const uint3 d = *reinterpret_cast<const uint3*>(p + lane * 12);
+        dst[t] = W12Raw{d.x, d.y, d.z,
+                        *reinterpret_cast<const uint32_t*>(p + (kW12SlotDword + (lane & 7)) * 4)};
+      } else {
+        dst[t] = wbase[t][(size_t)k * wk];
+      }
+    }
+  };
+  // the weight operand of one K-step (W12: decoded, exceptions restored;
+  // no memory access here, so the window's load counters stay exact)
+  auto wfrag = [&](const WReg& r, int t) -> Frag<T> {
+    if constexpr (W12) {
+      Frag<T> f;
+      f.v = w12_decode(r, eb2[t]);
+      w12_patch(f.v, r, lane);
+      return f;
+    } else {
+      (void)t;
+      return r;
+    }
   };
   // the first chunk is fetched now (before the W window, as in the steady
   // state); each chunk is stored into LDS at its start and the next one is
@@ -167,12 +204,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       for (int j = 0; j < CSTEPS; ++j) {
         const int u = cc * CSTEPS + j;
         if (j + 1 < CSTEPS) load_x(xn, j + 1);
+        Frag<T> wf[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) wf[t] = wfrag(w[u][t], t);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int t = 0; t < NTW; ++t)
 #pragma unroll
-            for (int p = 0; p < XF; ++p) mma32(acc[t][mt], w[u][t], xc[mt][p]);
+            for (int p = 0; p < XF; ++p) mma32(acc[t][mt], wf[t], xc[mt][p]);
         load_step(w[u], kw + u + WIN);
         if (j + 1 < CSTEPS) {
 #pragma unroll
@@ -257,9 +297,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, bool W12 = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D>;
+  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, W12>;
   constexpr int KC = ChunkK<MT>::value;
   const size_t stage_b = 2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * 4;
   const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
@@ -291,34 +331,43 @@ Variant gemm_variant(bool bf16, int N, int M) {
   return b256 >= 128 ? Variant{2, 8} : Variant{2, 4};
 }
 
-template <typename T, int EPI, int NTW, int WAVES, int D>
+template <typename T, int EPI, int NTW, int WAVES, int D, bool W12>
 hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_one<T, 1, NTW, WAVES, EPI, D>(a, s);
-    case 2: return launch_one<T, 2, NTW, WAVES, EPI, D>(a, s);
-    case 3: return launch_one<T, 3, NTW, WAVES, EPI, D>(a, s);
-    case 4: return launch_one<T, 4, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
-    case 5: return launch_one<T, 5, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
-    default: return launch_one<T, 8, NTW, WAVES, EPI, (NTW > 1 ? 4 : D)>(a, s);
+    case 1: return launch_one<T, 1, NTW, WAVES, EPI, D, W12>(a, s);
+    case 2: return launch_one<T, 2, NTW, WAVES, EPI, D, W12>(a, s);
+    case 3: return launch_one<T, 3, NTW, WAVES, EPI, D, W12>(a, s);
+    case 4: return launch_one<T, 4, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
+    case 5: return launch_one<T, 5, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
+    default: return launch_one<T, 8, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
   }
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, bool W12>
 hipError_t launch_var(Variant v, int mt, const GemmArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD>(mt, a, s);
-    if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD>(mt, a, s);
+    if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, W12>(mt, a, s);
+    if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD, W12>(mt, a, s);
   }
-  if (v.ntw == 1 && v.waves == 8) return launch_mt<T, EPI, 1, 8, kD>(mt, a, s);
+  if (v.ntw == 1 && v.waves == 8) return launch_mt<T, EPI, 1, 8, kD, W12>(mt, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, bool W12>
+hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
+  if (epi == EPI_PART) return launch_var<T, EPI_PART, W12>(v, mt, a, s);
+  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, W12>(v, mt, a, s);
+  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, W12>(v, mt, a, s);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
-  if (epi == EPI_PART) return launch_var<T, EPI_PART>(v, mt, a, s);
-  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU>(v, mt, a, s);
-  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX>(v, mt, a, s);
-  return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    if (a.w12) return launch_fmt<T, true>(epi, v, a, mt, s);
+  }
+  if (a.w12) return hipErrorInvalidValue;
+  return launch_fmt<T, false>(epi, v, a, mt, s);
 }
 
 }  // namespace

@@ -40,6 +40,7 @@ constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 constexpr bool kKmajorQkv = true;
 constexpr bool kKmajorOut = false;
 constexpr int kStagingBytes = 64 << 20;
+constexpr int kW12MaxExcHost = 7;  // exceptions one W12 tile holds (w12.h)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -50,27 +51,40 @@ struct Req {
   std::vector<int> pages;
 };
 
+// One weight matrix [N, K] in the tiled layout (kernels.h), as bf16 / fp32
+// tiles or as W12 tiles (w12.h).  The region is sized for the uncompressed
+// tiles (W12 uses ~78% of it).
+struct WMat {
+  void* p = nullptr;
+  size_t bytes = 0;      // region size
+  int n = 0, k = 0;      // padded output rows, reduction length
+  bool kmajor = false;   // tile order
+  uint8_t* eb = nullptr; // W12: per-row base exponents [n]
+  int* err = nullptr;    // W12: set when a tile does not fit the format
+};
+
 struct Layer {
   int kind = SPEC_LAYER_ATTN;
   int idx = 0;  // index among layers of its kind
   float* n1 = nullptr;
   float* n2 = nullptr;
-  void* wqkv = nullptr;  // attention: [Wq; Wk; Wv] tiled
-  void* wo = nullptr;
-  void* win = nullptr;   // recurrent: W_in tiled
-  void* wout = nullptr;
-  void* wgu = nullptr;   // gate/up tiles interleaved
-  void* wd = nullptr;
+  WMat wqkv;  // attention: [Wq; Wk; Wv]
+  WMat wo;
+  WMat win;   // recurrent: W_in
+  WMat wout;
+  WMat wgu;   // gate/up tiles interleaved
+  WMat wd;
 };
 
 // tensor id -> where it goes
 struct TensorSlot {
-  int kind;  // 0 embed, 1 norm, 2 matrix, 3 raw matrix part of a fused matrix
+  int kind;  // 0 embed, 1 norm, 2 matrix (or part of a fused matrix)
   int layer;
   int rows, cols;
   void* dst;
   int tile0, tile_stride;
-  int wsn = 0, wsk = 0;  // matrices: tile strides of the destination layout
+  int wsn = 0, wsk = 0;        // matrices: tile strides of the destination layout
+  const WMat* mat = nullptr;   // matrices: the destination
 };
 
 // Tile order of a weight matrix [N, K] (N padded to whole workgroup column
@@ -127,7 +141,10 @@ struct spec_ctx {
   std::vector<char> loaded;
 
   void* embed = nullptr;
-  void* lm_head = nullptr;
+  WMat lm_head;
+  bool w12 = false;          // weights stored as W12 tiles
+  uint8_t* eb_tmp = nullptr; // W12 encoding: base exponents of one slab's rows
+  size_t w12_side0 = 0, w12_side_bytes = 0;  // W12 side data (zeroed at create)
   float* final_norm = nullptr;
 
   // KV pool
@@ -231,6 +248,10 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->vocab % 16 || cfg->vocab <= 0) return bad("vocab must be a multiple of 16");
   if ((cfg->n_heads * cfg->head_dim) % 32) return bad("n_heads*head_dim");
   if (cfg->page_size != 16) return bad("page_size must be 16");
+  if (cfg->weight_format != SPEC_WEIGHTS_NATIVE && cfg->weight_format != SPEC_WEIGHTS_W12)
+    return bad("weight_format");
+  if (cfg->weight_format == SPEC_WEIGHTS_W12 && cfg->dtype != SPEC_DTYPE_BF16)
+    return bad("W12 weights need a bf16 model");
   if (cfg->max_requests <= 0 || cfg->max_ctx <= 0) return bad("capacity");
   if (cfg->max_nodes < 1 || cfg->max_nodes > 65) return bad("max_nodes must be in [1, 65]");
   if (cfg->max_rows < cfg->max_nodes) return bad("max_rows < max_nodes");
@@ -263,29 +284,65 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const int cb = gemm_pad_cols();
   auto npad = [&](int n) { return (n + cb - 1) / cb * cb; };
 
-  // weights
-  std::vector<size_t> off_l1, off_l2, off_qkv, off_o, off_in, off_out, off_gu, off_d;
+  // weights; every matrix region holds its uncompressed tiles, and with
+  // W12 also a base exponent per output row and two counters
+  const bool w12 = cfg.weight_format == SPEC_WEIGHTS_W12;
+  struct MatPlan {
+    size_t off = 0, bytes = 0, off_eb = 0, off_cnt = 0;
+    int n = 0, k = 0;
+    bool kmajor = false;
+  };
+  auto mat = [&](int N, int K, bool kmajor) {
+    MatPlan m;
+    m.n = npad(N);
+    m.k = K;
+    m.kmajor = kmajor;
+    m.bytes = (size_t)m.n * K * esz;
+    m.off = p.take(m.bytes);
+    return m;
+  };
+  std::vector<size_t> off_l1, off_l2;
+  std::vector<MatPlan> m_qkv, m_o, m_in, m_out, m_gu, m_d;
   const size_t o_embed = p.take((size_t)V * d * esz);
   for (int i = 0; i < cfg.n_layers; ++i) {
     off_l1.push_back(p.take((size_t)d * 4));
     if (cfg.layer_kind[i] == SPEC_LAYER_ATTN) {
-      off_qkv.push_back(p.take((size_t)npad(qkv_n) * d * esz));
-      off_o.push_back(p.take((size_t)npad(d) * nq * hd * esz));
-      off_in.push_back(0);
-      off_out.push_back(0);
+      m_qkv.push_back(mat(qkv_n, d, kKmajorQkv));
+      m_o.push_back(mat(d, nq * hd, kKmajorOut));
+      m_in.push_back(MatPlan{});
+      m_out.push_back(MatPlan{});
     } else {
-      off_qkv.push_back(0);
-      off_o.push_back(0);
-      off_in.push_back(p.take((size_t)npad(in_n) * d * esz));
-      off_out.push_back(p.take((size_t)npad(d) * d * esz));
+      m_qkv.push_back(MatPlan{});
+      m_o.push_back(MatPlan{});
+      m_in.push_back(mat(in_n, d, kKmajorQkv));
+      m_out.push_back(mat(d, d, kKmajorOut));
     }
     off_l2.push_back(p.take((size_t)d * 4));
-    off_gu.push_back(p.take((size_t)2 * F * d * esz));
-    off_d.push_back(p.take((size_t)npad(d) * F * esz));
+    m_gu.push_back(mat(2 * F, d, true));
+    m_d.push_back(mat(d, F, kKmajorOut));
   }
   const size_t o_fnorm = p.take((size_t)d * 4);
-  const size_t o_lm = p.take((size_t)npad(V) * d * esz);
+  MatPlan m_lm = mat(V, d, true);
   const size_t weights_end = p.cursor;
+  // W12 side data: base exponents and counters of every matrix, and the
+  // base exponents of one slab during encoding
+  auto side = [&](MatPlan& m) {
+    if (!w12 || m.n == 0) return;
+    m.off_eb = p.take((size_t)m.n);
+    m.off_cnt = p.take(sizeof(int));
+  };
+  for (int i = 0; i < cfg.n_layers; ++i) {
+    side(m_qkv[i]);
+    side(m_o[i]);
+    side(m_in[i]);
+    side(m_out[i]);
+    side(m_gu[i]);
+    side(m_d[i]);
+  }
+  side(m_lm);
+  const size_t o_ebtmp = w12 ? p.take((size_t)std::max({npad(V), npad(2 * F), npad(in_n),
+                                                        npad(qkv_n), npad(d)})) : 0;
+  const size_t w12_end = p.cursor;
 
   // KV pool: every request reserves max_ctx tokens
   const int max_pages = (cfg.max_ctx + 15) / 16;
@@ -346,9 +403,27 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const size_t o_commit = p.take((size_t)cfg.max_requests * sizeof(CommitReq));
 
   if (c && base) {
+    auto wmat = [&](const MatPlan& m) {
+      WMat w;
+      if (m.n == 0) return w;
+      w.p = at(m.off);
+      w.bytes = m.bytes;
+      w.n = m.n;
+      w.k = m.k;
+      w.kmajor = m.kmajor;
+      if (w12) {
+        w.eb = (uint8_t*)at(m.off_eb);
+        w.err = (int*)at(m.off_cnt);
+      }
+      return w;
+    };
     c->embed = at(o_embed);
     c->final_norm = (float*)at(o_fnorm);
-    c->lm_head = at(o_lm);
+    c->lm_head = wmat(m_lm);
+    c->w12 = w12;
+    c->eb_tmp = w12 ? (uint8_t*)at(o_ebtmp) : nullptr;
+    c->w12_side0 = weights_end;
+    c->w12_side_bytes = w12_end - weights_end;
     int ia = 0, il = 0;
     c->layers.resize(cfg.n_layers);
     for (int i = 0; i < cfg.n_layers; ++i) {
@@ -357,15 +432,12 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
       L.idx = L.kind == SPEC_LAYER_ATTN ? ia++ : il++;
       L.n1 = (float*)at(off_l1[i]);
       L.n2 = (float*)at(off_l2[i]);
-      if (L.kind == SPEC_LAYER_ATTN) {
-        L.wqkv = at(off_qkv[i]);
-        L.wo = at(off_o[i]);
-      } else {
-        L.win = at(off_in[i]);
-        L.wout = at(off_out[i]);
-      }
-      L.wgu = at(off_gu[i]);
-      L.wd = at(off_d[i]);
+      L.wqkv = wmat(m_qkv[i]);
+      L.wo = wmat(m_o[i]);
+      L.win = wmat(m_in[i]);
+      L.wout = wmat(m_out[i]);
+      L.wgu = wmat(m_gu[i]);
+      L.wd = wmat(m_d[i]);
     }
     c->kpool = at(o_k);
     c->vpool = at(o_v);
@@ -413,12 +485,12 @@ void build_slots(spec_ctx* c) {
   const spec_config& cfg = c->cfg;
   const int d = c->d, hd = c->hd, F = c->F;
   c->slots.clear();
-  auto mat = [&](int layer, int rows, int cols, void* dst, int tile0, int tstride, int N,
-                 bool kmajor) {
-    const TileOrder o = tile_order(N, cols, kmajor);
-    TensorSlot t{2, layer, rows, cols, dst, tile0, tstride};
+  auto mat = [&](int layer, int rows, int cols, const WMat& m, int tile0, int tstride) {
+    const TileOrder o = tile_order(m.n, cols, m.kmajor);
+    TensorSlot t{2, layer, rows, cols, m.p, tile0, tstride};
     t.wsn = o.wsn;
     t.wsk = o.wsk;
+    t.mat = &m;
     c->slots.push_back(t);
   };
   c->slots.push_back({0, -1, c->V, d, c->embed, 0, 1});
@@ -426,21 +498,21 @@ void build_slots(spec_ctx* c) {
     Layer& L = c->layers[i];
     c->slots.push_back({1, i, d, 1, L.n1, 0, 1});
     if (L.kind == SPEC_LAYER_ATTN) {
-      mat(i, c->nq * hd, d, L.wqkv, 0, 1, c->qkv_n, kKmajorQkv);
-      mat(i, c->nkv * hd, d, L.wqkv, c->nq * hd / 16, 1, c->qkv_n, kKmajorQkv);
-      mat(i, c->nkv * hd, d, L.wqkv, (c->nq + c->nkv) * hd / 16, 1, c->qkv_n, kKmajorQkv);
-      mat(i, d, c->nq * hd, L.wo, 0, 1, d, kKmajorOut);
+      mat(i, c->nq * hd, d, L.wqkv, 0, 1);
+      mat(i, c->nkv * hd, d, L.wqkv, c->nq * hd / 16, 1);
+      mat(i, c->nkv * hd, d, L.wqkv, (c->nq + c->nkv) * hd / 16, 1);
+      mat(i, d, c->nq * hd, L.wo, 0, 1);
     } else {
-      mat(i, c->in_n, d, L.win, 0, 1, c->in_n, kKmajorQkv);
-      mat(i, d, d, L.wout, 0, 1, d, kKmajorOut);
+      mat(i, c->in_n, d, L.win, 0, 1);
+      mat(i, d, d, L.wout, 0, 1);
     }
     c->slots.push_back({1, i, d, 1, L.n2, 0, 1});
-    mat(i, F, d, L.wgu, 0, 2, 2 * F, true);   // gate -> even tiles
-    mat(i, F, d, L.wgu, 1, 2, 2 * F, true);   // up   -> odd tiles
-    mat(i, d, F, L.wd, 0, 1, d, kKmajorOut);
+    mat(i, F, d, L.wgu, 0, 2);   // gate -> even tiles
+    mat(i, F, d, L.wgu, 1, 2);   // up   -> odd tiles
+    mat(i, d, F, L.wd, 0, 1);
   }
   c->slots.push_back({1, -1, d, 1, c->final_norm, 0, 1});
-  mat(-1, c->V, d, c->lm_head, 0, 1, c->V, true);
+  mat(-1, c->V, d, c->lm_head, 0, 1);
   c->loaded.assign(c->slots.size(), 0);
 }
 
@@ -478,13 +550,15 @@ size_t lo_off(const spec_ctx* c, int width) {
   return c->bf16 ? (size_t)c->Rmax * width : 0;
 }
 
-GemmArgs gemm_args(const spec_ctx* c, const void* W, bool kmajor, const void* X,
-                   int ldx, int M, int K, int N) {
+GemmArgs gemm_args(const spec_ctx* c, const WMat& W, const void* X, int ldx, int M,
+                   int K, int N) {
   GemmArgs a{};
-  a.W = W;
-  const TileOrder o = tile_order(N, K, kmajor);
+  a.W = W.p;
+  const TileOrder o = tile_order(N, K, W.kmajor);
   a.wsn = o.wsn;
   a.wsk = o.wsk;
+  a.w12 = c->w12 ? 1 : 0;
+  a.eb = W.eb;
   a.X = X;
   a.ldx = ldx;
   a.xlo = (int64_t)lo_off(c, ldx);
@@ -627,7 +701,7 @@ int launch_pass(spec_ctx* c, const Pass& P) {
     // norm, or the final norm in front of the LM head
     const float* next_norm = li + 1 < cfg.n_layers ? c->layers[li + 1].n1 : c->final_norm;
     if (L.kind == SPEC_LAYER_ATTN) {
-      GemmArgs g = gemm_args(c, L.wqkv, kKmajorQkv, c->u, d, R, d, c->qkv_n);
+      GemmArgs g = gemm_args(c, L.wqkv, c->u, d, R, d, c->qkv_n);
       const int S = gemm_part(c, g, &e);
       HIP_TRY(e);
       char* kc = c->kpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
@@ -641,14 +715,14 @@ int launch_pass(spec_ctx* c, const Pass& P) {
       HIP_TRY(launch_attention(bf, aa, s));
       time_end(c, 4);
       HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, lo_off(c, nq * hd), s));
-      GemmArgs o = gemm_args(c, L.wo, kKmajorOut, c->attn_o, nq * hd, R, nq * hd, d);
+      GemmArgs o = gemm_args(c, L.wo, c->attn_o, nq * hd, R, nq * hd, d);
       const int So = gemm_part(c, o, &e);
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
       HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
                                   L.n2, eps, c->u, u_lo, s));
     } else {
-      GemmArgs g = gemm_args(c, L.win, kKmajorQkv, c->u, d, R, d, c->in_n);
+      GemmArgs g = gemm_args(c, L.win, c->u, d, R, d, c->in_n);
       const int S = gemm_part(c, g, &e);
       HIP_TRY(e);
       const int ld = g.ntiles * 16;
@@ -657,21 +731,21 @@ int launch_pass(spec_ctx* c, const Pass& P) {
       HIP_TRY(launch_lr_fork(bf, c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
                              n_req, d, c->S, H, c->lr_o, lo_off(c, d), save, any_tree,
                              prefill, max_rows_req, s));
-      GemmArgs o = gemm_args(c, L.wout, kKmajorOut, c->lr_o, d, R, d, d);
+      GemmArgs o = gemm_args(c, L.wout, c->lr_o, d, R, d, d);
       const int So = gemm_part(c, o, &e);
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
       HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
                                   L.n2, eps, c->u, u_lo, s));
     }
-    GemmArgs gu = gemm_args(c, L.wgu, true, c->u, d, R, d, 2 * F);
+    GemmArgs gu = gemm_args(c, L.wgu, c->u, d, R, d, 2 * F);
     gu.Y = c->act;
     gu.ldy = F;
     gu.ylo = (int64_t)lo_off(c, F);
     time_begin(c, 1);
     HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, s));
     time_end(c, 1);
-    GemmArgs dn = gemm_args(c, L.wd, kKmajorOut, c->act, F, R, F, d);
+    GemmArgs dn = gemm_args(c, L.wd, c->act, F, R, F, d);
     time_begin(c, 2);
     const int Sd = gemm_part(c, dn, &e);
     HIP_TRY(e);
@@ -683,7 +757,7 @@ int launch_pass(spec_ctx* c, const Pass& P) {
 
   // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
   if (P.lm_rows > 0) {
-    GemmArgs lm = gemm_args(c, c->lm_head, true,
+    GemmArgs lm = gemm_args(c, c->lm_head,
                             (const char*)c->u + (size_t)P.lm_row0 * d * c->esz, d, P.lm_rows,
                             d, c->V);
     lm.part = c->am_part;
@@ -834,6 +908,8 @@ extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
       hipMemsetAsync(c->d_btab, 0, (size_t)cfg->max_requests * c->max_pages * 4,
                      c->stream) != hipSuccess ||
       hipMemsetAsync(c->ws, 0, c->weights_end, c->stream) != hipSuccess ||
+      (c->w12_side_bytes &&
+       hipMemsetAsync(c->ws + c->w12_side0, 0, c->w12_side_bytes, c->stream) != hipSuccess) ||
       (c->n_lr && hipMemsetAsync(c->H, 0, c->H_layer * 4 * c->n_lr, c->stream) != hipSuccess) ||
       hipStreamSynchronize(c->stream) != hipSuccess)
     return cleanup(SPEC_E_HIP);
@@ -864,7 +940,7 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
       from = c->staging;
     }
     HIP_TRY(launch_to_f32(c->bf16, from, t.rows, (float*)t.dst, s));
-  } else {  // matrix -> tiles
+  } else {  // matrix -> tiles (bf16 / fp32, or W12)
     if (t.rows % 16 || t.cols % 32)
       return fail(c, SPEC_E_UNSUPPORTED, "tensor %d shape %dx%d not tileable", tensor_id,
                   t.rows, t.cols);
@@ -872,6 +948,7 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
     int slab = src_on_device ? t.rows : (int)((size_t)kStagingBytes / row_bytes) / 16 * 16;
     if (slab <= 0)
       return fail(c, SPEC_E_UNSUPPORTED, "tensor %d rows too long for staging", tensor_id);
+    const WMat& m = *t.mat;
     for (int r0 = 0; r0 < t.rows; r0 += slab) {
       const int nr = std::min(slab, t.rows - r0);
       const char* from = (const char*)src + (size_t)r0 * row_bytes;
@@ -879,10 +956,25 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
         HIP_TRY(hipMemcpyAsync(c->staging, from, (size_t)nr * row_bytes, kind, s));
         from = (const char*)c->staging;
       }
-      HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst,
-                              t.tile0 + (r0 / 16) * t.tile_stride, t.tile_stride, t.wsn,
-                              t.wsk, s));
+      const int tile0 = t.tile0 + (r0 / 16) * t.tile_stride;
+      if (c->w12) {
+        HIP_TRY(launch_w12_rowexp(from, nr, t.cols, c->eb_tmp, s));
+        HIP_TRY(launch_w12_encode(from, nr, t.cols, c->eb_tmp, m.eb, t.dst, tile0,
+                                  t.tile_stride, t.wsn, t.wsk, m.err, s));
+      } else {
+        HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst, tile0, t.tile_stride,
+                                t.wsn, t.wsk, s));
+      }
       if (!src_on_device) HIP_TRY(hipStreamSynchronize(s));
+    }
+    if (c->w12) {
+      int err = 0;
+      HIP_TRY(hipMemcpyAsync(&err, m.err, sizeof(int), hipMemcpyDeviceToHost, s));
+      HIP_TRY(hipStreamSynchronize(s));
+      if (err)
+        return fail(c, SPEC_E_UNSUPPORTED,
+                    "tensor %d: a tile has more than %d weights outside the W12 exponent "
+                    "window; load these weights in native format", tensor_id, kW12MaxExcHost);
     }
   }
   HIP_TRY(hipStreamSynchronize(s));

@@ -6,8 +6,9 @@ from . import _lib as L
 
 
 def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
-                max_rows=None, prefill_chunk=512):
-    """spec_config from a model-shape dict (keys as in synth.configs)."""
+                max_rows=None, prefill_chunk=512, weight_format="native"):
+    """spec_config from a model-shape dict (keys as in synth.configs).
+    weight_format: "native" (the model's dtype) or "w12" (bf16 models only)."""
     c = L.spec_config()
     c.n_layers = model["n_layers"]
     c.d_model = model["d_model"]
@@ -28,6 +29,10 @@ def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
     c.max_rows = max_rows if max_rows is not None else max_nodes * max_requests
     c.prefill_chunk = prefill_chunk
     c.page_size = 16
+    if weight_format not in ("native", "w12"):
+        raise ValueError(f"unknown weight format {weight_format!r}")
+    c.weight_format = (L.SPEC_WEIGHTS_W12 if weight_format == "w12"
+                       else L.SPEC_WEIGHTS_NATIVE)
     return c
 
 

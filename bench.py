@@ -1,7 +1,9 @@
 """Benchmark of the speculative-decoding verify step on one MI355X.
 
 Default workload (the headline): 8B-shaped dense decoder (36 layers,
-d=4096, 32/8 GQA heads, FFN 12288, vocab 151936, bf16 weights, random init),
+d=4096, 32/8 GQA heads, FFN 12288, vocab 151936, bf16 weights, random init,
+stored as W12: lossless 12-bit tiles whose GEMM results are bitwise those
+of bf16 storage; --weights native keeps bf16 tiles),
 2048-token random prompt, batch 1, chain drafts of K=16 tokens synthesised
 from the target's own greedy continuation with per-position match
 probability alpha (0.7 headline; 0.5 and 0.9 reported too).  A step is one
@@ -13,7 +15,8 @@ one fused pass per step, and the 27B-shaped hybrid with 32-node trees.
 Reported: accepted tokens/s (emitted tokens over the summed wall time of
 the verify + commit calls, inputs resident in HBM; host draft synthesis
 excluded), the byte lower bound of a step (max(FLOPs at 60% of 2.5 PFLOP/s,
-bytes at 90% of 8 TB/s)) and the fraction of it reached, the GPU
+bytes at 90% of 8 TB/s, weights counted in their stored format)) and the
+fraction of it reached, the GPU
 autoregressive rate (K=0, same library) and, for the dominant kernel (the
 FFN gate/up GEMM), algorithmic GB/s from per-launch HIP events against the
 8 TB/s HBM peak.  The CPU oracle's AR decode rate on the same model is
@@ -39,27 +42,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def model_bytes(cfg):
-    """Weight elements read by a verify pass (every matrix but the
+W12_BYTES_PER_WEIGHT = 800 / 512   # a W12 tile: 512 weights in 800 bytes
+
+
+def weight_bytes(rows, cols, fmt):
+    """Stored bytes of one [rows, cols] bf16 matrix: 2 per weight, or the
+    W12 tiles plus one base-exponent byte per row."""
+    if fmt == "w12":
+        return rows * cols * W12_BYTES_PER_WEIGHT + rows
+    return rows * cols * 2
+
+
+def model_bytes(cfg, fmt):
+    """Weight elements and bytes read by a verify pass (every matrix but the
     embedding, which is gathered) and the bytes of one cached position."""
-    import numpy as np
     import synth
-    mats = sum(int(np.prod(shape)) for name, shape, kind in synth.tensor_specs(cfg)
-               if kind == "mat" and name != "embed")
+    shapes = [shape for name, shape, kind in synth.tensor_specs(cfg)
+              if kind == "mat" and name != "embed"]
+    mats = sum(r * c for r, c in shapes)
+    wbytes = sum(weight_bytes(r, c, fmt) for r, c in shapes)
     n_attn = cfg["layer_kinds"].count("A")
     kv_pos = n_attn * cfg["n_kv_heads"] * cfg["head_dim"] * 2 * 2
-    return mats, n_attn, kv_pos
+    return mats, wbytes, n_attn, kv_pos
 
 
-def step_bounds(cfg, req_rows, req_ctx):
+def step_bounds(cfg, req_rows, req_ctx, fmt):
     """Algorithmic bytes, FLOPs and lower-bound seconds of one verify step:
-    weights once, every request's committed KV once, the pass's new KV, the
-    recurrent states read once and committed once."""
-    mats, n_attn, kv_pos = model_bytes(cfg)
+    weights once (in their stored format), every request's committed KV
+    once, the pass's new KV, the recurrent states read once and committed
+    once."""
+    mats, wbytes, n_attn, kv_pos = model_bytes(cfg, fmt)
     n_lr = cfg["layer_kinds"].count("L")
     R = sum(req_rows)
     state = 2 * n_lr * cfg["d_model"] * cfg["lr_state"] * 4 * len(req_rows)
-    nbytes = mats * 2 + sum(req_ctx) * kv_pos + R * kv_pos + state
+    nbytes = wbytes + sum(req_ctx) * kv_pos + R * kv_pos + state
     attn = sum(r * (c + r) for r, c in zip(req_rows, req_ctx))
     flops = 2 * mats * R + 4 * cfg["n_heads"] * cfg["head_dim"] * n_attn * attn
     lb = max(flops / (0.6 * PEAK_BF16), nbytes / (0.9 * PEAK_HBM))
@@ -73,7 +89,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense8b_chain", choices=WORKLOADS)
     ap.add_argument("--alpha", type=float, default=None)
-    ap.add_argument("--weights", default="native", choices=("w12", "native"),
+    ap.add_argument("--weights", default="w12", choices=("w12", "native"),
                     help="weight storage: W12 (lossless 12-bit, bitwise-identical "
                          "results) or the model's bf16")
     ap.add_argument("--no-sweep", action="store_true")
@@ -216,7 +232,7 @@ def main():
                 tot += dt
                 toks += sum(n_new)
                 dev_ms.append(ev0.elapsed_time(ev1))
-                nb, fl, lb = step_bounds(cfg, [K + 1] * B, ctx)
+                nb, fl, lb = step_bounds(cfg, [K + 1] * B, ctx, args.weights)
                 lbs.append(lb)
                 lbs_b.append(nb)
             for r in range(B):
@@ -254,7 +270,7 @@ def main():
 
     # roofline of the dominant kernel: FFN gate/up GEMM, weights streamed once
     # per launch (passes of more than 128 rows launch it once per 128 rows)
-    gu_bytes = 2 * cfg["ffn_dim"] * cfg["d_model"] * 2
+    gu_bytes = weight_bytes(2 * cfg["ffn_dim"], cfg["d_model"], args.weights)
     k_ms, k_n = rl["ktime"]
     k_avg_s = k_ms / 1e3 / max(1, k_n)
     achieved = gu_bytes / k_avg_s / 1e9
@@ -308,10 +324,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                     "traffic": (measured_traffic() if args.workload == "dense8b_chain"
-                                 else None),
-                     "kernel": "FFN gate/up GEMM + SwiGLU (%.1f MB of weights per launch)"
-                               % (gu_bytes / 1e6),
+                     "traffic": (measured_traffic(args.weights)
+                                 if args.workload == "dense8b_chain" else None),
+                     "kernel": "FFN gate/up GEMM + SwiGLU (%.1f MB of %s weights per launch)"
+                               % (gu_bytes / 1e6, "W12" if args.weights == "w12" else "bf16"),
                      "launches": k_n, "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
     }
@@ -319,9 +335,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_swiglu_dense8b_chain_k16_traffic.md")
+TRAFFIC_FILES = {
+    "native": os.path.join(ROOT, "profiles", "gemm_gateup_swiglu_bf16_dense8b_chain_k16_traffic.md"),
+    "w12": os.path.join(ROOT, "profiles", "gemm_gateup_swiglu_w12_dense8b_chain_k16_traffic.md"),
+}
 TRAFFIC_SOURCES = [os.path.join(ROOT, "tree_verification_spec_amd", "csrc", f)
-                   for f in ("gemm.hip", "common.h", "kernels.h")]
+                   for f in ("gemm.hip", "common.h", "kernels.h", "w12.h")]
 
 
 def kernel_source_hash():
@@ -333,13 +352,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
-    None when the kernel sources changed since the counters were taken."""
+def measured_traffic(fmt):
+    """HBM bytes per gate/up launch from the committed counter summary for
+    this weight format (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of
+    known size), or None when the kernel sources changed since the counters
+    were taken."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILES[fmt]) as fh:
             for line in fh:
                 if line.startswith("- ") and ": " in line:
                     k, v = line[2:].strip().split(": ", 1)

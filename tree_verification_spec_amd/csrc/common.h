@@ -27,6 +27,16 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
+
+// A raw (untyped, unswizzled) buffer resource over 4 GB from p, for
+// streaming weights with scalar base and offsets.  Word 3 = 0x00020000 is
+// the raw-buffer configuration of the gfx9-family CDNA descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)0xFFFFFFFFu,
+                                           0x00020000);
+}
+
 template <typename T> struct Frag;
 
 // 8 bf16 = 16 bytes

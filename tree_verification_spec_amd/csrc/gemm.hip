@@ -51,7 +51,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
   constexpr int QUADS = KC / 4;                      // float4 per staged row
   constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // float4 per thread
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (kept in scalar registers, so weight addresses are a
+  // scalar base plus a per-lane offset)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int nblk = a.ntiles / (WAVES * NTW);
   const int nb = blockIdx.x % nblk;
@@ -67,22 +70,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // per lane plus one exception-slot word, decoded to a Frag before use)
   static_assert(!W12 || sizeof(T) == 2, "W12 holds bf16 weights");
   using WReg = typename std::conditional<W12, W12Raw, Frag<T>>::type;
-  const Frag<T>* wbase[NTW];
-  const uint8_t* w12base[NTW];
-  uint32_t eb2[NTW];
+  constexpr uint32_t TB = W12 ? kW12TileBytes : 64 * sizeof(Frag<T>);  // tile bytes
+  // one buffer resource per tile row (scalar registers); a K-step's tile is
+  // at the scalar offset k * wk, a lane's words at a fixed per-lane offset
+  __amdgpu_buffer_rsrc_t wrs[NTW];
+  uint32_t eb7[NTW];  // W12: the row's base exponent, (eb | eb << 16) << 7
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const size_t tr = (size_t)((nb * WAVES + wave) * NTW + t);  // tile row
+    wrs[t] = weight_rsrc(reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * TB);
     if constexpr (W12) {
-      w12base[t] = reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * kW12TileBytes;
       const uint32_t e = a.eb[tr * 16 + r16];
-      eb2[t] = e | (e << 16);
+      eb7[t] = (e | (e << 16)) << 7;
     } else {
-      wbase[t] = reinterpret_cast<const Frag<T>*>(a.W) + tr * a.wsn * 64 + lane;
-      eb2[t] = 0;
+      eb7[t] = 0;
     }
   }
-  const size_t wk = (size_t)a.wsk * (W12 ? kW12TileBytes : 64);  // stride between K-steps
+  const uint32_t wk = (uint32_t)a.wsk * TB;  // bytes between K-steps (host-checked)
 
   floatx4_t acc[NTW][MT];
 #pragma unroll
@@ -144,15 +148,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   WReg w[WIN][NTW];
   auto load_step = [&](WReg (&dst)[NTW], int kb) {
     const int k = kb < kb_end ? kb : kb_end - 1;
+    const int so = (int)((uint32_t)k * wk);
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       if constexpr (W12) {
-        const uint8_t* p = w12base[t] + (size_t)k * wk;
-        const uint3 d = *reinterpret_cast<const uint3*>(p + lane * 12);
+        const u32x3_t d = __builtin_amdgcn_raw_buffer_load_b96(wrs[t], lane * 12, so, 0);
         dst[t] = W12Raw{d.x, d.y, d.z,
-                        *reinterpret_cast<const uint32_t*>(p + (kW12SlotDword + (lane & 7)) * 4)};
+                        __builtin_amdgcn_raw_buffer_load_b32(
+                            wrs[t], (kW12SlotDword + (lane & 7)) * 4, so, 0)};
+      } else if constexpr (kBf) {
+        dst[t].v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs[t], lane * 16, so, 0));
       } else {
-        dst[t] = wbase[t][(size_t)k * wk];
+        dst[t].lo = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(wrs[t], lane * 32, so, 0));
+        dst[t].hi = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(wrs[t], lane * 32 + 16, so, 0));
       }
     }
   };
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   auto wfrag = [&](const WReg& r, int t) -> Frag<T> {
     if constexpr (W12) {
       Frag<T> f;
-      f.v = w12_decode(r, eb2[t]);
+      f.v = w12_decode(r, eb7[t]);
       w12_patch(f.v, r, lane);
       return f;
     } else {
@@ -396,6 +407,9 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
     return hipErrorInvalidValue;
   a.KR = a.K / a.S;
   if (a.wsn <= 0 || a.wsk <= 0) return hipErrorInvalidValue;
+  // weights are addressed through 32-bit buffer offsets: at most 4 GB a matrix
+  const size_t tile_bytes = a.w12 ? kW12TileBytes : (bf16 ? 1024 : 2048);
+  if ((size_t)a.ntiles * (a.K / 32) * tile_bytes > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // one workgroup shape for all row chunks (the ARGMAX block layout and the
   // partial sums must not depend on the chunk)
   const Variant v = gemm_variant(bf16, a.ntiles * 16, a.M);

@@ -14,8 +14,13 @@
 // Tile (16 rows x 32 reduction indices, the MFMA tile of kernels.h), 800
 // bytes:
 //   bytes [0, 768): lane l's 8 weights (row l % 16, indices (l / 16) * 8 +
-//     e) in 3 dwords: dword 0 = byte e of (sign << 7 | mantissa) for e =
-//     0..3, dword 1 the same for e = 4..7, dword 2 = nibble e of d.
+//     e) in 3 dwords A, B, C.  With d = d0 + 2 d' (d0 one bit, d' three):
+//     byte e of A (e < 4) or byte e - 4 of B = d0 << 7 | mantissa;
+//     byte k of C (k < 4) = d'_k | s_(4 + (k + 3) % 4) << 3 | d'_(k + 4) << 4
+//     | s_k << 7 (s = sign).  C rotated right by 4 bits puts weight 4 + k's
+//     d' and sign where C has weight k's, so a mask and one byte permute per
+//     weight pair leave sign << 15 | d << 7 | mantissa per 16 bits, and
+//     adding eb << 7 gives the bf16 (eb + d <= 254 never carries).
 //   bytes [768, 800): the exception slot, 8 dwords.  Dword 0 = number of
 //     exceptions n <= 7, dwords 1..n = lane << 19 | e << 16 | bf16 bits.
 // A matrix with a tile of more than 7 exceptions is not stored as W12 (the
@@ -35,27 +40,19 @@ struct W12Raw {
   uint32_t d0, d1, d2, slot;
 };
 
-// One pair of weights (e = 2j, 2j + 1) as two bf16 in one dword.
-__device__ __forceinline__ uint32_t w12_pair(uint32_t lo8x4, uint32_t nib, int j,
-                                             uint32_t eb2) {
-  // the two (sign | mantissa) bytes into the low byte of each 16-bit half
-  const uint32_t b = (j & 1) ? ((lo8x4 >> 16) & 0xFFu) | ((lo8x4 >> 8) & 0xFF0000u)
-                             : (lo8x4 & 0xFFu) | ((lo8x4 << 8) & 0xFF0000u);
-  // the two exponent offsets into the low bits of each half
-  const uint32_t n = (nib >> (8 * j)) & 0xFFu;
-  const uint32_t d = (n & 0xFu) | ((n & 0xF0u) << 12);
-  // bf16 = sign << 15 | (eb + d) << 7 | mantissa, per half
-  return ((b & 0x00800080u) << 8) | ((d + eb2) << 7) | (b & 0x007F007Fu);
-}
-
 // Decode one lane's 8 weights into MFMA operand order (e = 0..7 as 4
-// dwords of bf16 pairs).  eb2 = eb | eb << 16 of the lane's row.
-__device__ __forceinline__ uint4 w12_decode(const W12Raw& w, uint32_t eb2) {
+// dwords of bf16 pairs).  eb7 = (eb | eb << 16) << 7 of the lane's row.
+__device__ __forceinline__ uint4 w12_decode(const W12Raw& w, uint32_t eb7) {
+  // the sign and d' bits of weights 0..3 (C) and 4..7 (C rotated right by 4)
+  constexpr uint32_t kMask = 0x87878787u;
+  const uint32_t c0 = w.d2 & kMask;
+  const uint32_t c4 = __builtin_amdgcn_alignbit(w.d2, w.d2, 4) & kMask;
+  constexpr uint32_t kLo = 0x05010400u, kHi = 0x07030602u;  // bytes {0,4,1,5}, {2,6,3,7}
   uint4 v;
-  v.x = w12_pair(w.d0, w.d2, 0, eb2);
-  v.y = w12_pair(w.d0, w.d2, 1, eb2);
-  v.z = w12_pair(w.d1, w.d2, 2, eb2);
-  v.w = w12_pair(w.d1, w.d2, 3, eb2);
+  v.x = __builtin_amdgcn_perm(c0, w.d0, kLo) + eb7;
+  v.y = __builtin_amdgcn_perm(c0, w.d0, kHi) + eb7;
+  v.z = __builtin_amdgcn_perm(c4, w.d1, kLo) + eb7;
+  v.w = __builtin_amdgcn_perm(c4, w.d1, kHi) + eb7;
   return v;
 }
 

@@ -54,19 +54,27 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
   const uint32_t base = eb[row];
   if (kb == 0 && lane < 16)  // the destination rows' bases, once per tile row
     eb_dst[(size_t)(dst_tile0 + nb * tile_stride) * 16 + lane] = (uint8_t)base;
-  uint32_t lo01 = 0, lo23 = 0, nib = 0, excmask = 0;
+  // the three data dwords (layout in w12.h); exceptions leave zeros
+  uint32_t da = 0, db = 0, dc = 0, excmask = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t bits = w[e];
     const int exp = (int)((bits >> 7) & 0xFFu);
     const int d = exp - (int)base;
     const bool exc = d < 0 || d > 15 || exp == 255;
-    const uint32_t b = ((bits >> 8) & 0x80u) | (bits & 0x7Fu);
-    const uint32_t dn = exc ? 0u : (uint32_t)d;
-    const uint32_t bb = exc ? 0u : b;
-    if (e < 4) lo01 |= bb << (8 * e);
-    else lo23 |= bb << (8 * (e - 4));
-    nib |= dn << (4 * e);
+    const uint32_t dd = exc ? 0u : (uint32_t)d;
+    const uint32_t sign = exc ? 0u : bits >> 15;
+    const uint32_t lo = exc ? 0u : ((dd & 1u) << 7) | (bits & 0x7Fu);
+    const uint32_t dh = dd >> 1;
+    if (e < 4) {
+      da |= lo << (8 * e);
+      dc |= (dh | sign << 7) << (8 * e);
+    } else {
+      const int k = e - 4;
+      db |= lo << (8 * k);
+      dc |= dh << (8 * k + 4);
+      dc |= sign << (8 * ((k + 1) & 3) + 3);
+    }
     excmask |= (exc ? 1u : 0u) << e;
   }
   // exclusive prefix of the exception counts over the wave
@@ -94,9 +102,9 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
   if (lane == 0) slot[0] = total;
   __syncthreads();
   uint32_t* td = reinterpret_cast<uint32_t*>(t);
-  td[lane * 3 + 0] = lo01;
-  td[lane * 3 + 1] = lo23;
-  td[lane * 3 + 2] = nib;
+  td[lane * 3 + 0] = da;
+  td[lane * 3 + 1] = db;
+  td[lane * 3 + 2] = dc;
   if (lane < 8) td[kW12SlotDword + lane] = slot[lane];
 }
 

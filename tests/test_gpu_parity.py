@@ -334,16 +334,19 @@ def test_full_width_trees(name, budget):
 
 # ------------------------------------------------- W12 weight storage
 
-def _run_steps(eng, cfg, prompt, steps, seed):
-    """Prefill, then verify + commit steps alternating chains and trees;
-    returns every pass's paths, bonus tokens and logits."""
+def _run_steps(eng, cfg, prompt, steps, seed, big=0):
+    """Prefill, then verify + commit steps alternating chains and trees
+    (every third step a chain of `big` nodes when big > 0); returns every
+    pass's paths, bonus tokens and logits."""
     V = cfg["vocab"]
     rng = np.random.default_rng(seed)
     tree_par = np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5])
     first, lg = eng.prefill(0, prompt, logits=True)
     out = [(first, lg.cpu().numpy().copy())]
     for k in range(steps):
-        if k % 2:
+        if big and k % 3 == 2:
+            toks, par = rng.integers(0, V, big), np.arange(-1, big - 1)
+        elif k % 2:
             toks, par = rng.integers(0, V, 12), tree_par
         else:
             toks, par = rng.integers(0, V, 8), np.arange(-1, 7)
@@ -408,8 +411,10 @@ def test_w12_exceptions():
     prompt = synth.prompt_tokens(cfg["vocab"], 60, 56)
     runs = []
     for fmt in ("native", "w12"):
-        eng = engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format=fmt)
-        runs.append(_run_steps(eng, cfg, prompt, 4, 56))
+        # 47 drafts + root = 48 rows: the GEMMs at 3 row tiles (the other
+        # loop shape)
+        eng = engine_for(cfg, W, max_ctx=512, max_nodes=48, weight_format=fmt)
+        runs.append(_run_steps(eng, cfg, prompt, 6, 56, big=47))
         eng.close()
     assert np.all(np.isfinite(runs[0][0][1]))
     _assert_same(*runs)

@@ -51,6 +51,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
   constexpr int QUADS = KC / 4;                      // float4 per staged row
   constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // float4 per thread
+  // Loop shape by row tiles (measured on the 8B shapes): up to 32 rows the
+  // compiler's own schedule streams best; from 48 rows on, activation loads
+  // are unpredicated, each step's weight refill is pinned after its MFMAs,
+  // and the W12 exception patch is one opaque block (its loop would
+  // otherwise cost registers, and with them occupancy).
+  constexpr bool kOrdered = MT >= 3;
   const int lane = threadIdx.x & 63;
   // wave-uniform (kept in scalar registers, so weight addresses are a
   // scalar base plus a per-lane offset)
@@ -110,13 +116,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       const int r = e / QUADS, c = (e % QUADS) * 4;
       const int m = a.row0 + r;
       const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
-      const size_t off = (size_t)m * a.ldx + kc0 + c;
-      if constexpr (kBf) {
-        xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
-        xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+      if constexpr (kOrdered) {
+        // every lane loads (from the plane's first element when out of
+        // range) and masks afterwards: no predicated loads, which the
+        // compiler would otherwise count conservatively across the loop
+        const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
+        const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
+        if constexpr (kBf) {
+          const uint2 h = *reinterpret_cast<const uint2*>(Xh + off);
+          const uint2 l = *reinterpret_cast<const uint2*>(Xl + off);
+          xr[q] = make_uint2(h.x & mk, h.y & mk);
+          xl[q] = make_uint2(l.x & mk, l.y & mk);
+        } else {
+          const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
+          xr[q] = make_float4(__uint_as_float(h.x & mk), __uint_as_float(h.y & mk),
+                              __uint_as_float(h.z & mk), __uint_as_float(h.w & mk));
+        }
       } else {
-        xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const size_t off = (size_t)m * a.ldx + kc0 + c;
+        if constexpr (kBf) {
+          xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
+          xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+        } else {
+          xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
   };
@@ -173,7 +197,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     if constexpr (W12) {
       Frag<T> f;
       f.v = w12_decode(r, eb7[t]);
-      w12_patch(f.v, r, lane);
+      if constexpr (kOrdered) w12_patch_opaque(f.v, r, lane);
+      else w12_patch(f.v, r, lane);
       return f;
     } else {
       (void)t;
@@ -225,6 +250,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int p = 0; p < XF; ++p) mma32(acc[t][mt], wf[t], xc[mt][p]);
         load_step(w[u], kw + u + WIN);
+        // ordered: each step's refill is issued right after its MFMAs (the
+        // scheduler would otherwise sink all refills to the end of the
+        // chunk, and the next chunk would wait a full memory latency)
+        if constexpr (kOrdered) __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < CSTEPS) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)

@@ -56,8 +56,9 @@ __device__ __forceinline__ uint4 w12_decode(const W12Raw& w, uint32_t eb7) {
   return v;
 }
 
-// Patch the exceptions of a tile (count from lane 0's slot word); the
-// element is selected arithmetically so the fragment stays in registers.
+// Patch the exceptions of a tile (count from lane 0's slot word, entries
+// from lanes 1..7); the element is selected arithmetically so the fragment
+// stays in registers.
 __device__ __forceinline__ void w12_patch(uint4& v, const W12Raw& w, int lane) {
   const uint32_t head = __builtin_amdgcn_readfirstlane(w.slot);
   if (head == 0) return;
@@ -73,4 +74,75 @@ __device__ __forceinline__ void w12_patch(uint4& v, const W12Raw& w, int lane) {
     v.z = (mine && dw == 2) ? ((v.z & keep) | put) : v.z;
     v.w = (mine && dw == 3) ? ((v.w & keep) | put) : v.w;
   }
+}
+
+// The same patch as one assembly block (all 64 lanes active), so the
+// rarely taken loop adds no control flow to the compiler's view of the
+// GEMM loop (which otherwise costs registers at many row tiles).  Every scalar
+// value a vector instruction uses as a lane select or mask, and every
+// scalar written by a vector instruction, is followed by s_nop 4 before
+// use (these wait states cost nothing in the common path, which is the
+// first four instructions).
+__device__ __forceinline__ void w12_patch_opaque(uint4& v, const W12Raw& w, int lane) {
+  uint32_t x = v.x, y = v.y, z = v.z, q = v.w, tmp;
+  uint32_t head, k, ent, t, e, val, keep, put, dw;
+  uint64_t m, mi;
+  asm(
+      "v_readfirstlane_b32 %[head], %[slot]\n\t"
+      "s_nop 4\n\t"
+      "s_cmp_eq_u32 %[head], 0\n\t"
+      "s_cbranch_scc1 .Lw12done%=\n\t"
+      "s_mov_b32 %[k], 1\n"
+      ".Lw12loop%=:\n\t"
+      "s_nop 4\n\t"
+      "v_readlane_b32 %[ent], %[slot], %[k]\n\t"
+      "s_nop 4\n\t"
+      "s_lshr_b32 %[t], %[ent], 19\n\t"
+      "s_bfe_u32 %[e], %[ent], 0x30010\n\t"
+      "s_and_b32 %[val], %[ent], 0xffff\n\t"
+      "s_lshl_b32 %[put], %[val], 16\n\t"
+      "s_mov_b32 %[keep], 0xffff0000\n\t"
+      "s_bitcmp1_b32 %[e], 0\n\t"
+      "s_cselect_b32 %[put], %[put], %[val]\n\t"
+      "s_cselect_b32 %[keep], 0xffff, %[keep]\n\t"
+      "s_lshr_b32 %[dw], %[e], 1\n\t"
+      "s_nop 4\n\t"
+      "v_cmp_eq_u32_e64 %[m], %[t], %[lane]\n\t"
+      "s_nop 4\n\t"
+      "s_cmp_eq_u32 %[dw], 0\n\t"
+      "s_cselect_b64 %[mi], %[m], 0\n\t"
+      "s_nop 4\n\t"
+      "v_and_b32 %[tmp], %[keep], %[x]\n\t"
+      "v_or_b32 %[tmp], %[put], %[tmp]\n\t"
+      "v_cndmask_b32_e64 %[x], %[x], %[tmp], %[mi]\n\t"
+      "s_cmp_eq_u32 %[dw], 1\n\t"
+      "s_cselect_b64 %[mi], %[m], 0\n\t"
+      "s_nop 4\n\t"
+      "v_and_b32 %[tmp], %[keep], %[y]\n\t"
+      "v_or_b32 %[tmp], %[put], %[tmp]\n\t"
+      "v_cndmask_b32_e64 %[y], %[y], %[tmp], %[mi]\n\t"
+      "s_cmp_eq_u32 %[dw], 2\n\t"
+      "s_cselect_b64 %[mi], %[m], 0\n\t"
+      "s_nop 4\n\t"
+      "v_and_b32 %[tmp], %[keep], %[z]\n\t"
+      "v_or_b32 %[tmp], %[put], %[tmp]\n\t"
+      "v_cndmask_b32_e64 %[z], %[z], %[tmp], %[mi]\n\t"
+      "s_cmp_eq_u32 %[dw], 3\n\t"
+      "s_cselect_b64 %[mi], %[m], 0\n\t"
+      "s_nop 4\n\t"
+      "v_and_b32 %[tmp], %[keep], %[q]\n\t"
+      "v_or_b32 %[tmp], %[put], %[tmp]\n\t"
+      "v_cndmask_b32_e64 %[q], %[q], %[tmp], %[mi]\n\t"
+      "s_add_u32 %[k], %[k], 1\n\t"
+      "s_cmp_le_u32 %[k], %[head]\n\t"
+      "s_cbranch_scc1 .Lw12loop%=\n"
+      ".Lw12done%=:\n\t"
+      "s_nop 4"
+      : [x] "+v"(x), [y] "+v"(y), [z] "+v"(z), [q] "+v"(q), [tmp] "=&v"(tmp),
+        [head] "=&s"(head), [k] "=&s"(k), [ent] "=&s"(ent), [t] "=&s"(t), [e] "=&s"(e),
+        [val] "=&s"(val), [keep] "=&s"(keep), [put] "=&s"(put), [dw] "=&s"(dw),
+        [m] "=&s"(m), [mi] "=&s"(mi)
+      : [slot] "v"(w.slot), [lane] "v"(lane)
+      : "scc");
+  v = make_uint4(x, y, z, q);
 }

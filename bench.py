@@ -89,9 +89,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense8b_chain", choices=WORKLOADS)
     ap.add_argument("--alpha", type=float, default=None)
-    ap.add_argument("--weights", default="w12", choices=("w12", "native"),
+    ap.add_argument("--weights", default=None, choices=("w12", "native"),
                     help="weight storage: W12 (lossless 12-bit, bitwise-identical "
-                         "results) or the model's bf16")
+                         "results) or the model's bf16; default: the faster of the two "
+                         "for the workload (W12 up to 32 rows per pass, bf16 above)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -123,6 +124,9 @@ def main():
 
     w = synth.workload(args.workload)
     cfg = synth.model_config(w["model"])
+    if args.weights is None:
+        rows = w["K"] + 1 if args.workload != "dense8b_batched" else w["batch"] * (w["K"] + 1)
+        args.weights = "w12" if rows <= 32 else "native"
     V, K, idx = cfg["vocab"], w["K"], w["index"]
     batched = args.workload == "dense8b_batched"
     tree = w["draft"] == "tree"

@@ -32,12 +32,13 @@ namespace {
 
 constexpr int kD = 8;  // minimum K-steps of W loads in flight per wave (rolling window)
 
-// Staged chunk width (K elements) per row-tile count: two LDS buffers of
-// MT*16 rows x (KC + pad) x 4 bytes stay near 64 KB (two workgroups per CU;
-// measured faster than larger chunks at every row count).
+// Staged chunk width (K elements) per row-tile count: up to 3 row tiles,
+// two LDS buffers of MT*16 rows x (KC + pad) x 4 bytes stay near 64 KB (two
+// workgroups per CU); from 4 row tiles the registers allow one workgroup
+// per CU anyway, and chunks of ~130 KB halve the barriers.
 template <int MT> struct ChunkK {
   static constexpr int value = MT <= 1 ? 256 : MT <= 2 ? 256 : MT <= 3 ? 160
-                             : MT <= 4 ? 128 : MT <= 5 ? 96 : 64;
+                             : MT <= 4 ? 256 : MT <= 5 ? 192 : 128;
 };
 
 template <typename T, int MT, int NTW, int WAVES, int EPI, int D, bool W12>

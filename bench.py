@@ -42,44 +42,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-W12_BYTES_PER_WEIGHT = 800 / 512   # a W12 tile: 512 weights in 800 bytes
-
-
-def weight_bytes(rows, cols, fmt):
-    """Stored bytes of one [rows, cols] bf16 matrix: 2 per weight, or the
-    W12 tiles plus one base-exponent byte per row."""
-    if fmt == "w12":
-        return rows * cols * W12_BYTES_PER_WEIGHT + rows
-    return rows * cols * 2
-
-
-def model_bytes(cfg, fmt):
-    """Weight elements and bytes read by a verify pass (every matrix but the
-    embedding, which is gathered) and the bytes of one cached position."""
-    import synth
-    shapes = [shape for name, shape, kind in synth.tensor_specs(cfg)
-              if kind == "mat" and name != "embed"]
-    mats = sum(r * c for r, c in shapes)
-    wbytes = sum(weight_bytes(r, c, fmt) for r, c in shapes)
-    n_attn = cfg["layer_kinds"].count("A")
-    kv_pos = n_attn * cfg["n_kv_heads"] * cfg["head_dim"] * 2 * 2
-    return mats, wbytes, n_attn, kv_pos
-
-
 def step_bounds(cfg, req_rows, req_ctx, fmt):
-    """Algorithmic bytes, FLOPs and lower-bound seconds of one verify step:
-    weights once (in their stored format), every request's committed KV
-    once, the pass's new KV, the recurrent states read once and committed
-    once."""
-    mats, wbytes, n_attn, kv_pos = model_bytes(cfg, fmt)
-    n_lr = cfg["layer_kinds"].count("L")
-    R = sum(req_rows)
-    state = 2 * n_lr * cfg["d_model"] * cfg["lr_state"] * 4 * len(req_rows)
-    nbytes = wbytes + sum(req_ctx) * kv_pos + R * kv_pos + state
-    attn = sum(r * (c + r) for r, c in zip(req_rows, req_ctx))
-    flops = 2 * mats * R + 4 * cfg["n_heads"] * cfg["head_dim"] * n_attn * attn
-    lb = max(flops / (0.6 * PEAK_BF16), nbytes / (0.9 * PEAK_HBM))
-    return nbytes, flops, lb
+    """Algorithmic bytes, FLOPs and lower-bound seconds of one verify step,
+    and the per-kernel-type (bytes, FLOPs): weights once (in their stored
+    format), every request's committed KV once, the pass's new KV, the
+    recurrent states read once and committed once."""
+    import synth
+    from tree_verification_spec_amd import costmodel
+    types = costmodel.type_bounds(synth.tensor_specs(cfg), cfg, req_rows, req_ctx, fmt)
+    nbytes = sum(b for b, _ in types.values())
+    flops = sum(f for _, f in types.values())
+    return nbytes, flops, costmodel.lower_bound(nbytes, flops), types
 
 
 def main():
@@ -194,7 +167,7 @@ def main():
         for r in range(B):
             eng.prefill(slots[r], prompts[r])
         g = [1] * B
-        tot, toks, mism, lbs, lbs_b, dev_ms = 0.0, 0, 0, [], [], []
+        tot, toks, mism, lbs, lbs_b, dev_ms, types = 0.0, 0, 0, [], [], [], []
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         al = [float(a) for a in alphas] if batched else [alpha] * B
@@ -236,9 +209,10 @@ def main():
                 tot += dt
                 toks += sum(n_new)
                 dev_ms.append(ev0.elapsed_time(ev1))
-                nb, fl, lb = step_bounds(cfg, [K + 1] * B, ctx, args.weights)
+                nb, fl, lb, ty = step_bounds(cfg, [K + 1] * B, ctx, args.weights)
                 lbs.append(lb)
                 lbs_b.append(nb)
+                types.append(ty)
             for r in range(B):
                 g[r] += n_new[r]
         kt = None
@@ -252,7 +226,10 @@ def main():
                     dev_ms=float(np.median(dev_ms)),
                     dev_pct=[float(x) for x in np.percentile(dev_ms, [10, 50, 90])],
                     lb_ms=1e3 * float(np.mean(lbs)),
-                    bytes=float(np.mean(lbs_b)), ktime=kt)
+                    bytes=float(np.mean(lbs_b)), ktime=kt,
+                    types={t: (float(np.mean([ty[t][0] for ty in types])),
+                               float(np.mean([ty[t][1] for ty in types])))
+                           for t in types[0]})
 
     res = run(alpha_main, args.steps, args.warmup)
     log(f"{args.workload} alpha={alpha_main}: {res}")
@@ -274,7 +251,8 @@ def main():
 
     # roofline of the dominant kernel: FFN gate/up GEMM, weights streamed once
     # per launch (passes of more than 128 rows launch it once per 128 rows)
-    gu_bytes = weight_bytes(2 * cfg["ffn_dim"], cfg["d_model"], args.weights)
+    from tree_verification_spec_amd import costmodel
+    gu_bytes = costmodel.weight_bytes(2 * cfg["ffn_dim"], cfg["d_model"], args.weights)
     k_ms, k_n = rl["ktime"]
     k_avg_s = k_ms / 1e3 / max(1, k_n)
     achieved = gu_bytes / k_avg_s / 1e9
@@ -334,6 +312,15 @@ def main():
                                % (gu_bytes / 1e6, "W12" if args.weights == "w12" else "bf16"),
                      "launches": k_n, "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
+        # per-kernel-type lower bounds of the mean step (the cost model's
+        # kernel and overhead factors need a kernel trace of the same run
+        # shape: python -m tree_verification_spec_amd.costmodel)
+        "cost_model": {
+            "row_tiles": costmodel.row_tiles(B * (K + 1)),
+            "types": {t: {"bytes": b, "flops": f,
+                          "bound_us": round(1e6 * costmodel.lower_bound(b, f), 2)}
+                      for t, (b, f) in res["types"].items()},
+        },
     }
     eng.close()
     print(json.dumps(out), flush=True)

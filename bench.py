@@ -66,6 +66,10 @@ def main():
                     help="weight storage: W12 (lossless 12-bit, bitwise-identical "
                          "results) or the model's bf16; default: the faster of the two "
                          "for the workload (W12 up to 32 rows per pass, bf16 above)")
+    ap.add_argument("--policy", default="fixed", choices=("fixed", "budget"),
+                    help="batched workload: fixed K drafts per request, or per-step draft "
+                         "lengths of 8/12/16 from each request's acceptance so far under a "
+                         "shared budget of batch x K draft nodes")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -84,6 +88,7 @@ def main():
     import torch
     import synth
     from tree_verification_spec_amd import Engine
+    import tree_verification_spec_amd as L
 
     if args.copy_probe_bytes:
         n = args.copy_probe_bytes // 4
@@ -117,7 +122,10 @@ def main():
     sweep_alphas = [] if (args.no_sweep or batched or tree) else \
         [a for a in w.get("alphas", ()) if abs(a - alpha_main) > 1e-9]
     # reference length: enough tokens for every run's expected acceptance
-    depth = w.get("max_depth", 8) if tree else K
+    planned = batched and args.policy == "budget"
+    choices, min_prob, decay = (8, 12, 16), 0.05, 0.9
+    budget = B * K
+    depth = w.get("max_depth", 8) if tree else (max(choices) if planned else K)
     runs = [(alpha_main if not batched else 0.9, args.warmup + args.steps),
             (alpha_main if not batched else 0.9, max(10, args.steps // 3) + 2)]
     runs += [(a, max(20, args.steps // 2) + 4) for a in sweep_alphas]
@@ -128,8 +136,9 @@ def main():
     t0 = time.time()
     W = synth.make_weights(cfg)
     log(f"weights generated in {time.time() - t0:.1f}s")
-    max_ctx = max(len(p) for p in prompts) + ref_len + 2 * (K + 1)
-    eng = Engine(cfg, device=0, max_requests=B, max_ctx=max_ctx, max_nodes=K + 1,
+    max_ctx = max(len(p) for p in prompts) + ref_len + 2 * (depth + 1)
+    eng = Engine(cfg, device=0, max_requests=B, max_ctx=max_ctx,
+                 max_nodes=(max(choices) if planned else K) + 1,
                  max_rows=B * (K + 1), prefill_chunk=512, weight_format=args.weights)
     t0 = time.time()
     eng.load_weights([W[n] for n, _, _ in synth.tensor_specs(cfg)])
@@ -156,11 +165,11 @@ def main():
     ar_tps = B * (ref_len - 1) / t_ar
     log(f"GPU AR: {ref_len - 1} tokens x {B} requests, {ar_tps:.1f} tok/s")
 
-    def drafts_for(r, g, step, alpha):
+    def drafts_for(r, g, step, alpha, k):
         if tree:
-            return synth.tree_drafts(S[r], g, K, w["branching"], w["max_depth"], alpha, V,
+            return synth.tree_drafts(S[r], g, k, w["branching"], w["max_depth"], alpha, V,
                                      idx, r, step)
-        return synth.chain_drafts(S[r], g, K, alpha, V, idx, r, step)
+        return synth.chain_drafts(S[r], g, k, alpha, V, idx, r, step)
 
     def run(alpha, steps, warmup, timing_cls=0):
         slots = list(range(B))  # the reference run released them
@@ -171,12 +180,17 @@ def main():
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         al = [float(a) for a in alphas] if batched else [alpha] * B
+        succ, fail = [0.0] * B, [0.0] * B
         for it in range(warmup + steps):
             timed = it >= warmup
             if timed and it == warmup and timing_cls:
                 eng.timing(timing_cls)
                 eng.timing_read()
-            dr = [drafts_for(r, g[r], it, al[r]) for r in range(B)]
+            t_plan = time.perf_counter()
+            lens = (L.spec_plan_drafts(succ, fail, choices, min_prob, budget) if planned
+                    else [K] * B)
+            t_plan = time.perf_counter() - t_plan
+            dr = [drafts_for(r, g[r], it, al[r], lens[r]) for r in range(B)]
             ctx = [eng.state(slots[r])[0] for r in range(B)]
             sync()
             a = time.perf_counter()
@@ -205,11 +219,16 @@ def main():
             ev1.record(eng.stream)
             sync()
             dt = time.perf_counter() - a
+            if planned:
+                t_upd = time.perf_counter()
+                succ, fail = L.spec_acceptance_update(lens, [len(p) for p in paths], decay,
+                                                      succ, fail)
+                dt += t_plan + time.perf_counter() - t_upd
             if timed:
                 tot += dt
                 toks += sum(n_new)
                 dev_ms.append(ev0.elapsed_time(ev1))
-                nb, fl, lb, ty = step_bounds(cfg, [K + 1] * B, ctx, args.weights)
+                nb, fl, lb, ty = step_bounds(cfg, [k + 1 for k in lens], ctx, args.weights)
                 lbs.append(lb)
                 lbs_b.append(nb)
                 types.append(ty)
@@ -265,6 +284,9 @@ def main():
         desc = ("8B-shaped dense decoder, 32 requests (contexts 512..4096 in 16-token "
                 "pages), chain drafts K=8, alpha 0.4..0.9 per request, one fused "
                 "verify per step")
+        if planned:
+            desc += (", draft lengths planned per step (8/12/16 by acceptance, shared "
+                     f"budget of {budget} draft nodes)")
     elif tree:
         model = ("8B-shaped dense decoder" if w["model"] == "dense8b" else
                  "27B-shaped hybrid (48 recurrent + 16 attention layers)")
@@ -290,7 +312,9 @@ def main():
                 "drafts from the target's greedy continuation)",
         "config": {"workload": desc, "name": args.workload, "batch": B, "draft_K": K,
                    "alpha": alpha_main, "prompt": None if batched else w["prompt"],
-                   "weights": args.weights},
+                   "weights": args.weights,
+                   "policy": (f"budget {budget}, lengths {list(choices)}, min_prob "
+                              f"{min_prob}, decay {decay}") if planned else "fixed"},
         "verify_step": {
             "device_ms_median": round(res["dev_ms"], 4),
             "byte_lower_bound_ms": round(res["lb_ms"], 4),

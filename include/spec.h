@@ -201,6 +201,39 @@ void spec_destroy(spec_ctx* ctx);
 /* Message describing the last error (never NULL). */
 const char* spec_last_error(const spec_ctx* ctx);
 
+/* ---- Batched draft planning (host only; no context, no GPU).
+ * besthub.dev, "SpecPilot: AI Agent Framework Boosts Speculative Decoding
+ * 10.87x for Qwen3.8-27B", section "(4) Three Batch Optimization
+ * Mechanisms": dynamic draft length (each request picks one of a few draft
+ * lengths from its recent acceptance) and a shared node budget (a batch's
+ * draft nodes go to the candidates with the highest path probability).
+ * These only choose how many draft positions each request offers; the
+ * verification itself, and so every emitted token, is unchanged.
+ *
+ * spec_acceptance_update: after a step in which request r offered
+ * offered[r] chain positions and accepted[r] of them (its accepted prefix),
+ * decays the request's counts and adds the step:
+ *   succ[r] = decay * succ[r] + accepted[r]
+ *   fail[r] = decay * fail[r] + (accepted[r] < offered[r] ? 1 : 0).
+ * Arrays of n_req (host memory, caller-owned; succ and fail start at 0).
+ * SPEC_E_INVAL if accepted > offered, a count is negative or decay is
+ * outside [0, 1] (nothing is changed then).
+ *
+ * spec_plan_drafts: the estimated per-position acceptance of request r is
+ * p_r = (succ[r] + 1) / (succ[r] + fail[r] + 2), and its position j (1-based)
+ * has path probability p_r^j.  Each request's maximum length L_r is the
+ * largest of choices[0..n_choices) whose last position has p_r^L >= min_prob
+ * (the smallest choice when none does).  Of all positions j <= L_r over the
+ * batch, the `budget` most probable are kept (ties: lower request, then lower
+ * position), which is a prefix of every request's chain; len[r] receives its
+ * length (0..L_r; sum(len) <= budget).  choices in [1, 1024].  SPEC_E_INVAL
+ * on bad arguments (len is then not written). */
+int32_t spec_acceptance_update(int32_t n_req, const int32_t* offered, const int32_t* accepted,
+                               float decay, float* succ, float* fail);
+int32_t spec_plan_drafts(int32_t n_req, const float* succ, const float* fail,
+                         const int32_t* choices, int32_t n_choices, float min_prob,
+                         int32_t budget, int32_t* len);
+
 #ifdef __cplusplus
 }
 #endif

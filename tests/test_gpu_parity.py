@@ -83,12 +83,19 @@ def test_prefill_chunking_and_long_prompt():
 
 # ---------------------------------------------------------------- batched
 
-def test_batched_requests():
+@pytest.mark.parametrize("planned", [False, True])
+def test_batched_requests(planned):
     """Several requests of different lengths in one fused verify per step,
-    each checked against its own oracle greedy run."""
+    each checked against its own oracle greedy run.  planned: each step's
+    draft lengths come from the batch planner (lengths up to 2, 4 or 8 from
+    the requests' acceptance so far, 16 draft nodes shared by 5 requests, so
+    a request may offer none); the emitted tokens must not depend on it."""
+    from tree_verification_spec_amd import spec_acceptance_update, spec_plan_drafts
     cfg, W = _setup("tiny_gqa_bf16")
     V = cfg["vocab"]
     n_req, K, n_gen = 5, 8, 30
+    succ, fail = [0.0] * n_req, [0.0] * n_req
+    lens_used = set()
     eng = engine_for(cfg, W, max_requests=8, max_ctx=512, max_nodes=K + 1,
                      max_rows=8 * (K + 1))
     orc = oracle_for(cfg, W)
@@ -108,9 +115,16 @@ def test_batched_requests():
     step, ties = 0, 0
     while min(g) < n_gen:
         live = [i for i in range(n_req) if g[i] < n_gen]
+        if planned:
+            plan = spec_plan_drafts([succ[i] for i in live], [fail[i] for i in live],
+                                    [2, 4, 8], 0.05, 16)
+            assert sum(plan) <= 16
+            lens_used.update(plan)
+        else:
+            plan = [K] * len(live)
         drafts, parents = [], []
-        for i in live:
-            t, p = synth.chain_drafts(refs[i][0], g[i], K, alphas[i], V, 60, i, step)
+        for k, i in enumerate(live):
+            t, p = synth.chain_drafts(refs[i][0], g[i], plan[k], alphas[i], V, 60, i, step)
             drafts.append(t)
             parents.append(p)
         paths, bonus, lg = eng.verify([reqs[i] for i in live], drafts, parents,
@@ -146,9 +160,18 @@ def test_batched_requests():
                 g[i] += len(emitted)
             row0 += len(drafts[k]) + 1
         eng.commit([reqs[i] for i in live], keep_all, roots)
+        if planned:
+            su, fa = spec_acceptance_update([len(d) for d in drafts],
+                                            [len(p) for p in paths], 0.9,
+                                            [succ[i] for i in live], [fail[i] for i in live])
+            for k, i in enumerate(live):
+                succ[i], fail[i] = su[k], fa[k]
         step += 1
-    _say("batched steps", step, "near-tie mismatches", ties)
+    _say("batched steps", step, "near-tie mismatches", ties,
+         "planned lengths", sorted(lens_used))
     assert ties <= 3
+    if planned:
+        assert len(lens_used) > 2 and max(lens_used) > 4
 
 
 # ------------------------------------------------- spec == GPU AR (protocol A)

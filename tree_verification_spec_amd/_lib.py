@@ -30,6 +30,7 @@ EXPORTS = [
     "spec_force_root", "spec_set_fault", "spec_use_graphs", "spec_timing_enable",
     "spec_timing_read",
     "spec_destroy", "spec_last_error",
+    "spec_acceptance_update", "spec_plan_drafts",
 ]
 
 
@@ -85,6 +86,10 @@ def lib():
         "spec_timing_read": (c_int32, [c_void_p, P(c_double), P(c_int64)]),
         "spec_destroy": (None, [c_void_p]),
         "spec_last_error": (ctypes.c_char_p, [c_void_p]),
+        "spec_acceptance_update": (c_int32, [c_int32, i32p, i32p, c_float, P(c_float),
+                                             P(c_float)]),
+        "spec_plan_drafts": (c_int32, [c_int32, P(c_float), P(c_float), i32p, c_int32,
+                                       c_float, c_int32, i32p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -193,6 +198,35 @@ def spec_timing_read(ctx):
     ms, n = c_double(), c_int64()
     _check(ctx, lib().spec_timing_read(ctx, byref(ms), byref(n)))
     return ms.value, n.value
+
+
+def _f32(seq):
+    arr = (c_float * max(1, len(seq)))()
+    for i, v in enumerate(seq):
+        arr[i] = float(v)
+    return arr
+
+
+def spec_acceptance_update(offered, accepted, decay, succ, fail):
+    """Decayed acceptance counts after one step (context-free); returns the
+    new (succ, fail) lists."""
+    n = len(offered)
+    s, f = _f32(succ), _f32(fail)
+    rc = lib().spec_acceptance_update(n, _i32(offered), _i32(accepted), decay, s, f)
+    if rc:
+        raise SpecError(rc, "spec_acceptance_update: invalid arguments")
+    return list(s[:n]), list(f[:n])
+
+
+def spec_plan_drafts(succ, fail, choices, min_prob, budget):
+    """Per-request draft lengths under a shared node budget (context-free)."""
+    n = len(succ)
+    out = (c_int32 * max(1, n))()
+    rc = lib().spec_plan_drafts(n, _f32(succ), _f32(fail), _i32(choices), len(choices),
+                                min_prob, budget, out)
+    if rc:
+        raise SpecError(rc, "spec_plan_drafts: invalid arguments")
+    return list(out[:n])
 
 
 def spec_destroy(ctx):

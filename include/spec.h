@@ -57,7 +57,11 @@ enum { SPEC_DTYPE_FP32 = 0, SPEC_DTYPE_BF16 = 1 };
  * restored exactly in registers by the GEMMs, so every result is bitwise
  * the same as with bf16 storage while the weights move in ~0.78x the bytes
  * (besthub.dev article, section "(1) W12: Lossless 12-bit Weight Format"). */
-enum { SPEC_WEIGHTS_NATIVE = 0, SPEC_WEIGHTS_W12 = 1 };
+/* SPEC_WEIGHTS_W12_LOWP: W12 plus the 8-bit view of every weight (sign,
+ * exponent offset, top 3 mantissa bits; one more byte per weight) that
+ * spec_verify_lowp reads (besthub.dev article, section "(3) Two-Level
+ * Verification"). */
+enum { SPEC_WEIGHTS_NATIVE = 0, SPEC_WEIGHTS_W12 = 1, SPEC_WEIGHTS_W12_LOWP = 2 };
 enum { SPEC_LAYER_ATTN = 0, SPEC_LAYER_LR = 1 };
 
 #define SPEC_MAX_LAYERS 128
@@ -83,7 +87,7 @@ typedef struct spec_config {
   int32_t max_rows;       /* rows of one verify over all its requests        */
   int32_t prefill_chunk;  /* prompt rows per prefill pass                    */
   int32_t page_size;      /* tokens per KV page; must be 16                  */
-  int32_t weight_format;  /* SPEC_WEIGHTS_*; W12 needs SPEC_DTYPE_BF16        */
+  int32_t weight_format;  /* SPEC_WEIGHTS_*; W12 (_LOWP) need SPEC_DTYPE_BF16 */
 } spec_config;
 
 typedef struct spec_ctx spec_ctx;
@@ -142,6 +146,20 @@ int32_t spec_verify(spec_ctx* ctx, int32_t n_req, const int32_t* req,
                     const int32_t* n_nodes, const int32_t* draft_tokens,
                     const int32_t* parent_idx, int32_t* path,
                     int32_t* path_len, int32_t* bonus, float* d_logits_opt);
+
+/* The low-precision first round of two-level verification (besthub.dev,
+ * "SpecPilot: AI Agent Framework Boosts Speculative Decoding 10.87x for
+ * Qwen3.8-27B", section "(3) Two-Level Verification"): the same pass and
+ * arguments as spec_verify, with every weight read through its 8-bit view
+ * (weights with mantissas truncated to 3 bits), returning that model's
+ * greedy path and bonus token as a candidate chain.  It accepts nothing:
+ * the committed state is not modified and a following spec_commit is
+ * refused (SPEC_E_STATE) until an exact spec_verify has run.  Needs weights
+ * loaded with SPEC_WEIGHTS_W12_LOWP (else SPEC_E_UNSUPPORTED). */
+int32_t spec_verify_lowp(spec_ctx* ctx, int32_t n_req, const int32_t* req,
+                         const int32_t* n_nodes, const int32_t* draft_tokens,
+                         const int32_t* parent_idx, int32_t* path, int32_t* path_len,
+                         int32_t* bonus, float* d_logits_opt);
 
 /* Commit after a spec_verify of the same requests (same order).  host
  * arrays: path concatenated with max_nodes - 1 slots per request as returned

@@ -459,3 +459,109 @@ def test_w12_tile_over_capacity_is_rejected():
         engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="w12")
     assert ei.value.code == SPEC_E_UNSUPPORTED
     engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="native").close()
+
+
+# ------------------------------------------------ two-level verification
+
+def _view8(w):
+    """The 8-bit view of bf16 weight bits, from the format's definition: per
+    output row the base eb = max(0, largest exponent (255 counted as 254) -
+    15); a weight whose exponent lies in [eb, eb + 15] keeps its sign,
+    exponent and top 3 mantissa bits; any other keeps only its sign, with
+    exponent eb and mantissa 0."""
+    w = w.astype(np.int64)
+    exp = (w >> 7) & 0xFF
+    eb = np.maximum(np.minimum(exp.max(axis=1), 254) - 15, 0)[:, None]
+    inwin = (exp >= eb) & (exp <= eb + 15) & (exp != 255)
+    return np.where(inwin, w & 0xFFF0, (w & 0x8000) | (eb << 7)).astype(np.uint16)
+
+
+def _lowp_setup():
+    cfg, W = _setup("tiny_gqa_bf16")
+    W8 = {n: (_view8(W[n]) if k == "mat" and n != "embed" else W[n])
+          for n, _, k in synth.tensor_specs(cfg)}
+    return cfg, W, W8
+
+
+def test_lowp_pass_matches_oracle_on_8bit_view():
+    """spec_verify_lowp = the model with every GEMM weight replaced by its
+    8-bit view, over the exact committed cache; it accepts nothing."""
+    from oracle.verify import verify_single_pass
+    from tree_verification_spec_amd import SpecError, SPEC_E_STATE
+    cfg, W, W8 = _lowp_setup()
+    V = cfg["vocab"]
+    orc, orc8 = oracle_for(cfg, W), oracle_for(cfg, W8)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=13, weight_format="w12_lowp")
+    prompt = synth.prompt_tokens(V, 50, 71)
+    S, L, M, st = ar_greedy(orc, prompt, 1)
+    first = eng.prefill(0, prompt)
+    assert first == S[0] or M[0] < NEAR_TIE
+    eng.force_root(0, int(S[0]))
+    rng = np.random.default_rng(71)
+    for kind, K in (("chain", 8), ("tree", 12)):
+        toks = rng.integers(0, V, K)
+        par = (np.arange(-1, K - 1) if kind == "chain" else
+               np.array([-1, 0, 0, 1, 2, 3, -1, 6, 7, 4, 9, 5])[:K])
+        state0 = eng.state(0)
+        paths, bonus, lg = eng.verify([0], [toks], [par], logits=True, lowp=True)
+        lg = lg.cpu().numpy()
+        ref, A, rpath, rbonus = verify_single_pass(orc8, st, int(S[0]), toks, par)
+        for i in range(K + 1):
+            assert np.max(np.abs(lg[i] - ref[i])) <= logit_tol(cfg["dtype"], ref[i]), (kind, i)
+        if all(top2_margin(ref[i]) >= NEAR_TIE for i in range(K + 1)):
+            assert paths[0] == rpath and bonus[0] == rbonus
+        assert eng.state(0) == state0
+        with pytest.raises(SpecError) as e:
+            eng.commit([0], paths, bonus)
+        assert e.value.code == SPEC_E_STATE
+    # the 8-bit view is not the exact model: some logits must differ
+    ref_exact, *_ = verify_single_pass(orc, st, int(S[0]), toks, par)
+    assert np.max(np.abs(ref_exact - ref)) > 10 * logit_tol(cfg["dtype"], ref_exact[0])
+    eng.close()
+
+
+def test_two_level_steps_emit_ar_tokens():
+    """Two-level steps: the low-precision pass turns 4 drafts into a
+    candidate chain (its accepted drafts and its bonus token), the drafter
+    continues 3 positions from the chain's end, and one exact pass verifies
+    the whole chain.  Emitted tokens equal the oracle's greedy run."""
+    cfg, W, _ = _lowp_setup()
+    V = cfg["vocab"]
+    orc = oracle_for(cfg, W)
+    n_gen, K1, K2, alpha = 48, 4, 3, 0.7
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=K1 + K2 + 2, weight_format="w12_lowp")
+    prompt = synth.prompt_tokens(V, 40, 72)
+    S, L, M, _ = ar_greedy(orc, prompt, n_gen)
+    first = eng.prefill(0, prompt)
+    if first != S[0]:
+        assert M[0] < NEAR_TIE
+        eng.force_root(0, int(S[0]))
+    g, step, ties, cand_total = 1, 0, 0, 0
+    while g < n_gen:
+        d1, p1 = synth.chain_drafts(S, g, K1, alpha, V, 72, 0, step)
+        lpath, lbonus = eng.verify([0], [d1], [p1], lowp=True)
+        cand = [int(d1[p]) for p in lpath[0]] + [lbonus[0]]
+        d2, _ = synth.chain_drafts(S, g + len(cand), K2, alpha, V, 73, 0, step)
+        chain = np.array(cand + [int(t) for t in d2], np.int64)
+        paths, bonus = eng.verify([0], [chain], [np.arange(-1, len(chain) - 1)])
+        emitted = [int(chain[p]) for p in paths[0]] + [bonus[0]]
+        n_ok = 0
+        for j, t in enumerate(emitted):
+            if g + j >= n_gen or t != S[g + j]:
+                break
+            n_ok += 1
+        if n_ok < len(emitted) and g + n_ok < n_gen:
+            assert M[g + n_ok] < NEAR_TIE, (step, g, emitted, S[g:g + 8])
+            ties += 1
+            keep = paths[0][:n_ok]
+            eng.commit([0], [keep], [int(S[g + n_ok])])
+            g += len(keep) + 1
+        else:
+            eng.commit([0], paths, bonus)
+            g += len(emitted)
+        cand_total += len(cand)
+        step += 1
+    _say("two-level steps", step, "tokens", g, "candidate tokens", cand_total, "ties", ties)
+    assert ties <= 3
+    assert g / step > 1.5
+    eng.close()

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import synth
@@ -49,6 +50,16 @@ def test_workspace_bytes_and_config_validation():
     assert L.spec_workspace_bytes(make_config(tiny, weight_format="w12")) == 0
     b16 = synth.model_config("tiny_gqa_bf16")
     assert L.spec_workspace_bytes(make_config(b16, weight_format="w12")) > 0
+    # W12 plus the 8-bit view: bf16 only, one more byte per weight
+    assert L.spec_workspace_bytes(make_config(tiny, weight_format="w12_lowp")) == 0
+    w12 = L.spec_workspace_bytes(make_config(b16, weight_format="w12"))
+    lowp = L.spec_workspace_bytes(make_config(b16, weight_format="w12_lowp"))
+    n_w = sum(int(np.prod(s)) for n, s, k in synth.tensor_specs(b16)
+              if k == "mat" and n != "embed")
+    assert lowp - w12 >= n_w
+    bad_fmt = make_config(b16)
+    bad_fmt.weight_format = 3
+    assert L.spec_workspace_bytes(bad_fmt) == 0
     # the attention split table covers 64 splits of 128 keys
     assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8192)) > 0
     assert L.spec_workspace_bytes(make_config(tiny, max_ctx=8193)) == 0

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, lib,
     SPEC_DTYPE_BF16, SPEC_DTYPE_FP32, SPEC_LAYER_ATTN, SPEC_LAYER_LR,
     SPEC_E_INVAL, SPEC_E_STATE, SPEC_E_CAPACITY, SPEC_E_HIP,
-    SPEC_E_UNSUPPORTED, SPEC_MAX_LAYERS,
+    SPEC_E_UNSUPPORTED, SPEC_MAX_LAYERS, SPEC_WEIGHTS_NATIVE, SPEC_WEIGHTS_W12,
+    SPEC_WEIGHTS_W12_LOWP,
 )
 from .engine import Engine, make_config  # noqa: F401

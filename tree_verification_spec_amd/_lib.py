@@ -22,6 +22,7 @@ SPEC_LAYER_ATTN = 0
 SPEC_LAYER_LR = 1
 SPEC_WEIGHTS_NATIVE = 0
 SPEC_WEIGHTS_W12 = 1
+SPEC_WEIGHTS_W12_LOWP = 2
 SPEC_MAX_LAYERS = 128
 
 EXPORTS = [
@@ -30,7 +31,7 @@ EXPORTS = [
     "spec_force_root", "spec_set_fault", "spec_use_graphs", "spec_timing_enable",
     "spec_timing_read",
     "spec_destroy", "spec_last_error",
-    "spec_acceptance_update", "spec_plan_drafts",
+    "spec_acceptance_update", "spec_plan_drafts", "spec_verify_lowp",
 ]
 
 
@@ -76,6 +77,8 @@ def lib():
         "spec_prefill": (c_int32, [c_void_p, c_int32, i32p, c_int32, i32p, c_void_p]),
         "spec_verify": (c_int32, [c_void_p, c_int32, i32p, i32p, i32p, i32p, i32p,
                                   i32p, i32p, c_void_p]),
+        "spec_verify_lowp": (c_int32, [c_void_p, c_int32, i32p, i32p, i32p, i32p, i32p,
+                                       i32p, i32p, c_void_p]),
         "spec_commit": (c_int32, [c_void_p, c_int32, i32p, i32p, i32p, i32p]),
         "spec_release": (c_int32, [c_void_p, c_int32]),
         "spec_request_state": (c_int32, [c_void_p, c_int32, i32p, i32p]),
@@ -140,16 +143,18 @@ def spec_prefill(ctx, req, prompt, d_logits=None):
     return first.value
 
 
-def spec_verify(ctx, reqs, n_nodes, drafts, parents, max_nodes, d_logits=None):
-    """Returns (paths: list of lists of draft indices, bonus: list)."""
+def spec_verify(ctx, reqs, n_nodes, drafts, parents, max_nodes, d_logits=None,
+                lowp=False):
+    """Returns (paths: list of lists of draft indices, bonus: list).
+    lowp: spec_verify_lowp (the 8-bit weight view; accepts nothing)."""
     n = len(reqs)
     slots = max_nodes - 1
     path = (c_int32 * max(1, n * slots))()
     plen = (c_int32 * n)()
     bonus = (c_int32 * n)()
-    _check(ctx, lib().spec_verify(ctx, n, _i32(reqs), _i32(n_nodes), _i32(drafts),
-                                  _i32(parents), path, plen, bonus,
-                                  c_void_p(d_logits or 0)))
+    f = lib().spec_verify_lowp if lowp else lib().spec_verify
+    _check(ctx, f(ctx, n, _i32(reqs), _i32(n_nodes), _i32(drafts), _i32(parents), path, plen,
+                  bonus, c_void_p(d_logits or 0)))
     paths = [[path[r * slots + k] for k in range(plen[r])] for r in range(n)]
     return paths, list(bonus)
 

@@ -41,7 +41,7 @@ template <int MT> struct ChunkK {
                              : MT <= 4 ? 256 : MT <= 5 ? 192 : 128;
 };
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D, bool W12>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D, int WF>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr bool kBf = sizeof(T) == 2;
@@ -75,9 +75,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 
   // weights: bf16 / fp32 tiles (a Frag per lane), or W12 tiles (12 bytes
   // per lane plus one exception-slot word, decoded to a Frag before use)
-  static_assert(!W12 || sizeof(T) == 2, "W12 holds bf16 weights");
-  using WReg = typename std::conditional<W12, W12Raw, Frag<T>>::type;
-  constexpr uint32_t TB = W12 ? kW12TileBytes : 64 * sizeof(Frag<T>);  // tile bytes
+  // weight format: 0 = bf16 / fp32 tiles, 1 = W12, 2 = the 8-bit view
+  constexpr bool W12 = WF == 1, W8 = WF == 2;
+  static_assert(WF == 0 || sizeof(T) == 2, "W12 and its 8-bit view hold bf16 weights");
+  using WReg = typename std::conditional<
+      W12, W12Raw, typename std::conditional<W8, uint2, Frag<T>>::type>::type;
+  constexpr uint32_t TB = W12  ? kW12TileBytes
+                          : W8 ? kW8TileBytes
+                               : 64 * sizeof(Frag<T>);  // tile bytes
   // one buffer resource per tile row (scalar registers); a K-step's tile is
   // at the scalar offset k * wk, a lane's words at a fixed per-lane offset
   __amdgpu_buffer_rsrc_t wrs[NTW];
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   for (int t = 0; t < NTW; ++t) {
     const size_t tr = (size_t)((nb * WAVES + wave) * NTW + t);  // tile row
     wrs[t] = weight_rsrc(reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * TB);
-    if constexpr (W12) {
+    if constexpr (W12 || W8) {
       const uint32_t e = a.eb[tr * 16 + r16];
       eb7[t] = (e | (e << 16)) << 7;
     } else {
@@ -181,6 +186,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
         dst[t] = W12Raw{d.x, d.y, d.z,
                         __builtin_amdgcn_raw_buffer_load_b32(
                             wrs[t], (kW12SlotDword + (lane & 7)) * 4, so, 0)};
+      } else if constexpr (W8) {
+        dst[t] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(wrs[t], lane * 8, so, 0));
       } else if constexpr (kBf) {
         dst[t].v = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs[t], lane * 16, so, 0));
@@ -200,6 +208,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       f.v = w12_decode(r, eb7[t]);
       if constexpr (kOrdered) w12_patch_opaque(f.v, r, lane);
       else w12_patch(f.v, r, lane);
+      return f;
+    } else if constexpr (W8) {
+      Frag<T> f;
+      f.v = w8_decode(r, eb7[t]);
       return f;
     } else {
       (void)t;
@@ -338,9 +350,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, bool W12 = false>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, int WF = 0>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, W12>;
+  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, WF>;
   constexpr int KC = ChunkK<MT>::value;
   const size_t stage_b = 2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * 4;
   const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
@@ -372,43 +384,44 @@ Variant gemm_variant(bool bf16, int N, int M) {
   return b256 >= 128 ? Variant{2, 8} : Variant{2, 4};
 }
 
-template <typename T, int EPI, int NTW, int WAVES, int D, bool W12>
+template <typename T, int EPI, int NTW, int WAVES, int D, int WF>
 hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_one<T, 1, NTW, WAVES, EPI, D, W12>(a, s);
-    case 2: return launch_one<T, 2, NTW, WAVES, EPI, D, W12>(a, s);
-    case 3: return launch_one<T, 3, NTW, WAVES, EPI, D, W12>(a, s);
-    case 4: return launch_one<T, 4, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
-    case 5: return launch_one<T, 5, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
-    default: return launch_one<T, 8, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), W12>(a, s);
+    case 1: return launch_one<T, 1, NTW, WAVES, EPI, D, WF>(a, s);
+    case 2: return launch_one<T, 2, NTW, WAVES, EPI, D, WF>(a, s);
+    case 3: return launch_one<T, 3, NTW, WAVES, EPI, D, WF>(a, s);
+    case 4: return launch_one<T, 4, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), WF>(a, s);
+    case 5: return launch_one<T, 5, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), WF>(a, s);
+    default: return launch_one<T, 8, NTW, WAVES, EPI, (NTW > 1 ? 4 : D), WF>(a, s);
   }
 }
 
-template <typename T, int EPI, bool W12>
+template <typename T, int EPI, int WF>
 hipError_t launch_var(Variant v, int mt, const GemmArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, W12>(mt, a, s);
-    if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD, W12>(mt, a, s);
+    if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, WF>(mt, a, s);
+    if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD, WF>(mt, a, s);
   }
-  if (v.ntw == 1 && v.waves == 8) return launch_mt<T, EPI, 1, 8, kD, W12>(mt, a, s);
+  if (v.ntw == 1 && v.waves == 8) return launch_mt<T, EPI, 1, 8, kD, WF>(mt, a, s);
   return hipErrorInvalidValue;
 }
 
-template <typename T, bool W12>
+template <typename T, int WF>
 hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
-  if (epi == EPI_PART) return launch_var<T, EPI_PART, W12>(v, mt, a, s);
-  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, W12>(v, mt, a, s);
-  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, W12>(v, mt, a, s);
+  if (epi == EPI_PART) return launch_var<T, EPI_PART, WF>(v, mt, a, s);
+  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, WF>(v, mt, a, s);
+  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, WF>(v, mt, a, s);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (a.w12) return launch_fmt<T, true>(epi, v, a, mt, s);
+    if (a.w12 == 1) return launch_fmt<T, 1>(epi, v, a, mt, s);
+    if (a.w12 == 2) return launch_fmt<T, 2>(epi, v, a, mt, s);
   }
   if (a.w12) return hipErrorInvalidValue;
-  return launch_fmt<T, false>(epi, v, a, mt, s);
+  return launch_fmt<T, 0>(epi, v, a, mt, s);
 }
 
 }  // namespace
@@ -438,7 +451,10 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
   a.KR = a.K / a.S;
   if (a.wsn <= 0 || a.wsk <= 0) return hipErrorInvalidValue;
   // weights are addressed through 32-bit buffer offsets: at most 4 GB a matrix
-  const size_t tile_bytes = a.w12 ? kW12TileBytes : (bf16 ? 1024 : 2048);
+  if (a.w12 < 0 || a.w12 > 2) return hipErrorInvalidValue;
+  const size_t tile_bytes = a.w12 == 1 ? kW12TileBytes
+                            : a.w12 == 2 ? kW8TileBytes
+                                         : (bf16 ? 1024 : 2048);
   if ((size_t)a.ntiles * (a.K / 32) * tile_bytes > 0xFFFFFFFFull) return hipErrorInvalidValue;
   // one workgroup shape for all row chunks (the ARGMAX block layout and the
   // partial sums must not depend on the chunk)

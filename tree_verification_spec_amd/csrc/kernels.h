@@ -47,7 +47,8 @@ enum GemmEpi { EPI_PART = 0, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 struct GemmArgs {
   const void* W;        // tiled weights (bf16 bits or fp32, or W12 tiles), ntiles x 16 rows
   int32_t wsn, wsk;     // tile strides of W between tile rows and between K-steps
-  int32_t w12;          // W holds W12 tiles (w12.h) ...
+  int32_t w12;          // W holds 0: bf16 / fp32 tiles, 1: W12 tiles, 2: tiles of
+                        // the 8-bit view (w12.h) ...
   const uint8_t* eb;    // ... with these per-row base exponents [ntiles * 16]
   const void* X;        // activation planes [M, ldx] (hi; lo at X + xlo)
   int32_t ldx;
@@ -188,13 +189,14 @@ hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
 // W12 encoding (w12.h): eb[r] for the rows of a row-major bf16 slab
 // [nrows, K]; then the slab's tiles, placed like launch_relayout places
 // them (tile index tr * wsn + kb * wsk, 800 bytes each), and the rows'
-// bases at their destination rows of eb_dst.  *err becomes nonzero if a
-// tile has more exceptions than W12 holds.
+// bases at their destination rows of eb_dst; with dst8, also the 8-bit
+// view's tiles (512 bytes) at the same tile indices.  *err becomes nonzero
+// if a tile has more exceptions than W12 holds.
 hipError_t launch_w12_rowexp(const void* src, int nrows, int K, uint8_t* eb,
                              hipStream_t s);
 hipError_t launch_w12_encode(const void* src, int nrows, int K, const uint8_t* eb,
-                             uint8_t* eb_dst, void* dst, int dst_tile0, int tile_stride,
-                             int wsn, int wsk, int* err, hipStream_t s);
+                             uint8_t* eb_dst, void* dst, void* dst8, int dst_tile0,
+                             int tile_stride, int wsn, int wsk, int* err, hipStream_t s);
 
 // Widen a norm vector (bf16 bits or fp32) to fp32.
 hipError_t launch_to_f32(bool bf16, const void* src, int n, float* dst,

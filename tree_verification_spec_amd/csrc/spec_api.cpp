@@ -61,6 +61,7 @@ struct WMat {
   bool kmajor = false;   // tile order
   uint8_t* eb = nullptr; // W12: per-row base exponents [n]
   int* err = nullptr;    // W12: set when a tile does not fit the format
+  void* p8 = nullptr;    // the 8-bit view's tiles (W12_LOWP)
 };
 
 struct Layer {
@@ -143,6 +144,8 @@ struct spec_ctx {
   void* embed = nullptr;
   WMat lm_head;
   bool w12 = false;          // weights stored as W12 tiles
+  bool w8 = false;           // ... and as their 8-bit view
+  bool cur_lowp = false;     // the pass being enqueued reads the 8-bit view
   uint8_t* eb_tmp = nullptr; // W12 encoding: base exponents of one slab's rows
   size_t w12_side0 = 0, w12_side_bytes = 0;  // W12 side data (zeroed at create)
   float* final_norm = nullptr;
@@ -248,9 +251,10 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->vocab % 16 || cfg->vocab <= 0) return bad("vocab must be a multiple of 16");
   if ((cfg->n_heads * cfg->head_dim) % 32) return bad("n_heads*head_dim");
   if (cfg->page_size != 16) return bad("page_size must be 16");
-  if (cfg->weight_format != SPEC_WEIGHTS_NATIVE && cfg->weight_format != SPEC_WEIGHTS_W12)
+  if (cfg->weight_format != SPEC_WEIGHTS_NATIVE && cfg->weight_format != SPEC_WEIGHTS_W12 &&
+      cfg->weight_format != SPEC_WEIGHTS_W12_LOWP)
     return bad("weight_format");
-  if (cfg->weight_format == SPEC_WEIGHTS_W12 && cfg->dtype != SPEC_DTYPE_BF16)
+  if (cfg->weight_format != SPEC_WEIGHTS_NATIVE && cfg->dtype != SPEC_DTYPE_BF16)
     return bad("W12 weights need a bf16 model");
   if (cfg->max_requests <= 0 || cfg->max_ctx <= 0) return bad("capacity");
   if (cfg->max_nodes < 1 || cfg->max_nodes > 65) return bad("max_nodes must be in [1, 65]");
@@ -286,9 +290,10 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
 
   // weights; every matrix region holds its uncompressed tiles, and with
   // W12 also a base exponent per output row and two counters
-  const bool w12 = cfg.weight_format == SPEC_WEIGHTS_W12;
+  const bool w12 = cfg.weight_format != SPEC_WEIGHTS_NATIVE;
+  const bool w8 = cfg.weight_format == SPEC_WEIGHTS_W12_LOWP;
   struct MatPlan {
-    size_t off = 0, bytes = 0, off_eb = 0, off_cnt = 0;
+    size_t off = 0, bytes = 0, off_eb = 0, off_cnt = 0, off8 = 0;
     int n = 0, k = 0;
     bool kmajor = false;
   };
@@ -330,6 +335,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     if (!w12 || m.n == 0) return;
     m.off_eb = p.take((size_t)m.n);
     m.off_cnt = p.take(sizeof(int));
+    if (w8) m.off8 = p.take((size_t)m.n * m.k);  // the 8-bit view: one byte a weight
   };
   for (int i = 0; i < cfg.n_layers; ++i) {
     side(m_qkv[i]);
@@ -415,12 +421,14 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
         w.eb = (uint8_t*)at(m.off_eb);
         w.err = (int*)at(m.off_cnt);
       }
+      if (w8) w.p8 = at(m.off8);
       return w;
     };
     c->embed = at(o_embed);
     c->final_norm = (float*)at(o_fnorm);
     c->lm_head = wmat(m_lm);
     c->w12 = w12;
+    c->w8 = w8;
     c->eb_tmp = w12 ? (uint8_t*)at(o_ebtmp) : nullptr;
     c->w12_side0 = weights_end;
     c->w12_side_bytes = w12_end - weights_end;
@@ -559,6 +567,10 @@ GemmArgs gemm_args(const spec_ctx* c, const WMat& W, const void* X, int ldx, int
   a.wsk = o.wsk;
   a.w12 = c->w12 ? 1 : 0;
   a.eb = W.eb;
+  if (c->cur_lowp) {
+    a.W = W.p8;
+    a.w12 = 2;
+  }
   a.X = X;
   a.ldx = ldx;
   a.xlo = (int64_t)lo_off(c, ldx);
@@ -591,6 +603,7 @@ struct Pass {
   float* d_logits = nullptr;
   int split = 0, max_splits = 0, tpw = 0, max_qgroups = 0, max_rows_req = 0;
   bool walk = false;  // append the accepted-path walk (verify passes)
+  bool lowp = false;  // read the weights' 8-bit view
   std::vector<int64_t> key(const spec_ctx* c) const;
 };
 
@@ -655,12 +668,12 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
 
 std::vector<int64_t> Pass::key(const spec_ctx* c) const {
   return {R, n_req, any_tree, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
-          split, max_splits, tpw, max_qgroups, max_rows_req, walk, c->fault_tok,
+          split, max_splits, tpw, max_qgroups, max_rows_req, walk, lowp, c->fault_tok,
           (int64_t)__builtin_bit_cast(uint32_t, c->fault_bias), c->fault_after};
 }
 
 // Enqueue the kernels of a planned pass on the context's stream.
-int launch_pass(spec_ctx* c, const Pass& P) {
+int launch_pass_impl(spec_ctx* c, const Pass& P) {
   const spec_config& cfg = c->cfg;
   const bool bf = c->bf16;
   hipStream_t s = c->stream;
@@ -778,6 +791,13 @@ int launch_pass(spec_ctx* c, const Pass& P) {
   return SPEC_OK;
 }
 
+int launch_pass(spec_ctx* c, const Pass& P) {
+  c->cur_lowp = P.lowp;  // read by gemm_args while the pass is enqueued
+  const int rc = launch_pass_impl(c, P);
+  c->cur_lowp = false;
+  return rc;
+}
+
 // Run a planned pass: replay a captured graph of its kernels when one with
 // the same launch parameters exists (capturing it on first use), else
 // launch eagerly.  Graphs are off while kernel timing is enabled.
@@ -819,12 +839,13 @@ int run_pass(spec_ctx* c, const Pass& P) {
 
 int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
             const std::vector<int>& rows_per_req, bool any_tree, int lm_row0, int lm_rows,
-            float* d_logits, bool prefill, bool walk) {
+            float* d_logits, bool prefill, bool walk, bool lowp = false) {
   Pass P;
   const int rc = plan_pass(c, P, R, n_req, keys_per_req, rows_per_req, any_tree, lm_row0,
                            lm_rows, d_logits, prefill);
   if (rc) return rc;
   P.walk = walk;
+  P.lowp = lowp;
   // prefill chunks run eagerly (their shapes vary); verify passes replay graphs
   return prefill ? launch_pass(c, P) : run_pass(c, P);
 }
@@ -959,7 +980,7 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
       const int tile0 = t.tile0 + (r0 / 16) * t.tile_stride;
       if (c->w12) {
         HIP_TRY(launch_w12_rowexp(from, nr, t.cols, c->eb_tmp, s));
-        HIP_TRY(launch_w12_encode(from, nr, t.cols, c->eb_tmp, m.eb, t.dst, tile0,
+        HIP_TRY(launch_w12_encode(from, nr, t.cols, c->eb_tmp, m.eb, t.dst, m.p8, tile0,
                                   t.tile_stride, t.wsn, t.wsk, m.err, s));
       } else {
         HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst, tile0, t.tile_stride,
@@ -1063,12 +1084,15 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
   return SPEC_OK;
 }
 
-extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
-                               const int32_t* n_nodes, const int32_t* draft_tokens,
-                               const int32_t* parent_idx, int32_t* path,
-                               int32_t* path_len, int32_t* bonus, float* d_logits_opt) {
+namespace {
+
+int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n_nodes,
+                const int32_t* draft_tokens, const int32_t* parent_idx, int32_t* path,
+                int32_t* path_len, int32_t* bonus, float* d_logits_opt, bool lowp) {
   int rc = check(c);
   if (rc) return rc;
+  if (lowp && !c->w8)
+    return fail(c, SPEC_E_UNSUPPORTED, "no 8-bit weight view (load with W12_LOWP)");
   const spec_config& cfg = c->cfg;
   if (n_req < 1 || n_req > cfg.max_requests || !req || !n_nodes || !path || !path_len ||
       !bonus)
@@ -1142,7 +1166,7 @@ extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
   }
   HIP_TRY(hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
                          c->stream));
-  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false, true);
+  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false, true, lowp);
   if (rc) return rc;
   const int max_path = kMaxPath;
   HIP_TRY(hipMemcpyAsync(c->h_res, c->res, (size_t)n_req * (2 + max_path) * 4,
@@ -1155,8 +1179,27 @@ extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
     bonus[r] = o[1];
     for (int k = 0; k < o[0] && k < slots; ++k) path[(size_t)r * slots + k] = o[2 + k] - 1;
   }
-  c->last = lv;
+  // only an exact verification may be committed
+  c->last = lowp ? LastVerify{} : lv;
   return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t spec_verify(spec_ctx* c, int32_t n_req, const int32_t* req,
+                               const int32_t* n_nodes, const int32_t* draft_tokens,
+                               const int32_t* parent_idx, int32_t* path,
+                               int32_t* path_len, int32_t* bonus, float* d_logits_opt) {
+  return verify_impl(c, n_req, req, n_nodes, draft_tokens, parent_idx, path, path_len, bonus,
+                     d_logits_opt, false);
+}
+
+extern "C" int32_t spec_verify_lowp(spec_ctx* c, int32_t n_req, const int32_t* req,
+                                    const int32_t* n_nodes, const int32_t* draft_tokens,
+                                    const int32_t* parent_idx, int32_t* path,
+                                    int32_t* path_len, int32_t* bonus, float* d_logits_opt) {
+  return verify_impl(c, n_req, req, n_nodes, draft_tokens, parent_idx, path, path_len, bonus,
+                     d_logits_opt, true);
 }
 
 extern "C" int32_t spec_commit(spec_ctx* c, int32_t n_req, const int32_t* req,

@@ -146,3 +146,26 @@ __device__ __forceinline__ void w12_patch_opaque(uint4& v, const W12Raw& w, int 
       : "scc");
   v = make_uint4(x, y, z, q);
 }
+
+// ---- The 8-bit view (the low-precision pass of two-level verification):
+// per weight one byte s << 7 | d << 3 | (top 3 mantissa bits), with the
+// W12 base exponents of the same rows.  A tile is 512 bytes, lane l's 8
+// weights at bytes l * 8 + e.  A weight outside its row's window keeps only
+// its sign (d = 0, mantissa 0).  Decoding gives the weight with its
+// mantissa truncated to 3 bits.
+constexpr int kW8TileBytes = 512;
+
+__device__ __forceinline__ uint4 w8_decode(uint2 w, uint32_t eb7) {
+  // bytes 2j, 2j + 1 of a dword into the low byte of each 16-bit half
+  constexpr uint32_t kP0 = 0x0C010C00u, kP1 = 0x0C030C02u;  // 0x0C selects a zero byte
+  auto pair = [eb7](uint32_t h) -> uint32_t {
+    return (((h & 0x007F007Fu) << 4) + eb7) | ((h & 0x00800080u) << 8);
+  };
+  uint4 v;
+  v.x = pair(__builtin_amdgcn_perm(0u, w.x, kP0));
+  v.y = pair(__builtin_amdgcn_perm(0u, w.x, kP1));
+  v.z = pair(__builtin_amdgcn_perm(0u, w.y, kP0));
+  v.w = pair(__builtin_amdgcn_perm(0u, w.y, kP1));
+  return v;
+}
+

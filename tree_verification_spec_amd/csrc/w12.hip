@@ -37,10 +37,11 @@ __global__ __launch_bounds__(256) void w12_rowexp_kernel(const uint16_t* src, in
 // tile_stride; tile (row tr, K-step kb) sits at tile index tr * wsn + kb *
 // wsk of the destination.  eb: the bases of the slab's rows; eb_dst gets
 // them at the destination rows.  *err is set when a tile has more
-// exceptions than its list holds.
+// exceptions than its list holds.  dst8 (optional): the 8-bit view's tiles
+// at the same tile indices.
 __global__ __launch_bounds__(64) void w12_encode_kernel(
     const uint16_t* src, int K, const uint8_t* eb, uint8_t* eb_dst, uint8_t* dst,
-    int dst_tile0, int tile_stride, int wsn, int wsk, int* err) {
+    uint8_t* dst8, int dst_tile0, int tile_stride, int wsn, int wsk, int* err) {
   __shared__ uint32_t slot[8];
   const int ksteps = K / 32;
   const int tile = blockIdx.x;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
   if (kb == 0 && lane < 16)  // the destination rows' bases, once per tile row
     eb_dst[(size_t)(dst_tile0 + nb * tile_stride) * 16 + lane] = (uint8_t)base;
   // the three data dwords (layout in w12.h); exceptions leave zeros
-  uint32_t da = 0, db = 0, dc = 0, excmask = 0;
+  uint32_t da = 0, db = 0, dc = 0, excmask = 0, v8lo = 0, v8hi = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t bits = w[e];
@@ -76,6 +77,11 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
       dc |= sign << (8 * ((k + 1) & 3) + 3);
     }
     excmask |= (exc ? 1u : 0u) << e;
+    // the 8-bit view: sign, offset, top 3 mantissa bits (sign only when out
+    // of the window)
+    const uint32_t c8 = ((bits >> 15) << 7) | (exc ? 0u : (dd << 3) | ((bits >> 4) & 7u));
+    if (e < 4) v8lo |= c8 << (8 * e);
+    else v8hi |= c8 << (8 * (e - 4));
   }
   // exclusive prefix of the exception counts over the wave
   const uint32_t cnt = __builtin_popcount(excmask);
@@ -89,6 +95,8 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
   const uint32_t first = incl - cnt;
   const size_t tidx = (size_t)(dst_tile0 + nb * tile_stride) * wsn + (size_t)kb * wsk;
   uint8_t* t = dst + tidx * kW12TileBytes;
+  if (dst8)
+    *reinterpret_cast<uint2*>(dst8 + tidx * kW8TileBytes + lane * 8) = make_uint2(v8lo, v8hi);
   __syncthreads();
   if (total > (uint32_t)kW12MaxExc) {
     if (lane == 0) atomicOr(err, 1);
@@ -118,13 +126,13 @@ hipError_t launch_w12_rowexp(const void* src, int nrows, int K, uint8_t* eb,
 }
 
 hipError_t launch_w12_encode(const void* src, int nrows, int K, const uint8_t* eb,
-                             uint8_t* eb_dst, void* dst, int dst_tile0, int tile_stride,
-                             int wsn, int wsk, int* err, hipStream_t s) {
+                             uint8_t* eb_dst, void* dst, void* dst8, int dst_tile0,
+                             int tile_stride, int wsn, int wsk, int* err, hipStream_t s) {
   if (nrows % 16 || K % 32) return hipErrorInvalidValue;
   const unsigned tiles = (unsigned)(nrows / 16) * (K / 32);
   if (tiles == 0) return hipSuccess;
   w12_encode_kernel<<<tiles, 64, 0, s>>>((const uint16_t*)src, K, eb, eb_dst,
-                                         (uint8_t*)dst, dst_tile0, tile_stride, wsn, wsk,
-                                         err);
+                                         (uint8_t*)dst, (uint8_t*)dst8, dst_tile0,
+                                         tile_stride, wsn, wsk, err);
   return hipGetLastError();
 }

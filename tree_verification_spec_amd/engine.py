@@ -8,7 +8,8 @@ from . import _lib as L
 def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
                 max_rows=None, prefill_chunk=512, weight_format="native"):
     """spec_config from a model-shape dict (keys as in synth.configs).
-    weight_format: "native" (the model's dtype) or "w12" (bf16 models only)."""
+    weight_format: "native" (the model's dtype), "w12" or "w12_lowp" (W12 plus
+    the 8-bit view read by verify(lowp=True)); the W12 formats need bf16."""
     c = L.spec_config()
     c.n_layers = model["n_layers"]
     c.d_model = model["d_model"]
@@ -29,10 +30,11 @@ def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
     c.max_rows = max_rows if max_rows is not None else max_nodes * max_requests
     c.prefill_chunk = prefill_chunk
     c.page_size = 16
-    if weight_format not in ("native", "w12"):
+    formats = {"native": L.SPEC_WEIGHTS_NATIVE, "w12": L.SPEC_WEIGHTS_W12,
+               "w12_lowp": L.SPEC_WEIGHTS_W12_LOWP}
+    if weight_format not in formats:
         raise ValueError(f"unknown weight format {weight_format!r}")
-    c.weight_format = (L.SPEC_WEIGHTS_W12 if weight_format == "w12"
-                       else L.SPEC_WEIGHTS_NATIVE)
+    c.weight_format = formats[weight_format]
     return c
 
 
@@ -85,11 +87,12 @@ class Engine:
                                out.data_ptr() if out is not None else None)
         return (first, out) if logits else first
 
-    def verify(self, reqs, drafts, parents, logits=False):
+    def verify(self, reqs, drafts, parents, logits=False, lowp=False):
         """drafts/parents: one array per request.  Returns (paths, bonus
         [, logits tensor [rows, vocab]]).  The logits tensor is a view of one
         buffer owned by the engine (so repeated passes keep one launch
-        shape): it is valid until the next verify."""
+        shape): it is valid until the next verify.  lowp: the low-precision
+        first round of two-level verification (accepts nothing)."""
         n_nodes = [len(d) for d in drafts]
         flat_d = [int(t) for d in drafts for t in d]
         flat_p = [int(p) for ps in parents for p in ps]
@@ -103,7 +106,7 @@ class Engine:
             out = self._logits[:rows]
         paths, bonus = L.spec_verify(self.ctx, list(reqs), n_nodes, flat_d, flat_p,
                                      self.max_nodes,
-                                     out.data_ptr() if out is not None else None)
+                                     out.data_ptr() if out is not None else None, lowp)
         return (paths, bonus, out) if logits else (paths, bonus)
 
     def commit(self, reqs, paths, next_roots):

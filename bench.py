@@ -62,7 +62,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense8b_chain", choices=WORKLOADS)
     ap.add_argument("--alpha", type=float, default=None)
-    ap.add_argument("--weights", default=None, choices=("w12", "native"),
+    ap.add_argument("--weights", default=None, choices=("w12", "native", "w12_lowp"),
                     help="weight storage: W12 (lossless 12-bit, bitwise-identical "
                          "results) or the model's bf16; default: the faster of the two "
                          "for the workload (W12 up to 32 rows per pass, bf16 above)")
@@ -70,6 +70,10 @@ def main():
                     help="batched workload: fixed K drafts per request, or per-step draft "
                          "lengths of 8/12/16 from each request's acceptance so far under a "
                          "shared budget of batch x K draft nodes")
+    ap.add_argument("--two-level", default=None, metavar="K1,K2",
+                    help="chain workloads: two-level verification steps (a pass on the "
+                         "8-bit weight view over K1 drafts gives a candidate chain, the "
+                         "drafter continues K2 positions, one exact pass verifies all)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -123,9 +127,17 @@ def main():
         [a for a in w.get("alphas", ()) if abs(a - alpha_main) > 1e-9]
     # reference length: enough tokens for every run's expected acceptance
     planned = batched and args.policy == "budget"
+    two = tuple(int(x) for x in args.two_level.split(",")) if args.two_level else None
+    if two and (batched or tree):
+        print("bench.py: --two-level is for the chain workload", file=sys.stderr)
+        sys.exit(2)
+    if two:
+        args.weights = "w12_lowp"
     choices, min_prob, decay = (8, 12, 16), 0.05, 0.9
     budget = B * K
     depth = w.get("max_depth", 8) if tree else (max(choices) if planned else K)
+    if two:
+        depth = two[0] + two[1] + 1
     runs = [(alpha_main if not batched else 0.9, args.warmup + args.steps),
             (alpha_main if not batched else 0.9, max(10, args.steps // 3) + 2)]
     runs += [(a, max(20, args.steps // 2) + 4) for a in sweep_alphas]
@@ -139,7 +151,8 @@ def main():
     max_ctx = max(len(p) for p in prompts) + ref_len + 2 * (depth + 1)
     eng = Engine(cfg, device=0, max_requests=B, max_ctx=max_ctx,
                  max_nodes=(max(choices) if planned else K) + 1,
-                 max_rows=B * (K + 1), prefill_chunk=512, weight_format=args.weights)
+                 max_rows=B * ((depth if two else K) + 1), prefill_chunk=512,
+                 weight_format=args.weights)
     t0 = time.time()
     eng.load_weights([W[n] for n, _, _ in synth.tensor_specs(cfg)])
     log(f"weights loaded in {time.time() - t0:.1f}s")
@@ -190,11 +203,33 @@ def main():
             lens = (L.spec_plan_drafts(succ, fail, choices, min_prob, budget) if planned
                     else [K] * B)
             t_plan = time.perf_counter() - t_plan
-            dr = [drafts_for(r, g[r], it, al[r], lens[r]) for r in range(B)]
+            t_lp = 0.0
+            if two:
+                # low-precision round (timed), then the drafter's continuation
+                # from the candidate chain's end (host synthesis, untimed)
+                d1 = [drafts_for(r, g[r], it, al[r], two[0]) for r in range(B)]
+                sync()
+                a = time.perf_counter()
+                ev0.record(eng.stream)
+                lp_paths, lp_bonus = eng.verify(slots, [d[0] for d in d1], [d[1] for d in d1],
+                                                lowp=True)
+                t_lp = time.perf_counter() - a
+                dr = []
+                for r in range(B):
+                    cand = [int(d1[r][0][p]) for p in lp_paths[r]] + [lp_bonus[r]]
+                    cont, _ = synth.chain_drafts(S[r], g[r] + len(cand), two[1], al[r], V,
+                                                 idx + 50, r, it)
+                    ch = np.array(cand + [int(t) for t in cont], np.int32)
+                    dr.append((ch, np.arange(-1, len(ch) - 1, dtype=np.int32)))
+                lens = [len(d[0]) for d in dr]
+                lp_rows = [two[0] + 1] * B
+            else:
+                dr = [drafts_for(r, g[r], it, al[r], lens[r]) for r in range(B)]
             ctx = [eng.state(slots[r])[0] for r in range(B)]
             sync()
             a = time.perf_counter()
-            ev0.record(eng.stream)
+            if not two:
+                ev0.record(eng.stream)
             paths, bonus = eng.verify(slots, [d[0] for d in dr], [d[1] for d in dr])
             keep, roots, n_new = [], [], []
             for r in range(B):
@@ -218,7 +253,7 @@ def main():
             eng.commit(slots, keep, roots)
             ev1.record(eng.stream)
             sync()
-            dt = time.perf_counter() - a
+            dt = time.perf_counter() - a + t_lp
             if planned:
                 t_upd = time.perf_counter()
                 succ, fail = L.spec_acceptance_update(lens, [len(p) for p in paths], decay,
@@ -229,6 +264,12 @@ def main():
                 toks += sum(n_new)
                 dev_ms.append(ev0.elapsed_time(ev1))
                 nb, fl, lb, ty = step_bounds(cfg, [k + 1 for k in lens], ctx, args.weights)
+                if two:  # the low-precision pass reads the 8-bit view
+                    nb2, fl2, _, ty2 = step_bounds(cfg, lp_rows, ctx, "w8")
+                    nb, fl = nb + nb2, fl + fl2
+                    from tree_verification_spec_amd import costmodel as _cm
+                    lb = _cm.lower_bound(nb, fl)
+                    ty = {t: (ty[t][0] + ty2[t][0], ty[t][1] + ty2[t][1]) for t in ty}
                 lbs.append(lb)
                 lbs_b.append(nb)
                 types.append(ty)
@@ -287,6 +328,11 @@ def main():
         if planned:
             desc += (", draft lengths planned per step (8/12/16 by acceptance, shared "
                      f"budget of {budget} draft nodes)")
+    elif two:
+        desc = ("8B-shaped dense decoder, 2048-token prompt, two-level verification: "
+                f"{two[0]} drafts through the 8-bit weight view, candidate chain + "
+                f"{two[1]} continuation drafts through the exact pass, alpha=%.1f, batch 1"
+                % alpha_main)
     elif tree:
         model = ("8B-shaped dense decoder" if w["model"] == "dense8b" else
                  "27B-shaped hybrid (48 recurrent + 16 attention layers)")

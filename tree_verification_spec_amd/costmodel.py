@@ -62,10 +62,13 @@ def lower_bound(nbytes, flops):
 
 
 def weight_bytes(rows, cols, fmt):
-    """Stored bytes of one [rows, cols] matrix: 2 per bf16 weight, or W12
-    tiles (800 bytes per 512 weights) plus one base-exponent byte per row."""
-    if fmt == "w12":
+    """Stored bytes of one [rows, cols] matrix: 2 per bf16 weight, W12
+    tiles (800 bytes per 512 weights) or the 8-bit view (1 byte a weight),
+    each W12 format plus one base-exponent byte per row."""
+    if fmt in ("w12", "w12_lowp"):
         return rows * cols * 800 / 512 + rows
+    if fmt == "w8":
+        return rows * cols + rows
     return rows * cols * 2
 
 

@@ -91,7 +91,7 @@ def main():
     import numpy as np
     import torch
     import synth
-    from tree_verification_spec_amd import Engine
+    from tree_verification_spec_amd import Engine, costmodel
     import tree_verification_spec_amd as L
 
     if args.copy_probe_bytes:
@@ -267,8 +267,7 @@ def main():
                 if two:  # the low-precision pass reads the 8-bit view
                     nb2, fl2, _, ty2 = step_bounds(cfg, lp_rows, ctx, "w8")
                     nb, fl = nb + nb2, fl + fl2
-                    from tree_verification_spec_amd import costmodel as _cm
-                    lb = _cm.lower_bound(nb, fl)
+                    lb = costmodel.lower_bound(nb, fl)
                     ty = {t: (ty[t][0] + ty2[t][0], ty[t][1] + ty2[t][1]) for t in ty}
                 lbs.append(lb)
                 lbs_b.append(nb)
@@ -311,7 +310,6 @@ def main():
 
     # roofline of the dominant kernel: FFN gate/up GEMM, weights streamed once
     # per launch (passes of more than 128 rows launch it once per 128 rows)
-    from tree_verification_spec_amd import costmodel
     gu_bytes = costmodel.weight_bytes(2 * cfg["ffn_dim"], cfg["d_model"], args.weights)
     k_ms, k_n = rl["ktime"]
     k_avg_s = k_ms / 1e3 / max(1, k_n)

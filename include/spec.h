@@ -186,6 +186,12 @@ int32_t spec_request_state(const spec_ctx* ctx, int32_t req, int32_t* n_ctx,
  * near-tie).  Invalidates a pending verify of that request.  Host-only. */
 int32_t spec_force_root(spec_ctx* ctx, int32_t req, int32_t token);
 
+/* Test hook: flags bit 0 makes attention look every KV page up in the
+ * block table even where a request's pages are consecutive (where it
+ * otherwise computes the page from the first one).  Other bits:
+ * SPEC_E_INVAL. */
+int32_t spec_debug_flags(spec_ctx* ctx, int32_t flags);
+
 /* Fault injection for checking the token-forcing harness: adds `bias` to
  * the logit of `token` at every row whose position is >= after_position
  * (an analogue of the logit-bias fault of the besthub.dev article, "Phase 4:

@@ -83,10 +83,12 @@ def test_prefill_chunking_and_long_prompt():
 
 # ---------------------------------------------------------------- batched
 
-@pytest.mark.parametrize("planned", [False, True])
-def test_batched_requests(planned):
+@pytest.mark.parametrize("planned,table_only", [(False, False), (True, False),
+                                                (False, True)])
+def test_batched_requests(planned, table_only):
     """Several requests of different lengths in one fused verify per step,
-    each checked against its own oracle greedy run.  planned: each step's
+    each checked against its own oracle greedy run (table_only: with every
+    KV page looked up in the block table).  planned: each step's
     draft lengths come from the batch planner (lengths up to 2, 4 or 8 from
     the requests' acceptance so far, 16 draft nodes shared by 5 requests, so
     a request may offer none); the emitted tokens must not depend on it."""
@@ -98,6 +100,8 @@ def test_batched_requests(planned):
     lens_used = set()
     eng = engine_for(cfg, W, max_requests=8, max_ctx=512, max_nodes=K + 1,
                      max_rows=8 * (K + 1))
+    if table_only:  # every KV page through the block table
+        eng.debug_flags(1)
     orc = oracle_for(cfg, W)
     lens = [17, 40, 63, 100, 129]
     alphas = [0.4, 0.6, 0.7, 0.8, 0.9]

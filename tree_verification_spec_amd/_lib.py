@@ -31,7 +31,7 @@ EXPORTS = [
     "spec_force_root", "spec_set_fault", "spec_use_graphs", "spec_timing_enable",
     "spec_timing_read",
     "spec_destroy", "spec_last_error",
-    "spec_acceptance_update", "spec_plan_drafts", "spec_verify_lowp",
+    "spec_acceptance_update", "spec_plan_drafts", "spec_verify_lowp", "spec_debug_flags",
 ]
 
 
@@ -85,6 +85,7 @@ def lib():
         "spec_force_root": (c_int32, [c_void_p, c_int32, c_int32]),
         "spec_set_fault": (c_int32, [c_void_p, c_int32, c_float, c_int32]),
         "spec_use_graphs": (c_int32, [c_void_p, c_int32]),
+        "spec_debug_flags": (c_int32, [c_void_p, c_int32]),
         "spec_timing_enable": (c_int32, [c_void_p, c_int32]),
         "spec_timing_read": (c_int32, [c_void_p, P(c_double), P(c_int64)]),
         "spec_destroy": (None, [c_void_p]),
@@ -189,6 +190,10 @@ def spec_force_root(ctx, req, token):
 
 def spec_set_fault(ctx, token, bias, after_position):
     return _check(ctx, lib().spec_set_fault(ctx, token, bias, after_position))
+
+
+def spec_debug_flags(ctx, flags):
+    return _check(ctx, lib().spec_debug_flags(ctx, flags))
 
 
 def spec_use_graphs(ctx, enable):

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
         const int i = c / KCH_ROW, part = c % KCH_ROW;
         const int t = kbeg + i;
         if (t < kend) {
-          const int page = bt[t >> 4];
+          const int page = rm.page0 >= 0 ? rm.page0 + (t >> 4) : bt[t >> 4];
           kr[j] = *reinterpret_cast<const uint4*>(
               kc + (((size_t)page * a.nkv + kvh) * 16 + (t & 15)) * HD + part * EPC);
         }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
         const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
         const int t0 = kbeg + blk * 16 + part * EPC;
         if (t0 < kend) {
-          const int page = bt[t0 >> 4];
+          const int page = rm.page0 >= 0 ? rm.page0 + (t0 >> 4) : bt[t0 >> 4];
           vr[j] = *reinterpret_cast<const uint4*>(
               vc + (((size_t)page * a.nkv + kvh) * HD + dim) * 16 + (t0 & 15));
           T* ve = reinterpret_cast<T*>(&vr[j]);

@@ -26,7 +26,8 @@ struct ReqMeta {
   int32_t anc0;       // u64 offset of the request's ancestor masks
   int32_t anc_words;  // u64 words per row
   int32_t chain;      // rows form a chain (parent == node - 1)
-  int32_t pad;
+  int32_t page0;      // the request's pages are page0, page0 + 1, ... (its
+                      // block table needs no lookup), or -1
 };
 
 // Tiled weight layout: a matrix [N, K] is stored as 16 x 32 tiles, tile

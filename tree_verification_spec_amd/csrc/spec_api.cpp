@@ -25,6 +25,7 @@
 
 #include "../../include/spec.h"
 #include "kernels.h"
+#include "w12.h"
 
 namespace {
 
@@ -40,7 +41,6 @@ constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 constexpr bool kKmajorQkv = true;
 constexpr bool kKmajorOut = false;
 constexpr int kStagingBytes = 64 << 20;
-constexpr int kW12MaxExcHost = 7;  // exceptions one W12 tile holds (w12.h)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -49,6 +49,7 @@ struct Req {
   int n = 0;
   int root = 0;
   std::vector<int> pages;
+  int page0 = -1;  // pages[i] == page0 + i for all i, else -1
 };
 
 // One weight matrix [N, K] in the tiled layout (kernels.h), as bf16 / fp32
@@ -208,6 +209,7 @@ struct spec_ctx {
   std::string err;
   bool poisoned = false;
   int fault_tok = -1;
+  bool table_only = false;   // debug: always look pages up in the block table
   float fault_bias = 0.f;
   int fault_after = 0;
 
@@ -995,7 +997,7 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
       if (err)
         return fail(c, SPEC_E_UNSUPPORTED,
                     "tensor %d: a tile has more than %d weights outside the W12 exponent "
-                    "window; load these weights in native format", tensor_id, kW12MaxExcHost);
+                    "window; load these weights in native format", tensor_id, kW12MaxExc);
     }
   }
   HIP_TRY(hipStreamSynchronize(s));
@@ -1023,11 +1025,15 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
   rq.pages.assign(c->free_pages.end() - c->max_pages, c->free_pages.end());
   std::reverse(rq.pages.begin(), rq.pages.end());
   c->free_pages.resize(c->free_pages.size() - c->max_pages);
+  // pages return in reverse so the next request takes them ascending again
   auto undo = [&](int code) {
-    for (int p : rq.pages) c->free_pages.push_back(p);
+    for (auto it = rq.pages.rbegin(); it != rq.pages.rend(); ++it) c->free_pages.push_back(*it);
     rq.pages.clear();
     return code;
   };
+  rq.page0 = rq.pages[0];
+  for (int i = 1; i < c->max_pages; ++i)
+    if (rq.pages[i] != rq.pages[0] + i) rq.page0 = -1;
   for (int i = 0; i < c->max_pages; ++i) c->h_btab_row[i] = rq.pages[i];
   if (hipMemcpyAsync(c->d_btab + (size_t)req * c->max_pages, c->h_btab_row,
                      (size_t)c->max_pages * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess)
@@ -1059,7 +1065,7 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
       r.keys = done + C;
     }
     ReqMeta& m = h_reqs(c)[0];
-    m = ReqMeta{0, C, done, req, 0, 1, 1, 0};
+    m = ReqMeta{0, C, done, req, 0, 1, 1, c->table_only ? -1 : rq.page0};
     if (hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
                        c->stream) != hipSuccess) {
       c->poisoned = true;
@@ -1153,7 +1159,8 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
       a[i >> 6] |= 1ull << (i & 63);
     }
     if (!chain) any_tree = true;
-    rm[r] = ReqMeta{row, K + 1, rq.n, req[r], row * words, words, chain ? 1 : 0, 0};
+    rm[r] = ReqMeta{row, K + 1, rq.n, req[r], row * words, words, chain ? 1 : 0,
+                    c->table_only ? -1 : rq.page0};
     keys[r] = rq.n + K + 1;
     nrows[r] = K + 1;
     lv.req.push_back(req[r]);
@@ -1264,7 +1271,7 @@ extern "C" int32_t spec_release(spec_ctx* c, int32_t req) {
   if (req < 0 || req >= c->cfg.max_requests) return fail(c, SPEC_E_INVAL, "bad request id");
   Req& rq = c->reqs[req];
   if (!rq.active) return fail(c, SPEC_E_STATE, "request %d not active", req);
-  for (int p : rq.pages) c->free_pages.push_back(p);
+  for (auto it = rq.pages.rbegin(); it != rq.pages.rend(); ++it) c->free_pages.push_back(*it);
   rq = Req();
   c->last.valid = false;
   return SPEC_OK;
@@ -1287,6 +1294,14 @@ extern "C" int32_t spec_force_root(spec_ctx* c, int32_t req, int32_t token) {
   if (token < 0 || token >= c->V) return fail(c, SPEC_E_INVAL, "token out of range");
   c->reqs[req].root = token;
   c->last.valid = false;
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_debug_flags(spec_ctx* c, int32_t flags) {
+  int rc = check(c);
+  if (rc) return rc;
+  if (flags & ~1) return fail(c, SPEC_E_INVAL, "unknown debug flags %d", flags);
+  c->table_only = (flags & 1) != 0;
   return SPEC_OK;
 }
 

@@ -116,6 +116,9 @@ class Engine:
     def release(self, req):
         return L.spec_release(self.ctx, req)
 
+    def debug_flags(self, flags):
+        L.spec_debug_flags(self.ctx, flags)
+
     def state(self, req):
         return L.spec_request_state(self.ctx, req)
 

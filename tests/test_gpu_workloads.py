@@ -59,15 +59,23 @@ def _oracle_ref(orc, prompt, n, tag, chunk=512):
     return np.array(S, np.int32), np.array(L, np.float32), np.array(M, np.float32)
 
 
-def test_workload_dense8b_chain_full_size():
+_REF = {}
+
+
+@pytest.mark.parametrize("fmt", ["w12", "native"])
+def test_workload_dense8b_chain_full_size(fmt):
     """8B-shaped model, 2048-token prompt, chain K=16, alpha=0.7: the first
-    32 generated tokens and their logits against the oracle."""
+    32 generated tokens and their logits against the oracle, with the
+    weights stored as W12 (as the benchmark runs it) and as bf16."""
     w = synth.workload("dense8b_chain")
     cfg, W = _weights(w["model"])
-    eng = engine_for(cfg, W, max_ctx=w["prompt"] + 600, max_nodes=w["K"] + 1)
+    eng = engine_for(cfg, W, max_ctx=w["prompt"] + 600, max_nodes=w["K"] + 1,
+                     weight_format=fmt)
     prompt = synth.prompt_tokens(cfg["vocab"], w["prompt"], w["index"])
     orc = oracle_for(cfg, W, max_pos=4096)
-    ref = _oracle_ref(orc, prompt, 32, "8B chain")
+    if "dense8b_chain" not in _REF:
+        _REF["dense8b_chain"] = _oracle_ref(orc, prompt, 32, "8B chain")
+    ref = _REF["dense8b_chain"]
     rep = protocol_f(eng, cfg, orc, prompt, 32, w, "chain", cfg_index=w["index"],
                      oracle_ref=ref)
     _say(rep)

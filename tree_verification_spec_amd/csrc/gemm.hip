@@ -40,15 +40,24 @@ template <int MT> struct ChunkK {
   static constexpr int value = MT <= 1 ? 256 : MT <= 2 ? 256 : MT <= 3 ? 160
                              : MT <= 4 ? 256 : MT <= 5 ? 192 : 128;
 };
+// With stacked hi / lo rows (one staged plane) 256-wide chunks stay within
+// ~84 KB at every row-tile count used (up to 5).
+constexpr int kChunkStk = 256;
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D, int WF>
+// STK (bf16 activations, at most 40 rows a launch): the lo plane's rows are
+// stacked under the hi plane's (rows [0, mc) hi, [mc, 2 mc) lo) in one staged
+// plane, so each row tile is one MFMA per K-step instead of a hi and a lo
+// MFMA on half-empty tiles; the epilogue adds row m + mc to row m.
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D, int WF, bool STK>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr bool kBf = sizeof(T) == 2;
+  static_assert(!STK || kBf, "stacked rows need bf16 activation planes");
+  constexpr int NPL = (kBf && !STK) ? 2 : 1;  // staged planes
   constexpr int TROWS = MT * 16;
   constexpr int COLS = WAVES * NTW * 16;  // output columns of the workgroup
   constexpr int NTHR = WAVES * 64;
-  constexpr int KC = ChunkK<MT>::value;
+  constexpr int KC = STK ? kChunkStk : ChunkK<MT>::value;
   constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
   constexpr int QUADS = KC / 4;                      // float4 per staged row
   constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // float4 per thread
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // are unpredicated, each step's weight refill is pinned after its MFMAs,
   // and the W12 exception patch is one opaque block (its loop would
   // otherwise cost registers, and with them occupancy).
-  constexpr bool kOrdered = MT >= 3;
+  constexpr bool kOrdered = STK ? MT >= 4 : MT >= 3;
   const int lane = threadIdx.x & 63;
   // wave-uniform (kept in scalar registers, so weight addresses are a
   // scalar base plus a per-lane offset)
@@ -69,8 +78,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   const int kbeg = sk * a.KR;
   const int kend = min(a.K, kbeg + a.KR);
 
-  // two staging buffers; each holds a bf16 hi plane then a lo plane, or fp32
-  constexpr int BUF_ELEMS = TROWS * LDS_ROW * (kBf ? 2 : 1);
+  // two staging buffers; each holds a bf16 hi plane then a lo plane, one
+  // plane of stacked rows, or fp32
+  constexpr int BUF_ELEMS = TROWS * LDS_ROW * NPL;
+  // rows of this launch (stacked: the hi rows; their lo rows follow)
+  const int mc = min(a.M - a.row0, 128);
   T* xbuf = reinterpret_cast<T*>(smem);
 
   // weights: bf16 / fp32 tiles (a Frag per lane), or W12 tiles (12 bytes
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   using Unit = typename std::conditional<kBf, uint2, float4>::type;
   const T* Xh = reinterpret_cast<const T*>(a.X);
   const T* Xl = Xh + a.xlo;
-  Unit xr[XQ], xl[kBf ? XQ : 1];
+  Unit xr[XQ], xl[NPL == 2 ? XQ : 1];
   auto fetch = [&](int kc0, int kcl) {
     // columns kc0 .. kc0 + min(kcl, KC) of the real K range; the rest zero
     const int quads = kcl <= 0 ? 0 : (kcl >= KC ? QUADS : kcl >> 2);
@@ -120,32 +132,49 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     for (int q = 0; q < XQ; ++q) {
       const int e = threadIdx.x + q * NTHR;
       const int r = e / QUADS, c = (e % QUADS) * 4;
-      const int m = a.row0 + r;
-      const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
-      if constexpr (kOrdered) {
-        // every lane loads (from the plane's first element when out of
-        // range) and masks afterwards: no predicated loads, which the
-        // compiler would otherwise count conservatively across the loop
-        const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
-        const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
-        if constexpr (kBf) {
-          const uint2 h = *reinterpret_cast<const uint2*>(Xh + off);
-          const uint2 l = *reinterpret_cast<const uint2*>(Xl + off);
+      if constexpr (STK) {
+        // staged row r: hi row r, or lo row r - mc
+        const bool low = r >= mc;
+        const int m = a.row0 + (low ? r - mc : r);
+        const bool in = r < TROWS && r < 2 * mc && (c >> 2) < quads;
+        const T* src = low ? Xl : Xh;
+        if constexpr (kOrdered) {
+          const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
+          const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
+          const uint2 h = *reinterpret_cast<const uint2*>((in ? src : Xh) + off);
           xr[q] = make_uint2(h.x & mk, h.y & mk);
-          xl[q] = make_uint2(l.x & mk, l.y & mk);
         } else {
-          const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
-          xr[q] = make_float4(__uint_as_float(h.x & mk), __uint_as_float(h.y & mk),
-                              __uint_as_float(h.z & mk), __uint_as_float(h.w & mk));
+          const size_t off = (size_t)m * a.ldx + kc0 + c;
+          xr[q] = in ? *reinterpret_cast<const uint2*>(src + off) : make_uint2(0, 0);
         }
       } else {
-        const size_t off = (size_t)m * a.ldx + kc0 + c;
-        if constexpr (kBf) {
-          xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
-          xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+        const int m = a.row0 + r;
+        const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
+        if constexpr (kOrdered) {
+          // every lane loads (from the plane's first element when out of
+          // range) and masks afterwards: no predicated loads, which the
+          // compiler would otherwise count conservatively across the loop
+          const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
+          const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
+          if constexpr (NPL == 2) {
+            const uint2 h = *reinterpret_cast<const uint2*>(Xh + off);
+            const uint2 l = *reinterpret_cast<const uint2*>(Xl + off);
+            xr[q] = make_uint2(h.x & mk, h.y & mk);
+            xl[q] = make_uint2(l.x & mk, l.y & mk);
+          } else {
+            const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
+            xr[q] = make_float4(__uint_as_float(h.x & mk), __uint_as_float(h.y & mk),
+                                __uint_as_float(h.z & mk), __uint_as_float(h.w & mk));
+          }
         } else {
-          xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+          const size_t off = (size_t)m * a.ldx + kc0 + c;
+          if constexpr (NPL == 2) {
+            xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
+            xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+          } else {
+            xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
       }
     }
@@ -160,7 +189,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       const int r = e / QUADS, c = (e % QUADS) * 4;
       if (r >= TROWS) continue;
       *reinterpret_cast<Unit*>(&hi[r * LDS_ROW + c]) = xr[q];
-      if constexpr (kBf) *reinterpret_cast<Unit*>(&lo[r * LDS_ROW + c]) = xl[q];
+      if constexpr (NPL == 2) *reinterpret_cast<Unit*>(&lo[r * LDS_ROW + c]) = xl[q];
     }
   };
 
@@ -237,7 +266,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       buf ^= 1;
       // activation fragments of K-step j + 1 are read from LDS while the
       // MFMAs of step j run (software pipelining hides the LDS latency)
-      constexpr int XF = kBf ? 2 : 1;  // hi (+ lo) planes
+      constexpr int XF = NPL;  // hi (+ lo) planes
       Frag<T> xc[MT][XF], xn[MT][XF];
       auto load_x = [&](Frag<T> (&x)[MT][XF], int j) {
         const int kk = j * 32 + g * 8;
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
         for (int mt = 0; mt < MT; ++mt) {
           const int r = mt * 16 + r16;
           x[mt][0].load(&hi[r * LDS_ROW + kk]);
-          if constexpr (kBf) x[mt][1].load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
+          if constexpr (NPL == 2) x[mt][1].load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
         }
       };
       load_x(xc, 0);
@@ -280,7 +309,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // ---- results
   const int col0 = nb * COLS;
   const int N = a.ntiles * 16;
-  if (EPI == EPI_PART) {
+  if (EPI == EPI_PART && !STK) {
     float* P = a.P + (size_t)sk * a.P_ld * N;
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
@@ -295,7 +324,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       }
     return;
   }
-  // S == 1: tile [TROWS][COLS] in LDS (reusing the staging area)
+  // S == 1 (or stacked rows): tile [TROWS][COLS] in LDS (reusing the
+  // staging area)
   constexpr int LDT = COLS + 1;
   float* tile = reinterpret_cast<float*>(smem);
   __syncthreads();
@@ -307,17 +337,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 4; ++r)
         tile[(mt * 16 + r16) * LDT + (wave * NTW + t) * 16 + 4 * g + r] = acc[t][mt][r];
   __syncthreads();
+  // output rows of the tile, and an output value (stacked: hi row + lo row)
+  const int orows = STK ? mc : TROWS;
+  auto val = [&](int row, int col) -> float {
+    float v = tile[row * LDT + col];
+    if constexpr (STK) v += tile[(row + mc) * LDT + col];
+    return v;
+  };
+
+  if (EPI == EPI_PART) {  // stacked rows only
+    float* P = a.P + (size_t)sk * a.P_ld * N;
+    for (int e = threadIdx.x; e < orows * COLS; e += NTHR) {
+      const int row = e / COLS, col = e % COLS;
+      P[(size_t)(a.row0 + row) * N + col0 + col] = val(row, col);
+    }
+    return;
+  }
 
   if (EPI == EPI_SWIGLU) {
     // tile pair p: columns [p*32, p*32+16) gate, [p*32+16, p*32+32) up
     constexpr int OUTS = COLS / 2;
-    for (int e = threadIdx.x; e < TROWS * OUTS; e += NTHR) {
+    for (int e = threadIdx.x; e < orows * OUTS; e += NTHR) {
       const int row = e / OUTS, j = e % OUTS;
       const int m = a.row0 + row;
       if (m >= a.M) continue;
       const int p = j >> 4, c = j & 15;
-      const float gv = tile[row * LDT + p * 32 + c];
-      const float uv = tile[row * LDT + p * 32 + 16 + c];
+      const float gv = val(row, p * 32 + c);
+      const float uv = val(row, p * 32 + 16 + c);
       T* Yh = reinterpret_cast<T*>(a.Y);
       store_act(Yh, Yh + a.ylo, (size_t)m * a.ldy + nb * OUTS + j,
                 gv / (1.0f + expf(-gv)) * uv);
@@ -325,19 +371,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     return;
   }
   // EPI_ARGMAX
-  for (int e = threadIdx.x; e < TROWS * COLS; e += NTHR) {
+  for (int e = threadIdx.x; e < orows * COLS; e += NTHR) {
     const int row = e / COLS, col = e % COLS;
     const int m = a.row0 + row;
     if (m >= a.M) continue;
     const int n = col0 + col;
-    float v = tile[row * LDT + col];
+    float v = val(row, col);
     if (n >= a.ncols) v = -INFINITY;
     if (n == a.bias_tok && a.rows[m].pos >= a.bias_after) v += a.bias;
     if (a.logits && n < a.ncols) a.logits[(size_t)m * a.ldlog + n] = v;
     tile[row * LDT + col] = v;
   }
   __syncthreads();
-  for (int row = threadIdx.x; row < TROWS; row += NTHR) {
+  for (int row = threadIdx.x; row < orows; row += NTHR) {
     const int m = a.row0 + row;
     if (m >= a.M) continue;
     float best = -INFINITY;
@@ -350,11 +396,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, int WF = 0>
+template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, int WF = 0,
+          bool STK = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, WF>;
-  constexpr int KC = ChunkK<MT>::value;
-  const size_t stage_b = 2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * 4;
+  auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, WF, STK>;
+  constexpr int KC = STK ? kChunkStk : ChunkK<MT>::value;
+  // two buffers of MT*16 rows x (KC + pad) of 4 bytes (bf16 hi + lo, or fp32)
+  // or 2 bytes (one plane of stacked bf16 rows)
+  const size_t stage_b =
+      2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * (STK ? 2 : 4);
   const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
   const size_t lds = stage_b > tile_b ? stage_b : tile_b;
   if (lds > 64 * 1024) {
@@ -396,8 +446,26 @@ hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// stacked hi / lo rows (bf16, one tile per wave, 8 waves): mt = row tiles of
+// the 2 * rows stacked rows (1..5)
 template <typename T, int EPI, int WF>
-hipError_t launch_var(Variant v, int mt, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_stk(int mt, const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    switch (mt) {
+      case 1: return launch_one<T, 1, 1, 8, EPI, kD, WF, true>(a, s);
+      case 2: return launch_one<T, 2, 1, 8, EPI, kD, WF, true>(a, s);
+      case 3: return launch_one<T, 3, 1, 8, EPI, kD, WF, true>(a, s);
+      case 4: return launch_one<T, 4, 1, 8, EPI, kD, WF, true>(a, s);
+      case 5: return launch_one<T, 5, 1, 8, EPI, kD, WF, true>(a, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int EPI, int WF>
+hipError_t launch_var(Variant v, int mt, bool stk, const GemmArgs& a, hipStream_t s) {
+  if (stk) return launch_stk<T, EPI, WF>(mt, a, s);
   if constexpr (sizeof(T) == 2) {
     if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, WF>(mt, a, s);
     if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD, WF>(mt, a, s);
@@ -407,21 +475,23 @@ hipError_t launch_var(Variant v, int mt, const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename T, int WF>
-hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
-  if (epi == EPI_PART) return launch_var<T, EPI_PART, WF>(v, mt, a, s);
-  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, WF>(v, mt, a, s);
-  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, WF>(v, mt, a, s);
+hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
+                      hipStream_t s) {
+  if (epi == EPI_PART) return launch_var<T, EPI_PART, WF>(v, mt, stk, a, s);
+  if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, WF>(v, mt, stk, a, s);
+  if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, WF>(v, mt, stk, a, s);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, hipStream_t s) {
+hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
+                        hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (a.w12 == 1) return launch_fmt<T, 1>(epi, v, a, mt, s);
-    if (a.w12 == 2) return launch_fmt<T, 2>(epi, v, a, mt, s);
+    if (a.w12 == 1) return launch_fmt<T, 1>(epi, v, a, mt, stk, s);
+    if (a.w12 == 2) return launch_fmt<T, 2>(epi, v, a, mt, stk, s);
   }
   if (a.w12) return hipErrorInvalidValue;
-  return launch_fmt<T, 0>(epi, v, a, mt, s);
+  return launch_fmt<T, 0>(epi, v, a, mt, stk, s);
 }
 
 }  // namespace
@@ -463,11 +533,14 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
   if (epi == EPI_ARGMAX) a.nblocks = a.ntiles / (v.ntw * v.waves);
   for (int r0 = 0; r0 < a.M; r0 += 128) {
     const int rows = (a.M - r0 < 128) ? a.M - r0 : 128;
-    const int need = (rows + 15) / 16;
-    const int mt = need <= 5 ? need : 8;
+    // up to 40 rows (bf16, one tile per wave) the lo rows are stacked under
+    // the hi rows
+    const bool stk = bf16 && v.ntw == 1 && v.waves == 8 && 2 * rows <= 80;
+    const int need = ((stk ? 2 * rows : rows) + 15) / 16;
+    const int mt = stk ? need : (need <= 5 ? need : 8);
     a.row0 = r0;
-    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, v, a, mt, s)
-                        : launch_typed<float>(epi, v, a, mt, s);
+    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, v, a, mt, stk, s)
+                        : launch_typed<float>(epi, v, a, mt, false, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -51,8 +51,10 @@ def test_factor_identity():
 
 
 def test_row_tiles():
-    assert costmodel.row_tiles(1) == [1]
-    assert costmodel.row_tiles(17) == [2]
+    assert costmodel.row_tiles(1) == [1]          # stacked: 2 rows
+    assert costmodel.row_tiles(17) == [3]         # stacked: 34 rows
+    assert costmodel.row_tiles(32) == [4]
+    assert costmodel.row_tiles(17, bf16=False) == [2]
     assert costmodel.row_tiles(33) == [3]
     assert costmodel.row_tiles(65) == [5]
     assert costmodel.row_tiles(96) == [8]
@@ -91,8 +93,8 @@ def _row(name, t0, dt):
 
 
 def test_steps_from_trace_splits_and_filters():
-    g2 = "void (anonymous namespace)::gemm_kernel<unsigned short, 2, 1, 8, 2, 8, true>(GemmArgs)"
-    g1 = "void (anonymous namespace)::gemm_kernel<unsigned short, 1, 1, 8, 2, 8, true>(GemmArgs)"
+    g2 = "void (anonymous namespace)::gemm_kernel<unsigned short, 2, 1, 8, 2, 8, 1, true>(GemmArgs)"
+    g1 = "void (anonymous namespace)::gemm_kernel<unsigned short, 1, 1, 8, 2, 8, 1, true>(GemmArgs)"
     rows, t = [], 0
 
     def add(name, dt):

@@ -100,9 +100,13 @@ def type_bounds(specs, cfg, req_rows, req_ctx, fmt):
     }
 
 
-def row_tiles(total_rows):
-    """Row-tile counts of the GEMM launches of a pass of `total_rows` rows
-    (launches of at most 128 rows; 1..5 tiles, else 8)."""
+def row_tiles(total_rows, bf16=True):
+    """Row-tile counts of the GEMM launches of a pass of `total_rows` rows:
+    up to 32 rows of a bf16 model the hi and lo activation rows are stacked
+    (2 x rows); otherwise launches of at most 128 rows take 1..5 tiles, else
+    8."""
+    if bf16 and total_rows <= 32:
+        return [(2 * total_rows + 15) // 16]
     out = set()
     for r0 in range(0, total_rows, 128):
         need = (min(128, total_rows - r0) + 15) // 16

@@ -84,8 +84,8 @@ def main():
                          "bytes (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU; --gpus N with N > 1 is "
-              "not supported", file=sys.stderr)
+        print("bench.py: the verification path runs on one GPU; --gpus N with "
+              "N > 1 is not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -47,7 +47,7 @@ enum {
   SPEC_E_STATE = -2,       /* call-order violation or non-root path         */
   SPEC_E_CAPACITY = -3,    /* KV pages or max_ctx exhausted                 */
   SPEC_E_HIP = -4,         /* a HIP runtime error; the context is poisoned  */
-  SPEC_E_UNSUPPORTED = -5  /* shape or option this build does not handle    */
+  SPEC_E_UNSUPPORTED = -5  /* shape or option the library does not handle  */
 };
 
 enum { SPEC_DTYPE_FP32 = 0, SPEC_DTYPE_BF16 = 1 };

@@ -8,6 +8,8 @@
 * the lossless invariant: tree verification accepts exactly the AR prefix.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -235,6 +237,57 @@ def test_accept_path_hand_cases():
     A = [4, 6, 7, 1, 8, 3]            # nothing matches the root's choice
     path, bonus = accept_path(toks, par, A)
     assert path == [] and bonus == 4
+
+
+def _golden_accept_cases():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "accept_path_cases.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"name": vals[0]}
+            cases.append(cur)
+        elif key in ("path",):
+            cur[key] = [] if vals == ["-"] else [int(v) for v in vals]
+        elif key == "bonus":
+            cur[key] = int(vals[0])
+        else:
+            cur[key] = [int(v) for v in vals]
+    return cases
+
+
+def _accept_by_enumeration(toks, par, A):
+    """Every root-to-node path, kept when each node's token equals its
+    parent's argmax; the longest wins, then the one ending at the lowest
+    node index."""
+    best = (0, 0)
+    for end in range(len(toks)):
+        chain, v = [], end
+        while v != 0:
+            chain.append(v)
+            v = par[v]
+        if all(toks[c] == A[par[c]] for c in chain) and \
+                (len(chain), -end) > (best[0], -best[1]):
+            best = (len(chain), end)
+    chain, v = [], best[1]
+    while v != 0:
+        chain.append(v)
+        v = par[v]
+    return chain[::-1], A[best[1]]
+
+
+def test_accept_path_golden_cases():
+    cases = _golden_accept_cases()
+    assert len(cases) >= 10
+    for c in cases:
+        got = accept_path(c["tokens"], c["parents"], c["argmax"])
+        assert got == (c["path"], c["bonus"]), c["name"]
+        assert _accept_by_enumeration(c["tokens"], c["parents"], c["argmax"]) == \
+            (c["path"], c["bonus"]), c["name"]
 
 
 def test_top2_margin():

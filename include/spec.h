@@ -75,6 +75,8 @@ enum { SPEC_LAYER_ATTN = 0, SPEC_LAYER_LR = 1 };
  * h += (y_t * silu(z_t)) W_out^T.
  */
 typedef struct spec_config {
+  /* d_model: a multiple of 32, at most 16384; head_dim: 64 or 128;
+     ffn_dim: a multiple of 64; vocab: a multiple of 16 */
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t dtype;                       /* SPEC_DTYPE_*: weights and KV cache  */
   int32_t lr_state;                    /* recurrent state width (0: none)     */

@@ -46,6 +46,10 @@ def test_workspace_bytes_and_config_validation():
     assert L.spec_workspace_bytes(bad) == 0
     odd = dict(tiny, head_dim=96)
     assert L.spec_workspace_bytes(make_config(odd)) == 0
+    # model width: a multiple of 32 up to 16384 (the row kernels' register tiles)
+    assert L.spec_workspace_bytes(make_config(dict(tiny, d_model=48))) == 0
+    wide = dict(tiny, d_model=16384 + 32)
+    assert L.spec_workspace_bytes(make_config(wide)) == 0
     # W12 weight storage: bf16 models only
     assert L.spec_workspace_bytes(make_config(tiny, weight_format="w12")) == 0
     b16 = synth.model_config("tiny_gqa_bf16")

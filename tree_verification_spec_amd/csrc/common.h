@@ -102,6 +102,32 @@ __device__ __forceinline__ void store_act(float* hi, float* /*lo*/, size_t i,
                                           float v) {
   hi[i] = v;
 }
+// Four consecutive activations (i a multiple of 4; each plane 8-byte
+// aligned for bf16, 16-byte for fp32): one vector store per plane.
+__device__ __forceinline__ void store_act4(uint16_t* hi, uint16_t* lo, size_t i,
+                                           float4 v) {
+  const uint16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+  const uint16_t l0 = f2bf(v.x - bf2f(h0)), l1 = f2bf(v.y - bf2f(h1));
+  const uint16_t l2 = f2bf(v.z - bf2f(h2)), l3 = f2bf(v.w - bf2f(h3));
+  *reinterpret_cast<uint2*>(hi + i) =
+      make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16));
+  *reinterpret_cast<uint2*>(lo + i) =
+      make_uint2((uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16));
+}
+__device__ __forceinline__ void store_act4(float* hi, float* /*lo*/, size_t i, float4 v) {
+  *reinterpret_cast<float4*>(hi + i) = v;
+}
+
+// Four consecutive elements as fp32 (p 8-byte aligned for bf16, 16-byte
+// for fp32).
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float4 load4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} (one MFMA output
 // column's four row groups) with the gfx950 row-swap instructions: after a

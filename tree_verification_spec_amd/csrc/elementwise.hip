@@ -24,24 +24,46 @@ __device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
 
 // ---------------------------------------------------------------- embedding
 // One workgroup per row: h = float(E[token]), then u = RMSNorm(h) * nw as
-// activation planes for the first layer's input GEMM.
+// activation planes for the first layer's input GEMM.  A thread owns four
+// consecutive columns in every 1024 and issues all of its embedding loads
+// before its first store (d <= 1024 * kEmbQ).
+constexpr int kEmbQ = 16;
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* emb, const RowMeta* rows,
-                                                    int d, float* h, const float* nw,
-                                                    float eps, T* u, size_t ulo) {
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb,
+                                                    const RowMeta* __restrict__ rows, int d,
+                                                    float* __restrict__ h,
+                                                    const float* __restrict__ nw, float eps,
+                                                    T* __restrict__ u, size_t ulo) {
   __shared__ float part[4];
   const int row = blockIdx.x;
   const T* e = emb + (size_t)rows[row].token * d;
   float* hr = h + (size_t)row * d;
+  float4 v[kEmbQ];
+#pragma unroll
+  for (int j = 0; j < kEmbQ; ++j) {
+    const int c = (threadIdx.x + j * 256) * 4;
+    v[j] = c < d ? load4(e + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float acc = 0.f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float v = to_f<T>(e[c]);
-    hr[c] = v;
-    acc += v * v;
+#pragma unroll
+  for (int j = 0; j < kEmbQ; ++j) {
+    const int c = (threadIdx.x + j * 256) * 4;
+    if (c < d) {
+      *reinterpret_cast<float4*>(hr + c) = v[j];
+      acc += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
   }
   const float sc = rms_scale(block_sum(acc, part), d, eps);
-  for (int c = threadIdx.x; c < d; c += 256)  // this thread's own writes
-    store_act(u, u + ulo, (size_t)row * d + c, (hr[c] * sc) * nw[c]);
+#pragma unroll
+  for (int j = 0; j < kEmbQ; ++j) {
+    const int c = (threadIdx.x + j * 256) * 4;
+    if (c < d) {
+      const float4 w = *reinterpret_cast<const float4*>(nw + c);
+      store_act4(u, u + ulo, (size_t)row * d + c,
+                 make_float4((v[j].x * sc) * w.x, (v[j].y * sc) * w.y, (v[j].z * sc) * w.z,
+                             (v[j].w * sc) * w.w));
+    }
+  }
 }
 
 // ------------------------------------------------------------ RoPE + KV store
@@ -138,10 +160,9 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
     if (c >= d) break;
     const float4 w = wn[j];
     const size_t i = (size_t)row * d + c;
-    store_act(u, u + ulo, i + 0, (keep[j].x * sc) * w.x);
-    store_act(u, u + ulo, i + 1, (keep[j].y * sc) * w.y);
-    store_act(u, u + ulo, i + 2, (keep[j].z * sc) * w.z);
-    store_act(u, u + ulo, i + 3, (keep[j].w * sc) * w.w);
+    store_act4(u, u + ulo, i,
+               make_float4((keep[j].x * sc) * w.x, (keep[j].y * sc) * w.y,
+                           (keep[j].z * sc) * w.z, (keep[j].w * sc) * w.w));
   }
 }
 
@@ -183,35 +204,43 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* part,
 // ------------------------------------------------------------- path walk
 // ok(0) = 1; ok(i) = ok(parent) && token(i) == A(parent); best = deepest ok
 // node (lowest index among equals); path = root..best; bonus = A(best).
-__global__ void path_walk_kernel(const RowMeta* rows, const ReqMeta* reqs,
-                                 const int32_t* amax, int max_path,
-                                 int32_t* res) {
+// The request's parents, tokens and argmaxes are first loaded into LDS by
+// all lanes together; one lane then walks the nodes in index order.
+__global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
+                                                       const ReqMeta* reqs,
+                                                       const int32_t* amax, int max_path,
+                                                       int32_t* res) {
   const int r = blockIdx.x;
-  if (threadIdx.x != 0) return;
   const ReqMeta rm = reqs[r];
-  int32_t* out = res + (size_t)r * (2 + max_path);
-  // depth and ok of each node, kept in the result slots temporarily is not
-  // possible (sizes differ), so walk with small local arrays
   constexpr int MAXN = 512;
+  __shared__ int16_t par[MAXN], dep[MAXN];
+  __shared__ int32_t tok[MAXN], am[MAXN];
   __shared__ int8_t ok[MAXN];
-  __shared__ int16_t dep[MAXN];
+  const int n = min(rm.nrows, MAXN);
+  for (int i = threadIdx.x; i < n; i += 64) {
+    par[i] = (int16_t)rows[rm.row0 + i].parent;
+    tok[i] = rows[rm.row0 + i].token;
+    am[i] = amax[rm.row0 + i];
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int32_t* out = res + (size_t)r * (2 + max_path);
   int best = 0;
   ok[0] = 1;
   dep[0] = 0;
-  for (int i = 1; i < rm.nrows && i < MAXN; ++i) {
-    const RowMeta n = rows[rm.row0 + i];
-    const int p = n.parent;
-    ok[i] = ok[p] && n.token == amax[rm.row0 + p];
+  for (int i = 1; i < n; ++i) {
+    const int p = par[i];
+    ok[i] = ok[p] && tok[i] == am[p];
     dep[i] = dep[p] + 1;
     if (ok[i] && dep[i] > dep[best]) best = i;
   }
   const int plen = dep[best];
   out[0] = plen;
-  out[1] = amax[rm.row0 + best];
+  out[1] = am[best];
   int v = best;
   for (int k = plen - 1; k >= 0; --k) {
     out[2 + k] = v;
-    v = rows[rm.row0 + v].parent;
+    v = par[v];
   }
 }
 
@@ -373,6 +402,7 @@ __global__ void to_f32_kernel(const T* src, int n, float* dst) {
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
                         int d, float* h, const float* nw, float eps, void* u, size_t u_lo,
                         hipStream_t s) {
+  if (d % 4 || d > 1024 * kEmbQ) return hipErrorInvalidValue;
   if (bf16)
     embed_kernel<uint16_t><<<R, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, nw, eps,
                                              (uint16_t*)u, u_lo);

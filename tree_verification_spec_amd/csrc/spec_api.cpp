@@ -248,7 +248,8 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->dtype != SPEC_DTYPE_FP32 && cfg->dtype != SPEC_DTYPE_BF16) return bad("dtype");
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (cfg->n_kv_heads <= 0 || cfg->n_heads % cfg->n_kv_heads) return bad("heads");
-  if (cfg->d_model % 32) return bad("d_model must be a multiple of 32");
+  if (cfg->d_model % 32 || cfg->d_model <= 0 || cfg->d_model > 16384)
+    return bad("d_model must be a multiple of 32 in [32, 16384]");
   if (cfg->ffn_dim % 64) return bad("ffn_dim must be a multiple of 64");
   if (cfg->vocab % 16 || cfg->vocab <= 0) return bad("vocab must be a multiple of 16");
   if ((cfg->n_heads * cfg->head_dim) % 32) return bad("n_heads*head_dim");

@@ -292,8 +292,9 @@ def main():
 
     res = run(alpha_main, args.steps, args.warmup)
     log(f"{args.workload} alpha={alpha_main}: {res}")
-    # the dominant kernel's launch times, from HIP events the library records
-    # around each gate/up launch (kernels launched one by one for this run)
+    # the dominant kernel's launch times: each gate/up launch records its own
+    # start and end in a HIP event pair (extended launch; passes of this run
+    # are launched kernel by kernel, without graph replay)
     rl = run(alpha_main, max(10, args.steps // 3), 2, timing_cls=1)
     log(f"timed launches: {rl}")
     sweep = {}

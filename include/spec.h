@@ -213,11 +213,13 @@ int32_t spec_set_fault(spec_ctx* ctx, int32_t token, float bias,
 int32_t spec_use_graphs(spec_ctx* ctx, int32_t enable);
 
 /* Per-launch timing of one kernel class, for roofline measurement: while
- * enabled, the library brackets every launch of that class with HIP events
- * on its stream.  cls: 0 = off, 1 = FFN gate/up GEMM, 2 = FFN down GEMM,
- * 3 = LM head GEMM, 4 = attention.  spec_timing_read synchronizes the
- * stream, returns the summed milliseconds and launch count since the last
- * read, and resets them. */
+ * enabled, every launch of that class records the kernel's own start and
+ * end in a pair of HIP events on the library's stream (HIP's extended
+ * launch, which timestamps the dispatch as a kernel trace does; passes then
+ * run without graph replay).  cls: 0 = off, 1 = FFN gate/up GEMM, 2 = FFN
+ * down GEMM, 3 = LM head GEMM, 4 = attention.  spec_timing_read
+ * synchronizes the stream, returns the summed milliseconds and launch
+ * count since the last read, and resets them. */
 int32_t spec_timing_enable(spec_ctx* ctx, int32_t cls);
 int32_t spec_timing_read(spec_ctx* ctx, double* total_ms, int64_t* launches);
 

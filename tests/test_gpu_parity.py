@@ -343,6 +343,35 @@ def test_graph_replay_equals_individual_launches():
             assert np.array_equal(la, lb)
 
 
+def test_kernel_timing_counts_launches_and_leaves_results_unchanged():
+    """Timed passes (each launch of one kernel class records its own start
+    and end in a HIP event pair) give the same paths, bonus tokens and
+    logits as untimed ones, one timed launch per layer (per pass for the LM
+    head), and positive durations."""
+    cfg, W = _setup("tiny_gqa_bf16")
+    V = cfg["vocab"]
+    prompt = synth.prompt_tokens(V, 40, 56)
+    toks = np.arange(16) * 5 % V
+    par = np.arange(-1, 15)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=17)
+    eng.prefill(0, prompt)
+    ref = eng.verify([0], [toks], [par], logits=True)
+    ref_lg = ref[2].cpu().numpy().copy()
+    n_layers = cfg["n_layers"]
+    for cls, per_pass in ((1, n_layers), (2, n_layers), (3, 1), (4, n_layers)):
+        eng.timing(cls)
+        eng.timing_read()
+        for _ in range(2):
+            r = eng.verify([0], [toks], [par], logits=True)
+            assert r[0] == ref[0] and r[1] == ref[1]
+            assert np.array_equal(r[2].cpu().numpy(), ref_lg)
+        ms, n = eng.timing_read()
+        eng.timing(0)
+        _say(f"timing class {cls}: {n} launches, {ms:.4f} ms")
+        assert n == 2 * per_pass and 0.0 < ms < 1e3
+    eng.close()
+
+
 # ------------------------------------------------ full-width model variants
 
 @pytest.mark.parametrize("name,budget", [("dense8b_l2", 64), ("hybrid27b_l4", 32)])

@@ -19,6 +19,8 @@
 // the cache so that the V^T operand is read directly.  Each split writes
 // un-normalised partials (O, running max of the scores scaled by log2 e,
 // running sum), merged in split order by attn_combine.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
 }
 
 template <typename T, int HD>
-hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
+hipError_t attn_launch(const AttnArgs& a, const LaunchCtx& s) {
   auto k = attn_kernel<T, HD>;
   const size_t lds = SplitLds<T, HD>::bytes(a.split);
   if (lds > 64 * 1024) {
@@ -409,12 +411,18 @@ hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
-  k<<<grid, kAttnThreads, lds, s>>>(a);
+  if (s.t0 || s.t1) {
+    AttnArgs arg = a;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel((const void*)k, grid, dim3(kAttnThreads), args, lds, s.s, s.t0,
+                              s.t1, 0);
+  }
+  k<<<grid, kAttnThreads, lds, s.s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t attn_typed(const AttnArgs& a, hipStream_t s) {
+hipError_t attn_typed(const AttnArgs& a, const LaunchCtx& s) {
   if (a.split > kMaxSplitKeys || a.split < 32 || a.split % 32 || a.qtiles_per_wg < 1)
     return hipErrorInvalidValue;
   if (a.hd == 128) return attn_launch<T, 128>(a, s);
@@ -434,8 +442,10 @@ hipError_t combine_t(const AttnArgs& a, T* o, size_t olo, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s) {
-  return bf16 ? attn_typed<uint16_t>(a, s) : attn_typed<float>(a, s);
+hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s, hipEvent_t t0,
+                            hipEvent_t t1) {
+  const LaunchCtx lc{s, t0, t1};
+  return bf16 ? attn_typed<uint16_t>(a, lc) : attn_typed<float>(a, lc);
 }
 
 hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o, size_t o_lo,

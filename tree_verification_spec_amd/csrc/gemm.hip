@@ -22,6 +22,8 @@
 //    wave owns both halves of 16 outputs; S = 1), and the LM-head argmax
 //    partial (per-row max over the workgroup's columns, lowest index on ties;
 //    S = 1).
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 
 template <typename T, int MT, int NTW, int WAVES, int EPI, int D = kD, int WF = 0,
           bool STK = false>
-hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
   auto k = gemm_kernel<T, MT, NTW, WAVES, EPI, D, WF, STK>;
   constexpr int KC = STK ? kChunkStk : ChunkK<MT>::value;
   // two buffers of MT*16 rows x (KC + pad) of 4 bytes (bf16 hi + lo, or fp32)
@@ -414,7 +416,13 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int nblk = a.ntiles / (WAVES * NTW);
-  k<<<nblk * a.S, WAVES * 64, lds, s>>>(a);
+  if (s.t0 || s.t1) {
+    GemmArgs arg = a;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel((const void*)k, dim3(nblk * a.S), dim3(WAVES * 64), args, lds,
+                              s.s, s.t0, s.t1, 0);
+  }
+  k<<<nblk * a.S, WAVES * 64, lds, s.s>>>(a);
   return hipGetLastError();
 }
 
@@ -435,7 +443,7 @@ Variant gemm_variant(bool bf16, int N, int M) {
 }
 
 template <typename T, int EPI, int NTW, int WAVES, int D, int WF>
-hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_mt(int mt, const GemmArgs& a, const LaunchCtx& s) {
   switch (mt) {
     case 1: return launch_one<T, 1, NTW, WAVES, EPI, D, WF>(a, s);
     case 2: return launch_one<T, 2, NTW, WAVES, EPI, D, WF>(a, s);
@@ -449,7 +457,7 @@ hipError_t launch_mt(int mt, const GemmArgs& a, hipStream_t s) {
 // stacked hi / lo rows (bf16, one tile per wave, 8 waves): mt = row tiles of
 // the 2 * rows stacked rows (1..5)
 template <typename T, int EPI, int WF>
-hipError_t launch_stk(int mt, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_stk(int mt, const GemmArgs& a, const LaunchCtx& s) {
   if constexpr (sizeof(T) == 2) {
     switch (mt) {
       case 1: return launch_one<T, 1, 1, 8, EPI, kD, WF, true>(a, s);
@@ -464,7 +472,8 @@ hipError_t launch_stk(int mt, const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename T, int EPI, int WF>
-hipError_t launch_var(Variant v, int mt, bool stk, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_var(Variant v, int mt, bool stk, const GemmArgs& a,
+                      const LaunchCtx& s) {
   if (stk) return launch_stk<T, EPI, WF>(mt, a, s);
   if constexpr (sizeof(T) == 2) {
     if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, WF>(mt, a, s);
@@ -476,7 +485,7 @@ hipError_t launch_var(Variant v, int mt, bool stk, const GemmArgs& a, hipStream_
 
 template <typename T, int WF>
 hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
-                      hipStream_t s) {
+                      const LaunchCtx& s) {
   if (epi == EPI_PART) return launch_var<T, EPI_PART, WF>(v, mt, stk, a, s);
   if (epi == EPI_SWIGLU) return launch_var<T, EPI_SWIGLU, WF>(v, mt, stk, a, s);
   if (epi == EPI_ARGMAX) return launch_var<T, EPI_ARGMAX, WF>(v, mt, stk, a, s);
@@ -485,7 +494,7 @@ hipError_t launch_fmt(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
 
 template <typename T>
 hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
-                        hipStream_t s) {
+                        const LaunchCtx& s) {
   if constexpr (sizeof(T) == 2) {
     if (a.w12 == 1) return launch_fmt<T, 1>(epi, v, a, mt, stk, s);
     if (a.w12 == 2) return launch_fmt<T, 2>(epi, v, a, mt, stk, s);
@@ -513,7 +522,8 @@ int gemm_splits(bool bf16, int K, int N, int M) {
   return S;
 }
 
-hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
+hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s,
+                       hipEvent_t t0, hipEvent_t t1) {
   if (a0.M <= 0) return hipSuccess;
   GemmArgs a = a0;
   if (a.S < 1 || (epi != EPI_PART && a.S != 1) || a.K % a.S || (a.K / a.S) % 32)
@@ -539,8 +549,10 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s) {
     const int need = ((stk ? 2 * rows : rows) + 15) / 16;
     const int mt = stk ? need : (need <= 5 ? need : 8);
     a.row0 = r0;
-    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, v, a, mt, stk, s)
-                        : launch_typed<float>(epi, v, a, mt, false, s);
+    // timing: the first chunk's start and the last chunk's end
+    const LaunchCtx lc{s, r0 == 0 ? t0 : nullptr, r0 + 128 >= a.M ? t1 : nullptr};
+    hipError_t e = bf16 ? launch_typed<uint16_t>(epi, v, a, mt, stk, lc)
+                        : launch_typed<float>(epi, v, a, mt, false, lc);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

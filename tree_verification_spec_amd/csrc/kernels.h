@@ -82,9 +82,20 @@ int gemm_pad_cols();
 int gemm_splits(bool bf16, int K, int N, int M);
 int gemm_argmax_blocks(bool bf16, int N, int M);
 
+// A launch's stream and optional timing events: with t0 / t1 set, the
+// first kernel of the call records its start in t0 and the last kernel its
+// end in t1 (HIP's extended launch timestamps the dispatch itself, as a
+// kernel trace does, so event setup and dispatch latency are left out).
+struct LaunchCtx {
+  hipStream_t s;
+  hipEvent_t t0, t1;
+};
+
 // Launch the skinny GEMM for rows [0, M): picks the workgroup shape and the
-// row-tile count, and splits rows into chunks of 128.
-hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, hipStream_t s);
+// row-tile count, and splits rows into chunks of 128.  t0 / t1: optional
+// timing events (LaunchCtx).
+hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a, hipStream_t s,
+                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 struct AttnArgs {
   const void* q;            // [rows, nq, hd] (bf16 bits or fp32), after RoPE
@@ -106,7 +117,8 @@ struct AttnArgs {
   float scale;
 };
 
-hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s,
+                            hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Merge the per-split partials into the attention output, written as
 // activation planes o[rows, nq*hd] (lo plane at o + o_lo elements).

@@ -539,21 +539,25 @@ bool all_loaded(const spec_ctx* c) {
   return true;
 }
 
-// timing brackets
-void time_begin(spec_ctx* c, int cls) {
-  if (c->timing_cls != cls) return;
+// Timing: the event pair for one launch of kernel class cls (both null when
+// that class is not being timed).  The launch records the kernel's own start
+// and end in them.
+struct TimePair {
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+};
+TimePair time_pair(spec_ctx* c, int cls) {
+  if (c->timing_cls != cls) return {};
   if (c->events_used == c->events.size()) {
     hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+    if (hipEventCreate(&a) != hipSuccess) return {};
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return {};
+    }
     c->events.push_back({a, b});
   }
-  (void)hipEventRecord(c->events[c->events_used].first, c->stream);
-}
-
-void time_end(spec_ctx* c, int cls) {
-  if (c->timing_cls != cls || c->events_used >= c->events.size()) return;
-  (void)hipEventRecord(c->events[c->events_used].second, c->stream);
-  c->events_used++;
+  const auto& e = c->events[c->events_used++];
+  return {e.first, e.second};
 }
 
 // Element offset of the lo plane of an activation buffer of `width` columns.
@@ -590,9 +594,9 @@ GemmArgs gemm_args(const spec_ctx* c, const WMat& W, const void* X, int ldx, int
 }
 
 // Split GEMM into the partial buffer; returns the split count used.
-int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err) {
+int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err, TimePair tp = {}) {
   g.S = gemm_splits(c->bf16, g.K, g.ntiles * 16, g.M);
-  *err = launch_gemm(c->bf16, EPI_PART, g, c->stream);
+  *err = launch_gemm(c->bf16, EPI_PART, g, c->stream, tp.t0, tp.t1);
   return g.S;
 }
 
@@ -727,9 +731,8 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
                              c->cos_t, c->sin_t, c->q, c->q_lo, kc, vc, ld, s));
       aa.kc = kc;
       aa.vc = vc;
-      time_begin(c, 4);
-      HIP_TRY(launch_attention(bf, aa, s));
-      time_end(c, 4);
+      const TimePair ta = time_pair(c, 4);
+      HIP_TRY(launch_attention(bf, aa, s, ta.t0, ta.t1));
       HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, lo_off(c, nq * hd), s));
       GemmArgs o = gemm_args(c, L.wo, c->attn_o, nq * hd, R, nq * hd, d);
       const int So = gemm_part(c, o, &e);
@@ -758,14 +761,11 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
     gu.Y = c->act;
     gu.ldy = F;
     gu.ylo = (int64_t)lo_off(c, F);
-    time_begin(c, 1);
-    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, s));
-    time_end(c, 1);
+    const TimePair tg = time_pair(c, 1);
+    HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, s, tg.t0, tg.t1));
     GemmArgs dn = gemm_args(c, L.wd, c->act, F, R, F, d);
-    time_begin(c, 2);
-    const int Sd = gemm_part(c, dn, &e);
+    const int Sd = gemm_part(c, dn, &e, time_pair(c, 2));
     HIP_TRY(e);
-    time_end(c, 2);
     const int ldd = dn.ntiles * 16;
     HIP_TRY(launch_resid_reduce(bf, c->P, Sd, (size_t)c->Rmax * ldd, ldd, R, d, c->h,
                                 next_norm, eps, c->u, u_lo, s));
@@ -784,9 +784,8 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
     lm.bias_tok = c->fault_tok;
     lm.bias = c->fault_bias;
     lm.bias_after = c->fault_after;
-    time_begin(c, 3);
-    HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s));
-    time_end(c, 3);
+    const TimePair tl = time_pair(c, 3);
+    HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s, tl.t0, tl.t1));
     HIP_TRY(launch_argmax_reduce(c->am_part, P.lm_rows, lm.nblocks, c->amax, s));
   }
   if (P.walk)

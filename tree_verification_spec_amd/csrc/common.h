@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -160,3 +162,16 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Deferred RMSNorm.  A GEMM is linear in each input row, so
+// (s * (h * w)) W^T = s * ((h * w) W^T) for the row's norm scale
+// s = 1 / sqrt(mean(h^2) + eps).  The kernel that writes a normalised
+// GEMM input therefore stores the planes of h * w and, per row, the sums of
+// squares of h over chunks of kNormChunk columns (one workgroup each, so a
+// row spreads over several CUs); the kernel that consumes that GEMM's output
+// multiplies it by the row's scale, summing the chunks in order.
+__device__ __forceinline__ float row_scale(const RowNorm& n, int row) {
+  float t = 0.f;
+  for (int c = 0; c < n.nc; ++c) t += n.ss[(size_t)row * n.nc + c];
+  return 1.0f / sqrtf(t / (float)n.d + n.eps);
+}

@@ -5,7 +5,7 @@
 
 namespace {
 
-// -------------------------------------------------------------- RMSNorm
+// ------------------------------------------------------- block reduction
 // Block-wide sum over blockDim.x threads (a multiple of 64, <= 1024).
 __device__ __forceinline__ float block_sum(float v, float* part) {
   v = wave_sum(v);
@@ -17,53 +17,32 @@ __device__ __forceinline__ float block_sum(float v, float* part) {
   return t;
 }
 
-// The per-row RMSNorm scale 1 / sqrt(mean(h^2) + eps).
-__device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
-  return 1.0f / sqrtf(ss / (float)d + eps);
-}
-
 // ---------------------------------------------------------------- embedding
-// One workgroup per row: h = float(E[token]), then u = RMSNorm(h) * nw as
-// activation planes for the first layer's input GEMM.  A thread owns four
-// consecutive columns in every 1024 and issues all of its embedding loads
-// before its first store (d <= 1024 * kEmbQ).
-constexpr int kEmbQ = 16;
+// One workgroup per (row, chunk of kNormChunk columns): h = float(E[token]),
+// u = h * nw as activation planes for the first layer's input GEMM, and the
+// chunk's sum of squares of h (the deferred RMSNorm of u).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb,
                                                     const RowMeta* __restrict__ rows, int d,
                                                     float* __restrict__ h,
-                                                    const float* __restrict__ nw, float eps,
-                                                    T* __restrict__ u, size_t ulo) {
+                                                    const float* __restrict__ nw,
+                                                    T* __restrict__ u, size_t ulo,
+                                                    float* __restrict__ ss) {
   __shared__ float part[4];
   const int row = blockIdx.x;
-  const T* e = emb + (size_t)rows[row].token * d;
-  float* hr = h + (size_t)row * d;
-  float4 v[kEmbQ];
-#pragma unroll
-  for (int j = 0; j < kEmbQ; ++j) {
-    const int c = (threadIdx.x + j * 256) * 4;
-    v[j] = c < d ? load4(e + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  const int c = blockIdx.y * kNormChunk + threadIdx.x * 4;
   float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < kEmbQ; ++j) {
-    const int c = (threadIdx.x + j * 256) * 4;
-    if (c < d) {
-      *reinterpret_cast<float4*>(hr + c) = v[j];
-      acc += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    }
+  if (c < d) {
+    const T* e = emb + (size_t)rows[row].token * d;
+    const float4 w = *reinterpret_cast<const float4*>(nw + c);
+    const float4 v = load4(e + c);
+    *reinterpret_cast<float4*>(h + (size_t)row * d + c) = v;
+    acc = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    store_act4(u, u + ulo, (size_t)row * d + c,
+               make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w));
   }
-  const float sc = rms_scale(block_sum(acc, part), d, eps);
-#pragma unroll
-  for (int j = 0; j < kEmbQ; ++j) {
-    const int c = (threadIdx.x + j * 256) * 4;
-    if (c < d) {
-      const float4 w = *reinterpret_cast<const float4*>(nw + c);
-      store_act4(u, u + ulo, (size_t)row * d + c,
-                 make_float4((v[j].x * sc) * w.x, (v[j].y * sc) * w.y, (v[j].z * sc) * w.z,
-                             (v[j].w * sc) * w.w));
-    }
-  }
+  const float t = block_sum(acc, part);
+  if (threadIdx.x == 0) ss[(size_t)row * gridDim.y + blockIdx.y] = t;
 }
 
 // ------------------------------------------------------------ RoPE + KV store
@@ -73,11 +52,12 @@ template <typename T, int S>
 __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t sstride,
                                const RowMeta* rows, int nq, int nkv, int hd,
                                const float* cos_t, const float* sin_t, T* q_out,
-                               T* q_lo, T* kc, T* vc, int ld) {
+                               T* q_lo, T* kc, T* vc, int ld, RowNorm norm) {
   const int row = blockIdx.x;
   const int head = blockIdx.y;  // [0, nq) q, [nq, nq+nkv) k, then v
   const int half = hd >> 1;
   const RowMeta rm = rows[row];
+  const float sc = row_scale(norm, row);
   const float* x = qkv + (size_t)row * ld + (size_t)head * hd;
   const int page = rm.slot >> 4, off = rm.slot & 15;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
@@ -87,12 +67,14 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
       p1[k] = x[k * sstride + i];
       p2[k] = x[k * sstride + i + half];
     }
-    float x1 = 0.f, x2 = 0.f;  // added in split order
+    float x1 = 0.f, x2 = 0.f;  // added in split order, then scaled by the norm
 #pragma unroll
     for (int k = 0; k < S; ++k) {
       x1 += p1[k];
       x2 += p2[k];
     }
+    x1 *= sc;
+    x2 *= sc;
     if (head < nq + nkv) {
       const float c = cos_t[(size_t)rm.pos * half + i];
       const float s = sin_t[(size_t)rm.pos * half + i];
@@ -119,24 +101,22 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
 
 // ------------------------------------------------------- residual reduce
 // h[r] += (sum of the S split partials of the GEMM output, in split order),
-// then u = RMSNorm(h[r]) * nw as activation planes for the next GEMM.  One
-// workgroup of 1024 threads per row; all S partial loads of a thread are in
-// flight together; the row stays in registers between the two passes.
+// u = h[r] * nw as activation planes for the next GEMM and the chunk's sum of
+// squares of h (the deferred RMSNorm of u).  One workgroup of 256 threads
+// per (row, chunk of kNormChunk columns), a float4 per thread, so a row's
+// loads spread over several CUs; all S partial loads of a thread are in
+// flight together.
 template <int S, typename T>
-__global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size_t sstride,
-                                                            int ldp, int d, float* h,
-                                                            const float* nw, float eps,
-                                                            T* u, size_t ulo) {
-  __shared__ float part[16];
-  constexpr int MAXQ = 4;  // float4 per thread: d <= 16384
+__global__ __launch_bounds__(256) void resid_reduce_kernel(const float* P, size_t sstride,
+                                                           int ldp, int d, float* h,
+                                                           const float* nw, T* u,
+                                                           size_t ulo, float* ss) {
+  __shared__ float part[4];
   const int row = blockIdx.x;
-  float4 keep[MAXQ], wn[MAXQ];
+  const int c = blockIdx.y * kNormChunk + threadIdx.x * 4;
   float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < MAXQ; ++j) {
-    const int c = (threadIdx.x + j * 1024) * 4;
-    if (c >= d) break;
-    wn[j] = *reinterpret_cast<const float4*>(nw + c);  // needed after the reduction
+  if (c < d) {
+    const float4 w = *reinterpret_cast<const float4*>(nw + c);
     float4 pv[S];
 #pragma unroll
     for (int k = 0; k < S; ++k)
@@ -150,20 +130,12 @@ __global__ __launch_bounds__(1024) void resid_reduce_kernel(const float* P, size
       v.w += pv[k].w;
     }
     *reinterpret_cast<float4*>(h + (size_t)row * d + c) = v;
-    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    keep[j] = v;
+    acc = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    store_act4(u, u + ulo, (size_t)row * d + c,
+               make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w));
   }
-  const float sc = rms_scale(block_sum(acc, part), d, eps);
-#pragma unroll
-  for (int j = 0; j < MAXQ; ++j) {
-    const int c = (threadIdx.x + j * 1024) * 4;
-    if (c >= d) break;
-    const float4 w = wn[j];
-    const size_t i = (size_t)row * d + c;
-    store_act4(u, u + ulo, i,
-               make_float4((keep[j].x * sc) * w.x, (keep[j].y * sc) * w.y,
-                           (keep[j].z * sc) * w.z, (keep[j].w * sc) * w.w));
-  }
+  const float t = block_sum(acc, part);
+  if (threadIdx.x == 0) ss[(size_t)row * gridDim.y + blockIdx.y] = t;
 }
 
 // ----------------------------------------------------------- argmax reduce
@@ -254,7 +226,7 @@ template <int S, bool TREE, int NS>
 __global__ __launch_bounds__(256) void lr_fork_kernel(
     const float* proj, size_t sstride, int ld, const RowMeta* rows,
     const ReqMeta* reqs, int d, float* H, void* o, size_t olo, bool obf,
-    float* save, bool commit_last) {
+    float* save, bool commit_last, RowNorm norm) {
   extern __shared__ float hs[];  // [max_rows][256] for trees
   constexpr int CPB = 256 / S;   // channels per block
   const int r = blockIdx.y;
@@ -263,8 +235,9 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
   const int c = blockIdx.x * CPB + threadIdx.x / S;
   const bool live = c < d;
   const int cc = live ? c : 0;
-  // in_proj output of a row (sum of the GEMM's split partials, in order)
-  auto pv = [&](int row, int col) {
+  // in_proj output of a row (sum of the GEMM's split partials, in order,
+  // times the row's norm scale sc)
+  auto pv = [&](int row, int col, float sc) {
     const float* p = proj + (size_t)row * ld + col;
     float t[NS];
 #pragma unroll
@@ -272,7 +245,7 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) v += t[k];
-    return v;
+    return v * sc;
   };
   float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
   const float h0 = *H0;
@@ -286,10 +259,11 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     } else {
       hp = hprev;
     }
-    const float a = pv(row, d + cc);
-    const float x = pv(row, cc);
-    const float Bs = pv(row, 3 * d + s);
-    const float Cs = pv(row, 3 * d + S + s);
+    const float sc = row_scale(norm, row);
+    const float a = pv(row, d + cc, sc);
+    const float x = pv(row, cc, sc);
+    const float Bs = pv(row, 3 * d + s, sc);
+    const float Cs = pv(row, 3 * d + S + s, sc);
     const float sig = 1.0f / (1.0f + expf(-a));
     const float hi = __fadd_rn(__fmul_rn(sig, hp), __fmul_rn(Bs, x));
     if (TREE) hs[i * 256 + threadIdx.x] = hi;
@@ -298,7 +272,7 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
 #pragma unroll
     for (int off = S / 2; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
     if (s == 0 && live) {
-      const float z = pv(row, 2 * d + cc);
+      const float z = pv(row, 2 * d + cc, sc);
       const float ov = y * (z / (1.0f + expf(-z)));
       const size_t oi = (size_t)row * d + cc;
       if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
@@ -400,15 +374,16 @@ __global__ void to_f32_kernel(const T* src, int n, float* dst) {
 }  // namespace
 
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
-                        int d, float* h, const float* nw, float eps, void* u, size_t u_lo,
+                        int d, float* h, const float* nw, void* u, size_t u_lo, float* ss,
                         hipStream_t s) {
-  if (d % 4 || d > 1024 * kEmbQ) return hipErrorInvalidValue;
+  if (d % 4 || d > 16384) return hipErrorInvalidValue;
+  const dim3 grid(R, (d + kNormChunk - 1) / kNormChunk);
   if (bf16)
-    embed_kernel<uint16_t><<<R, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, nw, eps,
-                                             (uint16_t*)u, u_lo);
+    embed_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, nw,
+                                                (uint16_t*)u, u_lo, ss);
   else
-    embed_kernel<float><<<R, 256, 0, s>>>((const float*)emb, rows, d, h, nw, eps,
-                                          (float*)u, u_lo);
+    embed_kernel<float><<<grid, 256, 0, s>>>((const float*)emb, rows, d, h, nw, (float*)u,
+                                             u_lo, ss);
   return hipGetLastError();
 }
 
@@ -416,14 +391,14 @@ template <typename T>
 static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta* rows,
                          int R, int nq, int nkv, int hd, const float* cos_t,
                          const float* sin_t, T* q_out, T* q_lo, T* kc, T* vc, int ld,
-                         hipStream_t s) {
+                         RowNorm norm, hipStream_t s) {
   dim3 grid(R, nq + 2 * nkv);
   const int thr = 64;  // loops over hd / 2 rotation pairs
   switch (S) {
 #define RO_CASE(SV)                                                                    \
   case SV:                                                                             \
     rope_kv_kernel<T, SV><<<grid, thr, 0, s>>>(qkv, sstride, rows, nq, nkv, hd, cos_t, \
-                                               sin_t, q_out, q_lo, kc, vc, ld);        \
+                                               sin_t, q_out, q_lo, kc, vc, ld, norm);  \
     break;
     RO_CASE(1) RO_CASE(2) RO_CASE(4) RO_CASE(8) RO_CASE(16) RO_CASE(32)
 #undef RO_CASE
@@ -435,24 +410,26 @@ static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta*
 hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
                           const RowMeta* rows, int R, int nq, int nkv, int hd,
                           const float* cos_t, const float* sin_t, void* q_out,
-                          void* q_lo, void* kc, void* vc, int ld_qkv, hipStream_t s) {
+                          void* q_lo, void* kc, void* vc, int ld_qkv, RowNorm norm,
+                          hipStream_t s) {
   if (bf16)
     return rope_t<uint16_t>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
                             (uint16_t*)q_out, (uint16_t*)q_lo, (uint16_t*)kc,
-                            (uint16_t*)vc, ld_qkv, s);
+                            (uint16_t*)vc, ld_qkv, norm, s);
   return rope_t<float>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
-                       (float*)q_out, (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, s);
+                       (float*)q_out, (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, norm, s);
 }
 
 template <typename T>
 static hipError_t resid_t(const float* P, int S, size_t split_stride, int ld_p, int R,
-                          int d, float* h, const float* nw, float eps, T* u, size_t u_lo,
+                          int d, float* h, const float* nw, T* u, size_t u_lo, float* ss,
                           hipStream_t s) {
+  const dim3 grid(R, (d + kNormChunk - 1) / kNormChunk);
   switch (S) {
-#define RR_CASE(SV)                                                                \
-  case SV:                                                                         \
-    resid_reduce_kernel<SV, T><<<R, 1024, 0, s>>>(P, split_stride, ld_p, d, h, nw, eps, \
-                                                  u, u_lo);                        \
+#define RR_CASE(SV)                                                                 \
+  case SV:                                                                          \
+    resid_reduce_kernel<SV, T><<<grid, 256, 0, s>>>(P, split_stride, ld_p, d, h, nw, \
+                                                    u, u_lo, ss);                   \
     break;
     RR_CASE(1) RR_CASE(2) RR_CASE(4) RR_CASE(8) RR_CASE(16) RR_CASE(32)
 #undef RR_CASE
@@ -463,12 +440,12 @@ static hipError_t resid_t(const float* P, int S, size_t split_stride, int ld_p, 
 
 hipError_t launch_resid_reduce(bool bf16, const float* P, int S, size_t split_stride,
                                int ld_p, int R, int d, float* h, const float* nw,
-                               float eps, void* u, size_t u_lo, hipStream_t s) {
+                               void* u, size_t u_lo, float* ss, hipStream_t s) {
   if (d % 4 || d > 16384) return hipErrorInvalidValue;
   if (bf16)
-    return resid_t<uint16_t>(P, S, split_stride, ld_p, R, d, h, nw, eps, (uint16_t*)u,
-                             u_lo, s);
-  return resid_t<float>(P, S, split_stride, ld_p, R, d, h, nw, eps, (float*)u, u_lo, s);
+    return resid_t<uint16_t>(P, S, split_stride, ld_p, R, d, h, nw, (uint16_t*)u, u_lo, ss,
+                             s);
+  return resid_t<float>(P, S, split_stride, ld_p, R, d, h, nw, (float*)u, u_lo, ss, s);
 }
 
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
@@ -488,7 +465,8 @@ template <int S, int NS>
 static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                             const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
                             float* H, void* o, size_t olo, bool obf, float* save, bool tree,
-                            bool commit_last, int max_rows_per_req, hipStream_t s) {
+                            bool commit_last, int max_rows_per_req, RowNorm norm,
+                            hipStream_t s) {
   constexpr int CPB = 256 / S;
   dim3 grid((d + CPB - 1) / CPB, n_req);
   if (tree) {
@@ -498,10 +476,12 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                                        (int)lds);
     if (e != hipSuccess) return e;
     lr_fork_kernel<S, true, NS><<<grid, 256, lds, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                       H, o, olo, obf, save, commit_last);
+                                                       H, o, olo, obf, save, commit_last,
+                                                       norm);
   } else {
     lr_fork_kernel<S, false, NS><<<grid, 256, 0, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                      H, o, olo, obf, save, commit_last);
+                                                      H, o, olo, obf, save, commit_last,
+                                                      norm);
   }
   return hipGetLastError();
 }
@@ -510,12 +490,13 @@ template <int S>
 static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
                              const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
                              float* H, void* o, size_t olo, bool obf, float* save, bool tree,
-                             bool commit_last, int max_rows_per_req, hipStream_t s) {
+                             bool commit_last, int max_rows_per_req, RowNorm norm,
+                             hipStream_t s) {
   switch (NS) {
 #define NS_CASE(NV)                                                                    \
   case NV:                                                                             \
     return lr_fork_s<S, NV>(proj, sstride, ld, rows, reqs, n_req, d, H, o, olo, obf,    \
-                            save, tree, commit_last, max_rows_per_req, s);
+                            save, tree, commit_last, max_rows_per_req, norm, s);
     NS_CASE(1) NS_CASE(2) NS_CASE(4) NS_CASE(8) NS_CASE(16) NS_CASE(32)
 #undef NS_CASE
     default: return hipErrorInvalidValue;
@@ -526,12 +507,12 @@ hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_str
                           int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
                           int d, int S, float* H, void* o, size_t o_lo, float* save,
                           bool any_tree, bool commit_last, int max_rows_per_req,
-                          hipStream_t s) {
+                          RowNorm norm, hipStream_t s) {
   switch (S) {
 #define LR_CASE(SV)                                                                    \
   case SV:                                                                             \
     return lr_fork_ns<SV>(NS, proj, split_stride, ld, rows, reqs, n_req, d, H, o, o_lo, \
-                          bf16, save, any_tree, commit_last, max_rows_per_req, s);
+                          bf16, save, any_tree, commit_last, max_rows_per_req, norm, s);
     LR_CASE(16)
     LR_CASE(32)
     LR_CASE(64)

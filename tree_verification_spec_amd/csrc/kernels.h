@@ -39,7 +39,18 @@ struct ReqMeta {
 // them, as "activation planes" of the weight type: for bf16 weights two bf16
 // planes hi = bf16(v) and lo = bf16(v - hi) (lo at a fixed element offset
 // from hi), so a bf16 MFMA pair sees ~16 mantissa bits of the fp32 value;
-// for fp32 weights one fp32 plane.  RMSNorm is applied by the producer.
+// for fp32 weights one fp32 plane.
+
+// RMSNorm is deferred (see row_scale in common.h): the producer of a
+// normalised input writes the planes of h * w and the row's chunk sums of
+// squares; the consumer of the GEMM output applies the row's scale.
+constexpr int kNormChunk = 1024;  // columns per sum-of-squares chunk (one workgroup)
+struct RowNorm {
+  const float* ss;  // [rows][nc] sums of squares of h, chunk by chunk
+  int32_t nc;       // chunks per row: ceil(d / kNormChunk)
+  int32_t d;
+  float eps;
+};
 
 // EPI_PART: fp32 partial sums of split s at P[s][row][col] (any S); the
 // consumer adds the S partials in order.  EPI_SWIGLU / EPI_ARGMAX need S = 1.
@@ -72,6 +83,8 @@ struct GemmArgs {
   const RowMeta* rows;  // ARGMAX fault injection: row positions
   int32_t bias_tok, bias_after;
   float bias;
+  RowNorm norm;         // SWIGLU / ARGMAX: the input rows' deferred RMSNorm
+                        // (norm.ss == NULL: none), rows indexed like X
 };
 
 // Weight matrices have their output rows padded to a multiple of
@@ -125,25 +138,30 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s,
 hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o, size_t o_lo,
                                hipStream_t s);
 
-// h[r] = E[token_r] in fp32, and u[r] = RMSNorm(h[r]) * nw as activation
-// planes (lo plane at u + u_lo elements).
+// h[r] = E[token_r] in fp32, u[r] = h[r] * nw as activation planes (lo
+// plane at u + u_lo elements) and ss[r][c] = the sum of h[r]^2 over chunk c
+// of kNormChunk columns (the deferred RMSNorm of u).
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows,
-                        int R, int d, float* h, const float* nw, float eps,
-                        void* u, size_t u_lo, hipStream_t s);
+                        int R, int d, float* h, const float* nw, void* u,
+                        size_t u_lo, float* ss, hipStream_t s);
 
 // q -> RoPE -> q_out; k -> RoPE -> K cache; v -> V cache, at each row's slot.
-// qkv = sum of the S GEMM partials qkv[s * split_stride + row * ld_qkv + c].
+// qkv = the row's norm scale (norm) times the sum of the S GEMM partials
+// qkv[s * split_stride + row * ld_qkv + c].
 hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
                           const RowMeta* rows, int R, int nq, int nkv, int hd,
                           const float* cos_t, const float* sin_t, void* q_out,
-                          void* q_lo, void* kc, void* vc, int ld_qkv, hipStream_t s);
+                          void* q_lo, void* kc, void* vc, int ld_qkv, RowNorm norm,
+                          hipStream_t s);
 
 // h[r] += sum_s P[s * split_stride + r * ld_p + c] (c < d), then
-// u[r] = RMSNorm(h[r]) * nw as activation planes: the residual add of a split
-// GEMM and the input of the next GEMM.  One workgroup per row.
+// u[r] = h[r] * nw as activation planes and ss[r][c] = the sum of h[r]^2
+// over chunk c: the residual add of a split GEMM and the input of the next
+// GEMM (whose consumer applies the norm scale).  One workgroup per row and
+// chunk of kNormChunk columns.
 hipError_t launch_resid_reduce(bool bf16, const float* P, int S, size_t split_stride,
                                int ld_p, int R, int d, float* h, const float* nw,
-                               float eps, void* u, size_t u_lo, hipStream_t s);
+                               void* u, size_t u_lo, float* ss, hipStream_t s);
 
 // Per-row argmax over the column-block partials (lowest index on ties).
 hipError_t launch_argmax_reduce(const float2* part, int R, int nblocks,
@@ -157,7 +175,8 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
 
 // Gated diagonal recurrence over the pass's nodes for one recurrent layer.
 // proj: in_proj output as S split partials (stride split_stride floats), each
-// [R, ld] = [x | a | z | B | C | pad]; H: committed states
+// [R, ld] = [x | a | z | B | C | pad], scaled by the row's norm scale (norm)
+// after the partials are summed; H: committed states
 // [max_requests][d][S]; o: [R, d] activation planes (lo at o + o_lo).
 // save (or NULL): per row [x | a | B] ([R, 2d + S]) for the commit.  With
 // commit_last (chain passes only) the state of each request's last row is
@@ -166,7 +185,7 @@ hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_str
                           int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
                           int d, int S, float* H, void* o, size_t o_lo, float* save,
                           bool any_tree, bool commit_last, int max_rows_per_req,
-                          hipStream_t s);
+                          RowNorm norm, hipStream_t s);
 
 struct CommitReq {
   int32_t table;     // request id

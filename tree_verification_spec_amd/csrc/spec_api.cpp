@@ -170,7 +170,9 @@ struct spec_ctx {
   float* h = nullptr;
   // activation planes [Rmax, width] feeding the GEMMs (bf16: hi plane then
   // lo plane, lo at + Rmax * width elements; fp32: one plane)
-  void* u = nullptr;         // RMSNorm output (QKV / in_proj / gate-up / LM head input)
+  void* u = nullptr;         // h * norm weight (QKV / in_proj / gate-up / LM head input)
+  float* ss = nullptr;       // deferred RMSNorm of u: [Rmax][norm_nc] chunk sums of squares
+  int norm_nc = 0;
   void* act = nullptr;       // SwiGLU output (down input)
   void* attn_o = nullptr;    // attention output (O input)
   void* q = nullptr;
@@ -371,6 +373,8 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const size_t scratch0 = p.cursor;
   const size_t o_h = p.take((size_t)R * d * 4);
   const size_t o_u = p.take((size_t)R * d * 4);
+  const int norm_nc = (d + kNormChunk - 1) / kNormChunk;
+  const size_t o_ss = p.take((size_t)R * norm_nc * 4);
   const size_t o_act = p.take((size_t)R * F * 4);
   const size_t o_ao = p.take((size_t)R * nq * hd * 4);
   const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);  // bf16: hi and lo planes
@@ -464,6 +468,8 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     c->Rmax = R;
     c->h = (float*)at(o_h);
     c->u = at(o_u);
+    c->ss = (float*)at(o_ss);
+    c->norm_nc = norm_nc;
     c->act = at(o_act);
     c->attn_o = at(o_ao);
     c->q = at(o_q);
@@ -558,6 +564,12 @@ TimePair time_pair(spec_ctx* c, int cls) {
   }
   const auto& e = c->events[c->events_used++];
   return {e.first, e.second};
+}
+
+// The deferred RMSNorm of the rows of u from row0 on (the consumer of a
+// GEMM over those rows applies it).
+RowNorm row_norm(const spec_ctx* c, int row0 = 0) {
+  return RowNorm{c->ss + (size_t)row0 * c->norm_nc, c->norm_nc, c->d, c->cfg.rms_eps};
 }
 
 // Element offset of the lo plane of an activation buffer of `width` columns.
@@ -689,10 +701,10 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
   const bool any_tree = P.any_tree, prefill = P.prefill;
   hipError_t e = hipSuccess;
 
-  const float eps = cfg.rms_eps;
   const size_t u_lo = lo_off(c, d);
-  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, eps, c->u,
-                       u_lo, s));
+  HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, c->u, u_lo,
+                       c->ss, s));
+  const RowNorm norm = row_norm(c);
 
   AttnArgs aa{};
   aa.q = c->q;
@@ -728,7 +740,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       char* vc = c->vpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
       const int ld = g.ntiles * 16;
       HIP_TRY(launch_rope_kv(bf, c->P, S, (size_t)c->Rmax * ld, c->d_rows, R, nq, nkv, hd,
-                             c->cos_t, c->sin_t, c->q, c->q_lo, kc, vc, ld, s));
+                             c->cos_t, c->sin_t, c->q, c->q_lo, kc, vc, ld, norm, s));
       aa.kc = kc;
       aa.vc = vc;
       const TimePair ta = time_pair(c, 4);
@@ -739,7 +751,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
       HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
-                                  L.n2, eps, c->u, u_lo, s));
+                                  L.n2, c->u, u_lo, c->ss, s));
     } else {
       GemmArgs g = gemm_args(c, L.win, c->u, d, R, d, c->in_n);
       const int S = gemm_part(c, g, &e);
@@ -749,18 +761,19 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       float* save = prefill ? nullptr : c->lrsave + (size_t)L.idx * c->lrsave_layer;
       HIP_TRY(launch_lr_fork(bf, c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
                              n_req, d, c->S, H, c->lr_o, lo_off(c, d), save, any_tree,
-                             prefill, max_rows_req, s));
+                             prefill, max_rows_req, norm, s));
       GemmArgs o = gemm_args(c, L.wout, c->lr_o, d, R, d, d);
       const int So = gemm_part(c, o, &e);
       HIP_TRY(e);
       const int ldo = o.ntiles * 16;
       HIP_TRY(launch_resid_reduce(bf, c->P, So, (size_t)c->Rmax * ldo, ldo, R, d, c->h,
-                                  L.n2, eps, c->u, u_lo, s));
+                                  L.n2, c->u, u_lo, c->ss, s));
     }
     GemmArgs gu = gemm_args(c, L.wgu, c->u, d, R, d, 2 * F);
     gu.Y = c->act;
     gu.ldy = F;
     gu.ylo = (int64_t)lo_off(c, F);
+    gu.norm = norm;
     const TimePair tg = time_pair(c, 1);
     HIP_TRY(launch_gemm(bf, EPI_SWIGLU, gu, s, tg.t0, tg.t1));
     GemmArgs dn = gemm_args(c, L.wd, c->act, F, R, F, d);
@@ -768,7 +781,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
     HIP_TRY(e);
     const int ldd = dn.ntiles * 16;
     HIP_TRY(launch_resid_reduce(bf, c->P, Sd, (size_t)c->Rmax * ldd, ldd, R, d, c->h,
-                                next_norm, eps, c->u, u_lo, s));
+                                next_norm, c->u, u_lo, c->ss, s));
   }
 
   // final norm + LM head + argmax over rows [lm_row0, lm_row0 + lm_rows)
@@ -784,6 +797,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
     lm.bias_tok = c->fault_tok;
     lm.bias = c->fault_bias;
     lm.bias_after = c->fault_after;
+    lm.norm = row_norm(c, P.lm_row0);
     const TimePair tl = time_pair(c, 3);
     HIP_TRY(launch_gemm(bf, EPI_ARGMAX, lm, s, tl.t0, tl.t1));
     HIP_TRY(launch_argmax_reduce(c->am_part, P.lm_rows, lm.nblocks, c->amax, s));

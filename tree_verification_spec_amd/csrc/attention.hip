@@ -349,8 +349,9 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
 // One workgroup of 4 waves per (row, query head): merge the splits of the
 // row's request.  Every wave reads the (max, sum) of all splits (lane l:
 // splits l and l + 64) and forms the same weights; wave w then accumulates
-// splits w, w + 4, ... for its lanes' dims (all loads of a wave in flight
-// together), and the four sums are added in wave order.
+// splits w, w + 4, ... for its lanes' dims (up to 16 splits' loads of a
+// wave in flight together, the first 16 issued with the (max, sum) loads),
+// and the four sums are added in wave order.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, size_t olo) {
   __shared__ float red[4][HD];
@@ -362,25 +363,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = ml0;
   if (lane < nsplit) ml0 = a.part_ml[(size_t)lane * sstride + wid];
   if (lane + 64 < nsplit) ml1 = a.part_ml[(size_t)(lane + 64) * sstride + wid];
-  const float M = wave_max(fmaxf(ml0.x, ml1.x));
-  // the running maxima are in the base-2 domain of the split kernel
-  const float w0 = (ml0.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml0.x - M);
-  const float w1 = (ml1.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml1.x - M);
-  const float L = wave_sum(ml0.y * w0 + ml1.y * w1);
   constexpr int PER = HD / 64;
-  constexpr int U = 8;  // splits per wave loaded together
-  float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  constexpr int U = 16;  // splits per wave loaded together
   const float* po = a.part_o + (size_t)wid * HD + lane * PER;
-  for (int s0 = wave; s0 < nsplit; s0 += 4 * U) {
-    float v[U][PER];
+  auto load_group = [&](int s0, float (&v)[U][PER]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int sp = min(s0 + 4 * u, nsplit - 1);
 #pragma unroll
       for (int j = 0; j < PER; ++j) v[u][j] = po[(size_t)sp * sstride * HD + j];
     }
+  };
+  // the first group of partial outputs is loaded together with the (max,
+  // sum) pairs, ahead of the reductions that form the weights
+  float v[U][PER];
+  load_group(wave, v);
+  const float M = wave_max(fmaxf(ml0.x, ml1.x));
+  // the running maxima are in the base-2 domain of the split kernel
+  const float w0 = (ml0.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml0.x - M);
+  const float w1 = (ml1.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml1.x - M);
+  const float L = wave_sum(ml0.y * w0 + ml1.y * w1);
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int s0 = wave; s0 < nsplit; s0 += 4 * U) {
+    if (s0 != wave) load_group(s0, v);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int sp = s0 + 4 * u;

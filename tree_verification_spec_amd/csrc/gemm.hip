@@ -89,16 +89,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   const int mc = min(a.M - a.row0, 128);
   T* xbuf = reinterpret_cast<T*>(smem);
   // The SWIGLU and ARGMAX epilogues scale each row by its deferred RMSNorm
-  // scale.  The chunk sums of squares of this launch's rows are contiguous:
-  // up to NTHR of them are loaded now, one per thread into a register (no
-  // wait before the weight stream starts), and placed in LDS in the epilogue.
+  // scale, computed once per row in the epilogue (loading the chunk sums at
+  // the start measured slower: it delays the first weight loads).
   constexpr bool kNorm = EPI != EPI_PART;
-  __shared__ float rss[kNorm ? NTHR : 1];
-  const int nss = (kNorm && a.norm.ss) ? mc * a.norm.nc : 0;
-  const bool ss_early = nss <= NTHR;
-  float ssv = 0.f;
-  if (kNorm && ss_early && (int)threadIdx.x < nss)
-    ssv = a.norm.ss[(size_t)a.row0 * a.norm.nc + threadIdx.x];
+  __shared__ float rsc[kNorm ? 128 : 1];
 
   // weights: bf16 / fp32 tiles (a Frag per lane), or W12 tiles (12 bytes
   // per lane plus one exception-slot word, decoded to a Frag before use)
@@ -351,20 +345,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         tile[(mt * 16 + r16) * LDT + (wave * NTW + t) * 16 + 4 * g + r] = acc[t][mt][r];
-  if (kNorm && ss_early && (int)threadIdx.x < nss) rss[threadIdx.x] = ssv;
+  if (kNorm && (int)threadIdx.x < mc)
+    rsc[threadIdx.x] = a.norm.ss ? row_scale(a.norm, a.row0 + threadIdx.x) : 1.0f;
   __syncthreads();
-  // the norm scale of output row `row` (chunks summed in order, as row_scale)
-  auto rscale = [&](int row) -> float {
-    if (nss == 0) return 1.0f;
-    const int nc = a.norm.nc;
-    float t = 0.f;
-    if (ss_early) {
-      for (int c = 0; c < nc; ++c) t += rss[row * nc + c];
-    } else {
-      for (int c = 0; c < nc; ++c) t += a.norm.ss[(size_t)(a.row0 + row) * nc + c];
-    }
-    return 1.0f / sqrtf(t / (float)a.norm.d + a.norm.eps);
-  };
   // output rows of the tile, and an output value (stacked: hi row + lo row)
   const int orows = STK ? mc : TROWS;
   auto val = [&](int row, int col) -> float {
@@ -390,9 +373,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       const int m = a.row0 + row;
       if (m >= a.M) continue;
       const int p = j >> 4, c = j & 15;
-      const float sc = rscale(row);
-      const float gv = val(row, p * 32 + c) * sc;
-      const float uv = val(row, p * 32 + 16 + c) * sc;
+      const float gv = val(row, p * 32 + c) * rsc[row];
+      const float uv = val(row, p * 32 + 16 + c) * rsc[row];
       T* Yh = reinterpret_cast<T*>(a.Y);
       store_act(Yh, Yh + a.ylo, (size_t)m * a.ldy + nb * OUTS + j,
                 gv / (1.0f + expf(-gv)) * uv);
@@ -405,7 +387,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     const int m = a.row0 + row;
     if (m >= a.M) continue;
     const int n = col0 + col;
-    float v = val(row, col) * rscale(row);
+    float v = val(row, col) * rsc[row];
     if (n >= a.ncols) v = -INFINITY;
     if (n == a.bias_tok && a.rows[m].pos >= a.bias_after) v += a.bias;
     if (a.logits && n < a.ncols) a.logits[(size_t)m * a.ldlog + n] = v;

@@ -170,8 +170,16 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // squares of h over chunks of kNormChunk columns (one workgroup each, so a
 // row spreads over several CUs); the kernel that consumes that GEMM's output
 // multiplies it by the row's scale, summing the chunks in order.
+// All chunk loads are issued together (nc <= 16: d <= 16384); the chunks are
+// added in order.
 __device__ __forceinline__ float row_scale(const RowNorm& n, int row) {
+  const float* p = n.ss + (size_t)row * n.nc;
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v[c] = c < n.nc ? p[c] : 0.f;
   float t = 0.f;
-  for (int c = 0; c < n.nc; ++c) t += n.ss[(size_t)row * n.nc + c];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    if (c < n.nc) t += v[c];
   return 1.0f / sqrtf(t / (float)n.d + n.eps);
 }

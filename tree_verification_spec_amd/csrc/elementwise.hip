@@ -250,7 +250,16 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
   float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
   const float h0 = *H0;
   float hprev = h0;
+  // the rows' norm scales, computed before the (sequential) walk over the
+  // nodes, 256 rows at a time
+  __shared__ float scs[256];
   for (int i = 0; i < rm.nrows; ++i) {
+    if (i % 256 == 0) {
+      __syncthreads();  // the previous segment's scales are no longer read
+      if (i + (int)threadIdx.x < rm.nrows)
+        scs[threadIdx.x] = row_scale(norm, rm.row0 + i + threadIdx.x);
+      __syncthreads();
+    }
     const int row = rm.row0 + i;
     float hp;
     if (TREE) {
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     } else {
       hp = hprev;
     }
-    const float sc = row_scale(norm, row);
+    const float sc = scs[i % 256];
     const float a = pv(row, d + cc, sc);
     const float x = pv(row, cc, sc);
     const float Bs = pv(row, 3 * d + s, sc);

@@ -221,7 +221,14 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 // For each node in index order (parents first):
 //   H_i = sigmoid(a_i[c]) * H_parent + B_i[s] * x_i[c]   (no FMA contraction)
 //   y_i[c] = sum_s H_i[s] * C_i[s]; o_i[c] = y_i * silu(z_i[c])
-// Tree passes keep every node's state in LDS; chain passes keep one state.
+// Per segment of up to kLrSeg rows: (1) the block's x, a, z, every row's B
+// and C (sums of the in_proj split partials, in order, times the row's norm
+// scale), sigmoid(a) and the rows' parents are staged in LDS with all loads
+// in flight; (2) the walk over the nodes, which is sequential, only forms the
+// states (LDS in, LDS out: every node's state for trees, the segment's for
+// chains); (3) the outputs, independent per (node, channel), take one thread
+// each and sum y over s in order.
+constexpr int kLrSeg = 32;
 template <int S, bool TREE, int NS>
 __global__ __launch_bounds__(256) void lr_fork_kernel(
     const float* proj, size_t sstride, int ld, const RowMeta* rows,
@@ -229,70 +236,111 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
     float* save, bool commit_last, RowNorm norm) {
   extern __shared__ float hs[];  // [max_rows][256] for trees
   constexpr int CPB = 256 / S;   // channels per block
+  constexpr int NV = 3 * CPB + 2 * S;  // staged values per row: x, a, z (CPB each), B, C
+  __shared__ float sv[kLrSeg][NV];
+  __shared__ float sg[kLrSeg][CPB];  // sigmoid(a)
+  __shared__ float scs[kLrSeg];
+  __shared__ int spar[kLrSeg];
+  __shared__ float hseg[TREE ? 1 : kLrSeg * 256];  // chains: the segment's states
   const int r = blockIdx.y;
   const ReqMeta rm = reqs[r];
   const int s = threadIdx.x % S;
-  const int c = blockIdx.x * CPB + threadIdx.x / S;
+  const int lc = threadIdx.x / S;  // the lane's channel within the block
+  const int c = blockIdx.x * CPB + lc;
   const bool live = c < d;
   const int cc = live ? c : 0;
-  // in_proj output of a row (sum of the GEMM's split partials, in order,
-  // times the row's norm scale sc)
-  auto pv = [&](int row, int col, float sc) {
-    const float* p = proj + (size_t)row * ld + col;
-    float t[NS];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) t[k] = p[k * sstride];
-    float v = 0.f;
-#pragma unroll
-    for (int k = 0; k < NS; ++k) v += t[k];
-    return v * sc;
-  };
   float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
   const float h0 = *H0;
   float hprev = h0;
-  // the rows' norm scales, computed before the (sequential) walk over the
-  // nodes, 256 rows at a time
-  __shared__ float scs[256];
-  for (int i = 0; i < rm.nrows; ++i) {
-    if (i % 256 == 0) {
-      __syncthreads();  // the previous segment's scales are no longer read
-      if (i + (int)threadIdx.x < rm.nrows)
-        scs[threadIdx.x] = row_scale(norm, rm.row0 + i + threadIdx.x);
-      __syncthreads();
+  for (int i0 = 0; i0 < rm.nrows; i0 += kLrSeg) {
+    const int n = min(kLrSeg, rm.nrows - i0);
+    __syncthreads();  // the previous segment's values are no longer read
+    if ((int)threadIdx.x < n) {
+      scs[threadIdx.x] = row_scale(norm, rm.row0 + i0 + threadIdx.x);
+      if (TREE) spar[threadIdx.x] = rows[rm.row0 + i0 + threadIdx.x].parent;
     }
-    const int row = rm.row0 + i;
-    float hp;
-    if (TREE) {
-      const int p = rows[row].parent;
-      hp = (p < 0) ? h0 : hs[p * 256 + threadIdx.x];
-    } else {
-      hp = hprev;
-    }
-    const float sc = scs[i % 256];
-    const float a = pv(row, d + cc, sc);
-    const float x = pv(row, cc, sc);
-    const float Bs = pv(row, 3 * d + s, sc);
-    const float Cs = pv(row, 3 * d + S + s, sc);
-    const float sig = 1.0f / (1.0f + expf(-a));
-    const float hi = __fadd_rn(__fmul_rn(sig, hp), __fmul_rn(Bs, x));
-    if (TREE) hs[i * 256 + threadIdx.x] = hi;
-    hprev = hi;
-    float y = __fmul_rn(hi, Cs);
+    __syncthreads();
+    // (1) staging: U values per thread are loaded before any is stored
+    constexpr int U = NS >= 16 ? 1 : 16 / NS;
+    auto src = [&](int e) {
+      const int j = e / NV, k = e % NV;
+      int col;
+      if (k < 3 * CPB) {
+        const int ch = blockIdx.x * CPB + k % CPB;
+        col = (k / CPB) * d + (ch < d ? ch : 0);  // x, a or z
+      } else {
+        col = 3 * d + (k - 3 * CPB);  // B then C
+      }
+      return proj + (size_t)(rm.row0 + i0 + j) * ld + col;
+    };
+    for (int e0 = threadIdx.x; e0 < n * NV; e0 += 256 * U) {
+      float t[U][NS];
 #pragma unroll
-    for (int off = S / 2; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
-    if (s == 0 && live) {
-      const float z = pv(row, 2 * d + cc, sc);
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * 256;
+        if (e < n * NV) {
+          const float* p = src(e);
+#pragma unroll
+          for (int q = 0; q < NS; ++q) t[u][q] = p[q * sstride];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * 256;
+        if (e < n * NV) {
+          float v = 0.f;
+#pragma unroll
+          for (int q = 0; q < NS; ++q) v += t[u][q];
+          const int j = e / NV, k = e % NV;
+          v *= scs[j];
+          sv[j][k] = v;
+          if (k >= CPB && k < 2 * CPB) sg[j][k - CPB] = 1.0f / (1.0f + expf(-v));
+        }
+      }
+    }
+    __syncthreads();
+    // (2) the walk: states only
+    for (int j = 0; j < n; ++j) {
+      const int i = i0 + j;
+      float hp;
+      if (TREE) {
+        const int pp = spar[j];
+        hp = (pp < 0) ? h0 : hs[pp * 256 + threadIdx.x];
+      } else {
+        hp = hprev;
+      }
+      const float hi = __fadd_rn(__fmul_rn(sg[j][lc], hp), __fmul_rn(sv[j][3 * CPB + s], sv[j][lc]));
+      if (TREE) hs[i * 256 + threadIdx.x] = hi;
+      else hseg[j * 256 + threadIdx.x] = hi;
+      hprev = hi;
+    }
+    __syncthreads();
+    // (3) outputs: one thread per (node, channel)
+    for (int e = threadIdx.x; e < n * CPB; e += 256) {
+      const int j = e / CPB, l = e % CPB;
+      const int ch = blockIdx.x * CPB + l;
+      if (ch >= d) continue;
+      const int row = rm.row0 + i0 + j;
+      const float* hrow = TREE ? &hs[(i0 + j) * 256 + l * S] : &hseg[j * 256 + l * S];
+      float y = 0.f;
+#pragma unroll 16
+      for (int q = 0; q < S; ++q) y += __fmul_rn(hrow[q], sv[j][3 * CPB + S + q]);
+      const float z = sv[j][2 * CPB + l];
       const float ov = y * (z / (1.0f + expf(-z)));
-      const size_t oi = (size_t)row * d + cc;
+      const size_t oi = (size_t)row * d + ch;
       if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
       else store_act((float*)o, (float*)o + olo, oi, ov);
       if (save) {
-        save[(size_t)row * (2 * d + S) + cc] = x;
-        save[(size_t)row * (2 * d + S) + d + cc] = a;
+        save[(size_t)row * (2 * d + S) + ch] = sv[j][l];
+        save[(size_t)row * (2 * d + S) + d + ch] = sv[j][CPB + l];
       }
     }
-    if (save && blockIdx.x == 0 && threadIdx.x < S)
-      save[(size_t)row * (2 * d + S) + 2 * d + s] = Bs;
+    if (save && blockIdx.x == 0) {
+      for (int e = threadIdx.x; e < n * S; e += 256) {
+        const int j = e / S, q = e % S;
+        save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sv[j][3 * CPB + q];
+      }
+    }
   }
   if (commit_last && live) *H0 = hprev;
 }

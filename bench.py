@@ -65,7 +65,7 @@ def main():
     ap.add_argument("--weights", default=None, choices=("w12", "native", "w12_lowp"),
                     help="weight storage: W12 (lossless 12-bit, bitwise-identical "
                          "results) or the model's bf16; default: the faster of the two "
-                         "for the workload (W12 up to 32 rows per pass, bf16 above)")
+                         "for the workload (W12 up to 40 rows per pass, bf16 above)")
     ap.add_argument("--policy", default="fixed", choices=("fixed", "budget"),
                     help="batched workload: fixed K drafts per request, or per-step draft "
                          "lengths of 8/12/16 from each request's acceptance so far under a "
@@ -108,7 +108,7 @@ def main():
     cfg = synth.model_config(w["model"])
     if args.weights is None:
         rows = w["K"] + 1 if args.workload != "dense8b_batched" else w["batch"] * (w["K"] + 1)
-        args.weights = "w12" if rows <= 32 else "native"
+        args.weights = "w12" if rows <= 40 else "native"
     V, K, idx = cfg["vocab"], w["K"], w["index"]
     batched = args.workload == "dense8b_batched"
     tree = w["draft"] == "tree"

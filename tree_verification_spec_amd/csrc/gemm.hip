@@ -436,7 +436,7 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 }
 
 // Workgroup shapes: (tiles per wave, waves).  128 columns with one tile per
-// wave stream best when the rows are few; 256 columns with two tiles per
+// wave stream best when the rows are few (up to 40: the stacked-row limit); 256 columns with two tiles per
 // wave halve the LDS reads per MFMA and fill the CUs evenly when a
 // 128-column grid would leave a small second round; for narrow matrices,
 // two tiles per wave on 4 waves keep 128 columns at up to 95 rows, and from
@@ -449,7 +449,7 @@ struct Variant {
 Variant gemm_variant(bool bf16, int N, int M) {
   if (!bf16) return {1, 8};
   const int b128 = N / 128, b256 = N / 256;
-  if (M <= 32) return (b128 > 256 && b128 < 512) ? Variant{2, 8} : Variant{1, 8};
+  if (M <= 40) return (b128 > 256 && b128 < 512) ? Variant{2, 8} : Variant{1, 8};
   if (b256 >= 128) return Variant{2, 8};
   return M >= 96 ? Variant{1, 8} : Variant{2, 4};
 }

@@ -20,16 +20,28 @@ __device__ __forceinline__ float block_sum(float v, float* part) {
 // ---------------------------------------------------------------- embedding
 // One workgroup per (row, chunk of kNormChunk columns): h = float(E[token]),
 // u = h * nw as activation planes for the first layer's input GEMM, and the
-// chunk's sum of squares of h (the deferred RMSNorm of u).
+// chunk's sum of squares of h (the deferred RMSNorm of u).  The workgroups of
+// chunk 0 also copy the row's RoPE factors at its position into cs[row]
+// (cos then sin, hd / 2 each), so that RoPE needs no position lookup.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb,
                                                     const RowMeta* __restrict__ rows, int d,
                                                     float* __restrict__ h,
                                                     const float* __restrict__ nw,
                                                     T* __restrict__ u, size_t ulo,
-                                                    float* __restrict__ ss) {
+                                                    float* __restrict__ ss,
+                                                    const float* __restrict__ cos_t,
+                                                    const float* __restrict__ sin_t, int half,
+                                                    float* __restrict__ cs) {
   __shared__ float part[4];
   const int row = blockIdx.x;
+  if (blockIdx.y == 0) {
+    const size_t pos = (size_t)rows[row].pos;
+    for (int t = threadIdx.x; t < half; t += blockDim.x) {
+      cs[(size_t)row * 2 * half + t] = cos_t[pos * half + t];
+      cs[(size_t)row * 2 * half + half + t] = sin_t[pos * half + t];
+    }
+  }
   const int c = blockIdx.y * kNormChunk + threadIdx.x * 4;
   float acc = 0.f;
   if (c < d) {
@@ -51,8 +63,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ emb,
 template <typename T, int S>
 __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t sstride,
                                const RowMeta* rows, int nq, int nkv, int hd,
-                               const float* cos_t, const float* sin_t, T* q_out,
-                               T* q_lo, T* kc, T* vc, int ld, RowNorm norm) {
+                               const float* cs, T* q_out, T* q_lo, T* kc, T* vc, int ld,
+                               RowNorm norm) {
   const int row = blockIdx.x;
   const int head = blockIdx.y;  // [0, nq) q, [nq, nq+nkv) k, then v
   const int half = hd >> 1;
@@ -76,8 +88,8 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
     x1 *= sc;
     x2 *= sc;
     if (head < nq + nkv) {
-      const float c = cos_t[(size_t)rm.pos * half + i];
-      const float s = sin_t[(size_t)rm.pos * half + i];
+      const float c = cs[(size_t)row * hd + i];
+      const float s = cs[(size_t)row * hd + half + i];
       const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
       const float y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
       if (head < nq) {
@@ -432,30 +444,31 @@ __global__ void to_f32_kernel(const T* src, int n, float* dst) {
 
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows, int R,
                         int d, float* h, const float* nw, void* u, size_t u_lo, float* ss,
+                        const float* cos_t, const float* sin_t, int hd, float* cs,
                         hipStream_t s) {
-  if (d % 4 || d > 16384) return hipErrorInvalidValue;
+  if (d % 4 || d > 16384 || hd % 2) return hipErrorInvalidValue;
   const dim3 grid(R, (d + kNormChunk - 1) / kNormChunk);
   if (bf16)
     embed_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)emb, rows, d, h, nw,
-                                                (uint16_t*)u, u_lo, ss);
+                                                (uint16_t*)u, u_lo, ss, cos_t, sin_t,
+                                                hd / 2, cs);
   else
     embed_kernel<float><<<grid, 256, 0, s>>>((const float*)emb, rows, d, h, nw, (float*)u,
-                                             u_lo, ss);
+                                             u_lo, ss, cos_t, sin_t, hd / 2, cs);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta* rows,
-                         int R, int nq, int nkv, int hd, const float* cos_t,
-                         const float* sin_t, T* q_out, T* q_lo, T* kc, T* vc, int ld,
-                         RowNorm norm, hipStream_t s) {
+                         int R, int nq, int nkv, int hd, const float* cs, T* q_out,
+                         T* q_lo, T* kc, T* vc, int ld, RowNorm norm, hipStream_t s) {
   dim3 grid(R, nq + 2 * nkv);
   const int thr = 64;  // loops over hd / 2 rotation pairs
   switch (S) {
 #define RO_CASE(SV)                                                                    \
   case SV:                                                                             \
-    rope_kv_kernel<T, SV><<<grid, thr, 0, s>>>(qkv, sstride, rows, nq, nkv, hd, cos_t, \
-                                               sin_t, q_out, q_lo, kc, vc, ld, norm);  \
+    rope_kv_kernel<T, SV><<<grid, thr, 0, s>>>(qkv, sstride, rows, nq, nkv, hd, cs,    \
+                                               q_out, q_lo, kc, vc, ld, norm);         \
     break;
     RO_CASE(1) RO_CASE(2) RO_CASE(4) RO_CASE(8) RO_CASE(16) RO_CASE(32)
 #undef RO_CASE
@@ -466,15 +479,14 @@ static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta*
 
 hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
                           const RowMeta* rows, int R, int nq, int nkv, int hd,
-                          const float* cos_t, const float* sin_t, void* q_out,
-                          void* q_lo, void* kc, void* vc, int ld_qkv, RowNorm norm,
-                          hipStream_t s) {
+                          const float* cs, void* q_out, void* q_lo, void* kc, void* vc,
+                          int ld_qkv, RowNorm norm, hipStream_t s) {
   if (bf16)
-    return rope_t<uint16_t>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
+    return rope_t<uint16_t>(qkv, S, split_stride, rows, R, nq, nkv, hd, cs,
                             (uint16_t*)q_out, (uint16_t*)q_lo, (uint16_t*)kc,
                             (uint16_t*)vc, ld_qkv, norm, s);
-  return rope_t<float>(qkv, S, split_stride, rows, R, nq, nkv, hd, cos_t, sin_t,
-                       (float*)q_out, (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, norm, s);
+  return rope_t<float>(qkv, S, split_stride, rows, R, nq, nkv, hd, cs, (float*)q_out,
+                       (float*)q_lo, (float*)kc, (float*)vc, ld_qkv, norm, s);
 }
 
 template <typename T>

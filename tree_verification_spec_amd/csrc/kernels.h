@@ -140,19 +140,21 @@ hipError_t launch_attn_combine(bool bf16, const AttnArgs& a, void* o, size_t o_l
 
 // h[r] = E[token_r] in fp32, u[r] = h[r] * nw as activation planes (lo
 // plane at u + u_lo elements) and ss[r][c] = the sum of h[r]^2 over chunk c
-// of kNormChunk columns (the deferred RMSNorm of u).
+// of kNormChunk columns (the deferred RMSNorm of u); cs[r] = the RoPE
+// factors at row r's position ([hd]: cos_t then sin_t rows, hd / 2 each).
 hipError_t launch_embed(bool bf16, const void* emb, const RowMeta* rows,
                         int R, int d, float* h, const float* nw, void* u,
-                        size_t u_lo, float* ss, hipStream_t s);
+                        size_t u_lo, float* ss, const float* cos_t, const float* sin_t,
+                        int hd, float* cs, hipStream_t s);
 
 // q -> RoPE -> q_out; k -> RoPE -> K cache; v -> V cache, at each row's slot.
 // qkv = the row's norm scale (norm) times the sum of the S GEMM partials
-// qkv[s * split_stride + row * ld_qkv + c].
+// qkv[s * split_stride + row * ld_qkv + c]; cs: the rows' RoPE factors as
+// written by launch_embed.
 hipError_t launch_rope_kv(bool bf16, const float* qkv, int S, size_t split_stride,
                           const RowMeta* rows, int R, int nq, int nkv, int hd,
-                          const float* cos_t, const float* sin_t, void* q_out,
-                          void* q_lo, void* kc, void* vc, int ld_qkv, RowNorm norm,
-                          hipStream_t s);
+                          const float* cs, void* q_out, void* q_lo, void* kc, void* vc,
+                          int ld_qkv, RowNorm norm, hipStream_t s);
 
 // h[r] += sum_s P[s * split_stride + r * ld_p + c] (c < d), then
 // u[r] = h[r] * nw as activation planes and ss[r][c] = the sum of h[r]^2

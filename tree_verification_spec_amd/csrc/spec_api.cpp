@@ -172,6 +172,7 @@ struct spec_ctx {
   // lo plane, lo at + Rmax * width elements; fp32: one plane)
   void* u = nullptr;         // h * norm weight (QKV / in_proj / gate-up / LM head input)
   float* ss = nullptr;       // deferred RMSNorm of u: [Rmax][norm_nc] chunk sums of squares
+  float* rope_cs = nullptr;  // the pass rows' RoPE factors [Rmax][hd] (cos, then sin)
   int norm_nc = 0;
   void* act = nullptr;       // SwiGLU output (down input)
   void* attn_o = nullptr;    // attention output (O input)
@@ -375,6 +376,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
   const size_t o_u = p.take((size_t)R * d * 4);
   const int norm_nc = (d + kNormChunk - 1) / kNormChunk;
   const size_t o_ss = p.take((size_t)R * norm_nc * 4);
+  const size_t o_cs = p.take((size_t)R * hd * 4);
   const size_t o_act = p.take((size_t)R * F * 4);
   const size_t o_ao = p.take((size_t)R * nq * hd * 4);
   const size_t o_q = p.take((size_t)R * nq * hd * esz * 2);  // bf16: hi and lo planes
@@ -469,6 +471,7 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
     c->h = (float*)at(o_h);
     c->u = at(o_u);
     c->ss = (float*)at(o_ss);
+    c->rope_cs = (float*)at(o_cs);
     c->norm_nc = norm_nc;
     c->act = at(o_act);
     c->attn_o = at(o_ao);
@@ -703,7 +706,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
 
   const size_t u_lo = lo_off(c, d);
   HIP_TRY(launch_embed(bf, c->embed, c->d_rows, R, d, c->h, c->layers[0].n1, c->u, u_lo,
-                       c->ss, s));
+                       c->ss, c->cos_t, c->sin_t, hd, c->rope_cs, s));
   const RowNorm norm = row_norm(c);
 
   AttnArgs aa{};
@@ -740,7 +743,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       char* vc = c->vpool + (size_t)L.idx * c->kv_layer_elems * c->esz;
       const int ld = g.ntiles * 16;
       HIP_TRY(launch_rope_kv(bf, c->P, S, (size_t)c->Rmax * ld, c->d_rows, R, nq, nkv, hd,
-                             c->cos_t, c->sin_t, c->q, c->q_lo, kc, vc, ld, norm, s));
+                             c->rope_cs, c->q, c->q_lo, kc, vc, ld, norm, s));
       aa.kc = kc;
       aa.vc = vc;
       const TimePair ta = time_pair(c, 4);

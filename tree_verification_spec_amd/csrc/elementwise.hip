@@ -239,25 +239,30 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 // in flight; (2) the walk over the nodes, which is sequential, only forms the
 // states (LDS in, LDS out: every node's state for trees, the segment's for
 // chains); (3) the outputs, independent per (node, channel), take one thread
-// each and sum y over s in order.
+// each and sum y over s in order.  A node's states are stored channel by
+// channel with each channel's S states padded to S + 1 floats, so the
+// output phase's lanes (different nodes and channels, same s) fall in
+// different LDS banks.
 constexpr int kLrSeg = 32;
 template <int S, bool TREE, int NS>
 __global__ __launch_bounds__(256) void lr_fork_kernel(
     const float* proj, size_t sstride, int ld, const RowMeta* rows,
     const ReqMeta* reqs, int d, float* H, void* o, size_t olo, bool obf,
     float* save, bool commit_last, RowNorm norm) {
-  extern __shared__ float hs[];  // [max_rows][256] for trees
+  extern __shared__ float hs[];  // [max_rows][HSN] for trees
   constexpr int CPB = 256 / S;   // channels per block
+  constexpr int HSN = CPB * (S + 1);   // floats per node state (padded channels)
   constexpr int NV = 3 * CPB + 2 * S;  // staged values per row: x, a, z (CPB each), B, C
   __shared__ float sv[kLrSeg][NV];
   __shared__ float sg[kLrSeg][CPB];  // sigmoid(a)
   __shared__ float scs[kLrSeg];
   __shared__ int spar[kLrSeg];
-  __shared__ float hseg[TREE ? 1 : kLrSeg * 256];  // chains: the segment's states
+  __shared__ float hseg[TREE ? 1 : kLrSeg * HSN];  // chains: the segment's states
   const int r = blockIdx.y;
   const ReqMeta rm = reqs[r];
   const int s = threadIdx.x % S;
   const int lc = threadIdx.x / S;  // the lane's channel within the block
+  const int hsl = lc * (S + 1) + s;  // the lane's state within a node's states
   const int c = blockIdx.x * CPB + lc;
   const bool live = c < d;
   const int cc = live ? c : 0;
@@ -317,13 +322,13 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
       float hp;
       if (TREE) {
         const int pp = spar[j];
-        hp = (pp < 0) ? h0 : hs[pp * 256 + threadIdx.x];
+        hp = (pp < 0) ? h0 : hs[pp * HSN + hsl];
       } else {
         hp = hprev;
       }
       const float hi = __fadd_rn(__fmul_rn(sg[j][lc], hp), __fmul_rn(sv[j][3 * CPB + s], sv[j][lc]));
-      if (TREE) hs[i * 256 + threadIdx.x] = hi;
-      else hseg[j * 256 + threadIdx.x] = hi;
+      if (TREE) hs[i * HSN + hsl] = hi;
+      else hseg[j * HSN + hsl] = hi;
       hprev = hi;
     }
     __syncthreads();
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256) void lr_fork_kernel(
       const int ch = blockIdx.x * CPB + l;
       if (ch >= d) continue;
       const int row = rm.row0 + i0 + j;
-      const float* hrow = TREE ? &hs[(i0 + j) * 256 + l * S] : &hseg[j * 256 + l * S];
+      const float* hrow = TREE ? &hs[(i0 + j) * HSN + l * (S + 1)] : &hseg[j * HSN + l * (S + 1)];
       float y = 0.f;
 #pragma unroll 16
       for (int q = 0; q < S; ++q) y += __fmul_rn(hrow[q], sv[j][3 * CPB + S + q]);
@@ -539,7 +544,7 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
   constexpr int CPB = 256 / S;
   dim3 grid((d + CPB - 1) / CPB, n_req);
   if (tree) {
-    const size_t lds = (size_t)max_rows_per_req * 256 * sizeof(float);
+    const size_t lds = (size_t)max_rows_per_req * (256 / S) * (S + 1) * sizeof(float);
     hipError_t e = hipFuncSetAttribute((const void*)lr_fork_kernel<S, true, NS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);

@@ -409,12 +409,29 @@ __global__ __launch_bounds__(256) void lr_commit_kernel(
   float* hp = H + layer * H_layer_stride + (size_t)q.table * d * S + e;
   const float* proj = proj_all + layer * proj_layer_stride;
   float h = *hp;
-  for (int k = 0; k <= q.plen; ++k) {
-    const int node = (k == 0) ? 0 : q.nodes[k - 1];
-    const float* pr = proj + (size_t)(q.row0 + node) * ld;  // [x | a | B]
-    const float a = pr[d + c];
-    const float sig = 1.0f / (1.0f + expf(-a));
-    h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(pr[2 * d + s], pr[c]));
+  // the path's inputs are loaded 8 nodes at a time, ahead of the sequential
+  // recurrence over them
+  constexpr int B = 8;
+  for (int k0 = 0; k0 <= q.plen; k0 += B) {
+    float av[B], bv[B], xv[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int k = k0 + u;
+      if (k <= q.plen) {
+        const int node = (k == 0) ? 0 : q.nodes[k - 1];
+        const float* pr = proj + (size_t)(q.row0 + node) * ld;  // [x | a | B]
+        av[u] = pr[d + c];
+        bv[u] = pr[2 * d + s];
+        xv[u] = pr[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (k0 + u <= q.plen) {
+        const float sig = 1.0f / (1.0f + expf(-av[u]));
+        h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(bv[u], xv[u]));
+      }
+    }
   }
   *hp = h;
 }

@@ -525,12 +525,16 @@ int gemm_argmax_blocks(bool bf16, int N, int M) {
 }
 
 int gemm_splits(bool bf16, int K, int N, int M) {
-  // at most one workgroup per CU (the largest power-of-two split whose grid
-  // fits the 256 CUs) and at least 256 reduction indices per split
+  // at most one workgroup per CU: the largest split count (of those the
+  // consumers of the partials are built for) whose grid fits the 256 CUs,
+  // with whole K-steps and at least 256 reduction indices per split (5
+  // splits: 200 workgroups for the 40 column blocks of a 5120-wide matrix,
+  // where 4 leave 96 CUs idle)
   const Variant v = gemm_variant(bf16, N, M);
   const int nblk = N / (v.ntw * v.waves * 16);
   int S = 1;
-  while (2 * S * nblk <= 256 && K / (S * 2) >= 256 && (K / (S * 2)) % 32 == 0) S *= 2;
+  for (int c : {2, 4, 5, 8, 16, 32})
+    if (c * nblk <= 256 && K % (32 * c) == 0 && K / c >= 256) S = c;
   return S;
 }
 

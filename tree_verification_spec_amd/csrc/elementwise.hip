@@ -492,7 +492,7 @@ static hipError_t rope_t(const float* qkv, int S, size_t sstride, const RowMeta*
     rope_kv_kernel<T, SV><<<grid, thr, 0, s>>>(qkv, sstride, rows, nq, nkv, hd, cs,    \
                                                q_out, q_lo, kc, vc, ld, norm);         \
     break;
-    RO_CASE(1) RO_CASE(2) RO_CASE(4) RO_CASE(5) RO_CASE(8) RO_CASE(16) RO_CASE(32)
+    RO_CASE(1) RO_CASE(2) RO_CASE(4) RO_CASE(5) RO_CASE(6) RO_CASE(8) RO_CASE(16) RO_CASE(32)
 #undef RO_CASE
     default: return hipErrorInvalidValue;
   }
@@ -522,7 +522,7 @@ static hipError_t resid_t(const float* P, int S, size_t split_stride, int ld_p, 
     resid_reduce_kernel<SV, T><<<grid, 256, 0, s>>>(P, split_stride, ld_p, d, h, nw, \
                                                     u, u_lo, ss);                   \
     break;
-    RR_CASE(1) RR_CASE(2) RR_CASE(4) RR_CASE(5) RR_CASE(8) RR_CASE(16) RR_CASE(32)
+    RR_CASE(1) RR_CASE(2) RR_CASE(4) RR_CASE(5) RR_CASE(6) RR_CASE(8) RR_CASE(16) RR_CASE(32)
 #undef RR_CASE
     default: return hipErrorInvalidValue;
   }
@@ -588,7 +588,7 @@ static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
   case NV:                                                                             \
     return lr_fork_s<S, NV>(proj, sstride, ld, rows, reqs, n_req, d, H, o, olo, obf,    \
                             save, tree, commit_last, max_rows_per_req, norm, s);
-    NS_CASE(1) NS_CASE(2) NS_CASE(4) NS_CASE(5) NS_CASE(8) NS_CASE(16) NS_CASE(32)
+    NS_CASE(1) NS_CASE(2) NS_CASE(4) NS_CASE(5) NS_CASE(6) NS_CASE(8) NS_CASE(16) NS_CASE(32)
 #undef NS_CASE
     default: return hipErrorInvalidValue;
   }

@@ -70,7 +70,7 @@ struct GemmArgs {
   int32_t ncols;        // real output columns (<= ntiles * 16)
   int32_t row0;         // first row handled by this launch (set by launch_gemm)
   int32_t S;            // K splits (EPI_PART only; see gemm_splits)
-  int32_t KR;           // K per split (set by launch_gemm)
+  int32_t KR;           // K per split (set by launch_gemm; the last split may be shorter)
   float* P;             // EPI_PART: partials [S][P_ld][ntiles * 16]
   int32_t P_ld;
   void* Y;              // SWIGLU: activation planes [M, ldy] (lo at Y + ylo)

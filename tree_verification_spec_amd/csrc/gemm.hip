@@ -436,9 +436,10 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 }
 
 // Workgroup shapes: (tiles per wave, waves).  128 columns with one tile per
-// wave stream best when the rows are few (up to 40: the stacked-row limit); 256 columns with two tiles per
-// wave halve the LDS reads per MFMA and fill the CUs evenly when a
-// 128-column grid would leave a small second round; for narrow matrices,
+// wave stream best when the rows are few (up to 40: the stacked-row limit);
+// 256 columns with two tiles per wave halve the LDS reads per MFMA and fill
+// the CUs evenly when a 128-column grid would leave a small second round
+// (257-511 blocks of 128 columns: the 27B gate/up); for narrow matrices,
 // two tiles per wave on 4 waves keep 128 columns at up to 95 rows, and from
 // 96 rows (128-row launches: 8 row tiles) one tile per wave on 8 waves does
 // (two waves per SIMD instead of one; measured on the 8B shapes).

@@ -385,7 +385,7 @@ def main():
         # kernel and overhead factors need a kernel trace of the same run
         # shape: python -m tree_verification_spec_amd.costmodel)
         "cost_model": {
-            "row_tiles": costmodel.row_tiles(B * (K + 1)),
+            "rows": B * (K + 1),
             "types": {t: {"bytes": b, "flops": f,
                           "bound_us": round(1e6 * costmodel.lower_bound(b, f), 2)}
                       for t, (b, f) in res["types"].items()},

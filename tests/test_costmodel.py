@@ -50,18 +50,6 @@ def test_factor_identity():
     assert f["total_factor"] == pytest.approx(4300.0 / 1640.0)
 
 
-def test_row_tiles():
-    assert costmodel.row_tiles(1) == [1]          # stacked: 2 rows
-    assert costmodel.row_tiles(17) == [3]         # stacked: 34 rows
-    assert costmodel.row_tiles(32) == [4]
-    assert costmodel.row_tiles(17, bf16=False) == [2]
-    assert costmodel.row_tiles(33) == [3]
-    assert costmodel.row_tiles(65) == [5]
-    assert costmodel.row_tiles(96) == [8]
-    assert costmodel.row_tiles(128) == [8]
-    assert costmodel.row_tiles(288) == [2, 8]
-
-
 def test_type_bytes_match_closed_form_8b():
     """The 8B dense model's bytes per step written out: weights (36 layers of
     QKV, O, gate, up, down plus the LM head) and the KV of 2048 committed
@@ -88,29 +76,33 @@ def test_hybrid_state_bytes():
     assert tb["recurrent"][0] == 2 * 2 * n_lr * cfg["d_model"] * cfg["lr_state"] * 4
 
 
-def _row(name, t0, dt):
-    return {"Kernel_Name": name, "Start_Timestamp": str(t0), "End_Timestamp": str(t0 + dt)}
+def _row(name, t0, dt, grid_x=64):
+    return {"Kernel_Name": name, "Start_Timestamp": str(t0), "End_Timestamp": str(t0 + dt),
+            "Grid_Size_X": str(grid_x)}
 
 
 def test_steps_from_trace_splits_and_filters():
-    g2 = "void (anonymous namespace)::gemm_kernel<unsigned short, 2, 1, 8, 2, 8, 1, true>(GemmArgs)"
-    g1 = "void (anonymous namespace)::gemm_kernel<unsigned short, 1, 1, 8, 2, 8, 1, true>(GemmArgs)"
+    """Steps are found by the embedding launch's grid (256 threads per pass
+    row) and the path walk that ends a verify pass: an AR pass (1 row), a
+    prefill chunk (no walk) and the weight load are left out."""
+    g = "void (anonymous namespace)::gemm_kernel<unsigned short, 3, 1, 8, 2, 8, 1, true>(GemmArgs)"
     rows, t = [], 0
 
-    def add(name, dt):
+    def add(name, dt, grid_x=64):
         nonlocal t
-        rows.append(_row(name, t, dt))
+        rows.append(_row(name, t, dt, grid_x))
         t += dt + 500
 
-    for mt_name in (g1, g2, g2):           # an AR pass, then two verify steps
-        add("embed_kernel<unsigned short>(...)", 3000)
-        add(mt_name, 30000)
+    for n_rows, walk in ((1, True), (17, False), (17, True), (17, True)):
+        add("embed_kernel<unsigned short>(...)", 3000, 256 * n_rows)
+        add(g, 30000)
         add("attn_kernel<unsigned short, 128>(AttnArgs)", 12000)
         add("attn_combine_kernel<unsigned short, 128>(...)", 5000)
-        add("path_walk_kernel(...)", 6000)
+        if walk:
+            add("path_walk_kernel(...)", 6000)
         add("kv_compact_kernel(...)", 2000)
         add("w12_encode_kernel(...)", 9999)  # not part of a step
-    steps = costmodel.steps_from_trace(rows, [2])
+    steps = costmodel.steps_from_trace(rows, 17)
     assert len(steps) == 2
     for s in steps:
         assert s["gemm"] == 30.0 and s["attention"] == 17.0 and s["other"] == 11.0

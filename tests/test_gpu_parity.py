@@ -598,3 +598,122 @@ def test_two_level_steps_emit_ar_tokens():
     assert ties <= 3
     assert g / step > 1.5
     eng.close()
+
+
+# ------------------------------------- matches off the main branch, ties
+
+def _branch_trees(S, g, V, rng):
+    """Trees whose matching tokens sit on more than one branch (drafts,
+    draft parents with -1 = the root, and the accepted draft path the rule
+    gives when the target's greedy tokens are S[g], S[g+1], S[g+2]).
+    deep: two sibling copies of S[g]; the second one's branch reaches depth
+    3, the first one's stops at depth 2, so the walk must take the second
+    (non-main) branch.  equal: both branches reach depth 2; the lower node
+    index (on the second sibling's branch) wins."""
+    wrong = lambda t: int((t + 1 + rng.integers(0, V - 1)) % V)
+    a, b, c = int(S[g]), int(S[g + 1]), int(S[g + 2])
+    return {"deep": ([a, a, wrong(a), b, b, wrong(c), c], [-1, -1, -1, 1, 0, 4, 3], [1, 3, 6]),
+            "equal": ([a, a, b, b, wrong(c)], [-1, -1, 1, 0, 3], [1, 2])}
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa_bf16", "tiny_hybrid_bf16", "dense8b_l2"])
+def test_off_main_branch_accepted_and_compacted(name):
+    """The accepted path runs through a second sibling (deeper branch, then
+    equal depth with the lower index): the walk's choice, every row's logits
+    against the oracle's tree pass, and then chain steps whose logits
+    depend on the compacted KV cache and the committed recurrent state of
+    that branch, against the oracle's AR logits."""
+    from oracle import accept_path
+    cfg, W = _setup(name)
+    V = cfg["vocab"]
+    orc = oracle_for(cfg, W)
+    prompt = synth.prompt_tokens(V, 80, 61)
+    n = 40
+    S, L, M, _ = ar_greedy(orc, prompt, n)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=17)
+    first = eng.prefill(0, prompt)
+    assert first == S[0]
+    ost = orc.new_state()
+    orc.prefill(ost, prompt)
+    rng = np.random.default_rng(62)
+    g, worst, branch_steps = 1, 0.0, 0
+    for kind in ("deep", "equal", "deep"):
+        toks, par, want = _branch_trees(S, g, V, rng)[kind]
+        nodes = [int(S[g - 1])] + toks
+        npar = [-1] + [p + 1 for p in par]
+        ref = orc.forward(ost, nodes, npar)
+        opath, obonus = accept_path(nodes, npar, ref.argmax(axis=1))
+        paths, bonus, lg = eng.verify([0], [toks], [par], logits=True)
+        lg = lg.cpu().numpy()
+        for i in range(len(nodes)):
+            worst = max(worst, float(np.max(np.abs(lg[i] - ref[i]))) / logit_tol(cfg["dtype"], ref[i]))
+        got = [p + 1 for p in paths[0]]
+        assert got == opath, (kind, got, opath)
+        branch_steps += [p - 1 for p in opath] == want
+        pos = g + len(opath)            # the bonus position
+        root = int(bonus[0])
+        if root != obonus or obonus != int(S[pos]):
+            assert M[pos] < NEAR_TIE, (kind, root, obonus, int(S[pos]))
+            root = int(S[pos])
+        eng.commit([0], paths, [root])
+        for t in [int(S[g - 1])] + [toks[p] for p in paths[0]]:
+            orc.decode(ost, t)
+        g = pos + 1
+    assert branch_steps == 3, "the designed branches were not the accepted ones"
+    # chain steps after the branch commits
+    step = 0
+    while g < n - 10:
+        toks, par = synth.chain_drafts(S, g, 8, 0.7, V, 61, 0, step)
+        paths, bonus, lg = eng.verify([0], [toks], [par], logits=True)
+        lg = lg.cpu().numpy()
+        em = [int(toks[p]) for p in paths[0]] + [int(bonus[0])]
+        rows = [0] + [p + 1 for p in paths[0]]
+        n_ok = 0
+        while n_ok < len(em) and em[n_ok] == S[g + n_ok]:
+            n_ok += 1
+        for i in range(min(len(rows), n_ok + 1)):
+            worst = max(worst, float(np.max(np.abs(lg[rows[i]] - L[g + i]))) /
+                        logit_tol(cfg["dtype"], L[g + i]))
+        if n_ok < len(em):
+            assert M[g + n_ok] < NEAR_TIE, (g + n_ok, em[n_ok], S[g + n_ok])
+            keep = paths[0][:n_ok] if n_ok < len(paths[0]) else paths[0]
+            eng.commit([0], [keep], [int(S[g + len(keep)])])
+            g += len(keep) + 1
+        else:
+            eng.commit([0], paths, bonus)
+            g += len(em)
+        step += 1
+    _say(f"{name}: max logit error {worst:.3f} x tolerance")
+    assert worst <= 1.0
+    eng.close()
+
+
+def test_planted_argmax_ties_take_the_lowest_index():
+    """Exact ties planted in the LM head (a lower-index copy of a token's
+    row, once in the same column tile and once in another column block):
+    wherever the copied token would win, the lower index must be emitted,
+    bit-exactly, with no near-tie exemption."""
+    cfg, W0 = _setup("tiny_gqa")
+    V = cfg["vocab"]
+    prompt = synth.prompt_tokens(V, 64, 65)
+    S0, _, _, _ = ar_greedy(oracle_for(cfg, W0), prompt, 24)
+    t1 = next(int(t) for t in S0 if t % 16 != 0)
+    lm = W0["lm_head"].copy()
+    lm[t1 - 1] = lm[t1]          # same 16-column tile
+    S1, _, _, _ = ar_greedy(oracle_for(cfg, dict(W0, lm_head=lm)), prompt, 24)
+    t2 = next(int(t) for t in S1 if t >= 256 and abs(int(t) - t1) > 2
+              and t % 128 not in (t1, t1 - 1))
+    lm[t2 % 128] = lm[t2]        # the first column block
+    W = dict(W0, lm_head=lm)
+    orc = oracle_for(cfg, W)
+    S, L, M, _ = ar_greedy(orc, prompt, 48)
+    n_ties = int(np.sum(M == 0.0))
+    assert n_ties >= 2 and (t1 - 1 in S) and (t2 % 128 in S), (n_ties, t1, t2)
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=5)
+    w = dict(K=4, alpha=0.7)
+    rep = protocol_f(eng, cfg, orc, prompt, 48, w, "chain", cfg_index=65,
+                     oracle_ref=(S, L, M))
+    _say(rep, "exact ties in the reference:", n_ties)
+    assert rep.first_bad is None and rep.near_tie_mismatch == 0, rep
+    assert rep.max_logit_err <= 1.0
+    eng.close()

@@ -100,20 +100,6 @@ def type_bounds(specs, cfg, req_rows, req_ctx, fmt):
     }
 
 
-def row_tiles(total_rows, bf16=True):
-    """Row-tile counts of the GEMM launches of a pass of `total_rows` rows:
-    up to 32 rows of a bf16 model the hi and lo activation rows are stacked
-    (2 x rows); otherwise launches of at most 128 rows take 1..5 tiles, else
-    8."""
-    if bf16 and total_rows <= 32:
-        return [(2 * total_rows + 15) // 16]
-    out = set()
-    for r0 in range(0, total_rows, 128):
-        need = (min(128, total_rows - r0) + 15) // 16
-        out.add(need if need <= 5 else 8)
-    return sorted(out)
-
-
 def factors(measured_us, bound_us, wall_us):
     """Kernel factor = profiled step time / summed lower bounds; overhead
     factor = wall step time / profiled step time.  Their product is the
@@ -132,31 +118,32 @@ def factors(measured_us, bound_us, wall_us):
 
 # ------------------------------------------------------------ trace parsing
 
-def _gemm_mt(name):
-    m = re.search(r"gemm_kernel<[^,]+, (\d+),", name)
-    return int(m.group(1)) if m else None
+def _pass_rows(row):
+    """Rows of the pass an embedding launch belongs to: the embedding kernel
+    runs one 256-thread workgroup per row (and chunk of columns, in y)."""
+    return int(row.get("Grid_Size_X", 0)) // 256
 
 
-def steps_from_trace(rows, tiles):
+def steps_from_trace(rows, n_rows):
     """Split kernel-trace rows (sorted by start) into verify steps: from an
-    embedding launch to the next one, keeping steps whose GEMMs run at
-    exactly the row-tile counts `tiles` (this excludes prefill chunks and AR
-    passes).  Returns a list of {type: microseconds}."""
-    steps, cur = [], None
+    embedding launch to the next one, keeping the steps of exactly `n_rows`
+    rows that end in the accepted-path walk (this leaves out prefill chunks,
+    which have no walk, and passes of other sizes such as the AR run).
+    Returns a list of {type: microseconds}."""
+    steps, cur, cur_rows = [], None, 0
     for r in rows:
         n = r["Kernel_Name"]
         if "embed_kernel" in n:
             if cur is not None:
-                steps.append(cur)
-            cur = []
+                steps.append((cur_rows, cur))
+            cur, cur_rows = [], _pass_rows(r)
         if cur is not None and kernel_type(n) is not None:
             cur.append(r)
     if cur:
-        steps.append(cur)
+        steps.append((cur_rows, cur))
     out = []
-    for st in steps:
-        mts = {_gemm_mt(r["Kernel_Name"]) for r in st if "gemm_kernel" in r["Kernel_Name"]}
-        if mts != set(tiles):
+    for nr, st in steps:
+        if nr != n_rows or not any("path_walk_kernel" in r["Kernel_Name"] for r in st):
             continue
         per = collections.Counter()
         for r in st:
@@ -175,9 +162,9 @@ def report(trace_dir, bench):
         raise SystemExit(f"no kernel trace under {trace_dir}")
     rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Start_Timestamp"]))
     cm = bench["cost_model"]
-    steps = steps_from_trace(rows, cm["row_tiles"])
+    steps = steps_from_trace(rows, cm["rows"])
     if not steps:
-        raise SystemExit("no verify steps with the bench's row-tile count in the trace")
+        raise SystemExit("no verify steps with the bench's row count in the trace")
     measured = {t: statistics.mean(s.get(t, 0.0) for s in steps) for t in TYPES}
     bound = {t: cm["types"][t]["bound_us"] for t in TYPES}
     fac = factors(measured, bound, 1e3 * bench["ms_per_step"])

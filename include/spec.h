@@ -116,7 +116,11 @@ int32_t spec_create(const spec_config* cfg, void* d_workspace, size_t bytes,
  * patterns), `bytes` long, on the host (src_on_device = 0) or the device
  * (src_on_device = 1).  src is only borrowed for the call; the library
  * re-lays the tensor out once into its own tiled layout.  The call is
- * synchronous.  Errors: SPEC_E_INVAL for a bad id or size. */
+ * synchronous.  Errors: SPEC_E_INVAL for a bad id or size;
+ * SPEC_E_UNSUPPORTED with W12 storage when a 16 x 32 tile of the tensor
+ * holds more than 63 weights outside its rows' exponent windows (the
+ * tensor may be loaded again, e.g. after a change of weights; such a model
+ * loads in native storage). */
 int32_t spec_load_weights(spec_ctx* ctx, int32_t tensor_id, const void* src,
                           size_t bytes, int32_t src_on_device);
 

@@ -476,22 +476,78 @@ def test_w12_exceptions():
     _assert_same(*runs)
 
 
-def test_w12_tile_over_capacity_is_rejected():
-    """A tile with more than 7 weights outside its rows' exponent windows
-    does not fit W12: the load fails with SPEC_E_UNSUPPORTED and the same
-    weights load in native format."""
-    from tree_verification_spec_amd import SpecError, SPEC_E_UNSUPPORTED
+def _crowd(w, tile_row, kstep, n, rng, val=0):
+    """Set n weights of one 16 x 32 tile of w (bf16 bits) to `val` (0: an
+    exact zero, which W12 cannot hold in the window)."""
+    sel = rng.choice(512, n, replace=False)
+    w[tile_row * 16 + sel // 32, kstep * 32 + sel % 32] = val
+
+
+def test_w12_crowded_tiles_spill_to_overflow_blocks():
+    """Tiles with more exceptions than the 7-entry slot (8, 20 and 63, the
+    most a tile holds) keep the rest in their overflow blocks; every GEMM
+    shape that patches them (up to 32 rows: the compiler's loop; 36 and 48
+    rows: the assembly block) must give results bitwise equal to bf16
+    storage.  The crowded tiles sit in fused matrices (Wk inside QKV, the
+    up half of gate/up) and in plain ones (O, down, LM head)."""
     cfg, W0 = _setup("tiny_gqa_bf16")
     W = dict(W0)
-    n = [n for n, _, k in synth.tensor_specs(cfg) if k == "mat" and n != "embed"][1]
-    w = W[n].copy()
-    sel = np.random.default_rng(3).choice(512, 8, replace=False)
-    w[16 + sel // 32, 64 + sel % 32] = 0
-    W[n] = w
-    with pytest.raises(SpecError) as ei:
-        engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="w12")
-    assert ei.value.code == SPEC_E_UNSUPPORTED
-    engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="native").close()
+    rng = np.random.default_rng(57)
+    for name, plants in (("layers.0.wk", [(1, 2, 8), (3, 5, 63)]),
+                         ("layers.1.wu", [(0, 0, 20), (7, 3, 9)]),
+                         ("layers.0.wo", [(2, 1, 63)]),
+                         ("layers.1.wd", [(4, 9, 33)]),
+                         ("lm_head", [(5, 4, 40), (100, 15, 8)])):
+        w = W[name].copy()
+        for tr, kb, n in plants:
+            _crowd(w, tr, kb, n, rng)
+        W[name] = w
+    prompt = synth.prompt_tokens(cfg["vocab"], 60, 57)
+    for big in (35, 47):
+        runs = []
+        for fmt in ("native", "w12"):
+            eng = engine_for(cfg, W, max_ctx=512, max_nodes=48, weight_format=fmt)
+            runs.append(_run_steps(eng, cfg, prompt, 6, 57, big=big))
+            eng.close()
+        _assert_same(*runs)
+
+
+def test_w12_tile_over_capacity_is_rejected_and_retried():
+    """A tile with more exceptions than the slot and its overflow block hold
+    (64) does not fit W12: that load fails with SPEC_E_UNSUPPORTED, the
+    error does not stick to the matrix (a retry with fitting weights and
+    the fused partners load), and the results then equal bf16 storage."""
+    from tree_verification_spec_amd import SpecError, SPEC_E_UNSUPPORTED, Engine
+    import tree_verification_spec_amd._lib as L
+    import torch
+    cfg, W = _setup("tiny_gqa_bf16")
+    specs = synth.tensor_specs(cfg)
+    names = [n for n, _, _ in specs]
+    bad_id = names.index("layers.0.wq")
+    bad = W["layers.0.wq"].copy()
+    _crowd(bad, 2, 3, 64, np.random.default_rng(3))
+    eng = Engine(cfg, max_ctx=512, max_nodes=17, weight_format="w12")
+    dev = eng.device
+
+    def load(tid, a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                             else np.ascontiguousarray(a)).to(dev)
+        torch.cuda.synchronize(dev)
+        L.spec_load_weights(eng.ctx, tid, t.data_ptr(), a.nbytes, 1)
+
+    for tid, n in enumerate(names):
+        if tid == bad_id:
+            with pytest.raises(SpecError) as ei:
+                load(tid, bad)
+            assert ei.value.code == SPEC_E_UNSUPPORTED
+        load(tid, W[n])
+    prompt = synth.prompt_tokens(cfg["vocab"], 60, 58)
+    got = _run_steps(eng, cfg, prompt, 4, 58)
+    eng.close()
+    ref_eng = engine_for(cfg, W, max_ctx=512, max_nodes=17, weight_format="native")
+    ref = _run_steps(ref_eng, cfg, prompt, 4, 58)
+    ref_eng.close()
+    _assert_same(got, ref)
 
 
 # ------------------------------------------------ two-level verification

@@ -120,6 +120,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     }
   }
   const uint32_t wk = (uint32_t)a.wsk * TB;  // bytes between K-steps (host-checked)
+  // W12: the overflow blocks of crowded tiles (w12.h)
+  const uint32_t* ovf = W12 ? w12_overflow(a.W, (size_t)a.ntiles * (a.K / 32)) : nullptr;
 
   floatx4_t acc[NTW][MT];
 #pragma unroll
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     if constexpr (W12) {
       Frag<T> f;
       f.v = w12_decode(r, eb7[t]);
-      if constexpr (kOrdered) w12_patch_opaque(f.v, r, lane);
-      else w12_patch(f.v, r, lane);
+      if constexpr (kOrdered) w12_patch_opaque(f.v, r, lane, ovf);
+      else w12_patch(f.v, r, lane, ovf);
       return f;
     } else if constexpr (W8) {
       Frag<T> f;

@@ -222,15 +222,17 @@ hipError_t launch_relayout(bool bf16, const void* src, int nrows, int K,
 
 // W12 encoding (w12.h): eb[r] for the rows of a row-major bf16 slab
 // [nrows, K]; then the slab's tiles, placed like launch_relayout places
-// them (tile index tr * wsn + kb * wsk, 800 bytes each), and the rows'
+// them (tile index tr * wsn + kb * wsk, 800 bytes each, in a matrix of
+// dst_tiles tiles whose overflow blocks follow its tiles), and the rows'
 // bases at their destination rows of eb_dst; with dst8, also the 8-bit
 // view's tiles (512 bytes) at the same tile indices.  *err becomes nonzero
 // if a tile has more exceptions than W12 holds.
 hipError_t launch_w12_rowexp(const void* src, int nrows, int K, uint8_t* eb,
                              hipStream_t s);
 hipError_t launch_w12_encode(const void* src, int nrows, int K, const uint8_t* eb,
-                             uint8_t* eb_dst, void* dst, void* dst8, int dst_tile0,
-                             int tile_stride, int wsn, int wsk, int* err, hipStream_t s);
+                             uint8_t* eb_dst, void* dst, size_t dst_tiles, void* dst8,
+                             int dst_tile0, int tile_stride, int wsn, int wsk, int* err,
+                             hipStream_t s);
 
 // Widen a norm vector (bf16 bits or fp32) to fp32.
 hipError_t launch_to_f32(bool bf16, const void* src, int n, float* dst,

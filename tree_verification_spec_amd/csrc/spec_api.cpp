@@ -989,6 +989,8 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
     if (slab <= 0)
       return fail(c, SPEC_E_UNSUPPORTED, "tensor %d rows too long for staging", tensor_id);
     const WMat& m = *t.mat;
+    // the matrix's overflow flag reports this tensor's tiles only
+    if (c->w12) HIP_TRY(hipMemsetAsync(m.err, 0, sizeof(int), s));
     for (int r0 = 0; r0 < t.rows; r0 += slab) {
       const int nr = std::min(slab, t.rows - r0);
       const char* from = (const char*)src + (size_t)r0 * row_bytes;
@@ -999,7 +1001,8 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
       const int tile0 = t.tile0 + (r0 / 16) * t.tile_stride;
       if (c->w12) {
         HIP_TRY(launch_w12_rowexp(from, nr, t.cols, c->eb_tmp, s));
-        HIP_TRY(launch_w12_encode(from, nr, t.cols, c->eb_tmp, m.eb, t.dst, m.p8, tile0,
+        HIP_TRY(launch_w12_encode(from, nr, t.cols, c->eb_tmp, m.eb, t.dst,
+                                  (size_t)(m.n / 16) * (m.k / 32), m.p8, tile0,
                                   t.tile_stride, t.wsn, t.wsk, m.err, s));
       } else {
         HIP_TRY(launch_relayout(c->bf16, from, nr, t.cols, t.dst, tile0, t.tile_stride,
@@ -1014,7 +1017,7 @@ extern "C" int32_t spec_load_weights(spec_ctx* c, int32_t tensor_id,
       if (err)
         return fail(c, SPEC_E_UNSUPPORTED,
                     "tensor %d: a tile has more than %d weights outside the W12 exponent "
-                    "window; load these weights in native format", tensor_id, kW12MaxExc);
+                    "windows; load these weights in native format", tensor_id, kW12MaxExc);
     }
   }
   HIP_TRY(hipStreamSynchronize(s));

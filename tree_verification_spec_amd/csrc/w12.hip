@@ -6,7 +6,9 @@
 
 namespace {
 
-// eb[row] = max(0, largest exponent of the row - 15): one workgroup per row.
+// eb[row] = max(0, largest finite exponent of the row - 15): one workgroup
+// per row.  Non-finite weights (exponent code 255) are exceptions whatever
+// the window, so they do not move it; a row with no finite weight gets 0.
 __global__ __launch_bounds__(256) void w12_rowexp_kernel(const uint16_t* src, int K,
                                                          uint8_t* eb) {
   __shared__ uint32_t part[4];
@@ -14,7 +16,7 @@ __global__ __launch_bounds__(256) void w12_rowexp_kernel(const uint16_t* src, in
   uint32_t m = 0;
   for (int c = threadIdx.x; c < K; c += 256) {
     const uint32_t e = (r[c] >> 7) & 0xFFu;
-    m = e > m ? e : m;
+    m = (e != 255u && e > m) ? e : m;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -26,8 +28,6 @@ __global__ __launch_bounds__(256) void w12_rowexp_kernel(const uint16_t* src, in
   if (threadIdx.x == 0) {
     uint32_t t = part[0];
     for (int w = 1; w < 4; ++w) t = part[w] > t ? part[w] : t;
-    // an all-non-finite row keeps its window below the non-finite code
-    t = t == 255 ? 254 : t;
     eb[blockIdx.x] = (uint8_t)(t >= 15 ? t - 15 : 0);
   }
 }
@@ -36,12 +36,15 @@ __global__ __launch_bounds__(256) void w12_rowexp_kernel(const uint16_t* src, in
 // Source tile row nb becomes destination tile row dst_tile0 + nb *
 // tile_stride; tile (row tr, K-step kb) sits at tile index tr * wsn + kb *
 // wsk of the destination.  eb: the bases of the slab's rows; eb_dst gets
-// them at the destination rows.  *err is set when a tile has more
-// exceptions than its list holds.  dst8 (optional): the 8-bit view's tiles
-// at the same tile indices.
+// them at the destination rows.  A crowded tile (more than 7 exceptions)
+// spills the rest into its overflow block (ovf: the matrix's blocks,
+// w12.h); *err is set when a tile has more exceptions than the slot and its
+// block hold.  dst8 (optional): the 8-bit view's tiles at the same tile
+// indices.
 __global__ __launch_bounds__(64) void w12_encode_kernel(
     const uint16_t* src, int K, const uint8_t* eb, uint8_t* eb_dst, uint8_t* dst,
-    uint8_t* dst8, int dst_tile0, int tile_stride, int wsn, int wsk, int* err) {
+    uint32_t* ovf, uint8_t* dst8, int dst_tile0, int tile_stride, int wsn, int wsk,
+    int* err) {
   __shared__ uint32_t slot[8];
   const int ksteps = K / 32;
   const int tile = blockIdx.x;
@@ -98,16 +101,25 @@ __global__ __launch_bounds__(64) void w12_encode_kernel(
   if (dst8)
     *reinterpret_cast<uint2*>(dst8 + tidx * kW8TileBytes + lane * 8) = make_uint2(v8lo, v8hi);
   __syncthreads();
-  if (total > (uint32_t)kW12MaxExc) {
+  if (total > (uint32_t)kW12MaxExc || (total > (uint32_t)kW12SlotExc && tidx >= (1u << 24))) {
     if (lane == 0) atomicOr(err, 1);
     return;
   }
+  // entries k < 7 go to the slot, the rest to the tile's overflow block
+  uint32_t* ob = ovf + tidx * kW12OvfDwords;
   uint32_t k = first;
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    if ((excmask >> e) & 1u)
-      slot[1 + k++] = ((uint32_t)lane << 19) | ((uint32_t)e << 16) | w[e];
-  if (lane == 0) slot[0] = total;
+    if ((excmask >> e) & 1u) {
+      const uint32_t ent = ((uint32_t)lane << 19) | ((uint32_t)e << 16) | w[e];
+      if (k < (uint32_t)kW12SlotExc) slot[1 + k] = ent;
+      else ob[k - kW12SlotExc] = ent;
+      ++k;
+    }
+  if (lane == 0)
+    slot[0] = total <= (uint32_t)kW12SlotExc
+                  ? total
+                  : (1u << 31) | ((total - kW12SlotExc) << 24) | (uint32_t)tidx;
   __syncthreads();
   uint32_t* td = reinterpret_cast<uint32_t*>(t);
   td[lane * 3 + 0] = da;
@@ -126,13 +138,15 @@ hipError_t launch_w12_rowexp(const void* src, int nrows, int K, uint8_t* eb,
 }
 
 hipError_t launch_w12_encode(const void* src, int nrows, int K, const uint8_t* eb,
-                             uint8_t* eb_dst, void* dst, void* dst8, int dst_tile0,
-                             int tile_stride, int wsn, int wsk, int* err, hipStream_t s) {
+                             uint8_t* eb_dst, void* dst, size_t dst_tiles, void* dst8,
+                             int dst_tile0, int tile_stride, int wsn, int wsk, int* err,
+                             hipStream_t s) {
   if (nrows % 16 || K % 32) return hipErrorInvalidValue;
   const unsigned tiles = (unsigned)(nrows / 16) * (K / 32);
   if (tiles == 0) return hipSuccess;
+  uint32_t* ovf = const_cast<uint32_t*>(w12_overflow(dst, dst_tiles));
   w12_encode_kernel<<<tiles, 64, 0, s>>>((const uint16_t*)src, K, eb, eb_dst,
-                                         (uint8_t*)dst, (uint8_t*)dst8, dst_tile0,
+                                         (uint8_t*)dst, ovf, (uint8_t*)dst8, dst_tile0,
                                          tile_stride, wsn, wsk, err);
   return hipGetLastError();
 }

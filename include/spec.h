@@ -227,6 +227,22 @@ int32_t spec_use_graphs(spec_ctx* ctx, int32_t enable);
 int32_t spec_timing_enable(spec_ctx* ctx, int32_t cls);
 int32_t spec_timing_read(spec_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Diagnostics (no context): the device's achievable streaming-read
+ * bandwidth, measured by a kernel with the weight GEMMs' access pattern.
+ * Enqueues one read of `bytes` of device memory at d_src on hip_stream:
+ * grid workgroups of `waves` (1..16) wavefronts; each wavefront reads whole
+ * 1 KB blocks, 16 bytes per lane, keeping `depth` (4, 8, 12 or 16) block
+ * loads in flight; pattern 0: each wavefront reads its own contiguous
+ * range, pattern 1: all wavefronts sweep the buffer together (block
+ * k * grid * waves + wavefront).  d_sink: device memory of grid * waves
+ * uint32 that receives a checksum per wavefront.  bytes must be a multiple
+ * of 1024 * grid * waves.  The caller times the enqueued kernel (events on
+ * the same stream).  SPEC_E_INVAL on bad arguments, SPEC_E_HIP if the
+ * launch fails. */
+int32_t spec_probe_read_bandwidth(const void* d_src, size_t bytes, int32_t grid,
+                                  int32_t waves, int32_t depth, int32_t pattern,
+                                  uint32_t* d_sink, void* hip_stream);
+
 /* Destroy the context (the workspace stays the caller's). */
 void spec_destroy(spec_ctx* ctx);
 

@@ -773,3 +773,52 @@ def test_planted_argmax_ties_take_the_lowest_index():
     assert rep.first_bad is None and rep.near_tie_mismatch == 0, rep
     assert rep.max_logit_err <= 1.0
     eng.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_hybrid", "tiny_hybrid_bf16"])
+def test_recurrent_walk_deep_trees_and_mixed_passes(name):
+    """The recurrent layers walk trees depth-first with the root path's
+    states in registers: a 16-deep stack when every node of the pass is at
+    most 16 deep, a 64-deep one otherwise.  Cases: a tree 30 deep (a spine
+    with side branches), a pass mixing that tree with a 24-long chain, a
+    pass mixing a shallow tree with a 20-long chain (deep class because of
+    the chain), and a shallow tree alone; every row's logits against the
+    oracle's tree pass from the same committed state."""
+    cfg, W = _setup(name)
+    V = cfg["vocab"]
+    orc = oracle_for(cfg, W)
+    eng = engine_for(cfg, W, max_requests=2, max_ctx=512, max_nodes=40, max_rows=80)
+    rng = np.random.default_rng(71)
+    ost, roots = [], []
+    for r in range(2):
+        prompt = synth.prompt_tokens(V, 40, 70 + r)
+        roots.append(eng.prefill(r, prompt))
+        st = orc.new_state()
+        orc.prefill(st, prompt)
+        ost.append(st)
+    # drafts: parents (-1 = the root)
+    spine = list(range(-1, 29))                       # 30 drafts, depth 30
+    deep = spine + [2, 2, 9, 31, 19, 20, 33]          # side branches at depths 4, 11, 21
+    shallow = [-1, -1, 0, 0, 1, 2, 3, 3, 4, -1, 9]    # depth <= 4
+    chain = lambda k: list(range(-1, k - 1))
+    cases = [[(0, deep)], [(0, deep), (1, chain(24))], [(0, shallow), (1, chain(20))],
+             [(0, shallow)]]
+    worst = 0.0
+    for case in cases:
+        reqs = [r for r, _ in case]
+        par = [np.array(p, np.int32) for _, p in case]
+        toks = [rng.integers(0, V, len(p)).astype(np.int32) for p in par]
+        paths, bonus, lg = eng.verify(reqs, toks, par, logits=True)
+        lg = lg.cpu().numpy()
+        row = 0
+        for k, r in enumerate(reqs):
+            nodes = np.concatenate([[roots[r]], toks[k]])
+            npar = np.concatenate([[-1], par[k] + 1])
+            ref = orc.forward(ost[r], nodes, npar)
+            for i in range(len(nodes)):
+                err = float(np.max(np.abs(lg[row + i] - ref[i])))
+                worst = max(worst, err / logit_tol(cfg["dtype"], ref[i]))
+            row += len(nodes)
+    _say(f"{name}: max logit error {worst:.3f} x tolerance")
+    assert worst <= 1.0
+    eng.close()

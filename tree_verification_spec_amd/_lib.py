@@ -32,6 +32,7 @@ EXPORTS = [
     "spec_timing_read",
     "spec_destroy", "spec_last_error",
     "spec_acceptance_update", "spec_plan_drafts", "spec_verify_lowp", "spec_debug_flags",
+    "spec_probe_read_bandwidth",
 ]
 
 
@@ -94,6 +95,8 @@ def lib():
                                              P(c_float)]),
         "spec_plan_drafts": (c_int32, [c_int32, P(c_float), P(c_float), i32p, c_int32,
                                        c_float, c_int32, i32p]),
+        "spec_probe_read_bandwidth": (c_int32, [c_void_p, c_size_t, c_int32, c_int32,
+                                                c_int32, c_int32, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -246,3 +249,11 @@ def spec_destroy(ctx):
 def spec_last_error(ctx):
     s = lib().spec_last_error(ctx)
     return s.decode() if s else ""
+
+
+def spec_probe_read_bandwidth(d_src, nbytes, grid, waves, depth, pattern, d_sink, stream):
+    """Enqueue the streaming-read probe on `stream` (device pointers as ints)."""
+    rc = lib().spec_probe_read_bandwidth(c_void_p(d_src), nbytes, grid, waves, depth,
+                                         pattern, c_void_p(d_sink), c_void_p(stream))
+    if rc != SPEC_OK:
+        raise SpecError(rc, "spec_probe_read_bandwidth: invalid arguments or launch failure")

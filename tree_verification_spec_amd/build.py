@@ -16,7 +16,8 @@ OUT = os.path.join(HERE, "libspec.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["spec_api.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "w12.hip", "plan.cpp"]
+SOURCES = ["spec_api.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "w12.hip", "plan.cpp",
+           "probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

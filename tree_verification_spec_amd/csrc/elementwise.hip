@@ -3,6 +3,11 @@
 #include "common.h"
 #include "kernels.h"
 
+// Products and sums are rounded separately, as written (RoPE and the
+// recurrence follow the oracle's operation order; a fused multiply-add would
+// round differently).
+#pragma clang fp contract(off)
+
 namespace {
 
 // ------------------------------------------------------- block reduction
@@ -90,8 +95,8 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
     if (head < nq + nkv) {
       const float c = cs[(size_t)row * hd + i];
       const float s = cs[(size_t)row * hd + half + i];
-      const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
-      const float y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+      const float y1 = ((x1 * c) - (x2 * s));
+      const float y2 = ((x2 * c) + (x1 * s));
       if (head < nq) {
         const size_t base = ((size_t)row * nq + head) * hd;
         store_act(q_out, q_lo, base + i, y1);
@@ -229,137 +234,255 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 }
 
 // ------------------------------------------------------ recurrence (verify)
-// Lanes: S consecutive lanes own one channel c (lane % S = state index s).
-// For each node in index order (parents first):
+// A lane owns 4 states (s = 4 l + k, k = 0..3) of one channel c; the S / 4
+// lanes of a channel are adjacent, and a 256-thread workgroup covers
+// CPB = 1024 / S channels.  For node i
 //   H_i = sigmoid(a_i[c]) * H_parent + B_i[s] * x_i[c]   (no FMA contraction)
-//   y_i[c] = sum_s H_i[s] * C_i[s]; o_i[c] = y_i * silu(z_i[c])
-// Per segment of up to kLrSeg rows: (1) the block's x, a, z, every row's B
-// and C (sums of the in_proj split partials, in order, times the row's norm
-// scale), sigmoid(a) and the rows' parents are staged in LDS with all loads
-// in flight; (2) the walk over the nodes, which is sequential, only forms the
-// states (LDS in, LDS out: every node's state for trees, the segment's for
-// chains); (3) the outputs, independent per (node, channel), take one thread
-// each and sum y over s in order.  A node's states are stored channel by
-// channel with each channel's S states padded to S + 1 floats, so the
-// output phase's lanes (different nodes and channels, same s) fall in
-// different LDS banks.
-constexpr int kLrSeg = 32;
-template <int S, bool TREE, int NS>
-__global__ __launch_bounds__(256) void lr_fork_kernel(
-    const float* proj, size_t sstride, int ld, const RowMeta* rows,
-    const ReqMeta* reqs, int d, float* H, void* o, size_t olo, bool obf,
-    float* save, bool commit_last, RowNorm norm) {
-  extern __shared__ float hs[];  // [max_rows][HSN] for trees
-  constexpr int CPB = 256 / S;   // channels per block
-  constexpr int HSN = CPB * (S + 1);   // floats per node state (padded channels)
-  constexpr int NV = 3 * CPB + 2 * S;  // staged values per row: x, a, z (CPB each), B, C
-  __shared__ float sv[kLrSeg][NV];
-  __shared__ float sg[kLrSeg][CPB];  // sigmoid(a)
-  __shared__ float scs[kLrSeg];
-  __shared__ int spar[kLrSeg];
-  __shared__ float hseg[TREE ? 1 : kLrSeg * HSN];  // chains: the segment's states
+//   y_i[c] = sum_s H_i[s] * C_i[s];  o_i[c] = y_i * silu(z_i[c])
+// where the root's parent state is the committed H_0.  The inputs of the
+// staged rows (x, a, silu(z) of the workgroup's channels and every row's B
+// and C, summed over the in_proj split partials in order and scaled by the
+// row's norm scale) and sigmoid(a) are staged in LDS once per workgroup with
+// all loads in flight; the walk then reads LDS only for inputs.  A chain
+// keeps its running states in registers.  A tree is walked in depth-first
+// order, in which the ancestors of the node being visited are exactly the
+// last nodes visited at each smaller depth, so each lane keeps the states of
+// the current root path in registers indexed by depth (16-entry vectors with
+// a uniform index: indirect register moves, no copies).  Trees deeper than
+// that recompute every node's state along its root path from H_0.  Either
+// way a node's state comes from its own root path only, by the operations of
+// a sequential walk along that path, in the same order.  y is summed over a
+// lane's 4 states, then over the channel's lanes in one fixed order, the
+// same for every pass.
+constexpr int kLrTreeRows = 72;  // rows of a tree pass staged at once (max_nodes <= 65)
+constexpr int kLrSeg = 64;       // rows per staged segment of a chain pass
+constexpr int kLrStack = 16;     // root-path states kept in registers (depths 0..15)
+constexpr int kLrThreads = 256;
+
+typedef float lr_stack_t __attribute__((ext_vector_type(kLrStack)));
+
+// Sum of v over each aligned segment of L lanes (L = 4, 8 or 16); the sum is
+// exact in the segment's last lane.  L = 16: DPP row shifts (a row is 16
+// lanes); smaller segments: a butterfly of lane exchanges.
+template <int L>
+__device__ __forceinline__ float seg_sum(float v) {
+  if constexpr (L == 16) {
+#define LR_DPP_ADD(ctrl)                                                                 \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, true))
+    LR_DPP_ADD(0x111);  // row_shr:1
+    LR_DPP_ADD(0x112);  // row_shr:2
+    LR_DPP_ADD(0x114);  // row_shr:4
+    LR_DPP_ADD(0x118);  // row_shr:8: lane 15 of each row holds the row's sum
+#undef LR_DPP_ADD
+  } else {
+#pragma unroll
+    for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  }
+  return v;
+}
+
+// MODE 0: chains; 1: trees of depth <= kLrStack (register stack); 2: deeper trees
+template <int S, int MODE, int NS>
+__global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
+    const float* __restrict__ proj, size_t sstride, int ld, const RowMeta* __restrict__ rows,
+    const ReqMeta* __restrict__ reqs, int d, float* __restrict__ H, void* o, size_t olo,
+    bool obf, float* save, bool commit_last, RowNorm norm) {
+  static_assert(S == 16 || S == 32 || S == 64, "state width");
+  constexpr bool TREE = MODE > 0;
+  constexpr int LPC = S / 4;                 // lanes per channel
+  constexpr int CPB = kLrThreads / LPC;      // channels per workgroup
+  constexpr int NV = 3 * CPB + 2 * S;        // staged per row: x, a, silu(z) (CPB each), B, C
+  constexpr int ROWS = TREE ? kLrTreeRows : kLrSeg;
+  __shared__ __align__(16) float sv[ROWS][NV];
+  __shared__ float sg[ROWS][CPB];            // sigmoid(a)
+  __shared__ float scs[ROWS];
+  __shared__ int sord[ROWS], sdep[ROWS], spar[ROWS];
   const int r = blockIdx.y;
   const ReqMeta rm = reqs[r];
-  const int s = threadIdx.x % S;
-  const int lc = threadIdx.x / S;  // the lane's channel within the block
-  const int hsl = lc * (S + 1) + s;  // the lane's state within a node's states
+  const int l = threadIdx.x % LPC;           // the lane's place in its channel
+  const int lc = threadIdx.x / LPC;          // the lane's channel within the workgroup
   const int c = blockIdx.x * CPB + lc;
   const bool live = c < d;
   const int cc = live ? c : 0;
-  float* H0 = H + ((size_t)rm.table * d + cc) * S + s;
-  const float h0 = *H0;
-  float hprev = h0;
-  for (int i0 = 0; i0 < rm.nrows; i0 += kLrSeg) {
-    const int n = min(kLrSeg, rm.nrows - i0);
+  float* H0 = H + ((size_t)rm.table * d + cc) * S + 4 * l;
+  const float4 h0 = *reinterpret_cast<const float4*>(H0);
+  float hp0 = h0.x, hp1 = h0.y, hp2 = h0.z, hp3 = h0.w;  // chains: the running states
+  lr_stack_t st0 = {}, st1 = {}, st2 = {}, st3 = {};  // trees: root-path states by depth
+  for (int i0 = 0; i0 < rm.nrows; i0 += ROWS) {
+    const int n = min(ROWS, rm.nrows - i0);
     __syncthreads();  // the previous segment's values are no longer read
     if ((int)threadIdx.x < n) {
       scs[threadIdx.x] = row_scale(norm, rm.row0 + i0 + threadIdx.x);
-      if (TREE) spar[threadIdx.x] = rows[rm.row0 + i0 + threadIdx.x].parent;
-    }
-    __syncthreads();
-    // (1) staging: U values per thread are loaded before any is stored
-    constexpr int U = NS >= 16 ? 1 : 16 / NS;
-    auto src = [&](int e) {
-      const int j = e / NV, k = e % NV;
-      int col;
-      if (k < 3 * CPB) {
-        const int ch = blockIdx.x * CPB + k % CPB;
-        col = (k / CPB) * d + (ch < d ? ch : 0);  // x, a or z
-      } else {
-        col = 3 * d + (k - 3 * CPB);  // B then C
-      }
-      return proj + (size_t)(rm.row0 + i0 + j) * ld + col;
-    };
-    for (int e0 = threadIdx.x; e0 < n * NV; e0 += 256 * U) {
-      float t[U][NS];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * 256;
-        if (e < n * NV) {
-          const float* p = src(e);
-#pragma unroll
-          for (int q = 0; q < NS; ++q) t[u][q] = p[q * sstride];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * 256;
-        if (e < n * NV) {
-          float v = 0.f;
-#pragma unroll
-          for (int q = 0; q < NS; ++q) v += t[u][q];
-          const int j = e / NV, k = e % NV;
-          v *= scs[j];
-          sv[j][k] = v;
-          if (k >= CPB && k < 2 * CPB) sg[j][k - CPB] = 1.0f / (1.0f + expf(-v));
-        }
-      }
-    }
-    __syncthreads();
-    // (2) the walk: states only
-    for (int j = 0; j < n; ++j) {
-      const int i = i0 + j;
-      float hp;
       if (TREE) {
-        const int pp = spar[j];
-        hp = (pp < 0) ? h0 : hs[pp * HSN + hsl];
-      } else {
-        hp = hprev;
+        const RowMeta m = rows[rm.row0 + threadIdx.x];
+        sord[threadIdx.x] = m.order;
+        sdep[threadIdx.x] = m.pos - rm.nctx;
+        spar[threadIdx.x] = m.parent;
       }
-      const float hi = __fadd_rn(__fmul_rn(sg[j][lc], hp), __fmul_rn(sv[j][3 * CPB + s], sv[j][lc]));
-      if (TREE) hs[i * HSN + hsl] = hi;
-      else hseg[j * HSN + hsl] = hi;
-      hprev = hi;
     }
     __syncthreads();
-    // (3) outputs: one thread per (node, channel)
-    for (int e = threadIdx.x; e < n * CPB; e += 256) {
-      const int j = e / CPB, l = e % CPB;
-      const int ch = blockIdx.x * CPB + l;
-      if (ch >= d) continue;
-      const int row = rm.row0 + i0 + j;
-      const float* hrow = TREE ? &hs[(i0 + j) * HSN + l * (S + 1)] : &hseg[j * HSN + l * (S + 1)];
-      float y = 0.f;
-#pragma unroll 16
-      for (int q = 0; q < S; ++q) y += __fmul_rn(hrow[q], sv[j][3 * CPB + S + q]);
-      const float z = sv[j][2 * CPB + l];
-      const float ov = y * (z / (1.0f + expf(-z)));
-      const size_t oi = (size_t)row * d + ch;
-      if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
-      else store_act((float*)o, (float*)o + olo, oi, ov);
-      if (save) {
-        save[(size_t)row * (2 * d + S) + ch] = sv[j][l];
-        save[(size_t)row * (2 * d + S) + d + ch] = sv[j][CPB + l];
+    // staging in units of 4 consecutive values (x, a, z of 4 channels, or 4
+    // of B or C): every unit's NS partials of a batch are loaded before any
+    // is summed
+    constexpr int NU = NV / 4;                 // units per row
+    constexpr int XU = CPB / 4;                // units of each of x, a, z
+    constexpr int UB = NS >= 8 ? 2 : 12 / NS;  // units per thread in a batch
+    for (int e0 = threadIdx.x; e0 < n * NU; e0 += kLrThreads * UB) {
+      float4 t[UB][NS];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int e = e0 + u * kLrThreads;
+        if (e < n * NU) {
+          const int j = e / NU, k = e % NU;
+          int col;
+          if (k < 3 * XU) {
+            const int ch = min(blockIdx.x * CPB + (k % XU) * 4, d - 4);
+            col = (k / XU) * d + ch;  // x, a or z of 4 channels
+          } else {
+            col = 3 * d + (k - 3 * XU) * 4;  // B then C
+          }
+          const float* p = proj + (size_t)(rm.row0 + i0 + j) * ld + col;
+#pragma unroll
+          for (int q = 0; q < NS; ++q) t[u][q] = *reinterpret_cast<const float4*>(p + q * sstride);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int e = e0 + u * kLrThreads;
+        if (e < n * NU) {
+          const int j = e / NU, k = e % NU;
+          float4 v = t[u][0];
+#pragma unroll
+          for (int q = 1; q < NS; ++q) {
+            v.x += t[u][q].x;
+            v.y += t[u][q].y;
+            v.z += t[u][q].z;
+            v.w += t[u][q].w;
+          }
+          const float sc = scs[j];
+          v.x *= sc;
+          v.y *= sc;
+          v.z *= sc;
+          v.w *= sc;
+          if (k >= XU && k < 2 * XU) {  // a: also sigmoid(a)
+            const int q0 = (k - XU) * 4;
+            sg[j][q0] = 1.0f / (1.0f + expf(-v.x));
+            sg[j][q0 + 1] = 1.0f / (1.0f + expf(-v.y));
+            sg[j][q0 + 2] = 1.0f / (1.0f + expf(-v.z));
+            sg[j][q0 + 3] = 1.0f / (1.0f + expf(-v.w));
+          } else if (k >= 2 * XU && k < 3 * XU) {  // z: stored as silu(z)
+            v.x = v.x / (1.0f + expf(-v.x));
+            v.y = v.y / (1.0f + expf(-v.y));
+            v.z = v.z / (1.0f + expf(-v.z));
+            v.w = v.w / (1.0f + expf(-v.w));
+          }
+          *reinterpret_cast<float4*>(&sv[j][4 * k]) = v;
+        }
       }
     }
-    if (save && blockIdx.x == 0) {
-      for (int e = threadIdx.x; e < n * S; e += 256) {
-        const int j = e / S, q = e % S;
-        save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sv[j][3 * CPB + q];
+    __syncthreads();
+    // The walk.  Each wave keeps the walk order (node, depth) in two lanes'
+    // registers (position k in lane k % 64 of word k / 64) so a node index is
+    // a register read, not an LDS round trip, and the next node's inputs are
+    // read from LDS while the current node computes.
+    int ordw0 = 0, ordw1 = 0;  // node | depth << 8 of positions lane, 64 + lane
+    {
+      const int lane = threadIdx.x & 63;
+      auto at = [&](int q) {
+        if (q >= n) return 0;
+        return TREE ? (sord[q] | (sdep[sord[q]] << 8)) : q;
+      };
+      ordw0 = at(lane);
+      ordw1 = at(64 + lane);
+    }
+    auto pos = [&](int k) {  // (node, depth) at walk position k (uniform)
+      const int w = __builtin_amdgcn_readlane(k < 64 ? ordw0 : ordw1, k & 63);
+      return w;
+    };
+    struct In {
+      float g, x, sz;
+      float4 b, c;
+    };
+    auto fetch = [&](int j) {
+      In v;
+      v.g = sg[j][lc];
+      v.x = sv[j][lc];
+      v.sz = sv[j][2 * CPB + lc];
+      v.b = *reinterpret_cast<const float4*>(&sv[j][3 * CPB + 4 * l]);
+      v.c = *reinterpret_cast<const float4*>(&sv[j][3 * CPB + S + 4 * l]);
+      return v;
+    };
+    // one node's update from its parent's states
+    auto step = [&](const In& v, float& a0, float& a1, float& a2, float& a3) {
+      a0 = ((v.g * a0) + (v.b.x * v.x));
+      a1 = ((v.g * a1) + (v.b.y * v.x));
+      a2 = ((v.g * a2) + (v.b.z * v.x));
+      a3 = ((v.g * a3) + (v.b.w * v.x));
+    };
+    int wk = n > 0 ? pos(0) : 0;
+    In cur = fetch(wk & 0xFF);
+    for (int k = 0; k < n; ++k) {
+      const int j = wk & 0xFF, dj = wk >> 8;
+      In nxt = cur;
+      if (k + 1 < n) {
+        wk = pos(k + 1);
+        nxt = fetch(wk & 0xFF);
       }
+      float a0, a1, a2, a3;
+      if constexpr (MODE == 1) {
+        if (dj == 0) {
+          a0 = h0.x; a1 = h0.y; a2 = h0.z; a3 = h0.w;
+        } else {
+          a0 = st0[dj - 1]; a1 = st1[dj - 1]; a2 = st2[dj - 1]; a3 = st3[dj - 1];
+        }
+        step(cur, a0, a1, a2, a3);
+        if (dj < kLrStack) {  // a node of depth kLrStack is a leaf
+          st0[dj] = a0; st1[dj] = a1; st2[dj] = a2; st3[dj] = a3;
+        }
+      } else if constexpr (MODE == 2) {
+        // recompute along the root path of j, root first
+        a0 = h0.x; a1 = h0.y; a2 = h0.z; a3 = h0.w;
+        for (int t = 0; t <= dj; ++t) {
+          int v = j;  // the ancestor of j at depth t
+          for (int u = dj; u > t; --u) v = spar[v];
+          step(fetch(__builtin_amdgcn_readfirstlane(v)), a0, a1, a2, a3);
+        }
+      } else {
+        a0 = hp0; a1 = hp1; a2 = hp2; a3 = hp3;
+        step(cur, a0, a1, a2, a3);
+        hp0 = a0; hp1 = a1; hp2 = a2; hp3 = a3;
+      }
+      float y = (a0 * cur.c.x);
+      y = (y + (a1 * cur.c.y));
+      y = (y + (a2 * cur.c.z));
+      y = (y + (a3 * cur.c.w));
+      y = seg_sum<LPC>(y);
+      if (l == LPC - 1 && live) {
+        const float ov = y * cur.sz;
+        const size_t oi = (size_t)(rm.row0 + i0 + j) * d + c;
+        if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
+        else store_act((float*)o, (float*)o + olo, oi, ov);
+      }
+      cur = nxt;
+    }
+    if (save) {  // [x | a | B] of every row, for the commit
+      for (int e = threadIdx.x; e < n * CPB; e += kLrThreads) {
+        const int j = e / CPB, q = e % CPB;
+        const int ch = blockIdx.x * CPB + q;
+        if (ch >= d) continue;
+        const size_t row = (size_t)(rm.row0 + i0 + j);
+        save[row * (2 * d + S) + ch] = sv[j][q];
+        save[row * (2 * d + S) + d + ch] = sv[j][CPB + q];
+      }
+      if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e < n * S; e += kLrThreads) {
+          const int j = e / S, q = e % S;
+          save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sv[j][3 * CPB + q];
+        }
     }
   }
-  if (commit_last && live) *H0 = hprev;
+  if (commit_last && live)
+    *reinterpret_cast<float4*>(H0) = make_float4(hp0, hp1, hp2, hp3);
 }
 
 // ----------------------------------------------------------- KV compaction
@@ -429,7 +552,7 @@ __global__ __launch_bounds__(256) void lr_commit_kernel(
     for (int u = 0; u < B; ++u) {
       if (k0 + u <= q.plen) {
         const float sig = 1.0f / (1.0f + expf(-av[u]));
-        h = __fadd_rn(__fmul_rn(sig, h), __fmul_rn(bv[u], xv[u]));
+        h = ((sig * h) + (bv[u] * xv[u]));
       }
     }
   }
@@ -555,32 +678,28 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
 template <int S, int NS>
 static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                             const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                            float* H, void* o, size_t olo, bool obf, float* save, bool tree,
+                            float* H, void* o, size_t olo, bool obf, float* save, int tree_depth,
                             bool commit_last, int max_rows_per_req, RowNorm norm,
                             hipStream_t s) {
-  constexpr int CPB = 256 / S;
+  constexpr int CPB = kLrThreads / (S / 4);
+  if (tree_depth > 0 && max_rows_per_req > kLrTreeRows) return hipErrorInvalidValue;
   dim3 grid((d + CPB - 1) / CPB, n_req);
-  if (tree) {
-    const size_t lds = (size_t)max_rows_per_req * (256 / S) * (S + 1) * sizeof(float);
-    hipError_t e = hipFuncSetAttribute((const void*)lr_fork_kernel<S, true, NS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    lr_fork_kernel<S, true, NS><<<grid, 256, lds, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                       H, o, olo, obf, save, commit_last,
-                                                       norm);
-  } else {
-    lr_fork_kernel<S, false, NS><<<grid, 256, 0, s>>>(proj, sstride, ld, rows, reqs, d,
-                                                      H, o, olo, obf, save, commit_last,
-                                                      norm);
-  }
+  if (tree_depth > kLrStack)
+    lr_fork_kernel<S, 2, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
+                                                         olo, obf, save, commit_last, norm);
+  else if (tree_depth > 0)
+    lr_fork_kernel<S, 1, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
+                                                         olo, obf, save, commit_last, norm);
+  else
+    lr_fork_kernel<S, 0, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
+                                                         olo, obf, save, commit_last, norm);
   return hipGetLastError();
 }
 
 template <int S>
 static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
                              const RowMeta* rows, const ReqMeta* reqs, int n_req, int d,
-                             float* H, void* o, size_t olo, bool obf, float* save, bool tree,
+                             float* H, void* o, size_t olo, bool obf, float* save, int tree,
                              bool commit_last, int max_rows_per_req, RowNorm norm,
                              hipStream_t s) {
   switch (NS) {
@@ -597,13 +716,13 @@ static hipError_t lr_fork_ns(int NS, const float* proj, size_t sstride, int ld,
 hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_stride,
                           int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
                           int d, int S, float* H, void* o, size_t o_lo, float* save,
-                          bool any_tree, bool commit_last, int max_rows_per_req,
+                          int tree_depth, bool commit_last, int max_rows_per_req,
                           RowNorm norm, hipStream_t s) {
   switch (S) {
 #define LR_CASE(SV)                                                                    \
   case SV:                                                                             \
     return lr_fork_ns<SV>(NS, proj, split_stride, ld, rows, reqs, n_req, d, H, o, o_lo, \
-                          bf16, save, any_tree, commit_last, max_rows_per_req, norm, s);
+                          bf16, save, tree_depth, commit_last, max_rows_per_req, norm, s);
     LR_CASE(16)
     LR_CASE(32)
     LR_CASE(64)

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   static_assert(!STK || kBf, "stacked rows need bf16 activation planes");
   constexpr int NPL = (kBf && !STK) ? 2 : 1;  // staged planes
   constexpr int TROWS = MT * 16;
-  constexpr int COLS = WAVES * NTW * 16;  // output columns of the workgroup
+  constexpr int COLS = WAVES * NTW * 16;  // most output columns of a workgroup
   constexpr int NTHR = WAVES * 64;
   constexpr int KC = STK ? kChunkStk : ChunkK<MT>::value;
   constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
@@ -76,9 +76,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // scalar base plus a per-lane offset)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int nblk = a.ntiles / (WAVES * NTW);
-  const int nb = blockIdx.x % nblk;
-  const int sk = blockIdx.x / nblk;
+  // Column partition: the launch has a.ncb workgroups per K split; workgroup
+  // nb owns a balanced share [t0, t1) of the matrix's tiles, in whole
+  // granules of a.gt tiles (a wave's NTW tiles; gate/up pairs stay in one
+  // workgroup), one wave per NTW tiles.  Waves beyond the share shadow the
+  // last live wave's tiles (their loads hit L2) and store nothing.
+  const int nb = blockIdx.x % a.ncb;
+  const int sk = blockIdx.x / a.ncb;
+  const int ug = a.ntiles / a.gt;
+  const int t0 = a.gt * (int)(((int64_t)nb * ug) / a.ncb);
+  const int t1 = a.gt * (int)(((int64_t)(nb + 1) * ug) / a.ncb);
+  const int live_waves = (t1 - t0) / NTW;
+  const bool live = wave < live_waves;
+  const int tbase = t0 + (live ? wave : live_waves - 1) * NTW;  // the wave's first tile
   const int kbeg = sk * a.KR;
   const int kend = min(a.K, kbeg + a.KR);
 
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   uint32_t eb7[NTW];  // W12: the row's base exponent, (eb | eb << 16) << 7
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
-    const size_t tr = (size_t)((nb * WAVES + wave) * NTW + t);  // tile row
+    const size_t tr = (size_t)(tbase + t);  // tile row
     wrs[t] = weight_rsrc(reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * TB);
     if constexpr (W12 || W8) {
       const uint32_t e = a.eb[tr * 16 + r16];
@@ -318,7 +328,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   }
 
   // ---- results
-  const int col0 = nb * COLS;
+  const int col0 = t0 * 16;             // first output column of the workgroup
+  const int width = (t1 - t0) * 16;     // its output columns (<= COLS)
   const int N = a.ntiles * 16;
   if (EPI == EPI_PART && !STK) {
     float* P = a.P + (size_t)sk * a.P_ld * N;
@@ -327,8 +338,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = a.row0 + mt * 16 + r16;
-        if (m < a.M) {
-          float* pp = P + (size_t)m * N + col0 + (wave * NTW + t) * 16 + 4 * g;
+        if (m < a.M && live) {
+          float* pp = P + (size_t)m * N + (tbase + t) * 16 + 4 * g;
           *reinterpret_cast<float4*>(pp) =
               make_float4(acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
         }
@@ -360,8 +371,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 
   if (EPI == EPI_PART) {  // stacked rows only
     float* P = a.P + (size_t)sk * a.P_ld * N;
-    for (int e = threadIdx.x; e < orows * COLS; e += NTHR) {
-      const int row = e / COLS, col = e % COLS;
+    for (int e = threadIdx.x; e < orows * width; e += NTHR) {
+      const int row = e / width, col = e % width;
       P[(size_t)(a.row0 + row) * N + col0 + col] = val(row, col);
     }
     return;
@@ -369,23 +380,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 
   if (EPI == EPI_SWIGLU) {
     // tile pair p: columns [p*32, p*32+16) gate, [p*32+16, p*32+32) up
-    constexpr int OUTS = COLS / 2;
-    for (int e = threadIdx.x; e < orows * OUTS; e += NTHR) {
-      const int row = e / OUTS, j = e % OUTS;
+    const int outs = width / 2;
+    for (int e = threadIdx.x; e < orows * outs; e += NTHR) {
+      const int row = e / outs, j = e % outs;
       const int m = a.row0 + row;
       if (m >= a.M) continue;
       const int p = j >> 4, c = j & 15;
       const float gv = val(row, p * 32 + c) * rsc[row];
       const float uv = val(row, p * 32 + 16 + c) * rsc[row];
       T* Yh = reinterpret_cast<T*>(a.Y);
-      store_act(Yh, Yh + a.ylo, (size_t)m * a.ldy + nb * OUTS + j,
+      store_act(Yh, Yh + a.ylo, (size_t)m * a.ldy + col0 / 2 + j,
                 gv / (1.0f + expf(-gv)) * uv);
     }
     return;
   }
   // EPI_ARGMAX
-  for (int e = threadIdx.x; e < orows * COLS; e += NTHR) {
-    const int row = e / COLS, col = e % COLS;
+  for (int e = threadIdx.x; e < orows * width; e += NTHR) {
+    const int row = e / width, col = e % width;
     const int m = a.row0 + row;
     if (m >= a.M) continue;
     const int n = col0 + col;
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     if (m >= a.M) continue;
     float best = -INFINITY;
     int bi = col0;
-    for (int col = 0; col < COLS; ++col) {
+    for (int col = 0; col < width; ++col) {
       const float v = tile[row * LDT + col];
       if (v > best) { best = v; bi = col0 + col; }  // NaN never wins
     }
@@ -426,35 +437,44 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int nblk = a.ntiles / (WAVES * NTW);
   if (s.t0 || s.t1) {
     GemmArgs arg = a;
     void* args[] = {&arg};
-    return hipExtLaunchKernel((const void*)k, dim3(nblk * a.S), dim3(WAVES * 64), args, lds,
+    return hipExtLaunchKernel((const void*)k, dim3(a.ncb * a.S), dim3(WAVES * 64), args, lds,
                               s.s, s.t0, s.t1, 0);
   }
-  k<<<nblk * a.S, WAVES * 64, lds, s.s>>>(a);
+  k<<<a.ncb * a.S, WAVES * 64, lds, s.s>>>(a);
   return hipGetLastError();
 }
 
-// Workgroup shapes: (tiles per wave, waves).  128 columns with one tile per
-// wave stream best when the rows are few (up to 40: the stacked-row limit);
-// 256 columns with two tiles per wave halve the LDS reads per MFMA and fill
-// the CUs evenly when a 128-column grid would leave a small second round
-// (257-511 blocks of 128 columns: the 27B gate/up); for narrow matrices,
-// two tiles per wave on 4 waves keep 128 columns at up to 95 rows, and from
-// 96 rows (128-row launches: 8 row tiles) one tile per wave on 8 waves does
-// (two waves per SIMD instead of one; measured on the 8B shapes).
+// Workgroup shapes: (tiles per wave, waves, workgroups per K split).  Up to
+// 40 rows (bf16: the stacked-row limit) one tile per wave: up to 2048 tiles
+// 8-tile workgroups (one round on 256 CUs); 2049-2560 tiles (the 27B gate/up,
+// 2176 tiles) 256 workgroups of 8-10 tiles on 10 waves (a balanced share
+// of every CU: 64.8 us against 77.5 us for 136 workgroups of two tiles per
+// wave on 8 waves, and 96 us for 272 workgroups of 8, which leave a second
+// round); more tiles (the LM heads) rounds of 256 workgroups of at most 8
+// tiles (27B LM head 252 us against 268 us for 1188 workgroups of 8).  From
+// 41 rows: 256 columns with two tiles per wave for wide matrices (>= 128
+// blocks of 256 columns: the LM head; half the LDS reads per MFMA), two
+// tiles per wave on 4 waves for narrow ones up to 95 rows, and one tile per
+// wave on 8 waves from 96 rows (128-row launches: 8 row tiles; two waves
+// per SIMD instead of one).  Measured on the 8B and 27B shapes, weights
+// streamed from HBM.
 struct Variant {
-  int ntw, waves;
+  int ntw, waves, ncb;
 };
 
 Variant gemm_variant(bool bf16, int N, int M) {
-  if (!bf16) return {1, 8};
-  const int b128 = N / 128, b256 = N / 256;
-  if (M <= 40) return (b128 > 256 && b128 < 512) ? Variant{2, 8} : Variant{1, 8};
-  if (b256 >= 128) return Variant{2, 8};
-  return M >= 96 ? Variant{1, 8} : Variant{2, 4};
+  const int nt = N / 16;
+  if (!bf16) return {1, 8, nt / 8};
+  if (M <= 40) {
+    if (nt <= 2048) return {1, 8, nt / 8};
+    if (nt <= 2560) return {1, 10, 256};
+    return {1, 8, 256 * ((nt + 2047) / 2048)};
+  }
+  if (N / 256 >= 128) return {2, 8, nt / 16};
+  return M >= 96 ? Variant{1, 8, nt / 8} : Variant{2, 4, nt / 8};
 }
 
 template <typename T, int EPI, int NTW, int WAVES, int D, int WF>
@@ -469,17 +489,17 @@ hipError_t launch_mt(int mt, const GemmArgs& a, const LaunchCtx& s) {
   }
 }
 
-// stacked hi / lo rows (bf16, one tile per wave, 8 waves): mt = row tiles of
-// the 2 * rows stacked rows (1..5)
-template <typename T, int EPI, int WF>
+// stacked hi / lo rows (bf16, one tile per wave, 8 or 10 waves): mt = row
+// tiles of the 2 * rows stacked rows (1..5)
+template <typename T, int EPI, int WF, int WAVES>
 hipError_t launch_stk(int mt, const GemmArgs& a, const LaunchCtx& s) {
   if constexpr (sizeof(T) == 2) {
     switch (mt) {
-      case 1: return launch_one<T, 1, 1, 8, EPI, kD, WF, true>(a, s);
-      case 2: return launch_one<T, 2, 1, 8, EPI, kD, WF, true>(a, s);
-      case 3: return launch_one<T, 3, 1, 8, EPI, kD, WF, true>(a, s);
-      case 4: return launch_one<T, 4, 1, 8, EPI, kD, WF, true>(a, s);
-      case 5: return launch_one<T, 5, 1, 8, EPI, kD, WF, true>(a, s);
+      case 1: return launch_one<T, 1, 1, WAVES, EPI, kD, WF, true>(a, s);
+      case 2: return launch_one<T, 2, 1, WAVES, EPI, kD, WF, true>(a, s);
+      case 3: return launch_one<T, 3, 1, WAVES, EPI, kD, WF, true>(a, s);
+      case 4: return launch_one<T, 4, 1, WAVES, EPI, kD, WF, true>(a, s);
+      case 5: return launch_one<T, 5, 1, WAVES, EPI, kD, WF, true>(a, s);
       default: break;
     }
   }
@@ -489,7 +509,8 @@ hipError_t launch_stk(int mt, const GemmArgs& a, const LaunchCtx& s) {
 template <typename T, int EPI, int WF>
 hipError_t launch_var(Variant v, int mt, bool stk, const GemmArgs& a,
                       const LaunchCtx& s) {
-  if (stk) return launch_stk<T, EPI, WF>(mt, a, s);
+  if (stk) return v.waves == 10 ? launch_stk<T, EPI, WF, 10>(mt, a, s)
+                                : launch_stk<T, EPI, WF, 8>(mt, a, s);
   if constexpr (sizeof(T) == 2) {
     if (v.ntw == 2 && v.waves == 8) return launch_mt<T, EPI, 2, 8, kD, WF>(mt, a, s);
     if (v.ntw == 2 && v.waves == 4) return launch_mt<T, EPI, 2, 4, kD, WF>(mt, a, s);
@@ -522,10 +543,7 @@ hipError_t launch_typed(int epi, Variant v, const GemmArgs& a, int mt, bool stk,
 
 int gemm_pad_cols() { return 256; }
 
-int gemm_argmax_blocks(bool bf16, int N, int M) {
-  const Variant v = gemm_variant(bf16, N, M);
-  return N / (v.ntw * v.waves * 16);
-}
+int gemm_argmax_blocks(bool bf16, int N, int M) { return gemm_variant(bf16, N, M).ncb; }
 
 // K per split: whole K-steps, the last split possibly shorter.
 static int split_k(int K, int S) { return (K / 32 + S - 1) / S * 32; }
@@ -541,8 +559,7 @@ int gemm_splits(bool bf16, int K, int N, int M) {
   // already fill three quarters, the extra partials cost more than the
   // extra workgroups gain: the 8B QKV at 5 splits instead of 4 measured 1%
   // slower per step)
-  const Variant v = gemm_variant(bf16, N, M);
-  const int nblk = N / (v.ntw * v.waves * 16);
+  const int nblk = gemm_variant(bf16, N, M).ncb;
   int S = 1;
   for (int c : {2, 4, 5, 8, 16, 32})
     if (c * nblk <= 256 && K % (32 * c) == 0 && K / c >= 256) S = c;
@@ -570,13 +587,18 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s,
   // one workgroup shape for all row chunks (the ARGMAX block layout and the
   // partial sums must not depend on the chunk)
   const Variant v = gemm_variant(bf16, a.ntiles * 16, a.M);
-  if (a.ntiles % (v.ntw * v.waves)) return hipErrorInvalidValue;
-  if (epi == EPI_ARGMAX) a.nblocks = a.ntiles / (v.ntw * v.waves);
+  a.ncb = v.ncb;
+  a.gt = (epi == EPI_SWIGLU && v.ntw == 1) ? 2 : v.ntw;
+  // every workgroup's share of whole granules must fit its waves
+  if (a.ntiles % a.gt || a.ncb < 1 || a.ncb > a.ntiles / a.gt ||
+      ((a.ntiles / a.gt + a.ncb - 1) / a.ncb) * a.gt > v.waves * v.ntw)
+    return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX) a.nblocks = a.ncb;
   for (int r0 = 0; r0 < a.M; r0 += 128) {
     const int rows = (a.M - r0 < 128) ? a.M - r0 : 128;
     // up to 40 rows (bf16, one tile per wave) the lo rows are stacked under
     // the hi rows
-    const bool stk = bf16 && v.ntw == 1 && v.waves == 8 && 2 * rows <= 80;
+    const bool stk = bf16 && v.ntw == 1 && (v.waves == 8 || v.waves == 10) && 2 * rows <= 80;
     const int need = ((stk ? 2 * rows : rows) + 15) / 16;
     const int mt = stk ? need : (need <= 5 ? need : 8);
     a.row0 = r0;

@@ -14,7 +14,8 @@ struct RowMeta {
   int32_t node;    // node index inside the request (0 = root)
   int32_t parent;  // node-local parent index, -1 for the root
   int32_t keys;    // keys of its request in this pass (committed + pass rows)
-  int32_t pad;
+  int32_t order;   // the node visited k-th in a depth-first (pre-order) walk of
+                   // the request's tree, for the row at node index k
 };
 
 // One request of a forward pass.
@@ -69,6 +70,8 @@ struct GemmArgs {
   int32_t ntiles;       // 16-column tiles of W (a multiple of 8)
   int32_t ncols;        // real output columns (<= ntiles * 16)
   int32_t row0;         // first row handled by this launch (set by launch_gemm)
+  int32_t ncb;          // workgroups per K split, each a balanced share of the tiles
+  int32_t gt;           // tiles per share granule (set by launch_gemm)
   int32_t S;            // K splits (EPI_PART only; see gemm_splits)
   int32_t KR;           // K per split (set by launch_gemm; the last split may be shorter)
   float* P;             // EPI_PART: partials [S][P_ld][ntiles * 16]
@@ -176,17 +179,20 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
                             int32_t* res, hipStream_t s);
 
 // Gated diagonal recurrence over the pass's nodes for one recurrent layer.
-// proj: in_proj output as S split partials (stride split_stride floats), each
-// [R, ld] = [x | a | z | B | C | pad], scaled by the row's norm scale (norm)
-// after the partials are summed; H: committed states
+// proj: in_proj output as NS split partials (stride split_stride floats),
+// each [R, ld] = [x | a | z | B | C | pad], scaled by the row's norm scale
+// (norm) after the partials are summed; H: committed states
 // [max_requests][d][S]; o: [R, d] activation planes (lo at o + o_lo).
 // save (or NULL): per row [x | a | B] ([R, 2d + S]) for the commit.  With
 // commit_last (chain passes only) the state of each request's last row is
-// written back to H.
+// written back to H.  tree_depth: 0 for a pass of chains, else at least the
+// deepest node's depth (<= 64) of the pass's trees, which are walked in the
+// rows' depth-first order (RowMeta.order) with depth = pos - the request's
+// nctx.
 hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_stride,
                           int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
                           int d, int S, float* H, void* o, size_t o_lo, float* save,
-                          bool any_tree, bool commit_last, int max_rows_per_req,
+                          int tree_depth, bool commit_last, int max_rows_per_req,
                           RowNorm norm, hipStream_t s);
 
 struct CommitReq {

@@ -387,7 +387,10 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
                                      (size_t)kMaxSplitsPrefill * R);
   const size_t o_po = p.take(split_rows * nq * hd * 4);
   const size_t o_pml = p.take(split_rows * nq * 8);
-  const size_t o_amp = p.take((size_t)R * (npad(V) / 128) * 8);  // <= 128-column blocks
+  int am_blocks = 1;  // LM-head argmax partials per row: the most column blocks of any row count
+  for (int m = 1; m <= R; ++m)
+    am_blocks = std::max(am_blocks, gemm_argmax_blocks(esz == 2, npad(V), m));
+  const size_t o_amp = p.take((size_t)R * am_blocks * 8);
   const size_t o_amax = p.take((size_t)R * 4);
   const size_t o_res = p.take((size_t)cfg.max_requests * (2 + kMaxPath) * 4);
   // GEMM split partials: the largest S x N over the model's matrices, for
@@ -620,7 +623,8 @@ int gemm_part(spec_ctx* c, GemmArgs& g, hipError_t* err, TimePair tp = {}) {
 // that two passes with equal parameters can replay one captured graph.
 struct Pass {
   int R = 0, n_req = 0;
-  bool any_tree = false, prefill = false;
+  int tree_depth = 0;  // 0: chains only; else the recurrent walk's depth class (16 or 64)
+  bool prefill = false;
   int lm_row0 = 0, lm_rows = 0;
   float* d_logits = nullptr;
   int split = 0, max_splits = 0, tpw = 0, max_qgroups = 0, max_rows_req = 0;
@@ -633,14 +637,14 @@ struct Pass {
 // d_anc.  lm_row0 / lm_rows: rows that go through the LM head (argmax into
 // amax).  prefill: chain pass whose final recurrent states are committed.
 int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& keys_per_req,
-              const std::vector<int>& rows_per_req, bool any_tree, int lm_row0, int lm_rows,
+              const std::vector<int>& rows_per_req, int tree_depth, int lm_row0, int lm_rows,
               float* d_logits, bool prefill) {
   const spec_config& cfg = c->cfg;
   const int nq = c->nq, nkv = c->nkv;
   const int G = nq / nkv;
   P.R = R;
   P.n_req = n_req;
-  P.any_tree = any_tree;
+  P.tree_depth = tree_depth;
   P.prefill = prefill;
   P.lm_row0 = lm_row0;
   P.lm_rows = lm_rows;
@@ -689,7 +693,7 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
 }
 
 std::vector<int64_t> Pass::key(const spec_ctx* c) const {
-  return {R, n_req, any_tree, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
+  return {R, n_req, tree_depth, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
           split, max_splits, tpw, max_qgroups, max_rows_req, walk, lowp, c->fault_tok,
           (int64_t)__builtin_bit_cast(uint32_t, c->fault_bias), c->fault_after};
 }
@@ -701,7 +705,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
   hipStream_t s = c->stream;
   const int d = c->d, hd = c->hd, nq = c->nq, nkv = c->nkv, F = c->F;
   const int R = P.R, n_req = P.n_req, max_rows_req = P.max_rows_req;
-  const bool any_tree = P.any_tree, prefill = P.prefill;
+  const bool prefill = P.prefill;
   hipError_t e = hipSuccess;
 
   const size_t u_lo = lo_off(c, d);
@@ -763,7 +767,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       float* H = c->H + (size_t)L.idx * c->H_layer;
       float* save = prefill ? nullptr : c->lrsave + (size_t)L.idx * c->lrsave_layer;
       HIP_TRY(launch_lr_fork(bf, c->P, S, (size_t)c->Rmax * ld, ld, c->d_rows, c->d_reqs,
-                             n_req, d, c->S, H, c->lr_o, lo_off(c, d), save, any_tree,
+                             n_req, d, c->S, H, c->lr_o, lo_off(c, d), save, P.tree_depth,
                              prefill, max_rows_req, norm, s));
       GemmArgs o = gemm_args(c, L.wout, c->lr_o, d, R, d, d);
       const int So = gemm_part(c, o, &e);
@@ -857,10 +861,10 @@ int run_pass(spec_ctx* c, const Pass& P) {
 }
 
 int forward(spec_ctx* c, int R, int n_req, const std::vector<int>& keys_per_req,
-            const std::vector<int>& rows_per_req, bool any_tree, int lm_row0, int lm_rows,
+            const std::vector<int>& rows_per_req, int tree_depth, int lm_row0, int lm_rows,
             float* d_logits, bool prefill, bool walk, bool lowp = false) {
   Pass P;
-  const int rc = plan_pass(c, P, R, n_req, keys_per_req, rows_per_req, any_tree, lm_row0,
+  const int rc = plan_pass(c, P, R, n_req, keys_per_req, rows_per_req, tree_depth, lm_row0,
                            lm_rows, d_logits, prefill);
   if (rc) return rc;
   P.walk = walk;
@@ -1083,6 +1087,7 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
       r.node = i;
       r.parent = i - 1;
       r.keys = done + C;
+      r.order = i;
     }
     ReqMeta& m = h_reqs(c)[0];
     m = ReqMeta{0, C, done, req, 0, 1, 1, c->table_only ? -1 : rq.page0};
@@ -1092,7 +1097,7 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
       return undo(fail(c, SPEC_E_HIP, "metadata upload failed"));
     }
     const bool last = done + C == n;
-    rc = forward(c, C, 1, {done + C}, {C}, false, C - 1, last ? 1 : 0,
+    rc = forward(c, C, 1, {done + C}, {C}, 0, C - 1, last ? 1 : 0,
                  last ? d_logits_opt : nullptr, true, false);
     if (rc) return undo(rc);
     done += C;
@@ -1155,6 +1160,7 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
   lv.valid = true;
   std::vector<int> keys(n_req), nrows(n_req);
   bool any_tree = false;
+  int max_depth = 0;  // deepest node of the pass (chains included)
   int row = 0, off = 0;
   for (int r = 0; r < n_req; ++r) {
     const Req& rq = c->reqs[req[r]];
@@ -1178,7 +1184,26 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
       for (int w = 0; w < words; ++w) a[w] = p < 0 ? 0 : anc[(size_t)(row + p) * words + w];
       a[i >> 6] |= 1ull << (i & 63);
     }
+    // depth-first (pre-order) walk of the tree, children in index order:
+    // the recurrent layers visit the nodes in this order
+    {
+      std::vector<int> kids_start(K + 2, 0), kids;
+      for (int i = 1; i <= K; ++i) ++kids_start[par[i] + 1];
+      for (int i = 0; i <= K; ++i) kids_start[i + 1] += kids_start[i];
+      kids.assign(K > 0 ? K : 1, 0);
+      std::vector<int> fill(kids_start.begin(), kids_start.end() - 1);
+      for (int i = 1; i <= K; ++i) kids[fill[par[i]]++] = i;
+      std::vector<int> stack{0};
+      int k = 0;
+      while (!stack.empty()) {
+        const int v = stack.back();
+        stack.pop_back();
+        rows[row + k++].order = v;
+        for (int e = kids_start[v + 1] - 1; e >= kids_start[v]; --e) stack.push_back(kids[e]);
+      }
+    }
     if (!chain) any_tree = true;
+    for (int i = 0; i <= K; ++i) max_depth = std::max(max_depth, dep[i]);
     rm[r] = ReqMeta{row, K + 1, rq.n, req[r], row * words, words, chain ? 1 : 0,
                     c->table_only ? -1 : rq.page0};
     keys[r] = rq.n + K + 1;
@@ -1193,7 +1218,12 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
   }
   HIP_TRY(hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
                          c->stream));
-  rc = forward(c, R, n_req, keys, nrows, any_tree, 0, R, d_logits_opt, false, true, lowp);
+  // the recurrent walk of a pass with a tree walks every request as a tree
+  // (a chain is a tree); its depth class: a 16-entry register stack unless a
+  // node of the pass is deeper (one class per pass keeps the captured graphs
+  // few)
+  const int depth_class = !any_tree ? 0 : max_depth <= 16 ? 16 : 64;
+  rc = forward(c, R, n_req, keys, nrows, depth_class, 0, R, d_logits_opt, false, true, lowp);
   if (rc) return rc;
   const int max_path = kMaxPath;
   HIP_TRY(hipMemcpyAsync(c->h_res, c->res, (size_t)n_req * (2 + max_path) * 4,

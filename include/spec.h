@@ -243,6 +243,20 @@ int32_t spec_probe_read_bandwidth(const void* d_src, size_t bytes, int32_t grid,
                                   int32_t waves, int32_t depth, int32_t pattern,
                                   uint32_t* d_sink, void* hip_stream);
 
+/* The same read for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the per-wavefront checksums go to a scratch array held by the library
+ * (256 KB per device, kept until the process ends), and d_checksum (device
+ * memory, one uint32, the caller's) receives their XOR, which equals the
+ * XOR of the d_sink words spec_probe_read_bandwidth writes for the same
+ * arguments.  Allocates nothing.  grid * waves must be at most 65536
+ * (SPEC_E_INVAL beyond, and for the same bad arguments as above).  Calls
+ * that overlap on one GPU share its scratch array and race; serialize them
+ * (one stream, or events).  SPEC_E_HIP if the launch fails. */
+int32_t spec_probe_read_bandwidth_noalloc(const void* d_src, size_t bytes, int32_t grid,
+                                          int32_t waves, int32_t depth, int32_t pattern,
+                                          uint32_t* d_checksum, void* hip_stream);
+
 /* Destroy the context (the workspace stays the caller's). */
 void spec_destroy(spec_ctx* ctx);
 

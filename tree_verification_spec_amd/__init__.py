@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     spec_load_weights, spec_prefill, spec_verify, spec_commit, spec_release,
     spec_request_state, spec_force_root, spec_set_fault, spec_timing_enable, spec_timing_read,
     spec_destroy, spec_last_error, spec_acceptance_update, spec_plan_drafts,
-    spec_probe_read_bandwidth,
+    spec_probe_read_bandwidth, spec_probe_read_bandwidth_noalloc,
     EXPORTS, LIB_PATH, lib,
     SPEC_DTYPE_BF16, SPEC_DTYPE_FP32, SPEC_LAYER_ATTN, SPEC_LAYER_LR,
     SPEC_E_INVAL, SPEC_E_STATE, SPEC_E_CAPACITY, SPEC_E_HIP,

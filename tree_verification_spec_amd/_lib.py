@@ -32,7 +32,7 @@ EXPORTS = [
     "spec_timing_read",
     "spec_destroy", "spec_last_error",
     "spec_acceptance_update", "spec_plan_drafts", "spec_verify_lowp", "spec_debug_flags",
-    "spec_probe_read_bandwidth",
+    "spec_probe_read_bandwidth", "spec_probe_read_bandwidth_noalloc",
 ]
 
 
@@ -97,6 +97,8 @@ def lib():
                                        c_float, c_int32, i32p]),
         "spec_probe_read_bandwidth": (c_int32, [c_void_p, c_size_t, c_int32, c_int32,
                                                 c_int32, c_int32, c_void_p, c_void_p]),
+        "spec_probe_read_bandwidth_noalloc": (c_int32, [c_void_p, c_size_t, c_int32, c_int32,
+                                                        c_int32, c_int32, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -257,3 +259,15 @@ def spec_probe_read_bandwidth(d_src, nbytes, grid, waves, depth, pattern, d_sink
                                          pattern, c_void_p(d_sink), c_void_p(stream))
     if rc != SPEC_OK:
         raise SpecError(rc, "spec_probe_read_bandwidth: invalid arguments or launch failure")
+
+
+def spec_probe_read_bandwidth_noalloc(d_src, nbytes, grid, waves, depth, pattern, d_checksum,
+                                      stream):
+    """Enqueue the streaming-read probe with the library's own scratch; the
+    XOR of every wavefront's checksum goes to d_checksum (one uint32)."""
+    rc = lib().spec_probe_read_bandwidth_noalloc(c_void_p(d_src), nbytes, grid, waves, depth,
+                                                 pattern, c_void_p(d_checksum),
+                                                 c_void_p(stream))
+    if rc != SPEC_OK:
+        raise SpecError(rc, "spec_probe_read_bandwidth_noalloc: invalid arguments or launch "
+                            "failure")

@@ -12,7 +12,7 @@ from tree_verification_spec_amd import costmodel
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 NOT_IN_STEP = {"relayout_kernel", "to_f32_kernel", "w12_rowexp_kernel", "w12_encode_kernel",
-               "stream_read_kernel"}
+               "stream_read_kernel", "xor_reduce_kernel"}
 
 
 def _kernel_names():

@@ -124,12 +124,14 @@ def _pass_rows(row):
     return int(row.get("Grid_Size_X", 0)) // 256
 
 
-def steps_from_trace(rows, n_rows):
+def verify_steps(rows, n_rows):
     """Split kernel-trace rows (sorted by start) into verify steps: from an
     embedding launch to the next one, keeping the steps of exactly `n_rows`
-    rows that end in the accepted-path walk (this leaves out prefill chunks,
-    which have no walk, and passes of other sizes such as the AR run).
-    Returns a list of {type: microseconds}."""
+    rows that contain the accepted-path walk (this leaves out prefill chunks,
+    which have no walk, and passes of other sizes such as the AR run).  A
+    step's kernels include its commit (KV compaction, recurrent state
+    commit), which runs before the next pass's embedding.  Returns a list of
+    row lists."""
     steps, cur, cur_rows = [], None, 0
     for r in rows:
         n = r["Kernel_Name"]
@@ -141,15 +143,41 @@ def steps_from_trace(rows, n_rows):
             cur.append(r)
     if cur:
         steps.append((cur_rows, cur))
+    return [st for nr, st in steps
+            if nr == n_rows and any("path_walk_kernel" in r["Kernel_Name"] for r in st)]
+
+
+def _dur_us(r):
+    return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+
+
+def steps_from_trace(rows, n_rows):
+    """Per verify step (see verify_steps) the summed kernel time of each
+    kernel type, as a list of {type: microseconds}."""
     out = []
-    for nr, st in steps:
-        if nr != n_rows or not any("path_walk_kernel" in r["Kernel_Name"] for r in st):
-            continue
+    for st in verify_steps(rows, n_rows):
         per = collections.Counter()
         for r in st:
-            per[kernel_type(r["Kernel_Name"])] += (
-                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per[kernel_type(r["Kernel_Name"])] += _dur_us(r)
         out.append(per)
+    return out
+
+
+def kernel_table(steps):
+    """Per kernel (name and grid size) over the given verify steps: launches
+    per step, mean microseconds per step and per launch, sorted by time."""
+    acc = collections.defaultdict(list)
+    for st in steps:
+        for r in st:
+            acc[(r["Kernel_Name"], int(r.get("Grid_Size_X", 0)),
+                 int(r.get("Grid_Size_Y", 1) or 1))].append(_dur_us(r))
+    n = len(steps)
+    out = []
+    for (name, gx, gy), d in acc.items():
+        out.append(dict(kernel=name, grid=(gx, gy), per_step=len(d) / n,
+                        us_per_step=sum(d) / n, avg_us=statistics.mean(d),
+                        median_us=statistics.median(d)))
+    out.sort(key=lambda k: -k["us_per_step"])
     return out
 
 
@@ -162,9 +190,10 @@ def report(trace_dir, bench):
         raise SystemExit(f"no kernel trace under {trace_dir}")
     rows = sorted(csv.DictReader(open(f[0])), key=lambda r: int(r["Start_Timestamp"]))
     cm = bench["cost_model"]
-    steps = steps_from_trace(rows, cm["rows"])
-    if not steps:
+    raw = verify_steps(rows, cm["rows"])
+    if not raw:
         raise SystemExit("no verify steps with the bench's row count in the trace")
+    steps = steps_from_trace(rows, cm["rows"])
     measured = {t: statistics.mean(s.get(t, 0.0) for s in steps) for t in TYPES}
     bound = {t: cm["types"][t]["bound_us"] for t in TYPES}
     fac = factors(measured, bound, 1e3 * bench["ms_per_step"])
@@ -193,8 +222,19 @@ def report(trace_dir, bench):
         f"- overhead factor: {fac['overhead_factor']:.3f}",
         f"- kernel factor x overhead factor: {fac['total_factor']:.3f}",
         f"- largest factor: {'kernel' if fac['kernel_factor'] >= fac['overhead_factor'] else 'overhead'}",
+        "",
+        "Kernels of a verify step (mean over the steps above; grid in threads):",
+        "",
+        "| kernel | grid x, y | launches per step | us per step | share | mean us per launch | median us |",
+        "|---|---|---|---|---|---|---|",
     ]
-    return "\n".join(lines) + "\n", dict(measured=measured, bound=bound, **fac)
+    kt = kernel_table(raw)
+    for k in kt:
+        lines.append(f"| `{k['kernel']}` | {k['grid'][0]}, {k['grid'][1]} | "
+                     f"{k['per_step']:.2f} | {k['us_per_step']:.1f} | "
+                     f"{k['us_per_step'] / fac['profiled_us']:.1%} | {k['avg_us']:.2f} | "
+                     f"{k['median_us']:.2f} |")
+    return "\n".join(lines) + "\n", dict(measured=measured, bound=bound, kernels=kt, **fac)
 
 
 def main():

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   constexpr int NTHR = WAVES * 64;
   constexpr int KC = STK ? kChunkStk : ChunkK<MT>::value;
   constexpr int LDS_ROW = KC + (kBf ? 8 : 4);       // elements per staged row
-  constexpr int QUADS = KC / 4;                      // float4 per staged row
-  constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // float4 per thread
+  constexpr int EPU = 16 / sizeof(T);               // K values per 16-byte unit
+  constexpr int QUADS = KC / EPU;                    // units per staged row
+  constexpr int XQ = (TROWS * QUADS + NTHR - 1) / NTHR;  // units per thread
   // Loop shape by row tiles (measured on the 8B shapes): up to 32 rows the
   // compiler's own schedule streams best; from 48 rows on, activation loads
   // are unpredicated, each step's weight refill is pinned after its MFMAs,
@@ -140,37 +141,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // ---- activation chunk prefetch (registers) and store (LDS)
-  // one unit = 4 consecutive K values of one row: 8 bytes of each bf16
-  // plane, or 16 bytes of fp32
-  using Unit = typename std::conditional<kBf, uint2, float4>::type;
+  // one unit = 16 bytes of one row: 8 consecutive K values of a bf16 plane,
+  // or 4 of fp32
+  using Unit = typename std::conditional<kBf, uint4, float4>::type;
   const T* Xh = reinterpret_cast<const T*>(a.X);
   const T* Xl = Xh + a.xlo;
   Unit xr[XQ], xl[NPL == 2 ? XQ : 1];
   auto fetch = [&](int kc0, int kcl) {
     // columns kc0 .. kc0 + min(kcl, KC) of the real K range; the rest zero
-    const int quads = kcl <= 0 ? 0 : (kcl >= KC ? QUADS : kcl >> 2);
+    const int quads = kcl <= 0 ? 0 : (kcl >= KC ? QUADS : kcl / EPU);
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const int e = threadIdx.x + q * NTHR;
-      const int r = e / QUADS, c = (e % QUADS) * 4;
+      const int r = e / QUADS, c = (e % QUADS) * EPU;
       if constexpr (STK) {
         // staged row r: hi row r, or lo row r - mc
         const bool low = r >= mc;
         const int m = a.row0 + (low ? r - mc : r);
-        const bool in = r < TROWS && r < 2 * mc && (c >> 2) < quads;
+        const bool in = r < TROWS && r < 2 * mc && c / EPU < quads;
         const T* src = low ? Xl : Xh;
         if constexpr (kOrdered) {
           const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
           const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
-          const uint2 h = *reinterpret_cast<const uint2*>((in ? src : Xh) + off);
-          xr[q] = make_uint2(h.x & mk, h.y & mk);
+          const uint4 h = *reinterpret_cast<const uint4*>((in ? src : Xh) + off);
+          xr[q] = make_uint4(h.x & mk, h.y & mk, h.z & mk, h.w & mk);
         } else {
           const size_t off = (size_t)m * a.ldx + kc0 + c;
-          xr[q] = in ? *reinterpret_cast<const uint2*>(src + off) : make_uint2(0, 0);
+          xr[q] = in ? *reinterpret_cast<const uint4*>(src + off) : make_uint4(0, 0, 0, 0);
         }
       } else {
         const int m = a.row0 + r;
-        const bool in = r < TROWS && m < a.M && (c >> 2) < quads;
+        const bool in = r < TROWS && m < a.M && c / EPU < quads;
         if constexpr (kOrdered) {
           // every lane loads (from the plane's first element when out of
           // range) and masks afterwards: no predicated loads, which the
@@ -178,10 +179,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
           const size_t off = in ? (size_t)m * a.ldx + kc0 + c : 0;
           const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
           if constexpr (NPL == 2) {
-            const uint2 h = *reinterpret_cast<const uint2*>(Xh + off);
-            const uint2 l = *reinterpret_cast<const uint2*>(Xl + off);
-            xr[q] = make_uint2(h.x & mk, h.y & mk);
-            xl[q] = make_uint2(l.x & mk, l.y & mk);
+            const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
+            const uint4 l = *reinterpret_cast<const uint4*>(Xl + off);
+            xr[q] = make_uint4(h.x & mk, h.y & mk, h.z & mk, h.w & mk);
+            xl[q] = make_uint4(l.x & mk, l.y & mk, l.z & mk, l.w & mk);
           } else {
             const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
             xr[q] = make_float4(__uint_as_float(h.x & mk), __uint_as_float(h.y & mk),
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
         } else {
           const size_t off = (size_t)m * a.ldx + kc0 + c;
           if constexpr (NPL == 2) {
-            xr[q] = in ? *reinterpret_cast<const uint2*>(Xh + off) : make_uint2(0, 0);
-            xl[q] = in ? *reinterpret_cast<const uint2*>(Xl + off) : make_uint2(0, 0);
+            xr[q] = in ? *reinterpret_cast<const uint4*>(Xh + off) : make_uint4(0, 0, 0, 0);
+            xl[q] = in ? *reinterpret_cast<const uint4*>(Xl + off) : make_uint4(0, 0, 0, 0);
           } else {
             xr[q] = in ? *reinterpret_cast<const float4*>(Xh + off)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const int e = threadIdx.x + q * NTHR;
-      const int r = e / QUADS, c = (e % QUADS) * 4;
+      const int r = e / QUADS, c = (e % QUADS) * EPU;
       if (r >= TROWS) continue;
       *reinterpret_cast<Unit*>(&hi[r * LDS_ROW + c]) = xr[q];
       if constexpr (NPL == 2) *reinterpret_cast<Unit*>(&lo[r * LDS_ROW + c]) = xl[q];

@@ -174,9 +174,12 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // added in order.
 __device__ __forceinline__ float row_scale(const RowNorm& n, int row) {
   const float* p = n.ss + (size_t)row * n.nc;
+  // every lane loads 16 values (indexes past the row's chunks repeat its
+  // last one), so the loads are unconditional and all in flight together
+  const int last = n.nc > 0 ? n.nc - 1 : 0;
   float v[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) v[c] = c < n.nc ? p[c] : 0.f;
+  for (int c = 0; c < 16; ++c) v[c] = p[c < last ? c : last];
   float t = 0.f;
 #pragma unroll
   for (int c = 0; c < 16; ++c)

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 // same for every pass.
 constexpr int kLrTreeRows = 72;  // rows of a tree pass staged at once (max_nodes <= 65)
 constexpr int kLrSeg = 64;       // rows per staged segment of a chain pass
-constexpr int kLrStack = 16;     // root-path states kept in registers (depths 0..15)
+constexpr int kLrStack = kLrRegisterDepth;  // root-path states kept in registers (depths 0..15)
 constexpr int kLrThreads = 256;
 
 typedef float lr_stack_t __attribute__((ext_vector_type(kLrStack)));
@@ -281,6 +281,15 @@ __device__ __forceinline__ float seg_sum(float v) {
   return v;
 }
 
+// Units per thread in one staging batch: enough for `units` (one batch)
+// but at most `cap` (and at least 1), which bounds the registers holding
+// loads in flight.
+constexpr int lr_batch(int units, int cap) {
+  const int need = (units + kLrThreads - 1) / kLrThreads;
+  const int c = cap > 0 ? cap : 1;
+  return need < c ? need : c;
+}
+
 // MODE 0: chains; 1: trees of depth <= kLrStack (register stack); 2: deeper trees
 template <int S, int MODE, int NS>
 __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
@@ -291,10 +300,14 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
   constexpr bool TREE = MODE > 0;
   constexpr int LPC = S / 4;                 // lanes per channel
   constexpr int CPB = kLrThreads / LPC;      // channels per workgroup
-  constexpr int NV = 3 * CPB + 2 * S;        // staged per row: x, a, silu(z) (CPB each), B, C
   constexpr int ROWS = TREE ? kLrTreeRows : kLrSeg;
-  __shared__ __align__(16) float sv[ROWS][NV];
-  __shared__ float sg[ROWS][CPB];            // sigmoid(a)
+  constexpr int XU = CPB / 4;                // 4-channel units of x, a, z per row
+  constexpr int BU = S / 2;                  // 4-value units of B and C per row
+  // per (row, channel): sigmoid(a), x, silu(z), a (all scaled by the row's
+  // norm scale); per row: B then C; per (row, channel): the output
+  __shared__ __align__(16) float4 sgx[ROWS][CPB];
+  __shared__ __align__(16) float sbc[ROWS][2 * S];
+  __shared__ float so[ROWS][CPB];
   __shared__ float scs[ROWS];
   __shared__ int sord[ROWS], sdep[ROWS], spar[ROWS];
   const int r = blockIdx.y;
@@ -320,71 +333,107 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
         spar[threadIdx.x] = m.parent;
       }
     }
-    __syncthreads();
-    // staging in units of 4 consecutive values (x, a, z of 4 channels, or 4
-    // of B or C): every unit's NS partials of a batch are loaded before any
-    // is summed
-    constexpr int NU = NV / 4;                 // units per row
-    constexpr int XU = CPB / 4;                // units of each of x, a, z
-    constexpr int UB = NS >= 8 ? 2 : 12 / NS;  // units per thread in a batch
-    for (int e0 = threadIdx.x; e0 < n * NU; e0 += kLrThreads * UB) {
-      float4 t[UB][NS];
+    // staging in batches: a batch's loads (the NS split partials of x, a, z
+    // of the workgroup's channels, and of the rows' B and C) are all issued
+    // before any is summed; x/a/z units and B/C units have loops of their
+    // own, so a wavefront's lanes take the same branch
+    // (more than 8 partials: the first 8 are in flight together, the rest
+    // are loaded and added in groups of 8 afterwards, in split order)
+    constexpr int G = NS < 8 ? NS : 8;
+    constexpr int UA = lr_batch(ROWS * XU, 6 / (3 * G));   // x/a/z units per thread
+    constexpr int UB = lr_batch(ROWS * BU, 12 / G);        // B/C units per thread
+    const float* pbase = proj + (size_t)(rm.row0 + i0) * ld;
+    // split-ordered sum of a unit's partials (the first G given), scaled
+    auto sum = [&](const float4 (&t)[G], const float* p, float sc) {
+      float4 v = t[0];
 #pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int e = e0 + u * kLrThreads;
-        if (e < n * NU) {
-          const int j = e / NU, k = e % NU;
-          int col;
-          if (k < 3 * XU) {
-            const int ch = min(blockIdx.x * CPB + (k % XU) * 4, d - 4);
-            col = (k / XU) * d + ch;  // x, a or z of 4 channels
-          } else {
-            col = 3 * d + (k - 3 * XU) * 4;  // B then C
+      for (int s2 = 1; s2 < G; ++s2) {
+        v.x += t[s2].x;
+        v.y += t[s2].y;
+        v.z += t[s2].z;
+        v.w += t[s2].w;
+      }
+      for (int q0 = G; q0 < NS; q0 += G) {
+        float4 u[G];
+#pragma unroll
+        for (int s2 = 0; s2 < G; ++s2)
+          if (q0 + s2 < NS) u[s2] = *reinterpret_cast<const float4*>(p + (q0 + s2) * sstride);
+#pragma unroll
+        for (int s2 = 0; s2 < G; ++s2)
+          if (q0 + s2 < NS) {
+            v.x += u[s2].x;
+            v.y += u[s2].y;
+            v.z += u[s2].z;
+            v.w += u[s2].w;
           }
-          const float* p = proj + (size_t)(rm.row0 + i0 + j) * ld + col;
+      }
+      return make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+    };
+    for (int ea = 0, eb = 0; ea < n * XU || eb < n * BU;
+         ea += kLrThreads * UA, eb += kLrThreads * UB) {
+      float4 ta[UA][3][G], tb[UB][G];
 #pragma unroll
-          for (int q = 0; q < NS; ++q) t[u][q] = *reinterpret_cast<const float4*>(p + q * sstride);
+      for (int u = 0; u < UA; ++u) {
+        const int e = ea + threadIdx.x + u * kLrThreads;
+        if (e < n * XU) {
+          const int j = e / XU, q = e % XU;
+          const int ch = min((int)blockIdx.x * CPB + q * 4, d - 4);
+          const float* p = pbase + (size_t)j * ld + ch;
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int s2 = 0; s2 < G; ++s2)
+              ta[u][t][s2] = *reinterpret_cast<const float4*>(p + t * d + s2 * sstride);
         }
       }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const int e = e0 + u * kLrThreads;
-        if (e < n * NU) {
-          const int j = e / NU, k = e % NU;
-          float4 v = t[u][0];
+        const int e = eb + threadIdx.x + u * kLrThreads;
+        if (e < n * BU) {
+          const int j = e / BU, k = e % BU;
+          const float* p = pbase + (size_t)j * ld + 3 * d + 4 * k;
 #pragma unroll
-          for (int q = 1; q < NS; ++q) {
-            v.x += t[u][q].x;
-            v.y += t[u][q].y;
-            v.z += t[u][q].z;
-            v.w += t[u][q].w;
-          }
+          for (int s2 = 0; s2 < G; ++s2)
+            tb[u][s2] = *reinterpret_cast<const float4*>(p + s2 * sstride);
+        }
+      }
+      __syncthreads();  // scs
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int e = ea + threadIdx.x + u * kLrThreads;
+        if (e < n * XU) {
+          const int j = e / XU, q = e % XU;
           const float sc = scs[j];
-          v.x *= sc;
-          v.y *= sc;
-          v.z *= sc;
-          v.w *= sc;
-          if (k >= XU && k < 2 * XU) {  // a: also sigmoid(a)
-            const int q0 = (k - XU) * 4;
-            sg[j][q0] = 1.0f / (1.0f + expf(-v.x));
-            sg[j][q0 + 1] = 1.0f / (1.0f + expf(-v.y));
-            sg[j][q0 + 2] = 1.0f / (1.0f + expf(-v.z));
-            sg[j][q0 + 3] = 1.0f / (1.0f + expf(-v.w));
-          } else if (k >= 2 * XU && k < 3 * XU) {  // z: stored as silu(z)
-            v.x = v.x / (1.0f + expf(-v.x));
-            v.y = v.y / (1.0f + expf(-v.y));
-            v.z = v.z / (1.0f + expf(-v.z));
-            v.w = v.w / (1.0f + expf(-v.w));
-          }
-          *reinterpret_cast<float4*>(&sv[j][4 * k]) = v;
+          const float* p = pbase + (size_t)j * ld + min((int)blockIdx.x * CPB + q * 4, d - 4);
+          const float4 x = sum(ta[u][0], p, sc), a = sum(ta[u][1], p + d, sc),
+                       z = sum(ta[u][2], p + 2 * d, sc);
+          sgx[j][4 * q] = make_float4(1.0f / (1.0f + expf(-a.x)), x.x,
+                                      z.x / (1.0f + expf(-z.x)), a.x);
+          sgx[j][4 * q + 1] = make_float4(1.0f / (1.0f + expf(-a.y)), x.y,
+                                          z.y / (1.0f + expf(-z.y)), a.y);
+          sgx[j][4 * q + 2] = make_float4(1.0f / (1.0f + expf(-a.z)), x.z,
+                                          z.z / (1.0f + expf(-z.z)), a.z);
+          sgx[j][4 * q + 3] = make_float4(1.0f / (1.0f + expf(-a.w)), x.w,
+                                          z.w / (1.0f + expf(-z.w)), a.w);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int e = eb + threadIdx.x + u * kLrThreads;
+        if (e < n * BU) {
+          const int j = e / BU, k = e % BU;
+          *reinterpret_cast<float4*>(&sbc[j][4 * k]) =
+              sum(tb[u], pbase + (size_t)j * ld + 3 * d + 4 * k, scs[j]);
         }
       }
     }
     __syncthreads();
     // The walk.  Each wave keeps the walk order (node, depth) in two lanes'
     // registers (position k in lane k % 64 of word k / 64) so a node index is
-    // a register read, not an LDS round trip, and the next node's inputs are
-    // read from LDS while the current node computes.
+    // a register read, not an LDS round trip.  Two nodes' inputs are in
+    // flight ahead of the one being computed (alternating register sets, no
+    // copies), and each node's output goes to LDS, written out coalesced
+    // after the walk.
     int ordw0 = 0, ordw1 = 0;  // node | depth << 8 of positions lane, 64 + lane
     {
       const int lane = threadIdx.x & 63;
@@ -396,38 +445,28 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       ordw1 = at(64 + lane);
     }
     auto pos = [&](int k) {  // (node, depth) at walk position k (uniform)
-      const int w = __builtin_amdgcn_readlane(k < 64 ? ordw0 : ordw1, k & 63);
-      return w;
+      return __builtin_amdgcn_readlane(k < 64 ? ordw0 : ordw1, k & 63);
     };
     struct In {
-      float g, x, sz;
+      float4 gx;  // sigmoid(a), x, silu(z), a
       float4 b, c;
     };
     auto fetch = [&](int j) {
       In v;
-      v.g = sg[j][lc];
-      v.x = sv[j][lc];
-      v.sz = sv[j][2 * CPB + lc];
-      v.b = *reinterpret_cast<const float4*>(&sv[j][3 * CPB + 4 * l]);
-      v.c = *reinterpret_cast<const float4*>(&sv[j][3 * CPB + S + 4 * l]);
+      v.gx = sgx[j][lc];
+      v.b = *reinterpret_cast<const float4*>(&sbc[j][4 * l]);
+      v.c = *reinterpret_cast<const float4*>(&sbc[j][S + 4 * l]);
       return v;
     };
     // one node's update from its parent's states
     auto step = [&](const In& v, float& a0, float& a1, float& a2, float& a3) {
-      a0 = ((v.g * a0) + (v.b.x * v.x));
-      a1 = ((v.g * a1) + (v.b.y * v.x));
-      a2 = ((v.g * a2) + (v.b.z * v.x));
-      a3 = ((v.g * a3) + (v.b.w * v.x));
+      a0 = ((v.gx.x * a0) + (v.b.x * v.gx.y));
+      a1 = ((v.gx.x * a1) + (v.b.y * v.gx.y));
+      a2 = ((v.gx.x * a2) + (v.b.z * v.gx.y));
+      a3 = ((v.gx.x * a3) + (v.b.w * v.gx.y));
     };
-    int wk = n > 0 ? pos(0) : 0;
-    In cur = fetch(wk & 0xFF);
-    for (int k = 0; k < n; ++k) {
+    auto node = [&](const In& cur, int wk) {
       const int j = wk & 0xFF, dj = wk >> 8;
-      In nxt = cur;
-      if (k + 1 < n) {
-        wk = pos(k + 1);
-        nxt = fetch(wk & 0xFF);
-      }
       float a0, a1, a2, a3;
       if constexpr (MODE == 1) {
         if (dj == 0) {
@@ -457,13 +496,36 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       y = (y + (a2 * cur.c.z));
       y = (y + (a3 * cur.c.w));
       y = seg_sum<LPC>(y);
-      if (l == LPC - 1 && live) {
-        const float ov = y * cur.sz;
-        const size_t oi = (size_t)(rm.row0 + i0 + j) * d + c;
-        if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, ov);
-        else store_act((float*)o, (float*)o + olo, oi, ov);
+      if (l == LPC - 1) so[j][lc] = y * cur.gx.z;
+    };
+    // Trees visit an odd count's last position twice: that repeats the same
+    // arithmetic on the same inputs and parent state, so it rewrites the
+    // same values.  Chains (a running state) skip it.
+    if (n > 0) {
+      auto at = [&](int k) { return pos(k < n ? k : n - 1); };
+      int w0 = at(0), w1 = at(1);
+      In A = fetch(w0 & 0xFF), B = fetch(w1 & 0xFF);
+      for (int k = 0; k < n; k += 2) {
+        node(A, w0);
+        if (k + 2 < n) {
+          w0 = at(k + 2);
+          A = fetch(w0 & 0xFF);
+        }
+        if (TREE || k + 1 < n) node(B, w1);
+        if (k + 3 < n) {
+          w1 = at(k + 3);
+          B = fetch(w1 & 0xFF);
+        }
       }
-      cur = nxt;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < n * CPB; e += kLrThreads) {
+      const int j = e / CPB, q = e % CPB;
+      const int ch = blockIdx.x * CPB + q;
+      if (ch >= d) continue;
+      const size_t oi = (size_t)(rm.row0 + i0 + j) * d + ch;
+      if (obf) store_act((uint16_t*)o, (uint16_t*)o + olo, oi, so[j][q]);
+      else store_act((float*)o, (float*)o + olo, oi, so[j][q]);
     }
     if (save) {  // [x | a | B] of every row, for the commit
       for (int e = threadIdx.x; e < n * CPB; e += kLrThreads) {
@@ -471,13 +533,14 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
         const int ch = blockIdx.x * CPB + q;
         if (ch >= d) continue;
         const size_t row = (size_t)(rm.row0 + i0 + j);
-        save[row * (2 * d + S) + ch] = sv[j][q];
-        save[row * (2 * d + S) + d + ch] = sv[j][CPB + q];
+        const float4 v = sgx[j][q];
+        save[row * (2 * d + S) + ch] = v.y;
+        save[row * (2 * d + S) + d + ch] = v.w;
       }
       if (blockIdx.x == 0)
         for (int e = threadIdx.x; e < n * S; e += kLrThreads) {
           const int j = e / S, q = e % S;
-          save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sv[j][3 * CPB + q];
+          save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sbc[j][q];
         }
     }
   }
@@ -684,7 +747,7 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
   constexpr int CPB = kLrThreads / (S / 4);
   if (tree_depth > 0 && max_rows_per_req > kLrTreeRows) return hipErrorInvalidValue;
   dim3 grid((d + CPB - 1) / CPB, n_req);
-  if (tree_depth > kLrStack)
+  if (tree_depth > kLrRegisterDepth)
     lr_fork_kernel<S, 2, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
                                                          olo, obf, save, commit_last, norm);
   else if (tree_depth > 0)

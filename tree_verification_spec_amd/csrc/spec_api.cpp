@@ -1222,7 +1222,7 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
   // (a chain is a tree); its depth class: a 16-entry register stack unless a
   // node of the pass is deeper (one class per pass keeps the captured graphs
   // few)
-  const int depth_class = !any_tree ? 0 : max_depth <= 16 ? 16 : 64;
+  const int depth_class = !any_tree ? 0 : max_depth <= kLrRegisterDepth ? kLrRegisterDepth : 64;
   rc = forward(c, R, n_req, keys, nrows, depth_class, 0, R, d_logits_opt, false, true, lowp);
   if (rc) return rc;
   const int max_path = kMaxPath;

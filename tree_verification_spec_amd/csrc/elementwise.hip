@@ -498,9 +498,6 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       y = seg_sum<LPC>(y);
       if (l == LPC - 1) so[j][lc] = y * cur.gx.z;
     };
-    // Trees visit an odd count's last position twice: that repeats the same
-    // arithmetic on the same inputs and parent state, so it rewrites the
-    // same values.  Chains (a running state) skip it.
     if (n > 0) {
       auto at = [&](int k) { return pos(k < n ? k : n - 1); };
       int w0 = at(0), w1 = at(1);
@@ -511,7 +508,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
           w0 = at(k + 2);
           A = fetch(w0 & 0xFF);
         }
-        if (TREE || k + 1 < n) node(B, w1);
+        if (k + 1 < n) node(B, w1);
         if (k + 3 < n) {
           w1 = at(k + 3);
           B = fetch(w1 & 0xFF);

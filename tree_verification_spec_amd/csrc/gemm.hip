@@ -448,6 +448,307 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tall GEMM
+// More than 40 rows (bf16 activation planes; fused multi-request verify
+// passes and prefill chunks): the skinny kernel above gives each wave one
+// column tile and every row, so each staged activation fragment feeds one
+// MFMA and the LDS reads grow with the rows.  Here a wave owns a block of
+// RT row tiles x kTallCT column tiles: per K-step it reads RT x 2 activation
+// fragments (hi, lo) from LDS and kTallCT weight fragments from memory and
+// issues RT x kTallCT x 2 MFMAs, so each fragment feeds 2..kTallCT MFMAs.
+// A workgroup is kTallWM x kTallWN waves: kTallWM row groups (all of a
+// launch's rows up to 288, so a weight tile is streamed once per 288 rows)
+// by kTallWN column groups (128 columns).  Activations are staged one K-step
+// (32 columns, both planes) at a time in two LDS buffers; weights stream
+// with the next K-step's tiles in flight.  Epilogues as in the skinny
+// kernel, written from registers: split partials, SwiGLU (the gate and up
+// tiles of a pair are a wave's column tiles 2q and 2q + 1), and the per-row
+// argmax partial of the workgroup's 128 columns.
+constexpr int kTallWM = 3;   // row groups
+constexpr int kTallWN = 2;   // column groups
+constexpr int kTallCT = 4;   // column tiles per wave
+constexpr int kTallWaves = kTallWM * kTallWN;
+constexpr int kTallCols = kTallWN * kTallCT * 16;  // columns of a workgroup (128)
+
+template <int RT, int EPI, int WF>
+__global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) {
+  constexpr int CT = kTallCT;
+  constexpr int RB = kTallWM * RT * 16;  // rows of a workgroup
+  constexpr int LROW = 32 + 8;           // staged row: one K-step + pad (bank spread)
+  constexpr int PLANE = RB * LROW;
+  constexpr int NTHR = kTallWaves * 64;
+  constexpr int UNITS = 2 * RB * 4;      // 16-byte units of a staged K-step (both planes)
+  constexpr int XQ = (UNITS + NTHR - 1) / NTHR;
+  constexpr bool W12 = WF == 1, W8 = WF == 2;
+  __shared__ __align__(16) uint16_t xs[2][2 * PLANE];
+  __shared__ float rsc[RB];
+  using WReg = typename std::conditional<
+      W12, W12Raw, typename std::conditional<W8, uint2, Frag<uint16_t>>::type>::type;
+  constexpr uint32_t TB = W12 ? kW12TileBytes : W8 ? kW8TileBytes : 1024;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % kTallWM, wn = wave / kTallWM;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int cb = blockIdx.x % a.ncb, sk = blockIdx.x / a.ncb;
+  const int rbase = blockIdx.y * RB;  // first row of the workgroup
+  const int rows = min(RB, a.M - rbase);
+  const int tile0 = cb * (kTallCols / 16) + wn * CT;  // the wave's first column tile
+  const int kbeg = sk * a.KR, kend = min(a.K, kbeg + a.KR);
+  const int kb_beg = kbeg >> 5, kb_end = kend >> 5;
+
+  __amdgpu_buffer_rsrc_t wrs[CT];
+  uint32_t eb7[CT];
+#pragma unroll
+  for (int t = 0; t < CT; ++t) {
+    const size_t tr = (size_t)(tile0 + t);
+    wrs[t] = weight_rsrc(reinterpret_cast<const uint8_t*>(a.W) + tr * a.wsn * TB);
+    if constexpr (W12 || W8) {
+      const uint32_t e = a.eb[tr * 16 + r16];
+      eb7[t] = (e | (e << 16)) << 7;
+    } else {
+      eb7[t] = 0;
+    }
+  }
+  const uint32_t wk = (uint32_t)a.wsk * TB;
+  const uint32_t* ovf = W12 ? w12_overflow(a.W, (size_t)a.ntiles * (a.K / 32)) : nullptr;
+  auto load_step = [&](WReg (&dst)[CT], int kb) {
+    const int k = kb < kb_end ? kb : kb_end - 1;  // past the end: the last tile again
+    const int so = (int)((uint32_t)k * wk);
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      if constexpr (W12) {
+        const u32x3_t d = __builtin_amdgcn_raw_buffer_load_b96(wrs[t], lane * 12, so, 0);
+        dst[t] = W12Raw{d.x, d.y, d.z,
+                        __builtin_amdgcn_raw_buffer_load_b32(
+                            wrs[t], (kW12SlotDword + (lane & 7)) * 4, so, 0)};
+      } else if constexpr (W8) {
+        dst[t] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(wrs[t], lane * 8, so, 0));
+      } else {
+        dst[t].v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs[t], lane * 16, so, 0));
+      }
+    }
+  };
+  auto wfrag = [&](const WReg& r, int t) -> Frag<uint16_t> {
+    if constexpr (W12) {
+      Frag<uint16_t> f;
+      f.v = w12_decode(r, eb7[t]);
+      w12_patch_opaque(f.v, r, lane, ovf);
+      return f;
+    } else if constexpr (W8) {
+      Frag<uint16_t> f;
+      f.v = w8_decode(r, eb7[t]);
+      return f;
+    } else {
+      (void)t;
+      return r;
+    }
+  };
+
+  // activation staging, one K-step (32 values of each row and plane) at a
+  // time: unit e = (plane, row, quarter); rows past M and K past the split
+  // stage zeros (loads are unconditional from the plane's first element and
+  // masked afterwards)
+  const uint16_t* Xh = reinterpret_cast<const uint16_t*>(a.X);
+  uint4 xr[XQ];
+  auto fetch = [&](int kb) {
+    const bool kin = kb < kb_end;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int e = threadIdx.x + q * NTHR;
+      const int pl = e / (RB * 4), rest = e % (RB * 4);
+      const int r = rest >> 2, c = (rest & 3) * 8;
+      const bool in = e < UNITS && kin && r < rows;
+      const size_t off = in ? (size_t)pl * a.xlo + (size_t)(rbase + r) * a.ldx + kb * 32 + c : 0;
+      const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
+      const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
+      xr[q] = make_uint4(h.x & mk, h.y & mk, h.z & mk, h.w & mk);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int e = threadIdx.x + q * NTHR;
+      if (e >= UNITS) continue;
+      const int pl = e / (RB * 4), rest = e % (RB * 4);
+      const int r = rest >> 2, c = (rest & 3) * 8;
+      *reinterpret_cast<uint4*>(&xs[buf][pl * PLANE + r * LROW + c]) = xr[q];
+    }
+  };
+
+  constexpr bool kNorm = EPI != EPI_PART;
+  if (kNorm) {
+    for (int r = threadIdx.x; r < RB; r += NTHR)
+      rsc[r] = (r < rows && a.norm.ss) ? row_scale(a.norm, rbase + r) : 1.0f;
+  }
+
+  floatx4_t acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[rt][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  WReg w[2][CT];
+  fetch(kb_beg);
+  load_step(w[0], kb_beg);
+  load_step(w[1], kb_beg + 1);
+  const int xrow = wm * RT * 16 + r16;  // the lane's row in the workgroup's first row tile
+  // one K-step from buffer `buf` with the weights of slot u; the slot is
+  // then refilled with the step two ahead
+  auto kstep = [&](int kb, int buf, WReg (&wu)[CT]) {
+    store(buf);
+    fetch(kb + 1);
+    __syncthreads();
+    Frag<uint16_t> xh[RT], xl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint16_t* p = &xs[buf][(xrow + rt * 16) * LROW + g * 8];
+      xh[rt].load(p);
+      xl[rt].load(p + PLANE);
+    }
+    Frag<uint16_t> wf[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) wf[t] = wfrag(wu[t], t);
+    load_step(wu, kb + 2);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        mma32(acc[rt][t], wf[t], xh[rt]);
+        mma32(acc[rt][t], wf[t], xl[rt]);
+      }
+  };
+  for (int kb = kb_beg; kb < kb_end; kb += 2) {
+    kstep(kb, 0, w[0]);
+    kstep(kb + 1, 1, w[1]);  // past the end: zero activations, nothing added
+  }
+
+  // ---- results (registers: lane (r16, g) holds row r16, columns 4g..4g+3
+  // of each tile)
+  const int N = a.ntiles * 16;
+  if constexpr (EPI == EPI_PART) {
+    float* P = a.P + (size_t)sk * a.P_ld * N;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int lr = xrow + rt * 16;
+      if (lr >= rows) continue;
+      const size_t m = (size_t)(rbase + lr);
+#pragma unroll
+      for (int t = 0; t < CT; ++t)
+        *reinterpret_cast<float4*>(P + m * N + (tile0 + t) * 16 + 4 * g) =
+            make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
+    }
+    return;
+  }
+  __syncthreads();  // rsc
+  if constexpr (EPI == EPI_SWIGLU) {
+    uint16_t* Yh = reinterpret_cast<uint16_t*>(a.Y);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int lr = xrow + rt * 16;
+      if (lr >= rows) continue;
+      const float sc = rsc[lr];
+      const size_t m = (size_t)(rbase + lr);
+#pragma unroll
+      for (int q = 0; q < CT / 2; ++q) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = acc[rt][2 * q][r] * sc;
+          const float uv = acc[rt][2 * q + 1][r] * sc;
+          o[r] = gv / (1.0f + expf(-gv)) * uv;
+        }
+        const int col = ((tile0 + 2 * q) >> 1) * 16 + 4 * g;
+        store_act4(Yh, Yh + a.ylo, m * a.ldy + col, make_float4(o[0], o[1], o[2], o[3]));
+      }
+    }
+    return;
+  }
+  // EPI_ARGMAX: per row, the largest value of the workgroup's columns and
+  // its lowest index: over the lane's 16 values, the 4 lanes of the row, then
+  // the column groups (through LDS)
+  float2* red = reinterpret_cast<float2*>(&xs[0][0]);  // [kTallWN][RB]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int lr = xrow + rt * 16;
+    const bool live = lr < rows;
+    const int m = rbase + (live ? lr : 0);
+    const float sc = rsc[lr];
+    float best = -INFINITY;
+    int bi = cb * kTallCols;
+#pragma unroll
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = (tile0 + t) * 16 + 4 * g + r;
+        float v = acc[rt][t][r] * sc;
+        if (n >= a.ncols) v = -INFINITY;
+        if (live && n == a.bias_tok && a.rows[m].pos >= a.bias_after) v += a.bias;
+        if (live && a.logits && n < a.ncols) a.logits[(size_t)m * a.ldlog + n] = v;
+        if (v > best || (v == best && n < bi)) {  // NaN never wins
+          best = v;
+          bi = n;
+        }
+      }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if (g == 0) red[wn * RB + lr] = make_float2(best, __int_as_float(bi));
+  }
+  __syncthreads();
+  for (int lr = threadIdx.x; lr < rows; lr += NTHR) {
+    float2 b = red[lr];
+#pragma unroll
+    for (int c = 1; c < kTallWN; ++c) {
+      const float2 o = red[c * RB + lr];
+      if (o.x > b.x || (o.x == b.x && __float_as_int(o.y) < __float_as_int(b.y))) b = o;
+    }
+    a.part[(size_t)(rbase + lr) * a.nblocks + cb] = b;
+  }
+}
+
+template <int RT, int EPI, int WF>
+hipError_t launch_tall_rt(const GemmArgs& a, int nrb, const LaunchCtx& s) {
+  auto k = gemm_tall_kernel<RT, EPI, WF>;
+  const dim3 grid(a.ncb * a.S, nrb);
+  if (s.t0 || s.t1) {
+    GemmArgs arg = a;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel((const void*)k, grid, dim3(kTallWaves * 64), args, 0, s.s, s.t0,
+                              s.t1, 0);
+  }
+  k<<<grid, kTallWaves * 64, 0, s.s>>>(a);
+  return hipGetLastError();
+}
+
+// Row tiles per wave by the launch's rows: 96, 192 or 288 rows per workgroup
+// (more rows: several row blocks of 288).
+template <int EPI, int WF>
+hipError_t launch_tall_fmt(const GemmArgs& a, const LaunchCtx& s) {
+  const int rt = a.M <= 96 ? 2 : a.M <= 192 ? 4 : 6;
+  const int rb = kTallWM * rt * 16;
+  const int nrb = (a.M + rb - 1) / rb;
+  if (rt == 2) return launch_tall_rt<2, EPI, WF>(a, nrb, s);
+  if (rt == 4) return launch_tall_rt<4, EPI, WF>(a, nrb, s);
+  return launch_tall_rt<6, EPI, WF>(a, nrb, s);
+}
+
+template <int WF>
+hipError_t launch_tall_epi(int epi, const GemmArgs& a, const LaunchCtx& s) {
+  if (epi == EPI_PART) return launch_tall_fmt<EPI_PART, WF>(a, s);
+  if (epi == EPI_SWIGLU) return launch_tall_fmt<EPI_SWIGLU, WF>(a, s);
+  if (epi == EPI_ARGMAX) return launch_tall_fmt<EPI_ARGMAX, WF>(a, s);
+  return hipErrorInvalidValue;
+}
+
 // Workgroup shapes: (tiles per wave, waves, workgroups per K split).  Up to
 // 40 rows (bf16: the stacked-row limit) one tile per wave: up to 2048 tiles
 // 8-tile workgroups (one round on 256 CUs); 2049-2560 tiles (the 27B gate/up,
@@ -456,12 +757,9 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 // wave on 8 waves, and 96 us for 272 workgroups of 8, which leave a second
 // round); more tiles (the LM heads) rounds of 256 workgroups of at most 8
 // tiles (27B LM head 252 us against 268 us for 1188 workgroups of 8).  From
-// 41 rows: 256 columns with two tiles per wave for wide matrices (>= 128
-// blocks of 256 columns: the LM head; half the LDS reads per MFMA), two
-// tiles per wave on 4 waves for narrow ones up to 95 rows, and one tile per
-// wave on 8 waves from 96 rows (128-row launches: 8 row tiles; two waves
-// per SIMD instead of one).  Measured on the 8B and 27B shapes, weights
-// streamed from HBM.
+// 41 rows with bf16 activations: the tall kernel, one workgroup per 128
+// columns (ntw 0).  fp32 models: one tile per wave on 8 waves.  Measured on
+// the 8B and 27B shapes, weights streamed from HBM.
 struct Variant {
   int ntw, waves, ncb;
 };
@@ -474,8 +772,8 @@ Variant gemm_variant(bool bf16, int N, int M) {
     if (nt <= 2560) return {1, 10, 256};
     return {1, 8, 256 * ((nt + 2047) / 2048)};
   }
-  if (N / 256 >= 128) return {2, 8, nt / 16};
-  return M >= 96 ? Variant{1, 8, nt / 8} : Variant{2, 4, nt / 8};
+  // more rows: the tall kernel (ntw 0), 128 columns a workgroup
+  return {0, kTallWaves, N / kTallCols};
 }
 
 template <typename T, int EPI, int NTW, int WAVES, int D, int WF>
@@ -589,6 +887,15 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s,
   // partial sums must not depend on the chunk)
   const Variant v = gemm_variant(bf16, a.ntiles * 16, a.M);
   a.ncb = v.ncb;
+  if (v.ntw == 0) {  // tall: all rows in one launch
+    if (a.ntiles % (kTallCols / 16) || a.ncb < 1) return hipErrorInvalidValue;
+    if (epi == EPI_ARGMAX) a.nblocks = a.ncb;
+    a.row0 = 0;
+    const LaunchCtx lc{s, t0, t1};
+    if (a.w12 == 1) return launch_tall_epi<1>(epi, a, lc);
+    if (a.w12 == 2) return launch_tall_epi<2>(epi, a, lc);
+    return launch_tall_epi<0>(epi, a, lc);
+  }
   a.gt = (epi == EPI_SWIGLU && v.ntw == 1) ? 2 : v.ntw;
   // every workgroup's share of whole granules must fit its waves
   if (a.ntiles % a.gt || a.ncb < 1 || a.ncb > a.ntiles / a.gt ||

@@ -269,61 +269,149 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
       return r;
     }
   };
-  // the first chunk is fetched now (before the W window, as in the steady
-  // state); each chunk is stored into LDS at its start and the next one is
-  // fetched into registers right after
-  fetch(kbeg, kend - kbeg);
+  // one staged chunk: CSTEPS K-steps from LDS (xat: the address of a row's
+  // 8 values at K offset kk), weights from window slots cc * CSTEPS + j
+  auto compute_chunk = [&](int kw, int cc, auto xat) {
+    // activation fragments of K-step j + 1 are read from LDS while the
+    // MFMAs of step j run (software pipelining hides the LDS latency)
+    constexpr int XF = NPL;  // hi (+ lo) planes
+    Frag<T> xc[MT][XF], xn[MT][XF];
+    auto load_x = [&](Frag<T> (&x)[MT][XF], int j) {
+      const int kk = j * 32 + g * 8;
 #pragma unroll
-  for (int u = 0; u < WIN; ++u) load_step(w[u], kb_beg + u);
-
-  int buf = 0;
-  for (int kw = kb_beg; kw < kb_end; kw += WIN) {
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mt * 16 + r16;
+        x[mt][0].load(xat(r, kk, 0));
+        if constexpr (NPL == 2) x[mt][1].load(xat(r, kk, 1));
+      }
+    };
+    load_x(xc, 0);
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int k0 = (kw + cc * CSTEPS) * 32;  // first K index of this chunk
-      store(buf);
-      fetch(k0 + KC, kend - k0 - KC);
-      __syncthreads();
-      const T* hi = xbuf + buf * BUF_ELEMS;
-      buf ^= 1;
-      // activation fragments of K-step j + 1 are read from LDS while the
-      // MFMAs of step j run (software pipelining hides the LDS latency)
-      constexpr int XF = NPL;  // hi (+ lo) planes
-      Frag<T> xc[MT][XF], xn[MT][XF];
-      auto load_x = [&](Frag<T> (&x)[MT][XF], int j) {
-        const int kk = j * 32 + g * 8;
+    for (int j = 0; j < CSTEPS; ++j) {
+      const int u = cc * CSTEPS + j;
+      if (j + 1 < CSTEPS) load_x(xn, j + 1);
+      Frag<T> wf[NTW];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int r = mt * 16 + r16;
-          x[mt][0].load(&hi[r * LDS_ROW + kk]);
-          if constexpr (NPL == 2) x[mt][1].load(&hi[TROWS * LDS_ROW + r * LDS_ROW + kk]);
-        }
-      };
-      load_x(xc, 0);
+      for (int t = 0; t < NTW; ++t) wf[t] = wfrag(w[u][t], t);
 #pragma unroll
-      for (int j = 0; j < CSTEPS; ++j) {
-        const int u = cc * CSTEPS + j;
-        if (j + 1 < CSTEPS) load_x(xn, j + 1);
-        Frag<T> wf[NTW];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) wf[t] = wfrag(w[u][t], t);
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int p = 0; p < XF; ++p) mma32(acc[t][mt], wf[t], xc[mt][p]);
+      load_step(w[u], kw + u + WIN);
+      // ordered: each step's refill is issued right after its MFMAs (the
+      // scheduler would otherwise sink all refills to the end of the
+      // chunk, and the next chunk would wait a full memory latency)
+      if constexpr (kOrdered) __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < CSTEPS) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int t = 0; t < NTW; ++t)
+          for (int p = 0; p < XF; ++p) xc[mt][p] = xn[mt][p];
+      }
+    }
+  };
+
+  if constexpr (STK) {
+    // Stacked rows: each chunk goes from memory straight into LDS (buffer
+    // loads that write LDS, no registers), two buffers in turn.  A 1 KB
+    // load of a wavefront fills two unpadded 512-byte rows; 16-byte unit u
+    // of row r sits at position u ^ (r % 16), so the 16 rows of a fragment
+    // read fall in distinct banks.  Rows past the stacked rows and K past
+    // the split are loaded from an offset past the buffer's range, which
+    // writes zeros.
+    static_assert(CPW == 1, "the window is one chunk");
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __align__(1024) T sx0[STK ? TROWS * KC : 1];
+    __shared__ __align__(1024) T sx1[STK ? TROWS * KC : 1];
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.X), (short)0, 0x7FFFFFFF, 0x00020000);
+    // every wave issues the same number of loads (a wave past the chunk's
+    // last load repeats it: the same bytes to the same place)
+    constexpr int NB = TROWS / 2;  // 1 KB loads of the chunk
+    constexpr int NQ = (NB + WAVES - 1) / WAVES;
+    auto dma = [&](T* dst, int kc0, int kcl) {
 #pragma unroll
-            for (int p = 0; p < XF; ++p) mma32(acc[t][mt], wf[t], xc[mt][p]);
-        load_step(w[u], kw + u + WIN);
-        // ordered: each step's refill is issued right after its MFMAs (the
-        // scheduler would otherwise sink all refills to the end of the
-        // chunk, and the next chunk would wait a full memory latency)
-        if constexpr (kOrdered) __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < CSTEPS) {
+      for (int q = 0; q < NQ; ++q) {
+        const int gi = min(q * WAVES + wave, NB - 1);  // wave-uniform
+        const int row = gi * 2 + (lane >> 5);
+        const int u = (lane & 31) ^ (row & 15);
+        const bool low = row >= mc;
+        const int m = a.row0 + (low ? row - mc : row);
+        const bool in = row < 2 * mc && u * 8 < kcl;
+        const uint32_t voff =
+            in ? (uint32_t)(((low ? (size_t)a.xlo : 0) + (size_t)m * a.ldx + kc0 + u * 8) *
+                            sizeof(T))
+               : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(dst + gi * 512), 16, voff, 0,
+                                                 0, 0);
+      }
+    };
+    // before a chunk is read: this wave's loads into it are done (they were
+    // issued just before one window of weight loads: LPS loads per tile per
+    // K-step, all issued in order after them), then every wave's are
+    constexpr int LPS = W12 ? 2 : 1;
+    constexpr int NAFTER = WIN * NTW * LPS;  // (the chunk's own loads: NQ, before them)
+    static_assert(NAFTER < 64, "vmcnt range");
+    constexpr int kWait = (NAFTER & 15) | ((NAFTER >> 4) << 14) | (7 << 4) | (15 << 8);
+    auto arrive = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWait);
+      __syncthreads();
+    };
+    auto swz = [](const T* buf) {
+      return [buf](int r, int kk, int) {
+        return buf + r * KC + ((((kk >> 3) ^ (r & 15))) << 3);
+      };
+    };
+    dma(sx0, kbeg, kend - kbeg);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+    for (int u = 0; u < WIN; ++u) load_step(w[u], kb_beg + u);
+    // the first chunk, then the rest in pairs (buffer 1, buffer 0): with the
+    // loop starting on buffer 1 the compiler's own load counting stays exact
+    // across the loop edge (it then waits only for the weights it uses)
+    arrive();
+    dma(sx1, (kb_beg + CSTEPS) * 32, kend - (kb_beg + CSTEPS) * 32);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_chunk(kb_beg, 0, swz(sx0));
+    for (int kw = kb_beg + CSTEPS; kw < kb_end; kw += 2 * CSTEPS) {
+      arrive();
+      dma(sx0, (kw + CSTEPS) * 32, kend - (kw + CSTEPS) * 32);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk(kw, 0, swz(sx1));
+      if (kw + CSTEPS < kb_end) {  // workgroup-uniform
+        arrive();
+        dma(sx1, (kw + 2 * CSTEPS) * 32, kend - (kw + 2 * CSTEPS) * 32);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_chunk(kw + CSTEPS, 0, swz(sx0));
+      }
+    }
+    // the loads of the chunk after the last (all zeros) land before the
+    // workgroup can end and its LDS be reused
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  } else {
+    // the first chunk is fetched now (before the W window, as in the steady
+    // state); each chunk is stored into LDS at its start and the next one is
+    // fetched into registers right after
+    fetch(kbeg, kend - kbeg);
 #pragma unroll
-            for (int p = 0; p < XF; ++p) xc[mt][p] = xn[mt][p];
-        }
+    for (int u = 0; u < WIN; ++u) load_step(w[u], kb_beg + u);
+
+    int buf = 0;
+    for (int kw = kb_beg; kw < kb_end; kw += WIN) {
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int k0 = (kw + cc * CSTEPS) * 32;  // first K index of this chunk
+        store(buf);
+        fetch(k0 + KC, kend - k0 - KC);
+        __syncthreads();
+        const T* hi = xbuf + buf * BUF_ELEMS;
+        buf ^= 1;
+        compute_chunk(kw, cc, [hi](int r, int kk, int pl) {
+          return hi + pl * TROWS * LDS_ROW + r * LDS_ROW + kk;
+        });
       }
     }
   }
@@ -431,7 +519,8 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
   const size_t stage_b =
       2 * (size_t)MT * 16 * (KC + (sizeof(T) == 2 ? 8 : 4)) * (STK ? 2 : 4);
   const size_t tile_b = (size_t)MT * 16 * (WAVES * NTW * 16 + 1) * 4;
-  const size_t lds = stage_b > tile_b ? stage_b : tile_b;
+  // stacked rows stage in static LDS; the dynamic area holds the result tile
+  const size_t lds = STK ? tile_b : (stage_b > tile_b ? stage_b : tile_b);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)k,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -455,7 +544,7 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 // MFMA and the LDS reads grow with the rows.  Here a wave owns a block of
 // RT row tiles x kTallCT column tiles: per K-step it reads RT x 2 activation
 // fragments (hi, lo) from LDS and kTallCT weight fragments from memory and
-// issues RT x kTallCT x 2 MFMAs, so each fragment feeds 2..kTallCT MFMAs.
+// issues RT x kTallCT x 2 MFMAs, so each fragment feeds several MFMAs.
 // A workgroup is kTallWM x kTallWN waves: kTallWM row groups (all of a
 // launch's rows up to 288, so a weight tile is streamed once per 288 rows)
 // by kTallWN column groups (128 columns).  Activations are staged one K-step
@@ -464,9 +553,13 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 // kernel, written from registers: split partials, SwiGLU (the gate and up
 // tiles of a pair are a wave's column tiles 2q and 2q + 1), and the per-row
 // argmax partial of the workgroup's 128 columns.
+// (3 x 4 waves of 6 x 2 tiles measured 158 us for the 8B gate/up at 288
+// rows against 169 us for 3 x 2 waves of 6 x 4 tiles, and 258 us for 64
+// columns a workgroup: each workgroup stages all its rows, so wider
+// column blocks stage less per MFMA)
 constexpr int kTallWM = 3;   // row groups
-constexpr int kTallWN = 2;   // column groups
-constexpr int kTallCT = 4;   // column tiles per wave
+constexpr int kTallWN = 4;   // column groups
+constexpr int kTallCT = 2;   // column tiles per wave
 constexpr int kTallWaves = kTallWM * kTallWN;
 constexpr int kTallCols = kTallWN * kTallCT * 16;  // columns of a workgroup (128)
 

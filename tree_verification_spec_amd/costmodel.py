@@ -229,11 +229,23 @@ def report(trace_dir, bench):
         "|---|---|---|---|---|---|---|",
     ]
     kt = kernel_table(raw)
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     for k in kt:
         lines.append(f"| `{k['kernel']}` | {k['grid'][0]}, {k['grid'][1]} | "
                      f"{k['per_step']:.2f} | {k['us_per_step']:.1f} | "
                      f"{k['us_per_step'] / fac['profiled_us']:.1%} | {k['avg_us']:.2f} | "
                      f"{k['median_us']:.2f} |")
+    if stats:
+        # rocprofv3 --stats over the whole traced run (every pass: prefill,
+        # the AR reference, verify steps), the largest total times
+        rows_s = sorted(csv.DictReader(open(stats[0])), key=lambda r: -float(r["TotalDurationNs"]))
+        lines += ["", "rocprofv3 --stats of the traced run (all passes), by total time:", "",
+                  "| kernel | calls | total ms | average us | min us | max us |",
+                  "|---|---|---|---|---|---|"]
+        for r in rows_s[:16]:
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} |")
     return "\n".join(lines) + "\n", dict(measured=measured, bound=bound, kernels=kt, **fac)
 
 
@@ -242,6 +254,8 @@ def main():
     ap.add_argument("--trace", required=True, help="rocprofv3 kernel-trace output directory")
     ap.add_argument("--bench", required=True, help="file holding bench.py's JSON line")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--commands", default=None,
+                    help="file holding the commands that produced the trace and the JSON line")
     a = ap.parse_args()
     bench = None
     for line in open(a.bench):
@@ -251,6 +265,10 @@ def main():
     if bench is None:
         raise SystemExit(f"no bench JSON line with a cost_model in {a.bench}")
     text, _ = report(a.trace, bench)
+    if a.commands:
+        head, rest = text.split("\n", 1)
+        text = (head + "\n\nCommands (from the repository root, on one MI355X):\n\n```\n" +
+                open(a.commands).read().strip() + "\n```\n" + rest)
     if a.out:
         with open(a.out, "w") as fh:
             fh.write(text)

@@ -850,9 +850,15 @@ hipError_t launch_tall_epi(int epi, const GemmArgs& a, const LaunchCtx& s) {
 // wave on 8 waves, and 96 us for 272 workgroups of 8, which leave a second
 // round); more tiles (the LM heads) rounds of 256 workgroups of at most 8
 // tiles (27B LM head 252 us against 268 us for 1188 workgroups of 8).  From
-// 41 rows with bf16 activations: the tall kernel, one workgroup per 128
-// columns (ntw 0).  fp32 models: one tile per wave on 8 waves.  Measured on
-// the 8B and 27B shapes, weights streamed from HBM.
+// 41 to 128 rows: 256 columns with two tiles per wave for wide matrices
+// (>= 128 blocks of 256 columns: the LM head; half the LDS reads per MFMA),
+// two tiles per wave on 4 waves for narrow ones up to 95 rows, and one tile
+// per wave on 8 waves from 96 rows (8 row tiles; two waves per SIMD instead
+// of one) (the 8B gate/up at 65 rows: 66 us, against 99 us for the tall
+// kernel's 96-row workgroups).  More than 128 rows with bf16 activations:
+// the tall kernel, one workgroup per 128 columns (ntw 0).  fp32 models: one
+// tile per wave on 8 waves.  Measured on the 8B and 27B shapes, weights
+// streamed from HBM.
 struct Variant {
   int ntw, waves, ncb;
 };
@@ -864,6 +870,10 @@ Variant gemm_variant(bool bf16, int N, int M) {
     if (nt <= 2048) return {1, 8, nt / 8};
     if (nt <= 2560) return {1, 10, 256};
     return {1, 8, 256 * ((nt + 2047) / 2048)};
+  }
+  if (M <= 128) {
+    if (N / 256 >= 128) return {2, 8, nt / 16};
+    return M >= 96 ? Variant{1, 8, nt / 8} : Variant{2, 4, nt / 8};
   }
   // more rows: the tall kernel (ntw 0), 128 columns a workgroup
   return {0, kTallWaves, N / kTallCols};

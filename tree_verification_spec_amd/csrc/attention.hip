@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "index_math.h"
 #include "kernels.h"
 
 namespace {
@@ -157,9 +158,9 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
         const int i = c / KCH_ROW, part = c % KCH_ROW;
         const int t = kbeg + i;
         if (t < kend) {
-          const int page = rm.page0 >= 0 ? rm.page0 + (t >> 4) : bt[t >> 4];
+          const int page = kv_page(rm.page0, bt, t);
           kr[j] = *reinterpret_cast<const uint4*>(
-              kc + (((size_t)page * a.nkv + kvh) * 16 + (t & 15)) * HD + part * EPC);
+              kc + kv_k_index(page, a.nkv, kvh, t & 15, HD, part * EPC));
         }
       }
       vr[j] = make_uint4(0, 0, 0, 0);
@@ -168,9 +169,9 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
         const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
         const int t0 = kbeg + blk * 16 + part * EPC;
         if (t0 < kend) {
-          const int page = rm.page0 >= 0 ? rm.page0 + (t0 >> 4) : bt[t0 >> 4];
+          const int page = kv_page(rm.page0, bt, t0);
           vr[j] = *reinterpret_cast<const uint4*>(
-              vc + (((size_t)page * a.nkv + kvh) * HD + dim) * 16 + (t0 & 15));
+              vc + kv_v_index(page, a.nkv, kvh, t0 & 15, HD, dim));
           T* ve = reinterpret_cast<T*>(&vr[j]);
 #pragma unroll
           for (int e = 0; e < EPC; ++e)  // keys past the end are not written this pass
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
     }
 
     if (qvalid) {
-      const size_t slot = (size_t)split * a.rows_total * a.nq + (size_t)grow * a.nq + qhead;
+      const size_t slot = attn_part_slot(split, a.rows_total, a.nq, grow, qhead);
       float* po = a.part_o + slot * HD;
 #pragma unroll
       for (int dt = 0; dt < HD / 16; ++dt)
@@ -361,8 +362,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   const int nsplit = (a.rows[grow].keys + a.split - 1) / a.split;  // <= 128
   const size_t sstride = (size_t)a.rows_total * a.nq;
   float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = ml0;
-  if (lane < nsplit) ml0 = a.part_ml[(size_t)lane * sstride + wid];
-  if (lane + 64 < nsplit) ml1 = a.part_ml[(size_t)(lane + 64) * sstride + wid];
+  if (lane < nsplit) ml0 = a.part_ml[attn_part_slot(lane, a.rows_total, a.nq, grow, qhead)];
+  if (lane + 64 < nsplit)
+    ml1 = a.part_ml[attn_part_slot(lane + 64, a.rows_total, a.nq, grow, qhead)];
   constexpr int PER = HD / 64;
   constexpr int U = 16;  // splits per wave loaded together
   const float* po = a.part_o + (size_t)wid * HD + lane * PER;

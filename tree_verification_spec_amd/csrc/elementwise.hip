@@ -1,6 +1,7 @@
 // Small kernels of the verify pass: embedding gather, RoPE + KV store, argmax reduction, accepted-path walk, the per-branch recurrence of
 // the hybrid layers, the commit kernels and the one-time weight re-layout.
 #include "common.h"
+#include "index_math.h"
 #include "kernels.h"
 
 // Products and sums are rounded separately, as written (RoPE and the
@@ -103,13 +104,13 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* qkv, size_t ss
         store_act(q_out, q_lo, base + i + half, y2);
       } else {
         const int kvh = head - nq;
-        T* dst = kc + (((size_t)page * nkv + kvh) * 16 + off) * hd;
+        T* dst = kc + kv_k_index(page, nkv, kvh, off, hd, 0);
         dst[i] = from_f<T>(y1);
         dst[i + half] = from_f<T>(y2);
       }
     } else {
       const int kvh = head - nq - nkv;
-      T* dst = vc + ((size_t)page * nkv + kvh) * hd * 16 + off;
+      T* dst = vc + kv_v_index(page, nkv, kvh, off, hd, 0);
       dst[(size_t)i * 16] = from_f<T>(x1);
       dst[(size_t)(i + half) * 16] = from_f<T>(x2);
     }
@@ -213,24 +214,7 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  int32_t* out = res + (size_t)r * (2 + max_path);
-  int best = 0;
-  ok[0] = 1;
-  dep[0] = 0;
-  for (int i = 1; i < n; ++i) {
-    const int p = par[i];
-    ok[i] = ok[p] && tok[i] == am[p];
-    dep[i] = dep[p] + 1;
-    if (ok[i] && dep[i] > dep[best]) best = i;
-  }
-  const int plen = dep[best];
-  out[0] = plen;
-  out[1] = am[best];
-  int v = best;
-  for (int k = plen - 1; k >= 0; --k) {
-    out[2 + k] = v;
-    v = par[v];
-  }
+  walk_accepted_path(n, par, tok, am, ok, dep, res + (size_t)r * (2 + max_path));
 }
 
 // ------------------------------------------------------ recurrence (verify)
@@ -563,18 +547,18 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int j = e / hd, dim = e % hd;
     const int t = q.nctx + q.nodes[j];
-    const int page = bt[t >> 4], off = t & 15;
-    buf[0][e] = kc[(((size_t)page * nkv + kvh) * 16 + off) * hd + dim];
-    buf[1][e] = vc[(((size_t)page * nkv + kvh) * hd + dim) * 16 + off];
+    const int page = kv_page(-1, bt, t), off = t & 15;
+    buf[0][e] = kc[kv_k_index(page, nkv, kvh, off, hd, dim)];
+    buf[1][e] = vc[kv_v_index(page, nkv, kvh, off, hd, dim)];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int j = e / hd, dim = e % hd;
     if (q.nodes[j] == j + 1) continue;  // already in place
     const int t = q.nctx + j + 1;
-    const int page = bt[t >> 4], off = t & 15;
-    kc[(((size_t)page * nkv + kvh) * 16 + off) * hd + dim] = buf[0][e];
-    vc[(((size_t)page * nkv + kvh) * hd + dim) * 16 + off] = buf[1][e];
+    const int page = kv_page(-1, bt, t), off = t & 15;
+    kc[kv_k_index(page, nkv, kvh, off, hd, dim)] = buf[0][e];
+    vc[kv_v_index(page, nkv, kvh, off, hd, dim)] = buf[1][e];
   }
 }
 

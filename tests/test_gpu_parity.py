@@ -778,12 +778,14 @@ def test_planted_argmax_ties_take_the_lowest_index():
 @pytest.mark.parametrize("name", ["tiny_hybrid", "tiny_hybrid_bf16"])
 def test_recurrent_walk_deep_trees_and_mixed_passes(name):
     """The recurrent layers walk trees depth-first with the root path's
-    states in registers: a 16-deep stack when every node of the pass is at
-    most 16 deep, a 64-deep one otherwise.  Cases: a tree 30 deep (a spine
-    with side branches), a pass mixing that tree with a 24-long chain, a
-    pass mixing a shallow tree with a 20-long chain (deep class because of
-    the chain), and a shallow tree alone; every row's logits against the
-    oracle's tree pass from the same committed state."""
+    states in registers when every node of the pass is at most 14 deep, and
+    recompute each node's state along its root path otherwise.  Cases: a
+    tree 30 deep (a spine with side branches), a pass mixing that tree with
+    a 24-long chain, a pass mixing a shallow tree with a 20-long chain (deep
+    class because of the chain), a shallow tree alone, and the two sides of
+    the class boundary (chains of 14 and 15 drafts beside a shallow tree);
+    every row's logits against the oracle's tree pass from the same
+    committed state."""
     cfg, W = _setup(name)
     V = cfg["vocab"]
     orc = oracle_for(cfg, W)
@@ -802,7 +804,7 @@ def test_recurrent_walk_deep_trees_and_mixed_passes(name):
     shallow = [-1, -1, 0, 0, 1, 2, 3, 3, 4, -1, 9]    # depth <= 4
     chain = lambda k: list(range(-1, k - 1))
     cases = [[(0, deep)], [(0, deep), (1, chain(24))], [(0, shallow), (1, chain(20))],
-             [(0, shallow)]]
+             [(0, shallow)], [(0, shallow), (1, chain(14))], [(0, shallow), (1, chain(15))]]
     worst = 0.0
     for case in cases:
         reqs = [r for r, _ in case]

@@ -172,17 +172,24 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // multiplies it by the row's scale, summing the chunks in order.
 // All chunk loads are issued together (nc <= 16: d <= 16384); the chunks are
 // added in order.
-__device__ __forceinline__ float row_scale(const RowNorm& n, int row) {
+// The scale in two parts, so a caller can issue other loads between them:
+// every lane loads 16 values (indexes past the row's chunks repeat its last
+// one), so the loads are unconditional and all in flight together.
+__device__ __forceinline__ void row_ss_load(const RowNorm& n, int row, float (&v)[16]) {
   const float* p = n.ss + (size_t)row * n.nc;
-  // every lane loads 16 values (indexes past the row's chunks repeat its
-  // last one), so the loads are unconditional and all in flight together
   const int last = n.nc > 0 ? n.nc - 1 : 0;
-  float v[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) v[c] = p[c < last ? c : last];
+}
+__device__ __forceinline__ float row_scale_of(const RowNorm& n, const float (&v)[16]) {
   float t = 0.f;
 #pragma unroll
   for (int c = 0; c < 16; ++c)
     if (c < n.nc) t += v[c];
   return 1.0f / sqrtf(t / (float)n.d + n.eps);
+}
+__device__ __forceinline__ float row_scale(const RowNorm& n, int row) {
+  float v[16];
+  row_ss_load(n, row, v);
+  return row_scale_of(n, v);
 }

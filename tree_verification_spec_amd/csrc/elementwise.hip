@@ -218,9 +218,9 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 }
 
 // ------------------------------------------------------ recurrence (verify)
-// A lane owns 4 states (s = 4 l + k, k = 0..3) of one channel c; the S / 4
-// lanes of a channel are adjacent, and a 256-thread workgroup covers
-// CPB = 1024 / S channels.  For node i
+// A lane owns SPL states (s = SPL l + k, k < SPL) of one channel c; the
+// S / SPL lanes of a channel are adjacent, and a workgroup of THR threads
+// covers CPB = THR SPL / S channels.  For node i
 //   H_i = sigmoid(a_i[c]) * H_parent + B_i[s] * x_i[c]   (no FMA contraction)
 //   y_i[c] = sum_s H_i[s] * C_i[s];  o_i[c] = y_i * silu(z_i[c])
 // where the root's parent state is the committed H_0.  The inputs of the
@@ -236,17 +236,16 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const RowMeta* rows,
 // that recompute every node's state along its root path from H_0.  Either
 // way a node's state comes from its own root path only, by the operations of
 // a sequential walk along that path, in the same order.  y is summed over a
-// lane's 4 states, then over the channel's lanes in one fixed order, the
-// same for every pass.
+// lane's states in order, then over the channel's lanes in one fixed order,
+// the same for every pass.
 constexpr int kLrTreeRows = 72;  // rows of a tree pass staged at once (max_nodes <= 65)
 constexpr int kLrSeg = 64;       // rows per staged segment of a chain pass
-constexpr int kLrStack = kLrRegisterDepth;  // root-path states kept in registers (depths 0..15)
-constexpr int kLrThreads = 256;
+constexpr int kLrStack = kLrRegisterDepth + 2;  // H_0, then the root path's states by depth
 
 typedef float lr_stack_t __attribute__((ext_vector_type(kLrStack)));
 
-// Sum of v over each aligned segment of L lanes (L = 4, 8 or 16); the sum is
-// exact in the segment's last lane.  L = 16: DPP row shifts (a row is 16
+// Sum of v over each aligned segment of L lanes (L = 2, 4, 8 or 16); the sum
+// is exact in the segment's last lane.  L = 16: DPP row shifts (a row is 16
 // lanes); smaller segments: a butterfly of lane exchanges.
 template <int L>
 __device__ __forceinline__ float seg_sum(float v) {
@@ -265,25 +264,60 @@ __device__ __forceinline__ float seg_sum(float v) {
   return v;
 }
 
+// N consecutive floats (N = 2, 4 or 8; p aligned to 4 N bytes, at most 16)
+// to or from registers by vector accesses.
+template <int N>
+__device__ __forceinline__ void lr_vload(float (&v)[N], const float* p) {
+  if constexpr (N == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4*>(p + 4 * q);
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void lr_vstore(float* p, const float (&v)[N]) {
+  if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      *reinterpret_cast<float4*>(p + 4 * q) =
+          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+}
+
 // Units per thread in one staging batch: enough for `units` (one batch)
 // but at most `cap` (and at least 1), which bounds the registers holding
 // loads in flight.
-constexpr int lr_batch(int units, int cap) {
-  const int need = (units + kLrThreads - 1) / kLrThreads;
+constexpr int lr_batch(int units, int cap, int threads) {
+  const int need = (units + threads - 1) / threads;
   const int c = cap > 0 ? cap : 1;
   return need < c ? need : c;
 }
 
-// MODE 0: chains; 1: trees of depth <= kLrStack (register stack); 2: deeper trees
-template <int S, int MODE, int NS>
-__global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
+// Lanes per channel and threads per workgroup of the walk for state width S:
+// 4 states a lane, 256 threads.
+constexpr int lr_spl(int S) { return 4; }
+constexpr int lr_threads(int S) { return 256; }
+
+// MODE 0: chains; 1: trees of depth <= kLrRegisterDepth (register stack);
+// 2: deeper trees
+template <int S, int MODE, int NS, int SPL, int THR>
+__global__ __launch_bounds__(THR) void lr_fork_kernel(
     const float* __restrict__ proj, size_t sstride, int ld, const RowMeta* __restrict__ rows,
     const ReqMeta* __restrict__ reqs, int d, float* __restrict__ H, void* o, size_t olo,
     bool obf, float* save, bool commit_last, RowNorm norm) {
   static_assert(S == 16 || S == 32 || S == 64, "state width");
   constexpr bool TREE = MODE > 0;
-  constexpr int LPC = S / 4;                 // lanes per channel
-  constexpr int CPB = kLrThreads / LPC;      // channels per workgroup
+  static_assert(SPL == 2 || SPL == 4 || SPL == 8, "states per lane");
+  constexpr int LPC = S / SPL;               // lanes per channel
+  constexpr int CPB = THR / LPC;             // channels per workgroup
+  static_assert(CPB % 4 == 0 && THR >= kLrTreeRows && THR >= kLrSeg, "workgroup shape");
   constexpr int ROWS = TREE ? kLrTreeRows : kLrSeg;
   constexpr int XU = CPB / 4;                // 4-channel units of x, a, z per row
   constexpr int BU = S / 2;                  // 4-value units of B and C per row
@@ -301,32 +335,73 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
   const int c = blockIdx.x * CPB + lc;
   const bool live = c < d;
   const int cc = live ? c : 0;
-  float* H0 = H + ((size_t)rm.table * d + cc) * S + 4 * l;
-  const float4 h0 = *reinterpret_cast<const float4*>(H0);
-  float hp0 = h0.x, hp1 = h0.y, hp2 = h0.z, hp3 = h0.w;  // chains: the running states
-  lr_stack_t st0 = {}, st1 = {}, st2 = {}, st3 = {};  // trees: root-path states by depth
-  for (int i0 = 0; i0 < rm.nrows; i0 += ROWS) {
+  float* H0 = H + ((size_t)rm.table * d + cc) * S + SPL * l;
+  float h0[SPL];
+  lr_vload<SPL>(h0, H0);
+  float hp[SPL];  // chains: the running states
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) hp[k] = h0[k];
+  if (rm.nrows <= 0) return;
+  // a tree pass is one segment (its rows fit kLrTreeRows): straight-line
+  // code, so no load waits at a loop header
+  const int seg_end = TREE ? 1 : rm.nrows;
+  for (int i0 = 0; i0 < seg_end; i0 += ROWS) {
     const int n = min(ROWS, rm.nrows - i0);
+    // staging in batches: a batch's loads (the NS split partials of x, a, z
+    // of the workgroup's channels, and of the rows' B and C) are all issued
+    // before any is summed, from indexes clamped to the last unit so that
+    // the loads are unconditional (no branch between them, so none waits for
+    // another); only the stores are guarded.  The first batch's loads go out
+    // with the rows' norm-scale loads, so the two round trips overlap.
+    // (more than 8 partials: the first 8 are in flight together, the rest
+    // are loaded and added in groups of 8 afterwards, in split order)
+    constexpr int G = NS < 8 ? NS : 8;
+    constexpr int UA = lr_batch(ROWS * XU, 6 / (3 * G), THR);  // x/a/z units per thread
+    constexpr int UB = lr_batch(ROWS * BU, 12 / G, THR);       // B/C units per thread
+    const float* pbase = proj + (size_t)(rm.row0 + i0) * ld;
+    const int na = n * XU, nb = n * BU;  // units of this segment (n >= 1)
+    // the first column of x/a/z unit q of a row (a partial workgroup's
+    // surplus units repeat the last channels)
+    auto a_col = [&](int q) { return min((int)blockIdx.x * CPB + q * 4, d - 4); };
+    float4 ta[UA][3][G], tb[UB][G];
+    auto issue = [&](int ea, int eb) {
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int e = min(ea + (int)threadIdx.x + u * THR, na - 1);
+        const float* p = pbase + (size_t)(e / XU) * ld + a_col(e % XU);
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < G; ++s2)
+            ta[u][t][s2] = *reinterpret_cast<const float4*>(p + t * d + s2 * sstride);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int e = min(eb + (int)threadIdx.x + u * THR, nb - 1);
+        const float* p = pbase + (size_t)(e / BU) * ld + 3 * d + 4 * (e % BU);
+#pragma unroll
+        for (int s2 = 0; s2 < G; ++s2)
+          tb[u][s2] = *reinterpret_cast<const float4*>(p + s2 * sstride);
+      }
+    };
+    // the rows' norm-scale chunks and metadata (thread t: row min(t, n - 1))
+    // first, then the first batch, all in flight together
+    const int tr = min((int)threadIdx.x, n - 1);
+    float ssv[16];
+    row_ss_load(norm, rm.row0 + i0 + tr, ssv);
+    RowMeta m{};
+    if (TREE) m = rows[rm.row0 + tr];
     __syncthreads();  // the previous segment's values are no longer read
+    issue(0, 0);
     if ((int)threadIdx.x < n) {
-      scs[threadIdx.x] = row_scale(norm, rm.row0 + i0 + threadIdx.x);
+      scs[threadIdx.x] = row_scale_of(norm, ssv);
       if (TREE) {
-        const RowMeta m = rows[rm.row0 + threadIdx.x];
         sord[threadIdx.x] = m.order;
         sdep[threadIdx.x] = m.pos - rm.nctx;
         spar[threadIdx.x] = m.parent;
       }
     }
-    // staging in batches: a batch's loads (the NS split partials of x, a, z
-    // of the workgroup's channels, and of the rows' B and C) are all issued
-    // before any is summed; x/a/z units and B/C units have loops of their
-    // own, so a wavefront's lanes take the same branch
-    // (more than 8 partials: the first 8 are in flight together, the rest
-    // are loaded and added in groups of 8 afterwards, in split order)
-    constexpr int G = NS < 8 ? NS : 8;
-    constexpr int UA = lr_batch(ROWS * XU, 6 / (3 * G));   // x/a/z units per thread
-    constexpr int UB = lr_batch(ROWS * BU, 12 / G);        // B/C units per thread
-    const float* pbase = proj + (size_t)(rm.row0 + i0) * ld;
+    __syncthreads();  // scs
     // split-ordered sum of a unit's partials (the first G given), scaled
     auto sum = [&](const float4 (&t)[G], const float* p, float sc) {
       float4 v = t[0];
@@ -353,42 +428,15 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       }
       return make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
     };
-    for (int ea = 0, eb = 0; ea < n * XU || eb < n * BU;
-         ea += kLrThreads * UA, eb += kLrThreads * UB) {
-      float4 ta[UA][3][G], tb[UB][G];
+    for (int ea = 0, eb = 0; ea < na || eb < nb; ea += THR * UA, eb += THR * UB) {
+      if (ea > 0 || eb > 0) issue(ea, eb);
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
-        const int e = ea + threadIdx.x + u * kLrThreads;
-        if (e < n * XU) {
-          const int j = e / XU, q = e % XU;
-          const int ch = min((int)blockIdx.x * CPB + q * 4, d - 4);
-          const float* p = pbase + (size_t)j * ld + ch;
-#pragma unroll
-          for (int t = 0; t < 3; ++t)
-#pragma unroll
-            for (int s2 = 0; s2 < G; ++s2)
-              ta[u][t][s2] = *reinterpret_cast<const float4*>(p + t * d + s2 * sstride);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int e = eb + threadIdx.x + u * kLrThreads;
-        if (e < n * BU) {
-          const int j = e / BU, k = e % BU;
-          const float* p = pbase + (size_t)j * ld + 3 * d + 4 * k;
-#pragma unroll
-          for (int s2 = 0; s2 < G; ++s2)
-            tb[u][s2] = *reinterpret_cast<const float4*>(p + s2 * sstride);
-        }
-      }
-      __syncthreads();  // scs
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const int e = ea + threadIdx.x + u * kLrThreads;
-        if (e < n * XU) {
+        const int e = ea + threadIdx.x + u * THR;
+        if (e < na) {
           const int j = e / XU, q = e % XU;
           const float sc = scs[j];
-          const float* p = pbase + (size_t)j * ld + min((int)blockIdx.x * CPB + q * 4, d - 4);
+          const float* p = pbase + (size_t)j * ld + a_col(q);
           const float4 x = sum(ta[u][0], p, sc), a = sum(ta[u][1], p + d, sc),
                        z = sum(ta[u][2], p + 2 * d, sc);
           sgx[j][4 * q] = make_float4(1.0f / (1.0f + expf(-a.x)), x.x,
@@ -403,8 +451,8 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const int e = eb + threadIdx.x + u * kLrThreads;
-        if (e < n * BU) {
+        const int e = eb + threadIdx.x + u * THR;
+        if (e < nb) {
           const int j = e / BU, k = e % BU;
           *reinterpret_cast<float4*>(&sbc[j][4 * k]) =
               sum(tb[u], pbase + (size_t)j * ld + 3 * d + 4 * k, scs[j]);
@@ -418,6 +466,13 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
     // flight ahead of the one being computed (alternating register sets, no
     // copies), and each node's output goes to LDS, written out coalesced
     // after the walk.
+    // trees: H_0, then the states of the current root path's nodes by depth + 1
+    lr_stack_t st[SPL];
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      st[k] = lr_stack_t{};
+      st[k][0] = h0[k];
+    }
     int ordw0 = 0, ordw1 = 0;  // node | depth << 8 of positions lane, 64 + lane
     {
       const int lane = threadIdx.x & 63;
@@ -433,52 +488,52 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
     };
     struct In {
       float4 gx;  // sigmoid(a), x, silu(z), a
-      float4 b, c;
+      float b[SPL], c[SPL];
     };
     auto fetch = [&](int j) {
       In v;
       v.gx = sgx[j][lc];
-      v.b = *reinterpret_cast<const float4*>(&sbc[j][4 * l]);
-      v.c = *reinterpret_cast<const float4*>(&sbc[j][S + 4 * l]);
+      lr_vload<SPL>(v.b, &sbc[j][SPL * l]);
+      lr_vload<SPL>(v.c, &sbc[j][S + SPL * l]);
       return v;
     };
     // one node's update from its parent's states
-    auto step = [&](const In& v, float& a0, float& a1, float& a2, float& a3) {
-      a0 = ((v.gx.x * a0) + (v.b.x * v.gx.y));
-      a1 = ((v.gx.x * a1) + (v.b.y * v.gx.y));
-      a2 = ((v.gx.x * a2) + (v.b.z * v.gx.y));
-      a3 = ((v.gx.x * a3) + (v.b.w * v.gx.y));
+    auto step = [&](const In& v, float (&a)[SPL]) {
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) a[k] = ((v.gx.x * a[k]) + (v.b[k] * v.gx.y));
     };
     auto node = [&](const In& cur, int wk) {
       const int j = wk & 0xFF, dj = wk >> 8;
-      float a0, a1, a2, a3;
+      float a[SPL];
       if constexpr (MODE == 1) {
-        if (dj == 0) {
-          a0 = h0.x; a1 = h0.y; a2 = h0.z; a3 = h0.w;
-        } else {
-          a0 = st0[dj - 1]; a1 = st1[dj - 1]; a2 = st2[dj - 1]; a3 = st3[dj - 1];
-        }
-        step(cur, a0, a1, a2, a3);
-        if (dj < kLrStack) {  // a node of depth kLrStack is a leaf
-          st0[dj] = a0; st1[dj] = a1; st2[dj] = a2; st3[dj] = a3;
-        }
+        // the parent's state is entry dj (H_0 for the root); every node's
+        // state goes to entry dj + 1 unconditionally (no node of this class
+        // is deeper than the last entry): a guarded insert into a register
+        // vector compiles to a copy and a select of the whole vector
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) a[k] = st[k][dj];
+        step(cur, a);
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) st[k][dj + 1] = a[k];
       } else if constexpr (MODE == 2) {
         // recompute along the root path of j, root first
-        a0 = h0.x; a1 = h0.y; a2 = h0.z; a3 = h0.w;
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) a[k] = h0[k];
         for (int t = 0; t <= dj; ++t) {
           int v = j;  // the ancestor of j at depth t
           for (int u = dj; u > t; --u) v = spar[v];
-          step(fetch(__builtin_amdgcn_readfirstlane(v)), a0, a1, a2, a3);
+          step(fetch(__builtin_amdgcn_readfirstlane(v)), a);
         }
       } else {
-        a0 = hp0; a1 = hp1; a2 = hp2; a3 = hp3;
-        step(cur, a0, a1, a2, a3);
-        hp0 = a0; hp1 = a1; hp2 = a2; hp3 = a3;
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) a[k] = hp[k];
+        step(cur, a);
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) hp[k] = a[k];
       }
-      float y = (a0 * cur.c.x);
-      y = (y + (a1 * cur.c.y));
-      y = (y + (a2 * cur.c.z));
-      y = (y + (a3 * cur.c.w));
+      float y = (a[0] * cur.c[0]);
+#pragma unroll
+      for (int k = 1; k < SPL; ++k) y = (y + (a[k] * cur.c[k]));
       y = seg_sum<LPC>(y);
       if (l == LPC - 1) so[j][lc] = y * cur.gx.z;
     };
@@ -500,7 +555,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < n * CPB; e += kLrThreads) {
+    for (int e = threadIdx.x; e < n * CPB; e += THR) {
       const int j = e / CPB, q = e % CPB;
       const int ch = blockIdx.x * CPB + q;
       if (ch >= d) continue;
@@ -509,7 +564,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
       else store_act((float*)o, (float*)o + olo, oi, so[j][q]);
     }
     if (save) {  // [x | a | B] of every row, for the commit
-      for (int e = threadIdx.x; e < n * CPB; e += kLrThreads) {
+      for (int e = threadIdx.x; e < n * CPB; e += THR) {
         const int j = e / CPB, q = e % CPB;
         const int ch = blockIdx.x * CPB + q;
         if (ch >= d) continue;
@@ -519,14 +574,13 @@ __global__ __launch_bounds__(kLrThreads) void lr_fork_kernel(
         save[row * (2 * d + S) + d + ch] = v.w;
       }
       if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e < n * S; e += kLrThreads) {
+        for (int e = threadIdx.x; e < n * S; e += THR) {
           const int j = e / S, q = e % S;
           save[(size_t)(rm.row0 + i0 + j) * (2 * d + S) + 2 * d + q] = sbc[j][q];
         }
     }
   }
-  if (commit_last && live)
-    *reinterpret_cast<float4*>(H0) = make_float4(hp0, hp1, hp2, hp3);
+  if (commit_last && live) lr_vstore<SPL>(H0, hp);
 }
 
 // ----------------------------------------------------------- KV compaction
@@ -725,18 +779,19 @@ static hipError_t lr_fork_s(const float* proj, size_t sstride, int ld,
                             float* H, void* o, size_t olo, bool obf, float* save, int tree_depth,
                             bool commit_last, int max_rows_per_req, RowNorm norm,
                             hipStream_t s) {
-  constexpr int CPB = kLrThreads / (S / 4);
+  constexpr int SPL = lr_spl(S), THR = lr_threads(S);
+  constexpr int CPB = THR / (S / SPL);
   if (tree_depth > 0 && max_rows_per_req > kLrTreeRows) return hipErrorInvalidValue;
   dim3 grid((d + CPB - 1) / CPB, n_req);
   if (tree_depth > kLrRegisterDepth)
-    lr_fork_kernel<S, 2, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
-                                                         olo, obf, save, commit_last, norm);
+    lr_fork_kernel<S, 2, NS, SPL, THR><<<grid, THR, 0, s>>>(proj, sstride, ld, rows, reqs, d, H,
+                                                            o, olo, obf, save, commit_last, norm);
   else if (tree_depth > 0)
-    lr_fork_kernel<S, 1, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
-                                                         olo, obf, save, commit_last, norm);
+    lr_fork_kernel<S, 1, NS, SPL, THR><<<grid, THR, 0, s>>>(proj, sstride, ld, rows, reqs, d, H,
+                                                            o, olo, obf, save, commit_last, norm);
   else
-    lr_fork_kernel<S, 0, NS><<<grid, kLrThreads, 0, s>>>(proj, sstride, ld, rows, reqs, d, H, o,
-                                                         olo, obf, save, commit_last, norm);
+    lr_fork_kernel<S, 0, NS, SPL, THR><<<grid, THR, 0, s>>>(proj, sstride, ld, rows, reqs, d, H,
+                                                            o, olo, obf, save, commit_last, norm);
   return hipGetLastError();
 }
 

@@ -190,8 +190,9 @@ hipError_t launch_path_walk(const RowMeta* rows, const ReqMeta* reqs,
 // rows' depth-first order (RowMeta.order) with depth = pos - the request's
 // nctx.
 // Deepest node depth that the recurrent walk keeps on its register stack
-// (deeper trees recompute each node's state along its root path).
-constexpr int kLrRegisterDepth = 16;
+// (16 entries: H_0, then one per depth 0..14; deeper trees recompute each
+// node's state along its root path).
+constexpr int kLrRegisterDepth = 14;
 hipError_t launch_lr_fork(bool bf16, const float* proj, int NS, size_t split_stride,
                           int ld, const RowMeta* rows, const ReqMeta* reqs, int n_req,
                           int d, int S, float* H, void* o, size_t o_lo, float* save,

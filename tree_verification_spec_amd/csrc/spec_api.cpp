@@ -1219,9 +1219,9 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
   HIP_TRY(hipMemcpyAsync(c->d_meta, c->h_meta, c->meta_bytes, hipMemcpyHostToDevice,
                          c->stream));
   // the recurrent walk of a pass with a tree walks every request as a tree
-  // (a chain is a tree); its depth class: a 16-entry register stack unless a
-  // node of the pass is deeper (one class per pass keeps the captured graphs
-  // few)
+  // (a chain is a tree); its depth class: a register stack (depths 0..14)
+  // unless a node of the pass is deeper (one class per pass keeps the
+  // captured graphs few)
   const int depth_class = !any_tree ? 0 : max_depth <= kLrRegisterDepth ? kLrRegisterDepth : 64;
   rc = forward(c, R, n_req, keys, nrows, depth_class, 0, R, d_logits_opt, false, true, lowp);
   if (rc) return rc;

@@ -19,6 +19,17 @@
 // the cache so that the V^T operand is read directly.  Each split writes
 // un-normalised partials (O, running max of the scores scaled by log2 e,
 // running sum), merged in split order by attn_combine.
+//
+// Streamed variant (a request with at most 8 query tiles per KV head:
+// batched verify passes, chains): a workgroup owns one range of keys of one
+// (request, KV head) and walks it in stages of 64 keys.  The next stage's K
+// and V are loaded into registers while the current one (in LDS) is used,
+// so a workgroup keeps loads in flight for its whole range instead of
+// loading once and computing once.  All 8 waves compute: wave w takes
+// query tile w % qt and every kp-th 32-key block (kp = 4, 2 or 1, the
+// largest with qt * kp <= 8, from block w / qt), and the kp states of a tile
+// are merged in LDS, pairwise in block-part order, before the range's
+// partial is written.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -77,8 +88,232 @@ __device__ __forceinline__ void pack_p(Frag<float>& f, const float* p) {
 __device__ __forceinline__ float op_round(float x, uint16_t) { return bf2f(f2bf(x)); }
 __device__ __forceinline__ float op_round(float x, float) { return x; }
 
+// One 32-key block [kb, kb + 32) of a staged split or stage against one
+// query tile: scores S^T = K Q^T for the block's two 16-key tiles, the
+// row's visibility mask, the online softmax update of (m_run, l_run, o) and
+// O^T += V^T P^T.  sk: K rows [.][KS] with the block's first key at row
+// kl; sv: V^T [HD][vs] with it at column kl.  Lane (g, r16) holds query row
+// r16 of the tile (node `node` of the request; rows past the pass are
+// !qvalid and see no key).
+template <typename T, int HD, int KS>
+__device__ __forceinline__ void attn_block(const T* sk, const T* sv, int vs, int kl, int kb,
+                                           int kend, const ReqMeta& rm, int node, bool qvalid,
+                                           uint64_t anc_lo, uint64_t anc_hi,
+                                           const Frag<T> (&qf)[HD / 32],
+                                           const Frag<T> (&qfl)[HD / 32], float scale2, int g,
+                                           int r16, float& m_run, float& l_run,
+                                           floatx4_t (&o)[HD / 16]) {
+  constexpr bool kSplit = sizeof(T) == 2;
+  // all K fragments of the block are read from LDS first, then the two
+  // independent score chains are interleaved (hi and lo halves of q
+  // accumulate separately: four chains of HD / 32 dependent MFMAs)
+  floatx4_t s[2], sl[2];
+  Frag<T> kf[2][HD / 32];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks)
+      kf[kt][ks].load(&sk[(size_t)(kl + kt * 16 + r16) * KS + ks * 32 + g * 8]);
+  s[0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  s[1] = s[0];
+  sl[0] = s[0];
+  sl[1] = s[0];
+#pragma unroll
+  for (int ks = 0; ks < HD / 32; ++ks) {
+    mma32(s[0], kf[0][ks], qf[ks]);
+    mma32(s[1], kf[1][ks], qf[ks]);
+    if (kSplit) {
+      mma32(sl[0], kf[0][ks], qfl[ks]);
+      mma32(sl[1], kf[1][ks], qfl[ks]);
+    }
+  }
+  if (kSplit) {
+    s[0] += sl[0];
+    s[1] += sl[1];
+  }
+  // visibility of the block's 32 keys for this lane's row, as a bit mask
+  // (bit i: key kb + i): keys past the range end are out; committed keys
+  // are in; a pass key (tree node tn = key - nctx) is in along a chain up to
+  // the row's own node, in a tree when tn is an ancestor or itself.  A block
+  // of committed keys only (the common case) needs no mask arithmetic.
+  uint32_t vis = 0;
+  if (kb + 32 <= rm.nctx && kb + 32 <= kend) {  // uniform
+    vis = qvalid ? 0xffffffffu : 0u;
+  } else if (qvalid) {
+    auto low_bits = [](int n) -> uint32_t {
+      return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : ((1u << n) - 1u);
+    };
+    const int c = rm.nctx - kb;  // committed keys in the block: [0, c)
+    uint32_t pass;
+    if (rm.chain) {
+      pass = low_bits(c + node + 1);
+    } else {
+      // block bit i <-> tree node i - c: the ancestor mask shifted by c
+      const int sh = -c;  // node of block bit 0 (may be negative)
+      uint64_t w;
+      if (sh >= 0) {
+        w = sh >= 128 ? 0 : sh >= 64 ? (anc_hi >> (sh - 64))
+                      : sh == 0 ? anc_lo : ((anc_lo >> sh) | (anc_hi << (64 - sh)));
+      } else {
+        w = -sh >= 64 ? 0 : (anc_lo << (-sh));
+      }
+      pass = (uint32_t)w;
+    }
+    vis = (low_bits(c) | pass) & low_bits(kend - kb);
+  }
+  // lane holds row r16, keys kb + kt*16 + 4g + r; scores in the base-2
+  // domain (scaled by log2 e) so that every weight is one v_exp_f32
+  float p[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (vis >> (kt * 16 + 4 * g + r)) & 1u;
+      const float v = ok ? s[kt][r] * scale2 : -INFINITY;
+      p[kt * 4 + r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = quad_max(mx);
+  // No lane may skip the MFMAs below (they read operands of all lanes), so
+  // a row with nothing visible yet uses a finite stand-in maximum: every
+  // weight is then 2^-inf = 0 and the state stays (-inf, 0, O = 0).
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 2^-inf = 0
+  float lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(p[e] - m_use);  // hidden keys: 2^-inf = 0
+    lsum += p[e];
+  }
+  lsum = quad_sum(lsum);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  // rescale only when some row's maximum moved (alpha is exactly 1
+  // otherwise, so skipping changes no bit)
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) o[dt] *= alpha;
+  }
+
+  // P as an operand of the KV type; for bf16 it is carried as a hi + lo
+  // pair (two MFMAs), which keeps ~16 mantissa bits of the weights
+  Frag<T> pf, pf_lo;
+  if (kSplit) {
+    float lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo[e] = p[e] - op_round(p[e], T(0));
+    pack_p(pf_lo, lo);
+  }
+  pack_p(pf, p);
+  // V fragments in groups of four dim tiles, read before their MFMAs
+#pragma unroll
+  for (int d0 = 0; d0 < HD / 16; d0 += 4) {
+    Frag<T> vf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const T* vrow = sv + (size_t)((d0 + u) * 16 + r16) * vs + kl;
+      load_vfrag<T>(vf[u], vrow + 4 * g, vrow + 16 + 4 * g);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf);
+    if (kSplit) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf_lo);
+    }
+  }
+}
+
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = kAttnWaves * 64;
+static_assert(kAttnStreamTiles <= kAttnWaves, "a streamed tile per wave");
+
+// Staging of one split (at most kMaxSplitKeys keys from kbeg) in chunks of
+// 16 bytes: thread t takes chunk t + j * kAttnThreads (j < NC) of K and of
+// V.  The loads are unconditional (chunk indexes past the split's repeat its
+// last chunk, keys past kend read the last key's page slots; spg holds the
+// split's pages, one per 16 keys) and the data is only stored to LDS
+// afterwards, so all of a thread's loads are in flight together.  (Loads
+// under per-lane conditions made the compiler wait for each one before
+// issuing the next.)
+template <typename T, int NC>
+struct SplitChunks {
+  uint4 k[NC], v[NC];
+};
+
+template <typename T, int HD, int NC>
+__device__ __forceinline__ SplitChunks<T, NC> split_issue(const T* kc, const T* vc,
+                                                          const int* spg, int nkv, int kvh,
+                                                          int kbeg, int nkeys, int kch) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int KCH_ROW = HD / EPC;
+  constexpr int VCH_ROW = 16 / EPC;
+  static_assert(KCH_ROW * 16 == HD * VCH_ROW, "as many V chunks as K chunks");
+  const int nslots = (nkeys + 15) >> 4;
+  SplitChunks<T, NC> r;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = min((int)threadIdx.x + j * kAttnThreads, kch - 1);
+    {
+      const int i = min(c / KCH_ROW, nkeys - 1), part = c % KCH_ROW;
+      r.k[j] = *reinterpret_cast<const uint4*>(
+          kc + kv_k_index(spg[i >> 4], nkv, kvh, (kbeg + i) & 15, HD, part * EPC));
+    }
+    {
+      // chunk c of V: page blk = c / (HD * VCH_ROW), then (dim, part) in the
+      // page's [dim][16 keys] order, so a wave reads contiguous memory
+      const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+      const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
+      r.v[j] = *reinterpret_cast<const uint4*>(
+          vc + kv_v_index(spg[min(blk, nslots - 1)], nkv, kvh, part * EPC, HD, dim));
+    }
+  }
+  return r;
+}
+
+// The chunks into LDS (K rows [key][KS], V^T [dim][vs]); V of keys past kend
+// (not written this pass) is cleared there after its chunk is stored (K of
+// those keys is masked out of the scores).
+// Chunks past the split's (c >= kch) are stored to `spill`, a 16-byte LDS
+// slot that nothing reads, so that every store is unconditional (a guarded
+// store let the compiler move its load under the guard, behind the wait for
+// the previous chunk).
+template <typename T, int HD, int KS, int NC>
+__device__ __forceinline__ void split_place(const SplitChunks<T, NC>& r, T* sk, T* sv, int vs,
+                                            int kbeg, int kend, int kch, uint4* spill) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int KCH_ROW = HD / EPC;
+  constexpr int VCH_ROW = 16 / EPC;
+  // every store first (one basic block, so no load is moved down to a
+  // guarded use), then the clearing of V past kend
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = threadIdx.x + j * kAttnThreads;
+    const bool in = c < kch;
+    {
+      const int i = c / KCH_ROW, part = c % KCH_ROW;
+      *(in ? reinterpret_cast<uint4*>(&sk[(size_t)i * KS + part * EPC]) : spill) = r.k[j];
+    }
+    const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+    const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
+    *(in ? reinterpret_cast<uint4*>(&sv[(size_t)dim * vs + blk * 16 + part * EPC]) : spill) =
+        r.v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = threadIdx.x + j * kAttnThreads;
+    const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+    const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
+    const int t0 = kbeg + blk * 16 + part * EPC;
+    if (c < kch && t0 + EPC > kend) {
+      T* dst = &sv[(size_t)dim * vs + blk * 16 + part * EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e)
+        if (t0 + e >= kend) dst[e] = T(0);
+    }
+  }
+}
 
 template <typename T, int HD>
 __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
@@ -130,67 +365,61 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  // the wave's first tile is fetched before the K/V staging (its latency
-  // overlaps the staging's)
+  // ancestor masks of a tile's row for this lane
+  auto load_anc = [&](int qtile, uint64_t& lo, uint64_t& hi) {
+    const int qr = qtile * 16 + r16;
+    lo = 0;
+    hi = 0;
+    if (qtile < t_end && qr < qrows && !rm.chain) {
+      const uint64_t* am = a.anc + rm.anc0 + (size_t)(qr / G) * rm.anc_words;
+      lo = am[0];
+      if (rm.anc_words > 1) hi = am[1];
+    }
+  };
+  // the split's pages (one per 16 keys), looked up once into LDS before any
+  // other load is in flight
+  __shared__ int spg[kMaxSplitKeys / 16];
+  __shared__ uint4 spill;  // the target of chunk stores past the split (never read)
+  if ((int)threadIdx.x < (kend - kbeg + 15) >> 4)
+    spg[threadIdx.x] = kv_page(rm.page0, bt, kbeg + 16 * threadIdx.x);
+  __syncthreads();
+  // the wave's first tile (q and ancestor masks) is fetched before the K/V
+  // staging (its latency overlaps the staging's)
   Frag<T> qf[HD / 32], qfl[HD / 32];
   load_q(t_beg + wave, qf, qfl);
+  uint64_t anc_lo, anc_hi;
+  load_anc(t_beg + wave, anc_lo, anc_hi);
   asm volatile("" ::: "memory");  // keep these loads ahead of the staging
 
   constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
   constexpr int KCH_ROW = HD / EPC;              // chunks per K row
   constexpr int VCH_ROW = 16 / EPC;              // chunks per (dim, 16 keys)
-  // ---- stage the whole split (K rows and V^T) with every load in flight;
-  // keys are padded with zeros to a multiple of 32
+  // ---- stage the whole split (K rows and V^T, padded with zeros to a
+  // multiple of 32 keys) with every load in flight, NC chunks of each per
+  // thread, NC as small as the split allows
   {
-    const int nkeys = kend - kbeg;                 // <= a.split <= kMaxSplitKeys
-    const int kch = ((nkeys + 31) & ~31) * KCH_ROW;
-    const int vblk = ((nkeys + 31) & ~31) / 16;    // 16-key pages of the split
-    const int vch = vblk * HD * VCH_ROW;
-    // chunk c of V: page blk = c / (HD * VCH_ROW), then (dim, part) in the
-    // page's [dim][16 keys] order, so a wave reads contiguous memory
-    constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / kAttnThreads;  // per thread, each of K, V
-    uint4 kr[MAXCH], vr[MAXCH];
-#pragma unroll
-    for (int j = 0; j < MAXCH; ++j) {
-      const int c = threadIdx.x + j * kAttnThreads;
-      kr[j] = make_uint4(0, 0, 0, 0);
-      if (c < kch) {
-        const int i = c / KCH_ROW, part = c % KCH_ROW;
-        const int t = kbeg + i;
-        if (t < kend) {
-          const int page = kv_page(rm.page0, bt, t);
-          kr[j] = *reinterpret_cast<const uint4*>(
-              kc + kv_k_index(page, a.nkv, kvh, t & 15, HD, part * EPC));
-        }
-      }
-      vr[j] = make_uint4(0, 0, 0, 0);
-      if (c < vch) {
-        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
-        const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
-        const int t0 = kbeg + blk * 16 + part * EPC;
-        if (t0 < kend) {
-          const int page = kv_page(rm.page0, bt, t0);
-          vr[j] = *reinterpret_cast<const uint4*>(
-              vc + kv_v_index(page, a.nkv, kvh, t0 & 15, HD, dim));
-          T* ve = reinterpret_cast<T*>(&vr[j]);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e)  // keys past the end are not written this pass
-            if (t0 + e >= kend) ve[e] = T(0);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < MAXCH; ++j) {
-      const int c = threadIdx.x + j * kAttnThreads;
-      if (c < kch) {
-        const int i = c / KCH_ROW, part = c % KCH_ROW;
-        *reinterpret_cast<uint4*>(&sk[(size_t)i * L::KS + part * EPC]) = kr[j];
-      }
-      if (c < vch) {
-        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
-        const int dim = rest / VCH_ROW, part = rest % VCH_ROW;
-        *reinterpret_cast<uint4*>(&sv[(size_t)dim * VS + blk * 16 + part * EPC]) = vr[j];
-      }
+    const int nkeys = kend - kbeg;  // <= a.split <= kMaxSplitKeys
+    const int kch = ((nkeys + 31) & ~31) * KCH_ROW;  // chunks of K, and of V
+    constexpr int MAXCH = kMaxSplitKeys * KCH_ROW / kAttnThreads;
+    static_assert(MAXCH >= 1 && MAXCH * kAttnThreads == kMaxSplitKeys * KCH_ROW,
+                  "chunks per thread");
+    const int nc = (kch + kAttnThreads - 1) / kAttnThreads;  // uniform
+    if (nc <= 1) {
+      const auto r = split_issue<T, HD, 1>(kc, vc, spg, a.nkv, kvh, kbeg, nkeys, kch);
+      split_place<T, HD, L::KS, 1>(r, sk, sv, VS, kbeg, kend, kch, &spill);
+    } else if (nc == 2 || MAXCH <= 2) {
+      const auto r = split_issue<T, HD, (MAXCH < 2 ? MAXCH : 2)>(kc, vc, spg, a.nkv, kvh, kbeg,
+                                                                  nkeys, kch);
+      split_place<T, HD, L::KS, (MAXCH < 2 ? MAXCH : 2)>(r, sk, sv, VS, kbeg, kend, kch,
+                                                          &spill);
+    } else if (nc == 3) {
+      const auto r = split_issue<T, HD, (MAXCH < 3 ? MAXCH : 3)>(kc, vc, spg, a.nkv, kvh, kbeg,
+                                                                  nkeys, kch);
+      split_place<T, HD, L::KS, (MAXCH < 3 ? MAXCH : 3)>(r, sk, sv, VS, kbeg, kend, kch,
+                                                          &spill);
+    } else {
+      const auto r = split_issue<T, HD, MAXCH>(kc, vc, spg, a.nkv, kvh, kbeg, nkeys, kch);
+      split_place<T, HD, L::KS, MAXCH>(r, sk, sv, VS, kbeg, kend, kch, &spill);
     }
     __syncthreads();
   }
@@ -202,12 +431,9 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
     const int node = qvalid ? qr / G : 0;
     const int qhead = kvh * G + (qvalid ? qr % G : 0);
     const int grow = rm.row0 + node;
-    if (qtile != t_beg + wave) load_q(qtile, qf, qfl);  // the first was prefetched
-    uint64_t anc_lo = 0, anc_hi = 0;
-    if (qvalid && !rm.chain) {
-      const uint64_t* am = a.anc + rm.anc0 + (size_t)node * rm.anc_words;
-      anc_lo = am[0];
-      if (rm.anc_words > 1) anc_hi = am[1];
+    if (qtile != t_beg + wave) {  // the first was prefetched
+      load_q(qtile, qf, qfl);
+      load_anc(qtile, anc_lo, anc_hi);
     }
 
     const float scale2 = a.scale * 1.44269504088896340736f;  // log2(e)
@@ -216,124 +442,9 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = kbeg; kb < kend; kb += 32) {
-      const int kl = kb - kbeg;  // key offset inside the staged split
-      // ---- scores: S^T tiles for keys [kb, kb+16) and [kb+16, kb+32)
-      // all K fragments of the block are read from LDS first, then the two
-      // independent score chains are interleaved (no exposed LDS latency,
-      // no back-to-back dependent MFMAs)
-      // (hi and lo halves of q accumulate separately: four chains of
-      // HD / 32 dependent MFMAs instead of two of twice that length)
-      floatx4_t s[2], sl[2];
-      Frag<T> kf[2][HD / 32];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < HD / 32; ++ks)
-          kf[kt][ks].load(&sk[(size_t)(kl + kt * 16 + r16) * L::KS + ks * 32 + g * 8]);
-      s[0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      s[1] = s[0];
-      sl[0] = s[0];
-      sl[1] = s[0];
-#pragma unroll
-      for (int ks = 0; ks < HD / 32; ++ks) {
-        mma32(s[0], kf[0][ks], qf[ks]);
-        mma32(s[1], kf[1][ks], qf[ks]);
-        if (kSplit) {
-          mma32(sl[0], kf[0][ks], qfl[ks]);
-          mma32(sl[1], kf[1][ks], qfl[ks]);
-        }
-      }
-      if (kSplit) {
-        s[0] += sl[0];
-        s[1] += sl[1];
-      }
-      // visibility of the block's 32 keys for this lane's row, as a bit mask
-      // (bit i: key kb + i): keys past the split end are out; committed keys
-      // are in; a pass key (tree node tn = key - nctx) is in along a chain up
-      // to the row's own node, in a tree when tn is an ancestor or itself
-      uint32_t vis = 0;
-      if (qvalid) {
-        auto low_bits = [](int n) -> uint32_t {
-          return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : ((1u << n) - 1u);
-        };
-        const int c = rm.nctx - kb;  // committed keys in the block: [0, c)
-        uint32_t pass;
-        if (rm.chain) {
-          pass = low_bits(c + node + 1);
-        } else {
-          // block bit i <-> tree node i - c: the ancestor mask shifted by c
-          const int sh = -c;  // node of block bit 0 (may be negative)
-          uint64_t w;
-          if (sh >= 0) {
-            w = sh >= 128 ? 0 : sh >= 64 ? (anc_hi >> (sh - 64))
-                          : sh == 0 ? anc_lo : ((anc_lo >> sh) | (anc_hi << (64 - sh)));
-          } else {
-            w = -sh >= 64 ? 0 : (anc_lo << (-sh));
-          }
-          pass = (uint32_t)w;
-        }
-        vis = (low_bits(c) | pass) & low_bits(kend - kb);
-      }
-      // lane holds row r16, keys kb + kt*16 + 4g + r; scores in the base-2
-      // domain (scaled by log2 e) so that every weight is one v_exp_f32
-      float p[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (vis >> (kt * 16 + 4 * g + r)) & 1u;
-          const float v = ok ? s[kt][r] * scale2 : -INFINITY;
-          p[kt * 4 + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = quad_max(mx);
-      // No lane may skip the MFMAs below (they read operands of all lanes),
-      // so a row with nothing visible yet uses a finite stand-in maximum:
-      // every weight is then 0 and the state stays (-inf, 0, O = 0).
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 2^-inf = 0
-      float lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = (p[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_use);
-        lsum += p[e];
-      }
-      lsum = quad_sum(lsum);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt) o[dt] *= alpha;
-
-      // P as an operand of the KV type; for bf16 it is carried as a hi + lo
-      // pair (two MFMAs), which keeps ~16 mantissa bits of the weights
-      Frag<T> pf, pf_lo;
-      if (kSplit) {
-        float lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lo[e] = p[e] - op_round(p[e], T(0));
-        pack_p(pf_lo, lo);
-      }
-      pack_p(pf, p);
-      // V fragments in groups of four dim tiles, read before their MFMAs
-#pragma unroll
-      for (int d0 = 0; d0 < HD / 16; d0 += 4) {
-        Frag<T> vf[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const T* vrow = sv + (size_t)((d0 + u) * 16 + r16) * VS + kl;
-          load_vfrag<T>(vf[u], vrow + 4 * g, vrow + 16 + 4 * g);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf);
-        if (kSplit) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) mma32(o[d0 + u], vf[u], pf_lo);
-        }
-      }
-    }
+    for (int kb = kbeg; kb < kend; kb += 32)
+      attn_block<T, HD, L::KS>(sk, sv, VS, kb - kbeg, kb, kend, rm, node, qvalid, anc_lo, anc_hi,
+                               qf, qfl, scale2, g, r16, m_run, l_run, o);
 
     if (qvalid) {
       const size_t slot = attn_part_slot(split, a.rows_total, a.nq, grow, qhead);
@@ -344,6 +455,229 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
             make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
       if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
     }
+  }
+}
+
+constexpr int kStage = 64;  // keys per stage of the streamed kernel
+constexpr int kStreamMaxPages = 512;  // 16-key pages of one workgroup's key range
+
+// LDS of the streamed kernel: one stage (K rows, then V^T), reused at the
+// end for the merge slots (per slot and lane: HD / 4 output values, then
+// the running max and sum).
+template <typename T, int HD>
+struct StreamLds {
+  using L = SplitLds<T, HD>;
+  static constexpr int VS = kStage + L::VPAD;
+  static constexpr size_t kv_bytes = ((size_t)kStage * L::KS + (size_t)HD * VS) * sizeof(T);
+  static constexpr int SLOT = 64 * (HD / 4 + 2);  // floats per merge slot
+  static constexpr size_t merge_bytes = (size_t)4 * SLOT * sizeof(float);
+  static constexpr size_t bytes = kv_bytes > merge_bytes ? kv_bytes : merge_bytes;
+};
+
+// one workgroup per CU (two waves per SIMD): the next stage's loads in
+// registers beside a tile's state need more than 128 registers
+template <typename T, int HD>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char attn_smem[];
+  using L = SplitLds<T, HD>;
+  using SL = StreamLds<T, HD>;
+  constexpr int VS = SL::VS;
+  T* sk = reinterpret_cast<T*>(attn_smem);      // [kStage][KS]
+  T* sv = sk + (size_t)kStage * L::KS;           // [HD][VS]
+
+  const int range = blockIdx.x;
+  const int req = blockIdx.z / a.nkv, kvh = blockIdx.z % a.nkv;
+  const ReqMeta rm = a.reqs[req];
+  const int G = a.nq / a.nkv;
+  const int qrows = rm.nrows * G;
+  const int qt = (qrows + 15) / 16;  // <= kAttnStreamTiles (the launcher checks the largest)
+  const int total_keys = rm.nctx + rm.nrows;
+  const int kbeg = range * a.split;
+  if (qt == 0 || kbeg >= total_keys) return;  // uniform per block
+  const int kend = min(total_keys, kbeg + a.split);
+  const int kp = 4 * qt <= kAttnWaves ? 4 : 2 * qt <= kAttnWaves ? 2 : 1;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int tile = wave % qt, part = wave / qt;
+  const bool active = part < kp;
+
+  const T* kc = reinterpret_cast<const T*>(a.kc);
+  const T* vc = reinterpret_cast<const T*>(a.vc);
+  const int32_t* bt = a.btab + (size_t)rm.table * a.max_pages;
+
+  constexpr bool kSplit = sizeof(T) == 2;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* qlo = reinterpret_cast<const T*>(a.q_lo);
+  // the wave's query rows: q fragments (hi + lo bf16 planes, or fp32) and
+  // the ancestor mask, loaded ahead of the first stage
+  const int qr = tile * 16 + r16;
+  const bool qvalid = active && qr < qrows;
+  const int node = qvalid ? qr / G : 0;
+  const int qhead = kvh * G + (qvalid ? qr % G : 0);
+  const int grow = rm.row0 + node;
+  Frag<T> qf[HD / 32], qfl[HD / 32];
+#pragma unroll
+  for (int ks = 0; ks < HD / 32; ++ks) {
+    const size_t off = ((size_t)grow * a.nq + qhead) * HD + ks * 32 + g * 8;
+    if (qvalid) {
+      qf[ks].load(q + off);
+      if (kSplit) qfl[ks].load(qlo + off);
+    } else {
+      qf[ks].zero();
+      qfl[ks].zero();
+    }
+  }
+  uint64_t anc_lo = 0, anc_hi = 0;
+  if (qvalid && !rm.chain) {
+    const uint64_t* am = a.anc + rm.anc0 + (size_t)node * rm.anc_words;
+    anc_lo = am[0];
+    if (rm.anc_words > 1) anc_hi = am[1];
+  }
+  asm volatile("" ::: "memory");  // keep these loads ahead of the staging
+
+  // ---- staging of one stage: K rows and V^T of keys [s0, s0 + kStage)
+  // (keys past kend are zeros)
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int KCH_ROW = HD / EPC;
+  constexpr int VCH_ROW = 16 / EPC;
+  constexpr int NCH = kStage * KCH_ROW / kAttnThreads;  // 16-byte chunks per thread, each of K, V
+  static_assert(NCH * kAttnThreads == kStage * KCH_ROW, "stage chunks");
+  // The range's pages (one per 16 keys) are looked up once into LDS; then
+  // every load of a stage is unconditional, from page slots clamped to the
+  // last one that holds keys, and the loaded data is only stored to LDS
+  // (keys past kend are cleared there afterwards).  (Loads under per-lane
+  // conditions, or arithmetic on the loaded data, made the compiler wait for
+  // each load before going on.)
+  __shared__ int spg[kStreamMaxPages];
+  const int nslots = (kend - kbeg + 15) >> 4;  // <= kStreamMaxPages (checked by the launcher)
+  for (int k = threadIdx.x; k < nslots; k += kAttnThreads)
+    spg[k] = kv_page(rm.page0, bt, kbeg + 16 * k);
+  __syncthreads();
+  struct StageRegs {
+    uint4 k[NCH], v[NCH];
+  };
+  auto issue = [&](int s0) __attribute__((always_inline)) {
+    StageRegs r;
+    const int slot0 = (s0 - kbeg) >> 4;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = threadIdx.x + j * kAttnThreads;
+      {
+        const int i = c / KCH_ROW, pt = c % KCH_ROW;  // key s0 + i (i < kStage)
+        const int page = spg[min(slot0 + (i >> 4), nslots - 1)];
+        r.k[j] = *reinterpret_cast<const uint4*>(
+            kc + kv_k_index(page, a.nkv, kvh, i & 15, HD, pt * EPC));
+      }
+      {
+        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+        const int dim = rest / VCH_ROW, pt = rest % VCH_ROW;
+        const int page = spg[min(slot0 + blk, nslots - 1)];
+        r.v[j] = *reinterpret_cast<const uint4*>(
+            vc + kv_v_index(page, a.nkv, kvh, pt * EPC, HD, dim));
+      }
+    }
+    return r;
+  };
+  auto place = [&](const StageRegs& r, int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = threadIdx.x + j * kAttnThreads;
+      {
+        const int i = c / KCH_ROW, pt = c % KCH_ROW;
+        *reinterpret_cast<uint4*>(&sk[(size_t)i * L::KS + pt * EPC]) = r.k[j];
+      }
+      {
+        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+        const int dim = rest / VCH_ROW, pt = rest % VCH_ROW;
+        *reinterpret_cast<uint4*>(&sv[(size_t)dim * VS + blk * 16 + pt * EPC]) = r.v[j];
+      }
+    }
+    // the last stage: V of keys past kend (not written this pass) becomes
+    // zeros in LDS, over the chunk just stored by the same thread (K needs
+    // none: those keys' scores are masked out)
+    if (s0 + kStage > kend) {  // uniform
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = threadIdx.x + j * kAttnThreads;
+        const int blk = c / (HD * VCH_ROW), rest = c % (HD * VCH_ROW);
+        const int dim = rest / VCH_ROW, pt = rest % VCH_ROW;
+        const int t0 = s0 + blk * 16 + pt * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (t0 + e >= kend) sv[(size_t)dim * VS + blk * 16 + pt * EPC + e] = T(0);
+      }
+    }
+  };
+
+  const float scale2 = a.scale * 1.44269504088896340736f;  // log2(e)
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4_t o[HD / 16];
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  StageRegs nx = issue(kbeg);
+  place(nx, kbeg);
+  __syncthreads();
+  for (int s0 = kbeg; s0 < kend; s0 += kStage) {
+    const bool more = s0 + kStage < kend;  // uniform
+    if (more) nx = issue(s0 + kStage);     // in flight while this stage is used
+    if (active) {
+#pragma unroll
+      for (int b = 0; b < kStage / 32; ++b) {
+        const int kb = s0 + 32 * b;
+        if (kb < kend && ((kb - kbeg) / 32) % kp == part)
+          attn_block<T, HD, L::KS>(sk, sv, VS, 32 * b, kb, kend, rm, node, qvalid, anc_lo,
+                                   anc_hi, qf, qfl, scale2, g, r16, m_run, l_run, o);
+      }
+    }
+    __syncthreads();  // every wave is done with this stage
+    if (more) {
+      place(nx, s0 + kStage);
+      __syncthreads();
+    }
+  }
+
+  // ---- merge the kp states of each tile, pairwise: parts [r, 2r) into
+  // parts [0, r), in part order (the stage area is free after the last
+  // barrier above)
+  float* slots = reinterpret_cast<float*>(attn_smem);
+  for (int r = kp / 2; r >= 1; r /= 2) {
+    if (active && part >= r && part < 2 * r) {
+      float* sp = slots + (size_t)(tile * r + (part - r)) * SL::SLOT;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<floatx4_t*>(sp + (dt * 64 + lane) * 4) = o[dt];
+      sp[HD / 4 * 64 + lane] = m_run;
+      sp[HD / 4 * 64 + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (active && part < r) {
+      const float* sp = slots + (size_t)(tile * r + part) * SL::SLOT;
+      const float mb = sp[HD / 4 * 64 + lane], lb = sp[HD / 4 * 64 + 64 + lane];
+      const float m_new = fmaxf(m_run, mb);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float wa = __builtin_amdgcn_exp2f(m_run - m_use);  // 2^-inf = 0
+      const float wb = __builtin_amdgcn_exp2f(mb - m_use);
+      l_run = l_run * wa + lb * wb;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        const floatx4_t ob = *reinterpret_cast<const floatx4_t*>(sp + (dt * 64 + lane) * 4);
+        o[dt] = o[dt] * wa + ob * wb;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (qvalid && part == 0) {
+    const size_t slot = attn_part_slot(range, a.rows_total, a.nq, grow, qhead);
+    float* po = a.part_o + slot * HD;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+      *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
   }
 }
 
@@ -430,8 +764,39 @@ hipError_t attn_launch(const AttnArgs& a, const LaunchCtx& s) {
   return hipGetLastError();
 }
 
+template <typename T, int HD>
+hipError_t attn_stream_launch(const AttnArgs& a, const LaunchCtx& s) {
+  auto k = attn_stream_kernel<T, HD>;
+  constexpr size_t lds = StreamLds<T, HD>::bytes;
+  static_assert(StreamLds<T, HD>::merge_bytes <= 160 * 1024 && lds <= 160 * 1024, "LDS");
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)k,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(a.max_splits, 1, a.n_req * a.nkv);
+  if (s.t0 || s.t1) {
+    AttnArgs arg = a;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel((const void*)k, grid, dim3(kAttnThreads), args, lds, s.s, s.t0,
+                              s.t1, 0);
+  }
+  k<<<grid, kAttnThreads, lds, s.s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t attn_typed(const AttnArgs& a, const LaunchCtx& s) {
+  if (a.stream) {
+    // every request's query tiles of a KV head fit the waves of one workgroup
+    if (a.split < kStage || a.split % kStage || a.split > 16 * kStreamMaxPages ||
+        a.qtiles_per_wg < 1 ||
+        a.qtiles_per_wg > kAttnStreamTiles || a.max_qgroups != 1)
+      return hipErrorInvalidValue;
+    if (a.hd == 128) return attn_stream_launch<T, 128>(a, s);
+    if (a.hd == 64) return attn_stream_launch<T, 64>(a, s);
+    return hipErrorInvalidValue;
+  }
   if (a.split > kMaxSplitKeys || a.split < 32 || a.split % 32 || a.qtiles_per_wg < 1)
     return hipErrorInvalidValue;
   if (a.hd == 128) return attn_launch<T, 128>(a, s);

@@ -126,12 +126,19 @@ struct AttnArgs {
   float* part_o;            // [split][rows * nq][hd]
   float2* part_ml;          // [split][rows * nq] (running max, sum)
   int32_t nq, nkv, hd;
-  int32_t split;            // keys per split (multiple of 32, <= 128)
+  int32_t split;            // keys per split: a multiple of 32, <= 128; streamed:
+                            // keys per workgroup range, a multiple of 64
   int32_t qtiles_per_wg;    // 16-row query tiles per workgroup (a query group)
+  int32_t stream;           // 1: each workgroup streams a key range in stages
+                            // (requests with at most 8 query tiles per KV head)
   int32_t max_splits, max_qgroups, n_req;
   int32_t rows_total;
   float scale;
 };
+
+// Most 16-row query tiles per (request, KV head) of a streamed attention
+// launch (one per wavefront of its workgroups).
+constexpr int kAttnStreamTiles = 8;
 
 hipError_t launch_attention(bool bf16, const AttnArgs& a, hipStream_t s,
                             hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);

@@ -33,6 +33,7 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxSplits = 128;  // attention key splits per request (verify passes)
 constexpr int kMaxSplitsPrefill = 64;  // prefill chunks: splits of 128 keys up to 8192
 constexpr int kAttnSlots = 512;  // attention workgroups resident at once (2 per CU)
+constexpr int kAttnStreamSlots = 256;  // streamed attention workgroups resident at once (1 per CU)
 constexpr int kMaxPath = 64;     // accepted-path slots per request in the walk result
 constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 // tile order of the input projections (QKV, in_proj) and of the matrices
@@ -213,6 +214,8 @@ struct spec_ctx {
   bool poisoned = false;
   int fault_tok = -1;
   bool table_only = false;   // debug: always look pages up in the block table
+  int attn_mode = 0;         // debug: 0 = planner's choice, 1 = stream whenever the
+                             // query tiles allow it, 2 = never stream
   float fault_bias = 0.f;
   int fault_after = 0;
 
@@ -628,6 +631,7 @@ struct Pass {
   int lm_row0 = 0, lm_rows = 0;
   float* d_logits = nullptr;
   int split = 0, max_splits = 0, tpw = 0, max_qgroups = 0, max_rows_req = 0;
+  bool attn_stream = false;  // streamed attention (every request: <= 8 query tiles a KV head)
   bool walk = false;  // append the accepted-path walk (verify passes)
   bool lowp = false;  // read the weights' 8-bit view
   std::vector<int64_t> key(const spec_ctx* c) const;
@@ -649,9 +653,11 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
   P.lm_row0 = lm_row0;
   P.lm_rows = lm_rows;
   P.d_logits = d_logits;
-  // attention launch shape: a workgroup stages one key split of one
-  // (request, KV head) and serves a group of up to 32 query tiles (16 query
-  // rows each; all of a verify pass's) of it.  The split is the smallest of
+  // attention launch shape.  Streamed (every request has at most
+  // kAttnStreamTiles query tiles of 16 query rows per KV head): a workgroup
+  // walks one range of keys of one (request, KV head) in stages.  Otherwise
+  // a workgroup stages one key split of one (request, KV head) and serves a
+  // group of up to 32 query tiles of it.  The split is the smallest of
   // 32, 64, 96, 128 keys whose grid fits the resident workgroup slots (one
   // round, most parallelism), else 128 keys; the split table bounds it.  Key
   // counts are rounded up to 256 so that the launch shape (and a captured
@@ -663,6 +669,33 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
     qt_max = std::max(qt_max, (rows_per_req[r] * G + 15) / 16);
     max_rows_req = std::max(max_rows_req, rows_per_req[r]);
   }
+  const int split_cap = R <= cfg.max_rows ? kMaxSplits : kMaxSplitsPrefill;
+  const long pairs = (long)n_req * nkv;
+  const bool big = pairs * keys_max >= 2L * 64 * kAttnStreamSlots;
+  if (qt_max <= kAttnStreamTiles && c->attn_mode != 2 && (big || c->attn_mode == 1)) {
+    // streamed: every request's query tiles of a KV head fit one workgroup's
+    // waves, and one round of resident workgroups has at least two stages
+    // each; each (request, KV head) gets enough key ranges (multiples of 64
+    // keys) for about one workgroup per CU
+    // (forced by the debug flag: two ranges, so each range has several stages)
+    const int ranges = c->attn_mode == 1
+                           ? 2
+                           : (int)std::max(1L, ((long)kAttnStreamSlots + pairs - 1) / pairs);
+    int span = std::max(64, ((keys_max + ranges - 1) / ranges + 63) / 64 * 64);
+    auto nsplit = [&](int sp) { return (keys_max + sp - 1) / sp; };
+    while (nsplit(span) > split_cap || (size_t)nsplit(span) * R > c->split_rows) {
+      if (span >= keys_max)
+        return fail(c, SPEC_E_UNSUPPORTED, "context too long for the attention split table");
+      span += 64;
+    }
+    P.attn_stream = true;
+    P.split = span;
+    P.max_splits = nsplit(span);
+    P.tpw = std::max(qt_max, 1);
+    P.max_qgroups = 1;
+    P.max_rows_req = max_rows_req;
+    return SPEC_OK;
+  }
   const int q_groups = (qt_max + 31) / 32;
   const int tpw = (qt_max + q_groups - 1) / q_groups;
   auto wgs_for = [&](int sp) {
@@ -672,7 +705,6 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
            ((keys_up(keys_per_req[r]) + sp - 1) / sp);
     return w;
   };
-  const int split_cap = R <= cfg.max_rows ? kMaxSplits : kMaxSplitsPrefill;
   int split = 128;
   for (int sp : {32, 64, 96, 128}) {
     const int ns = (keys_max + sp - 1) / sp;
@@ -682,6 +714,7 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
       break;
     }
   }
+  P.attn_stream = false;
   P.split = split;
   P.max_splits = (keys_max + split - 1) / split;
   P.tpw = tpw;
@@ -694,7 +727,8 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
 
 std::vector<int64_t> Pass::key(const spec_ctx* c) const {
   return {R, n_req, tree_depth, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
-          split, max_splits, tpw, max_qgroups, max_rows_req, walk, lowp, c->fault_tok,
+          split, max_splits, tpw, max_qgroups, max_rows_req, attn_stream, walk, lowp,
+          c->fault_tok,
           (int64_t)__builtin_bit_cast(uint32_t, c->fault_bias), c->fault_after};
 }
 
@@ -729,6 +763,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
   aa.split = P.split;
   aa.max_splits = P.max_splits;
   aa.qtiles_per_wg = P.tpw;
+  aa.stream = P.attn_stream ? 1 : 0;
   aa.max_qgroups = P.max_qgroups;
   aa.n_req = n_req;
   aa.rows_total = R;
@@ -1350,8 +1385,10 @@ extern "C" int32_t spec_force_root(spec_ctx* c, int32_t req, int32_t token) {
 extern "C" int32_t spec_debug_flags(spec_ctx* c, int32_t flags) {
   int rc = check(c);
   if (rc) return rc;
-  if (flags & ~1) return fail(c, SPEC_E_INVAL, "unknown debug flags %d", flags);
+  if ((flags & ~7) || (flags & 6) == 6)
+    return fail(c, SPEC_E_INVAL, "unknown debug flags %d", flags);
   c->table_only = (flags & 1) != 0;
+  c->attn_mode = (flags & 2) ? 1 : (flags & 4) ? 2 : 0;
   return SPEC_OK;
 }
 

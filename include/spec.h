@@ -194,13 +194,14 @@ int32_t spec_force_root(spec_ctx* ctx, int32_t req, int32_t token);
 
 /* Test hooks: flags bit 0 makes attention look every KV page up in the
  * block table even where a request's pages are consecutive (where it
- * otherwise computes the page from the first one).  Bit 1 streams attention
- * (each workgroup walks a range of keys in stages) in every pass whose
- * requests have at most 8 query tiles of 16 query rows per KV head, also
- * where the planner would not (short contexts, few requests), with two key
- * ranges per request and KV head; bit 2 never streams it.  Bits 1 and 2 together, or other bits: SPEC_E_INVAL.
- * Results agree within rounding either way (the key ranges, and so the
- * order of the softmax sums, differ). */
+ * otherwise computes the page from the first one).  Verify passes stream
+ * attention (each workgroup walks a range of keys in stages for a group of
+ * at most 8 query tiles of 16 query rows); bit 1 makes the ranges two per
+ * request, KV head and query group, so that each spans several stages;
+ * bit 2 never streams (every pass stages one key split per workgroup).
+ * Bits 1 and 2 together, or other bits: SPEC_E_INVAL.  Results agree within
+ * rounding either way (the key ranges, and so the order of the softmax
+ * sums, differ). */
 int32_t spec_debug_flags(spec_ctx* ctx, int32_t flags);
 
 /* Fault injection for checking the token-forcing harness: adds `bias` to

@@ -70,17 +70,19 @@ def test_small_models(name, kind):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_gqa", "tiny_gqa_bf16", "tiny_hybrid_bf16"])
-@pytest.mark.parametrize("kind", ["chain", "tree"])
+@pytest.mark.parametrize("kind", ["chain", "tree", "bigtree"])
 def test_streamed_attention_small_models(name, kind):
-    """Attention streamed in stages of 64 keys (forced by the debug flag, in
-    two key ranges per request and KV head, so a range spans several stages
-    and ends in a partial one) on chains and trees whose query tiles per KV
-    head leave 4, 2 or 1 key blocks in flight per tile (tiny: one tile per
-    chain pass; the GQA models: 3 tiles per chain pass, 6 per tree pass);
+    """Attention streamed in stages of 64 keys in two key ranges per
+    request, KV head and query group (the debug flag), so a range spans
+    several stages and ends in a partial one, on chains and trees whose
+    query tiles per KV head leave 4, 2 or 1 key blocks in flight per tile
+    (tiny: one tile per chain pass; the GQA models: 3 tiles per chain pass,
+    6 per tree pass, and 41-node trees of 11 tiles in two query groups);
     every row's logits against the oracle's tree-masked pass."""
     cfg, W = _setup(name)
-    w = dict(K=4 if name == "tiny" and kind == "chain" else 8 if kind == "chain" else 20,
-             alpha=0.8, branching=(4, 3, 2, 2, 1, 1, 1, 1), max_depth=8)
+    K = {"chain": 4 if name == "tiny" else 8, "tree": 20, "bigtree": 40}[kind]
+    w = dict(K=K, alpha=0.8, branching=(6, 4, 3, 2, 2, 1, 1, 1), max_depth=8)
+    kind = "chain" if kind == "chain" else "tree"
     eng = engine_for(cfg, W, max_ctx=512, max_nodes=w["K"] + 1)
     eng.debug_flags(2)
     orc = oracle_for(cfg, W)
@@ -104,13 +106,15 @@ def test_prefill_chunking_and_long_prompt():
 # ---------------------------------------------------------------- batched
 
 @pytest.mark.parametrize("planned,table_only,stream", [
-    (False, False, False), (True, False, False), (False, True, False), (False, False, True),
-    (False, True, True)])
+    (False, False, None), (True, False, None), (False, True, None), (False, False, True),
+    (False, True, True), (False, False, False)])
 def test_batched_requests(planned, table_only, stream):
     """Several requests of different lengths in one fused verify per step,
     each checked against its own oracle greedy run (table_only: with every
     KV page looked up in the block table; stream: attention streamed in key
-    ranges of several stages, forced by the debug flag).  planned: each step's
+    ranges of several stages (True), or one key split staged per workgroup
+    (False), forced by the debug flags; None: the planner's choice).
+    planned: each step's
     draft lengths come from the batch planner (lengths up to 2, 4 or 8 from
     the requests' acceptance so far, 16 draft nodes shared by 5 requests, so
     a request may offer none); the emitted tokens must not depend on it."""
@@ -122,8 +126,9 @@ def test_batched_requests(planned, table_only, stream):
     lens_used = set()
     eng = engine_for(cfg, W, max_requests=8, max_ctx=512, max_nodes=K + 1,
                      max_rows=8 * (K + 1))
-    if table_only or stream:  # every KV page through the block table; streamed attention
-        eng.debug_flags((1 if table_only else 0) | (2 if stream else 0))
+    flags = (1 if table_only else 0) | {None: 0, True: 2, False: 4}[stream]
+    if flags:  # every KV page through the block table; streamed or split attention
+        eng.debug_flags(flags)
     orc = oracle_for(cfg, W)
     lens = [17, 40, 63, 100, 129]
     alphas = [0.4, 0.6, 0.7, 0.8, 0.9]

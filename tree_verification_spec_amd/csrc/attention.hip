@@ -20,9 +20,9 @@
 // un-normalised partials (O, running max of the scores scaled by log2 e,
 // running sum), merged in split order by attn_combine.
 //
-// Streamed variant (a request with at most 8 query tiles per KV head:
-// batched verify passes, chains): a workgroup owns one range of keys of one
-// (request, KV head) and walks it in stages of 64 keys.  The next stage's K
+// Streamed variant (verify passes): a workgroup owns one range of keys of
+// one (request, KV head) and one group of at most 8 of its query tiles, and
+// walks the range in stages of 64 keys.  The next stage's K
 // and V are loaded into registers while the current one (in LDS) is used,
 // so a workgroup keeps loads in flight for its whole range instead of
 // loading once and computing once.  All 8 waves compute: wave w takes
@@ -490,16 +490,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a
   const ReqMeta rm = a.reqs[req];
   const int G = a.nq / a.nkv;
   const int qrows = rm.nrows * G;
-  const int qt = (qrows + 15) / 16;  // <= kAttnStreamTiles (the launcher checks the largest)
+  // this workgroup's query group: tiles [t_beg, t_beg + qt) of the request
+  const int t_beg = blockIdx.y * a.qtiles_per_wg;  // qtiles_per_wg <= kAttnStreamTiles
+  const int qt = min((qrows + 15) / 16 - t_beg, a.qtiles_per_wg);
   const int total_keys = rm.nctx + rm.nrows;
   const int kbeg = range * a.split;
-  if (qt == 0 || kbeg >= total_keys) return;  // uniform per block
+  if (qt <= 0 || kbeg >= total_keys) return;  // uniform per block
   const int kend = min(total_keys, kbeg + a.split);
   const int kp = 4 * qt <= kAttnWaves ? 4 : 2 * qt <= kAttnWaves ? 2 : 1;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;
-  const int tile = wave % qt, part = wave / qt;
+  const int tile = t_beg + wave % qt, part = wave / qt;
   const bool active = part < kp;
 
   const T* kc = reinterpret_cast<const T*>(a.kc);
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a
   float* slots = reinterpret_cast<float*>(attn_smem);
   for (int r = kp / 2; r >= 1; r /= 2) {
     if (active && part >= r && part < 2 * r) {
-      float* sp = slots + (size_t)(tile * r + (part - r)) * SL::SLOT;
+      float* sp = slots + (size_t)((tile - t_beg) * r + (part - r)) * SL::SLOT;
 #pragma unroll
       for (int dt = 0; dt < HD / 16; ++dt)
         *reinterpret_cast<floatx4_t*>(sp + (dt * 64 + lane) * 4) = o[dt];
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a
     }
     __syncthreads();
     if (active && part < r) {
-      const float* sp = slots + (size_t)(tile * r + part) * SL::SLOT;
+      const float* sp = slots + (size_t)((tile - t_beg) * r + part) * SL::SLOT;
       const float mb = sp[HD / 4 * 64 + lane], lb = sp[HD / 4 * 64 + 64 + lane];
       const float m_new = fmaxf(m_run, mb);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -774,7 +776,7 @@ hipError_t attn_stream_launch(const AttnArgs& a, const LaunchCtx& s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(a.max_splits, 1, a.n_req * a.nkv);
+  dim3 grid(a.max_splits, a.max_qgroups, a.n_req * a.nkv);
   if (s.t0 || s.t1) {
     AttnArgs arg = a;
     void* args[] = {&arg};
@@ -788,10 +790,9 @@ hipError_t attn_stream_launch(const AttnArgs& a, const LaunchCtx& s) {
 template <typename T>
 hipError_t attn_typed(const AttnArgs& a, const LaunchCtx& s) {
   if (a.stream) {
-    // every request's query tiles of a KV head fit the waves of one workgroup
+    // a query group's tiles fit the waves of one workgroup
     if (a.split < kStage || a.split % kStage || a.split > 16 * kStreamMaxPages ||
-        a.qtiles_per_wg < 1 ||
-        a.qtiles_per_wg > kAttnStreamTiles || a.max_qgroups != 1)
+        a.qtiles_per_wg < 1 || a.qtiles_per_wg > kAttnStreamTiles || a.max_qgroups < 1)
       return hipErrorInvalidValue;
     if (a.hd == 128) return attn_stream_launch<T, 128>(a, s);
     if (a.hd == 64) return attn_stream_launch<T, 64>(a, s);

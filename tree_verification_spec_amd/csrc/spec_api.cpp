@@ -653,11 +653,11 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
   P.lm_row0 = lm_row0;
   P.lm_rows = lm_rows;
   P.d_logits = d_logits;
-  // attention launch shape.  Streamed (every request has at most
-  // kAttnStreamTiles query tiles of 16 query rows per KV head): a workgroup
-  // walks one range of keys of one (request, KV head) in stages.  Otherwise
-  // a workgroup stages one key split of one (request, KV head) and serves a
-  // group of up to 32 query tiles of it.  The split is the smallest of
+  // attention launch shape.  Streamed (verify passes): a workgroup walks one
+  // range of keys of one (request, KV head) in stages for a group of up to
+  // kAttnStreamTiles query tiles of 16 query rows.  Otherwise (prefill
+  // chunks) a workgroup stages one key split of one (request, KV head) and
+  // serves a group of up to 32 query tiles of it.  The split is the smallest of
   // 32, 64, 96, 128 keys whose grid fits the resident workgroup slots (one
   // round, most parallelism), else 128 keys; the split table bounds it.  Key
   // counts are rounded up to 256 so that the launch shape (and a captured
@@ -671,16 +671,16 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
   }
   const int split_cap = R <= cfg.max_rows ? kMaxSplits : kMaxSplitsPrefill;
   const long pairs = (long)n_req * nkv;
-  const bool big = pairs * keys_max >= 2L * 64 * kAttnStreamSlots;
-  if (qt_max <= kAttnStreamTiles && c->attn_mode != 2 && (big || c->attn_mode == 1)) {
-    // streamed: every request's query tiles of a KV head fit one workgroup's
-    // waves, and one round of resident workgroups has at least two stages
-    // each; each (request, KV head) gets enough key ranges (multiples of 64
-    // keys) for about one workgroup per CU
+  if (R <= cfg.max_rows && c->attn_mode != 2) {
+    // streamed (verify passes): query groups of at most kAttnStreamTiles
+    // tiles, and for each (request, KV head, query group) enough key ranges
+    // (multiples of 64 keys) for about one workgroup per CU
     // (forced by the debug flag: two ranges, so each range has several stages)
+    const int qgroups = (std::max(qt_max, 1) + kAttnStreamTiles - 1) / kAttnStreamTiles;
+    const long units = pairs * qgroups;
     const int ranges = c->attn_mode == 1
                            ? 2
-                           : (int)std::max(1L, ((long)kAttnStreamSlots + pairs - 1) / pairs);
+                           : (int)std::max(1L, ((long)kAttnStreamSlots + units - 1) / units);
     int span = std::max(64, ((keys_max + ranges - 1) / ranges + 63) / 64 * 64);
     auto nsplit = [&](int sp) { return (keys_max + sp - 1) / sp; };
     while (nsplit(span) > split_cap || (size_t)nsplit(span) * R > c->split_rows) {
@@ -691,8 +691,8 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
     P.attn_stream = true;
     P.split = span;
     P.max_splits = nsplit(span);
-    P.tpw = std::max(qt_max, 1);
-    P.max_qgroups = 1;
+    P.tpw = (std::max(qt_max, 1) + qgroups - 1) / qgroups;  // tiles per group, balanced
+    P.max_qgroups = qgroups;
     P.max_rows_req = max_rows_req;
     return SPEC_OK;
   }

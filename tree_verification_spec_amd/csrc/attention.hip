@@ -22,7 +22,8 @@
 //
 // Streamed variant (verify passes): a workgroup owns one range of keys of
 // one (request, KV head) and one group of at most 8 of its query tiles, and
-// walks the range in stages of 64 keys.  The next stage's K
+// walks the range in stages of 64 keys (a range that spans every request's
+// keys writes the normalised output itself, with no combine).  The next stage's K
 // and V are loaded into registers while the current one (in LDS) is used,
 // so a workgroup keeps loads in flight for its whole range instead of
 // loading once and computing once.  All 8 waves compute: wave w takes
@@ -673,27 +674,36 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a
   }
 
   if (qvalid && part == 0) {
-    const size_t slot = attn_part_slot(range, a.rows_total, a.nq, grow, qhead);
-    float* po = a.part_o + slot * HD;
+    if (a.max_splits == 1) {  // uniform: the whole key range, so the output itself
+      // (what the combine computes from one partial: o * (1 / l))
+      const float inv = 1.0f / l_run;
+      T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt)
-      *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
-          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
+      for (int dt = 0; dt < HD / 16; ++dt)
+        store_act4(out, out + a.out_lo, ((size_t)grow * a.nq + qhead) * HD + dt * 16 + 4 * g,
+                   make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv));
+    } else {
+      const size_t slot = attn_part_slot(range, a.rows_total, a.nq, grow, qhead);
+      float* po = a.part_o + slot * HD;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
+            make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (g == 0) a.part_ml[slot] = make_float2(m_run, l_run);
+    }
   }
 }
 
-// One workgroup of 4 waves per (row, query head): merge the splits of the
-// row's request.  Every wave reads the (max, sum) of all splits (lane l:
-// splits l and l + 64) and forms the same weights; wave w then accumulates
-// splits w, w + 4, ... for its lanes' dims (up to 16 splits' loads of a
-// wave in flight together, the first 16 issued with the (max, sum) loads),
-// and the four sums are added in wave order.
+// One wave per (row, query head), four to a workgroup: merge the splits of
+// the row's request.  Lane l reads the (max, sum) of splits l and l + 64 and
+// every lane forms the same weights; each lane then adds the splits in order
+// for its HD / 64 dims (16 splits' loads in flight together, the first 16
+// issued with the (max, sum) loads).
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, size_t olo) {
-  __shared__ float red[4][HD];
-  const int wid = blockIdx.x;  // row * nq + head
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + wave;  // row * nq + head
+  if (wid >= a.rows_total * a.nq) return;  // uniform per wave (no barriers below)
   const int grow = wid / a.nq, qhead = wid % a.nq;
   const int nsplit = (a.rows[grow].keys + a.split - 1) / a.split;  // <= 128
   const size_t sstride = (size_t)a.rows_total * a.nq;
@@ -702,12 +712,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   if (lane + 64 < nsplit)
     ml1 = a.part_ml[attn_part_slot(lane + 64, a.rows_total, a.nq, grow, qhead)];
   constexpr int PER = HD / 64;
-  constexpr int U = 16;  // splits per wave loaded together
+  constexpr int U = 16;  // splits loaded together
   const float* po = a.part_o + (size_t)wid * HD + lane * PER;
   auto load_group = [&](int s0, float (&v)[U][PER]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int sp = min(s0 + 4 * u, nsplit - 1);
+      const int sp = min(s0 + u, nsplit - 1);
 #pragma unroll
       for (int j = 0; j < PER; ++j) v[u][j] = po[(size_t)sp * sstride * HD + j];
     }
@@ -715,7 +725,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   // the first group of partial outputs is loaded together with the (max,
   // sum) pairs, ahead of the reductions that form the weights
   float v[U][PER];
-  load_group(wave, v);
+  load_group(0, v);
   const float M = wave_max(fmaxf(ml0.x, ml1.x));
   // the running maxima are in the base-2 domain of the split kernel
   const float w0 = (ml0.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml0.x - M);
@@ -724,11 +734,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int s0 = wave; s0 < nsplit; s0 += 4 * U) {
-    if (s0 != wave) load_group(s0, v);
+  for (int s0 = 0; s0 < nsplit; s0 += U) {
+    if (s0 != 0) load_group(s0, v);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int sp = s0 + 4 * u;
+      const int sp = s0 + u;
       const float wu = __shfl(sp < 64 ? w0 : w1, sp & 63, 64);
       if (sp < nsplit) {
 #pragma unroll
@@ -736,14 +746,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, T* out, s
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) red[wave][lane * PER + j] = acc[j];
-  __syncthreads();
   const float inv = 1.0f / L;
-  for (int dim = threadIdx.x; dim < HD; dim += 256) {
-    const float t = ((red[0][dim] + red[1][dim]) + red[2][dim]) + red[3][dim];
-    store_act(out, out + olo, ((size_t)grow * a.nq + qhead) * HD + dim, t * inv);
-  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    store_act(out, out + olo, ((size_t)grow * a.nq + qhead) * HD + lane * PER + j, acc[j] * inv);
 }
 
 template <typename T, int HD>
@@ -792,7 +798,8 @@ hipError_t attn_typed(const AttnArgs& a, const LaunchCtx& s) {
   if (a.stream) {
     // a query group's tiles fit the waves of one workgroup
     if (a.split < kStage || a.split % kStage || a.split > 16 * kStreamMaxPages ||
-        a.qtiles_per_wg < 1 || a.qtiles_per_wg > kAttnStreamTiles || a.max_qgroups < 1)
+        a.qtiles_per_wg < 1 || a.qtiles_per_wg > kAttnStreamTiles || a.max_qgroups < 1 ||
+        (a.max_splits == 1 && !a.out))
       return hipErrorInvalidValue;
     if (a.hd == 128) return attn_stream_launch<T, 128>(a, s);
     if (a.hd == 64) return attn_stream_launch<T, 64>(a, s);
@@ -808,7 +815,7 @@ hipError_t attn_typed(const AttnArgs& a, const LaunchCtx& s) {
 template <typename T>
 hipError_t combine_t(const AttnArgs& a, T* o, size_t olo, hipStream_t s) {
   if (a.max_splits > 128) return hipErrorInvalidValue;
-  dim3 grid(a.rows_total * a.nq);
+  dim3 grid((a.rows_total * a.nq + 3) / 4);  // a wave per (row, head)
   if (a.hd == 128) attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a, o, olo);
   else if (a.hd == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a, o, olo);
   else return hipErrorInvalidValue;

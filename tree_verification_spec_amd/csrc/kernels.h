@@ -130,7 +130,11 @@ struct AttnArgs {
                             // keys per workgroup range, a multiple of 64
   int32_t qtiles_per_wg;    // 16-row query tiles per workgroup (a query group)
   int32_t stream;           // 1: each workgroup streams a key range in stages
-                            // (requests with at most 8 query tiles per KV head)
+                            // for a group of at most 8 query tiles
+  void* out;                // streamed with one range per request (max_splits == 1):
+  size_t out_lo;            // the normalised output, written as activation planes
+                            // o[rows, nq*hd] (lo plane at out + out_lo elements)
+                            // instead of partials (no combine)
   int32_t max_splits, max_qgroups, n_req;
   int32_t rows_total;
   float scale;

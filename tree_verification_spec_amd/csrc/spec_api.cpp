@@ -764,6 +764,8 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
   aa.max_splits = P.max_splits;
   aa.qtiles_per_wg = P.tpw;
   aa.stream = P.attn_stream ? 1 : 0;
+  aa.out = c->attn_o;
+  aa.out_lo = lo_off(c, nq * hd);
   aa.max_qgroups = P.max_qgroups;
   aa.n_req = n_req;
   aa.rows_total = R;
@@ -787,7 +789,8 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
       aa.vc = vc;
       const TimePair ta = time_pair(c, 4);
       HIP_TRY(launch_attention(bf, aa, s, ta.t0, ta.t1));
-      HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, lo_off(c, nq * hd), s));
+      if (!(P.attn_stream && P.max_splits == 1))  // else written by the attention itself
+        HIP_TRY(launch_attn_combine(bf, aa, c->attn_o, lo_off(c, nq * hd), s));
       GemmArgs o = gemm_args(c, L.wo, c->attn_o, nq * hd, R, nq * hd, d);
       const int So = gemm_part(c, o, &e);
       HIP_TRY(e);

@@ -39,7 +39,7 @@ TYPES = ("gemm", "attention", "recurrent", "other")
 
 _TYPE_OF = [
     (re.compile(r"\bgemm(_tall)?_kernel\b"), "gemm"),
-    (re.compile(r"\battn_(combine_)?kernel\b"), "attention"),
+    (re.compile(r"\battn_(combine_|stream_)?kernel\b"), "attention"),
     (re.compile(r"\blr_(fork|commit)_kernel\b"), "recurrent"),
     (re.compile(r"\b(embed|rope_kv|resid_reduce|argmax_reduce|path_walk|kv_compact)_kernel\b"),
      "other"),

@@ -90,13 +90,18 @@ typedef struct spec_config {
   int32_t prefill_chunk;  /* prompt rows per prefill pass                    */
   int32_t page_size;      /* tokens per KV page; must be 16                  */
   int32_t weight_format;  /* SPEC_WEIGHTS_*; W12 (_LOWP) need SPEC_DTYPE_BF16 */
+  int32_t kv_pages;       /* KV pages in the pool, shared by all requests and
+                             taken as their contexts grow (prefill: the
+                             prompt's; verify: the pass's new positions);
+                             0: max_requests * ceil(max_ctx / 16), enough
+                             for every request at max_ctx                   */
 } spec_config;
 
 typedef struct spec_ctx spec_ctx;
 
 /* Device bytes the caller must provide to spec_create for this config:
- * weights in the library's tiled layout, the KV page pool (max_requests *
- * max_ctx tokens), recurrent states and scratch.  0 if cfg is invalid. */
+ * weights in the library's tiled layout, the KV page pool (kv_pages pages
+ * of 16 tokens), recurrent states and scratch.  0 if cfg is invalid. */
 size_t spec_workspace_bytes(const spec_config* cfg);
 
 /* Create a context on the current HIP device.  d_workspace: device buffer of

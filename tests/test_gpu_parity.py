@@ -105,15 +105,19 @@ def test_prefill_chunking_and_long_prompt():
 
 # ---------------------------------------------------------------- batched
 
-@pytest.mark.parametrize("planned,table_only,stream", [
-    (False, False, None), (True, False, None), (False, True, None), (False, False, True),
-    (False, True, True), (False, False, False)])
-def test_batched_requests(planned, table_only, stream):
+@pytest.mark.parametrize("planned,table_only,stream,pool", [
+    (False, False, None, 0), (True, False, None, 0), (False, True, None, 0),
+    (False, False, True, 0), (False, True, True, 0), (False, False, False, 0),
+    (False, False, None, 40), (False, False, True, 40)])
+def test_batched_requests(planned, table_only, stream, pool):
     """Several requests of different lengths in one fused verify per step,
     each checked against its own oracle greedy run (table_only: with every
     KV page looked up in the block table; stream: attention streamed in key
     ranges of several stages (True), or one key split staged per workgroup
-    (False), forced by the debug flags; None: the planner's choice).
+    (False), forced by the debug flags; None: the planner's choice; pool: a
+    KV pool of that many pages shared by the requests, which take pages as
+    they grow, so a request's pages interleave with the others' (0: room for
+    every request at max_ctx)).
     planned: each step's
     draft lengths come from the batch planner (lengths up to 2, 4 or 8 from
     the requests' acceptance so far, 16 draft nodes shared by 5 requests, so
@@ -125,7 +129,7 @@ def test_batched_requests(planned, table_only, stream):
     succ, fail = [0.0] * n_req, [0.0] * n_req
     lens_used = set()
     eng = engine_for(cfg, W, max_requests=8, max_ctx=512, max_nodes=K + 1,
-                     max_rows=8 * (K + 1))
+                     max_rows=8 * (K + 1), kv_pages=pool)
     flags = (1 if table_only else 0) | {None: 0, True: 2, False: 4}[stream]
     if flags:  # every KV page through the block table; streamed or split attention
         eng.debug_flags(flags)
@@ -206,6 +210,45 @@ def test_batched_requests(planned, table_only, stream):
 
 
 # ------------------------------------------------- spec == GPU AR (protocol A)
+
+def test_kv_pool_exhaustion_and_reuse():
+    """A pool of 6 KV pages for two requests: each prompt takes its pages at
+    prefill; a verify that needs a page the pool no longer has fails with
+    SPEC_E_CAPACITY and leaves the request as it was; after the other
+    request is released, the same verify succeeds on a page that request
+    held (so the request's pages are no longer consecutive, and attention
+    reads them through the block table) and every row's logits match the
+    oracle's."""
+    from tree_verification_spec_amd._lib import SPEC_E_CAPACITY, SpecError
+    cfg, W = _setup("tiny_gqa_bf16")
+    V = cfg["vocab"]
+    eng = engine_for(cfg, W, max_requests=2, max_ctx=256, max_nodes=5, kv_pages=6)
+    orc = oracle_for(cfg, W)
+    p0 = synth.prompt_tokens(V, 44, 61, 0)
+    p1 = synth.prompt_tokens(V, 40, 61, 1)
+    S, L, M, _ = ar_greedy(orc, p0, 6)
+    eng.prefill(1, p1)                   # 40 tokens: pages 0-2
+    first = eng.prefill(0, p0)           # 44 tokens: pages 3-5, the pool is empty
+    root = first if first == S[0] else int(S[0])
+    if first != S[0]:
+        assert M[0] < NEAR_TIE
+        eng.force_root(0, root)
+    drafts = [np.array(S[1:5], np.int32)]  # positions 44..48: a fourth page
+    parents = [np.arange(-1, 3, dtype=np.int32)]
+    with pytest.raises(SpecError) as e:
+        eng.verify([0], drafts, parents)
+    assert e.value.code == SPEC_E_CAPACITY
+    assert eng.state(0) == (44, root)
+    eng.release(1)                       # request 0 then takes page 0 after 3-5
+    paths, bonus, lg = eng.verify([0], drafts, parents, logits=True)
+    lg = lg.cpu().numpy()
+    # row j holds S[j] (the root, then the drafts): its logits are L[j + 1]
+    for j in range(5):
+        assert np.max(np.abs(lg[j] - L[j + 1])) <= logit_tol(cfg["dtype"], L[j + 1])
+    if min(M[1:6]) >= NEAR_TIE:
+        assert list(paths[0]) == [0, 1, 2, 3] and bonus[0] == S[5]
+    eng.close()
+
 
 def test_spec_equals_gpu_autoregressive():
     cfg, W = _setup("tiny")

@@ -78,3 +78,20 @@ def test_product_path_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_kv_pool_size_follows_kv_pages():
+    """The KV pool is kv_pages pages of 16 tokens (K and V of every attention
+    layer); 0 sizes it for every request at max_ctx; negative is invalid."""
+    L = _lib()
+    from tree_verification_spec_amd import make_config
+    tiny = synth.model_config("tiny")
+    full = L.spec_workspace_bytes(make_config(tiny, max_requests=4, max_ctx=512, max_nodes=5))
+    default_pages = 4 * 512 // 16
+    small = L.spec_workspace_bytes(make_config(tiny, max_requests=4, max_ctx=512, max_nodes=5,
+                                               kv_pages=40))
+    n_attn = tiny["layer_kinds"].count("A")
+    per_page = 2 * n_attn * tiny["n_kv_heads"] * 16 * tiny["head_dim"] * 4
+    assert abs((full - small) - (default_pages - 40) * per_page) <= 4096
+    assert L.spec_workspace_bytes(make_config(tiny, kv_pages=-1)) == 0
+

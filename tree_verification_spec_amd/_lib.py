@@ -45,7 +45,7 @@ class spec_config(ctypes.Structure):
         ("rms_eps", c_float), ("rope_theta", c_float),
         ("max_requests", c_int32), ("max_ctx", c_int32), ("max_nodes", c_int32),
         ("max_rows", c_int32), ("prefill_chunk", c_int32), ("page_size", c_int32),
-        ("weight_format", c_int32),
+        ("weight_format", c_int32), ("kv_pages", c_int32),
     ]
 
 

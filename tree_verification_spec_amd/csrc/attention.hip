@@ -394,7 +394,6 @@ __global__ __launch_bounds__(kAttnThreads, 4) void attn_kernel(AttnArgs a) {
 
   constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
   constexpr int KCH_ROW = HD / EPC;              // chunks per K row
-  constexpr int VCH_ROW = 16 / EPC;              // chunks per (dim, 16 keys)
   // ---- stage the whole split (K rows and V^T, padded with zeros to a
   // multiple of 32 keys) with every load in flight, NC chunks of each per
   // thread, NC as small as the split allows

@@ -206,7 +206,7 @@ struct spec_ctx {
   size_t meta_bytes = 0, off_reqs = 0, off_anc = 0;
   CommitReq* h_commit = nullptr;
   int32_t* h_res = nullptr;
-  int32_t* h_btab_row = nullptr;
+  int32_t* h_btab = nullptr;  // pinned mirror of the block tables [max_requests][max_pages]
 
   std::vector<Req> reqs;
   LastVerify last;
@@ -271,6 +271,7 @@ bool valid_config(const spec_config* cfg, std::string* why) {
   if (cfg->prefill_chunk < 1 || cfg->prefill_chunk > 1024) return bad("prefill_chunk");
   if (cfg->max_ctx < cfg->max_nodes + 1) return bad("max_ctx");
   if (cfg->max_ctx > kMaxSplitsPrefill * 128) return bad("max_ctx must be <= 8192");
+  if (cfg->kv_pages < 0 || cfg->kv_pages > (1 << 24)) return bad("kv_pages");
   bool any_lr = false;
   for (int i = 0; i < cfg->n_layers; ++i) {
     if (cfg->layer_kind[i] == SPEC_LAYER_LR) any_lr = true;
@@ -359,9 +360,10 @@ size_t plan_workspace(spec_ctx* c, const spec_config& cfg, char* base) {
                                                         npad(qkv_n), npad(d)})) : 0;
   const size_t w12_end = p.cursor;
 
-  // KV pool: every request reserves max_ctx tokens
-  const int max_pages = (cfg.max_ctx + 15) / 16;
-  const int n_pages = max_pages * cfg.max_requests;
+  // KV pool: kv_pages pages (default: every request at max_ctx), taken by
+  // the requests as their contexts grow
+  const int max_pages = (cfg.max_ctx + 15) / 16;  // per request
+  const int n_pages = cfg.kv_pages > 0 ? cfg.kv_pages : max_pages * cfg.max_requests;
   const size_t kv_layer_elems = (size_t)n_pages * nkv * 16 * hd;
   const size_t o_k = p.take(kv_layer_elems * esz * std::max(n_attn, 1));
   const size_t o_v = p.take(kv_layer_elems * esz * std::max(n_attn, 1));
@@ -919,6 +921,44 @@ int slot_of(const spec_ctx* c, const Req& rq, int t) {
   return rq.pages[t >> 4] * 16 + (t & 15);
 }
 
+// Pages a request still needs to hold tokens [0, tokens).
+int pages_needed(const Req& rq, int tokens) {
+  return std::max(0, (tokens + 15) / 16 - (int)rq.pages.size());
+}
+
+// Give request `req` `count` more pages from the pool (the caller checked
+// that it has them): the free list's last entries, so a request that grows
+// alone takes ascending pages; page0 stays valid while its pages are
+// consecutive.  The new block-table entries go to the device through the
+// pinned mirror (an entry is written once per grant, before any pass reads
+// it).
+int take_pages(spec_ctx* c, int req, int count) {
+  if (count <= 0) return SPEC_OK;
+  Req& rq = c->reqs[req];
+  const int first = (int)rq.pages.size();
+  int32_t* row = c->h_btab + (size_t)req * c->max_pages;
+  for (int i = 0; i < count; ++i) {
+    const int p = c->free_pages.back();
+    c->free_pages.pop_back();
+    if (rq.pages.empty()) rq.page0 = p;
+    else if (rq.page0 >= 0 && p != rq.page0 + (int)rq.pages.size()) rq.page0 = -1;
+    rq.pages.push_back(p);
+    row[first + i] = p;
+  }
+  if (hipMemcpyAsync(c->d_btab + (size_t)req * c->max_pages + first, row + first,
+                     (size_t)count * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess)
+    return fail(c, SPEC_E_HIP, "block table upload failed");
+  return SPEC_OK;
+}
+
+// A request's pages back to the pool, last first, so that the next request
+// to grow takes them in ascending order again.
+void give_back_pages(spec_ctx* c, Req& rq) {
+  for (auto it = rq.pages.rbegin(); it != rq.pages.rend(); ++it) c->free_pages.push_back(*it);
+  rq.pages.clear();
+  rq.page0 = -1;
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -970,7 +1010,7 @@ extern "C" int32_t spec_create(const spec_config* cfg, void* d_workspace,
                     hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c->h_res, sizeof(int32_t) * cfg->max_requests * (2 + kMaxPath),
                     hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c->h_btab_row, sizeof(int32_t) * c->max_pages,
+      hipHostMalloc((void**)&c->h_btab, sizeof(int32_t) * cfg->max_requests * c->max_pages,
                     hipHostMallocDefault) != hipSuccess)
     return cleanup(SPEC_E_HIP);
   memset(c->h_meta, 0, c->meta_bytes);
@@ -1080,26 +1120,16 @@ extern "C" int32_t spec_prefill(spec_ctx* c, int32_t req, const int32_t* prompt,
     return fail(c, SPEC_E_CAPACITY, "prompt of %d tokens exceeds max_ctx", n);
   for (int i = 0; i < n; ++i)
     if (prompt[i] < 0 || prompt[i] >= c->V) return fail(c, SPEC_E_INVAL, "token out of range");
-  if ((int)c->free_pages.size() < c->max_pages)
-    return fail(c, SPEC_E_CAPACITY, "KV pages exhausted");
-
   Req& rq = c->reqs[req];
-  rq.pages.assign(c->free_pages.end() - c->max_pages, c->free_pages.end());
-  std::reverse(rq.pages.begin(), rq.pages.end());
-  c->free_pages.resize(c->free_pages.size() - c->max_pages);
-  // pages return in reverse so the next request takes them ascending again
+  // the prompt's pages (later passes take more as the context grows)
+  const int need = pages_needed(rq, n);
+  if ((int)c->free_pages.size() < need) return fail(c, SPEC_E_CAPACITY, "KV pages exhausted");
   auto undo = [&](int code) {
-    for (auto it = rq.pages.rbegin(); it != rq.pages.rend(); ++it) c->free_pages.push_back(*it);
-    rq.pages.clear();
+    give_back_pages(c, rq);
     return code;
   };
-  rq.page0 = rq.pages[0];
-  for (int i = 1; i < c->max_pages; ++i)
-    if (rq.pages[i] != rq.pages[0] + i) rq.page0 = -1;
-  for (int i = 0; i < c->max_pages; ++i) c->h_btab_row[i] = rq.pages[i];
-  if (hipMemcpyAsync(c->d_btab + (size_t)req * c->max_pages, c->h_btab_row,
-                     (size_t)c->max_pages * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess)
-    return undo(fail(c, SPEC_E_HIP, "block table upload failed"));
+  rc = take_pages(c, req, need);
+  if (rc) return undo(rc);
   // zero recurrent states of this request
   for (int l = 0; l < c->n_lr; ++l)
     if (hipMemsetAsync(c->H + l * c->H_layer + (size_t)req * c->d * c->S, 0,
@@ -1189,6 +1219,17 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
       if (p < -1 || p >= j) return fail(c, SPEC_E_INVAL, "parent_idx out of range");
       if (t < 0 || t >= c->V) return fail(c, SPEC_E_INVAL, "draft token out of range");
     }
+
+  // pages for every request's new positions (all or none are taken)
+  int new_pages = 0;
+  for (int r = 0; r < n_req; ++r)
+    new_pages += pages_needed(c->reqs[req[r]], c->reqs[req[r]].n + n_nodes[r] + 1);
+  if (new_pages > (int)c->free_pages.size())
+    return fail(c, SPEC_E_CAPACITY, "KV pages exhausted (%d more needed)", new_pages);
+  for (int r = 0; r < n_req; ++r) {
+    rc = take_pages(c, req[r], pages_needed(c->reqs[req[r]], c->reqs[req[r]].n + n_nodes[r] + 1));
+    if (rc) return rc;
+  }
 
   const int words = (cfg.max_nodes + 63) / 64;
   RowMeta* rows = h_rows(c);
@@ -1359,7 +1400,7 @@ extern "C" int32_t spec_release(spec_ctx* c, int32_t req) {
   if (req < 0 || req >= c->cfg.max_requests) return fail(c, SPEC_E_INVAL, "bad request id");
   Req& rq = c->reqs[req];
   if (!rq.active) return fail(c, SPEC_E_STATE, "request %d not active", req);
-  for (auto it = rq.pages.rbegin(); it != rq.pages.rend(); ++it) c->free_pages.push_back(*it);
+  give_back_pages(c, rq);
   rq = Req();
   c->last.valid = false;
   return SPEC_OK;
@@ -1451,7 +1492,7 @@ extern "C" void spec_destroy(spec_ctx* c) {
   if (c->h_meta) (void)hipHostFree(c->h_meta);
   if (c->h_commit) (void)hipHostFree(c->h_commit);
   if (c->h_res) (void)hipHostFree(c->h_res);
-  if (c->h_btab_row) (void)hipHostFree(c->h_btab_row);
+  if (c->h_btab) (void)hipHostFree(c->h_btab);
   delete c;
 }
 

@@ -6,10 +6,11 @@ from . import _lib as L
 
 
 def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
-                max_rows=None, prefill_chunk=512, weight_format="native"):
+                max_rows=None, prefill_chunk=512, weight_format="native", kv_pages=0):
     """spec_config from a model-shape dict (keys as in synth.configs).
     weight_format: "native" (the model's dtype), "w12" or "w12_lowp" (W12 plus
-    the 8-bit view read by verify(lowp=True)); the W12 formats need bf16."""
+    the 8-bit view read by verify(lowp=True)); the W12 formats need bf16.
+    kv_pages: KV pool size in 16-token pages (0: every request at max_ctx)."""
     c = L.spec_config()
     c.n_layers = model["n_layers"]
     c.d_model = model["d_model"]
@@ -35,6 +36,7 @@ def make_config(model, max_requests=1, max_ctx=4096, max_nodes=17,
     if weight_format not in formats:
         raise ValueError(f"unknown weight format {weight_format!r}")
     c.weight_format = formats[weight_format]
+    c.kv_pages = kv_pages
     return c
 
 

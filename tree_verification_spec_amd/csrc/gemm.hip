@@ -547,9 +547,12 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 // issues RT x kTallCT x 2 MFMAs, so each fragment feeds several MFMAs.
 // A workgroup is kTallWM x kTallWN waves: kTallWM row groups (all of a
 // launch's rows up to 288, so a weight tile is streamed once per 288 rows)
-// by kTallWN column groups (128 columns).  Activations are staged one K-step
-// (32 columns, both planes) at a time in two LDS buffers; weights stream
-// with the next K-step's tiles in flight.  Epilogues as in the skinny
+// by kTallWN column groups (128 columns).  Activations go from memory
+// straight into LDS in chunks of two K-steps (both planes), the next chunk
+// in flight while one is used; weights stream through a window of four
+// K-steps in registers.  (Staging one K-step at a time through registers,
+// with one step of weights ahead, left each step waiting for its loads:
+// 38% matrix-core use on the 8B gate/up at 288 rows.)  Epilogues as in the skinny
 // kernel, written from registers: split partials, SwiGLU (the gate and up
 // tiles of a pair are a wave's column tiles 2q and 2q + 1), and the per-row
 // argmax partial of the workgroup's 128 columns.
@@ -567,13 +570,8 @@ template <int RT, int EPI, int WF>
 __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) {
   constexpr int CT = kTallCT;
   constexpr int RB = kTallWM * RT * 16;  // rows of a workgroup
-  constexpr int LROW = 32 + 8;           // staged row: one K-step + pad (bank spread)
-  constexpr int PLANE = RB * LROW;
   constexpr int NTHR = kTallWaves * 64;
-  constexpr int UNITS = 2 * RB * 4;      // 16-byte units of a staged K-step (both planes)
-  constexpr int XQ = (UNITS + NTHR - 1) / NTHR;
   constexpr bool W12 = WF == 1, W8 = WF == 2;
-  __shared__ __align__(16) uint16_t xs[2][2 * PLANE];
   __shared__ float rsc[RB];
   using WReg = typename std::conditional<
       W12, W12Raw, typename std::conditional<W8, uint2, Frag<uint16_t>>::type>::type;
@@ -640,35 +638,51 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
     }
   };
 
-  // activation staging, one K-step (32 values of each row and plane) at a
-  // time: unit e = (plane, row, quarter); rows past M and K past the split
-  // stage zeros (loads are unconditional from the plane's first element and
-  // masked afterwards)
-  const uint16_t* Xh = reinterpret_cast<const uint16_t*>(a.X);
-  uint4 xr[XQ];
-  auto fetch = [&](int kb) {
+  // ---- activation staging: buffer loads that write LDS (no registers), in
+  // chunks of two K-steps (32 values of every row, both planes, per step),
+  // two chunk buffers in turn.  A step's part of a chunk is 2 x RB/16 blocks
+  // of 1 KB (plane, row tile); one wavefront load fills one block: lane L
+  // writes bytes [16 L, 16 L + 16) of it, row L / 4, 16-byte slot L % 4,
+  // which holds that row's unit (L % 4) ^ ((row / 4) % 4), so the 16 rows of
+  // a fragment read fall in distinct banks.  Rows past M and steps past the
+  // split load from an offset beyond the buffer's range, which writes zeros.
+  // A chunk's loads are issued when no other chunk's are in flight (the
+  // compiler orders loads into LDS that it cannot tell apart).
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int CS = 2;                            // K-steps per chunk
+  constexpr int NBLK = 2 * RB / 16;                // blocks per K-step
+  static_assert(NBLK % kTallWaves == 0, "whole block loads per wave");
+  constexpr int NQS = NBLK / kTallWaves;           // block loads per wave per K-step
+  constexpr int STEP = RB * 64;                    // elements per staged K-step
+  // one array per (buffer, step), so that the compiler can tell a chunk's
+  // loads from the reads of the other buffer
+  __shared__ __align__(1024) uint16_t xs00[STEP];
+  __shared__ __align__(1024) uint16_t xs01[STEP];
+  __shared__ __align__(1024) uint16_t xs10[STEP];
+  __shared__ __align__(1024) uint16_t xs11[STEP];
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.X), (short)0, 0x7FFFFFFF, 0x00020000);
+  auto dma_step = [&](uint16_t* dst, int kb) {
     const bool kin = kb < kb_end;
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const int e = threadIdx.x + q * NTHR;
-      const int pl = e / (RB * 4), rest = e % (RB * 4);
-      const int r = rest >> 2, c = (rest & 3) * 8;
-      const bool in = e < UNITS && kin && r < rows;
-      const size_t off = in ? (size_t)pl * a.xlo + (size_t)(rbase + r) * a.ldx + kb * 32 + c : 0;
-      const uint32_t mk = in ? 0xFFFFFFFFu : 0u;
-      const uint4 h = *reinterpret_cast<const uint4*>(Xh + off);
-      xr[q] = make_uint4(h.x & mk, h.y & mk, h.z & mk, h.w & mk);
+    for (int q = 0; q < NQS; ++q) {
+      const int b = q * kTallWaves + wave;  // wave-uniform
+      const int pl = b / (RB / 16), rt = b % (RB / 16);
+      const int r = lane >> 2;
+      const int u = (lane & 3) ^ ((r >> 2) & 3);
+      const int row = rt * 16 + r;
+      const bool in = kin && row < rows;
+      const uint32_t voff =
+          in ? (uint32_t)(((pl ? (size_t)a.xlo : 0) + (size_t)(rbase + row) * a.ldx + kb * 32 +
+                           u * 8) * 2)
+             : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(dst + b * 512), 16, voff, 0, 0,
+                                               0);
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const int e = threadIdx.x + q * NTHR;
-      if (e >= UNITS) continue;
-      const int pl = e / (RB * 4), rest = e % (RB * 4);
-      const int r = rest >> 2, c = (rest & 3) * 8;
-      *reinterpret_cast<uint4*>(&xs[buf][pl * PLANE + r * LROW + c]) = xr[q];
-    }
+  auto dma = [&](uint16_t* d0, uint16_t* d1, int kb0) {
+    dma_step(d0, kb0);
+    dma_step(d1, kb0 + 1);
   };
 
   constexpr bool kNorm = EPI != EPI_PART;
@@ -683,28 +697,44 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
 #pragma unroll
     for (int t = 0; t < CT; ++t) acc[rt][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  WReg w[2][CT];
-  fetch(kb_beg);
+  // Pipeline: weights stream through a window of kWin K-steps in
+  // registers (a slot is refilled with the step kWin ahead right after its
+  // MFMAs); chunk c + 1 is loaded into the other buffer while chunk c is
+  // used.  Before a chunk is read each wave waits for its own loads of it
+  // (the loads it issued after them are the previous chunk's weight
+  // refills, NAFTER; loads complete in order for the counter), then the
+  // barrier covers every wave's, and every wave is done with the other
+  // buffer.
+  constexpr int kWin = 2 * CS;
+  constexpr int LPS = W12 ? 2 : 1;  // loads per weight tile per K-step
+  constexpr int NAFTER = CS * CT * LPS;
+  static_assert(NAFTER < 64, "vmcnt range");
+  constexpr int kWait = (NAFTER & 15) | ((NAFTER >> 4) << 14) | (7 << 4) | (15 << 8);
+  // the first loads in the order the loop leaves them at its edge (weights
+  // of two steps, the first chunk, weights of two more steps), so that the
+  // compiler's load counting is exact across the edge
+  WReg w[kWin][CT];
   load_step(w[0], kb_beg);
   load_step(w[1], kb_beg + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(xs00, xs01, kb_beg);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step(w[2], kb_beg + 2);
+  load_step(w[3], kb_beg + 3);
+
   const int xrow = wm * RT * 16 + r16;  // the lane's row in the workgroup's first row tile
-  // one K-step from buffer `buf` with the weights of slot u; the slot is
-  // then refilled with the step two ahead
-  auto kstep = [&](int kb, int buf, WReg (&wu)[CT]) {
-    store(buf);
-    fetch(kb + 1);
-    __syncthreads();
+  const int sw = (g ^ ((r16 >> 2) & 3)) * 8;  // the lane's slot in a staged row
+  auto kstep = [&](int kb, const uint16_t* cur, WReg (&wu)[CT]) {
     Frag<uint16_t> xh[RT], xl[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const uint16_t* p = &xs[buf][(xrow + rt * 16) * LROW + g * 8];
+      const uint16_t* p = cur + (wm * RT + rt) * 512 + r16 * 32 + sw;
       xh[rt].load(p);
-      xl[rt].load(p + PLANE);
+      xl[rt].load(p + RB * 32);
     }
     Frag<uint16_t> wf[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) wf[t] = wfrag(wu[t], t);
-    load_step(wu, kb + 2);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -712,11 +742,34 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
         mma32(acc[rt][t], wf[t], xh[rt]);
         mma32(acc[rt][t], wf[t], xl[rt]);
       }
+    // the slot's refill goes after the MFMAs that read it (bf16 tiles are
+    // used as loaded): issued earlier, it would need other registers and a
+    // copy back at the loop edge, which waits for the load
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(wu, kb + kWin);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kb = kb_beg; kb < kb_end; kb += 2) {
-    kstep(kb, 0, w[0]);
-    kstep(kb + 1, 1, w[1]);  // past the end: zero activations, nothing added
+  auto arrive = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWait);
+    __syncthreads();
+  };
+  // steps past the end: zero activations (and the last weight tile again)
+  for (int kb = kb_beg; kb < kb_end; kb += 2 * CS) {
+    arrive();
+    dma(xs10, xs11, kb + CS);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep(kb, xs00, w[0]);
+    kstep(kb + 1, xs01, w[1]);
+    arrive();
+    dma(xs00, xs01, kb + 2 * CS);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep(kb + 2, xs10, w[2]);
+    kstep(kb + 3, xs11, w[3]);
   }
+  // the last chunk's loads (zeros) land before the LDS is reused or freed
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
 
   // ---- results (registers: lane (r16, g) holds row r16, columns 4g..4g+3
   // of each tile)
@@ -762,7 +815,7 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
   // EPI_ARGMAX: per row, the largest value of the workgroup's columns and
   // its lowest index: over the lane's 16 values, the 4 lanes of the row, then
   // the column groups (through LDS)
-  float2* red = reinterpret_cast<float2*>(&xs[0][0]);  // [kTallWN][RB]
+  float2* red = reinterpret_cast<float2*>(xs00);  // [kTallWN][RB]
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int lr = xrow + rt * 16;
@@ -992,6 +1045,8 @@ hipError_t launch_gemm(bool bf16, int epi, const GemmArgs& a0, hipStream_t s,
   a.ncb = v.ncb;
   if (v.ntw == 0) {  // tall: all rows in one launch
     if (a.ntiles % (kTallCols / 16) || a.ncb < 1) return hipErrorInvalidValue;
+    // activations are addressed through 31-bit byte offsets (both planes)
+    if (((size_t)a.xlo + (size_t)a.M * a.ldx) * 2 >= 0x7FFFFFFFull) return hipErrorInvalidValue;
     if (epi == EPI_ARGMAX) a.nblocks = a.ncb;
     a.row0 = 0;
     const LaunchCtx lc{s, t0, t1};

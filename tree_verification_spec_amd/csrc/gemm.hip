@@ -642,9 +642,12 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
   // chunks of two K-steps (32 values of every row, both planes, per step),
   // two chunk buffers in turn.  A step's part of a chunk is 2 x RB/16 blocks
   // of 1 KB (plane, row tile); one wavefront load fills one block: lane L
-  // writes bytes [16 L, 16 L + 16) of it, row L / 4, 16-byte slot L % 4,
-  // which holds that row's unit (L % 4) ^ ((row / 4) % 4), so the 16 rows of
-  // a fragment read fall in distinct banks.  Rows past M and steps past the
+  // writes bytes [16 L, 16 L + 16) of it, row r = L / 4, 16-byte slot L % 4,
+  // which holds that row's unit (L % 4) ^ sz(r), sz(r) = ((r / 2) % 4) ^
+  // ((r / 8) % 2): the rows of a fragment read then fall in distinct banks
+  // whether the LDS serves 8 lanes of 16 bytes a cycle (rows 0-7 and 8-15
+  // apart) or 16 (all 16 rows).  (sz(r) = (r / 4) % 4, right for 16 only,
+  // stalled half the LDS cycles on bank conflicts.)  Rows past M and steps past the
   // split load from an offset beyond the buffer's range, which writes zeros.
   // A chunk's loads are issued when no other chunk's are in flight (the
   // compiler orders loads into LDS that it cannot tell apart).
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
       const int b = q * kTallWaves + wave;  // wave-uniform
       const int pl = b / (RB / 16), rt = b % (RB / 16);
       const int r = lane >> 2;
-      const int u = (lane & 3) ^ ((r >> 2) & 3);
+      const int u = (lane & 3) ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
       const int row = rt * 16 + r;
       const bool in = kin && row < rows;
       const uint32_t voff =
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(kTallWaves * 64) void gemm_tall_kernel(GemmArgs a) 
   load_step(w[3], kb_beg + 3);
 
   const int xrow = wm * RT * 16 + r16;  // the lane's row in the workgroup's first row tile
-  const int sw = (g ^ ((r16 >> 2) & 3)) * 8;  // the lane's slot in a staged row
+  const int sw = (g ^ ((r16 >> 1) & 3) ^ ((r16 >> 3) & 1)) * 8;  // the lane's slot in a staged row
   auto kstep = [&](int kb, const uint16_t* cur, WReg (&wu)[CT]) {
     Frag<uint16_t> xh[RT], xl[RT];
 #pragma unroll

@@ -4,10 +4,10 @@ This module is the single source of inputs shared by the CPU oracle and the
 GPU library: model shapes, random-init weights, prompts, draft chains, draft
 trees and the batched request mix.  It holds none of the model's arithmetic:
 it draws numbers and shapes only.  Weights are plain N(0, 0.02) samples
-(rounded to bf16 for the bf16 models), matching the "randomly initialised
-models shaped like the targets" that stand in for the pages' trained
-Qwen-family targets (SpecPilot paper card, abstract; besthub.dev article,
-"Experimental Results").
+(rounded to bf16 for the bf16 models): random-init models of the same
+shapes stand in for the trained Qwen-family targets the pages evaluate
+(SpecPilot paper card, abstract; besthub.dev article, "Experimental
+Results").
 """
 
 from .configs import MODELS, WORKLOADS, model_config, workload

@@ -458,6 +458,59 @@ def test_full_width_trees(name, budget):
     _assert_ok(rep)
 
 
+# ------------------------------------------------ row-count invariance
+
+def _main_path_tree(K, main_len, rng):
+    """Parents of K draft nodes: nodes 0..main_len-1 a chain from the root
+    (the main path), every other node a child of a random earlier node or
+    of the root."""
+    par = np.empty(K, np.int32)
+    for i in range(K):
+        par[i] = i - 1 if i < main_len else rng.integers(-1, i)
+    return par, list(range(main_len))
+
+
+@pytest.mark.parametrize("name,plen,K,kind", [
+    ("tiny_gqa_bf16", 100, 16, "chain"), ("tiny_gqa_bf16", 236, 16, "chain"),
+    ("tiny_hybrid_bf16", 100, 20, "tree"), ("tiny_gqa", 100, 16, "chain"),
+    ("dense8b_l2", 120, 16, "chain"), ("hybrid27b_l4", 120, 32, "tree")])
+@pytest.mark.parametrize("stream", [True, False])
+def test_row_count_invariance(name, plen, K, kind, stream):
+    """A verify pass of one request with at most 40 rows computes each row's
+    logits with the same bits as a one-row pass (an AR step) at that row's
+    position: the root row against the AR step at the committed length, and
+    each main-path node against the AR step after committing the path up to
+    it (token forcing).  Chains of 17 rows and trees of 21 and 33 rows (the
+    full-width 27B shape with two query groups), attention streamed (the
+    planner's choice) or one key split per workgroup (the debug flag); the
+    236-token prompt crosses a 256-key boundary of the attention plan between
+    the verify and the last AR step."""
+    cfg, W = _setup(name)
+    V = cfg["vocab"]
+    eng = engine_for(cfg, W, max_ctx=512, max_nodes=K + 1)
+    if not stream:
+        eng.debug_flags(4)
+    eng.prefill(0, synth.prompt_tokens(V, plen, 77))
+    rng = np.random.default_rng(5)
+    drafts = rng.integers(0, V, K).astype(np.int32)
+    if kind == "chain":
+        parents, main = np.arange(-1, K - 1, dtype=np.int32), list(range(K))
+    else:
+        parents, main = _main_path_tree(K, 6, rng)
+    _, _, lg = eng.verify([0], [drafts], [parents], logits=True)
+    rows = lg.cpu().numpy().copy()
+    empty = np.zeros(0, np.int32)
+    for j in range(5):
+        _, _, l1 = eng.verify([0], [empty], [empty], logits=True)
+        one = l1.cpu().numpy()[0].copy()
+        ref = rows[0] if j == 0 else rows[main[j - 1] + 1]
+        _say(name, kind, "streamed" if stream else "split", "step", j,
+             float(np.max(np.abs(one - ref))))
+        assert np.array_equal(one.view(np.uint32), ref.view(np.uint32)), j
+        eng.commit([0], [[]], [int(drafts[main[j]])])
+    eng.close()
+
+
 # ------------------------------------------------- W12 weight storage
 
 def _run_steps(eng, cfg, prompt, steps, seed, big=0):

@@ -30,7 +30,9 @@
 // query tile w % qt and every kp-th 32-key block (kp = 4, 2 or 1, the
 // largest with qt * kp <= 8, from block w / qt), and the kp states of a tile
 // are merged in LDS, pairwise in block-part order, before the range's
-// partial is written.
+// partial is written.  With one_part every tile takes kp = 1 (one wave
+// walks all its blocks in key order), so a row's result does not depend on
+// how many query tiles share its workgroup.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -497,7 +499,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_stream_kernel(AttnArgs a
   const int kbeg = range * a.split;
   if (qt <= 0 || kbeg >= total_keys) return;  // uniform per block
   const int kend = min(total_keys, kbeg + a.split);
-  const int kp = 4 * qt <= kAttnWaves ? 4 : 2 * qt <= kAttnWaves ? 2 : 1;
+  // waves per query tile (each takes every kp-th key block of a stage; their
+  // states merge at the end, so the rounding depends on kp)
+  const int kp = a.one_part ? 1 : 4 * qt <= kAttnWaves ? 4 : 2 * qt <= kAttnWaves ? 2 : 1;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, r16 = lane & 15;

@@ -131,6 +131,9 @@ struct AttnArgs {
   int32_t qtiles_per_wg;    // 16-row query tiles per workgroup (a query group)
   int32_t stream;           // 1: each workgroup streams a key range in stages
                             // for a group of at most 8 query tiles
+  int32_t one_part;         // streamed: one wave per query tile walks each stage
+                            // (else 2 or 4 waves split a tile's keys when the
+                            // group has at most 4 tiles)
   void* out;                // streamed with one range per request (max_splits == 1):
   size_t out_lo;            // the normalised output, written as activation planes
                             // o[rows, nq*hd] (lo plane at out + out_lo elements)

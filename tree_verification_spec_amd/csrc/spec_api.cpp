@@ -34,6 +34,7 @@ constexpr int kMaxSplits = 128;  // attention key splits per request (verify pas
 constexpr int kMaxSplitsPrefill = 64;  // prefill chunks: splits of 128 keys up to 8192
 constexpr int kAttnSlots = 512;  // attention workgroups resident at once (2 per CU)
 constexpr int kAttnStreamSlots = 256;  // streamed attention workgroups resident at once (1 per CU)
+constexpr int kInvariantRows = 40;     // rows of the GEMMs' one shape (stacked hi / lo rows)
 constexpr int kMaxPath = 64;     // accepted-path slots per request in the walk result
 constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 // tile order of the input projections (QKV, in_proj) and of the matrices
@@ -634,6 +635,7 @@ struct Pass {
   float* d_logits = nullptr;
   int split = 0, max_splits = 0, tpw = 0, max_qgroups = 0, max_rows_req = 0;
   bool attn_stream = false;  // streamed attention (every request: <= 8 query tiles a KV head)
+  bool one_part = false;     // streamed, one wave per query tile (row-count invariant)
   bool walk = false;  // append the accepted-path walk (verify passes)
   bool lowp = false;  // read the weights' 8-bit view
   std::vector<int64_t> key(const spec_ctx* c) const;
@@ -678,6 +680,15 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
     // tiles, and for each (request, KV head, query group) enough key ranges
     // (multiples of 64 keys) for about one workgroup per CU
     // (forced by the debug flag: two ranges, so each range has several stages)
+    // One request, at most kInvariantRows rows: the GEMMs of such passes
+    // share one launch shape (split counts, K order), so with one wave per
+    // query tile and a plan that does not depend on the pass's rows (query
+    // groups sized for the largest tree, keys counted to the largest tree
+    // by the caller) a row's logits are the same bits whatever the pass's
+    // rows: a verify's rows and AR steps at their positions agree exactly
+    // while the committed length stays in one 256-key bucket.
+    const bool invariant = n_req == 1 && R <= kInvariantRows;
+    if (invariant) qt_max = std::max(qt_max, (cfg.max_nodes * G + 15) / 16);
     const int qgroups = (std::max(qt_max, 1) + kAttnStreamTiles - 1) / kAttnStreamTiles;
     const long units = pairs * qgroups;
     const int ranges = c->attn_mode == 1
@@ -691,6 +702,7 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
       span += 64;
     }
     P.attn_stream = true;
+    P.one_part = invariant;
     P.split = span;
     P.max_splits = nsplit(span);
     P.tpw = (std::max(qt_max, 1) + qgroups - 1) / qgroups;  // tiles per group, balanced
@@ -729,7 +741,7 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
 
 std::vector<int64_t> Pass::key(const spec_ctx* c) const {
   return {R, n_req, tree_depth, prefill, lm_row0, lm_rows, (int64_t)(uintptr_t)d_logits,
-          split, max_splits, tpw, max_qgroups, max_rows_req, attn_stream, walk, lowp,
+          split, max_splits, tpw, max_qgroups, max_rows_req, attn_stream, one_part, walk, lowp,
           c->fault_tok,
           (int64_t)__builtin_bit_cast(uint32_t, c->fault_bias), c->fault_after};
 }
@@ -765,6 +777,7 @@ int launch_pass_impl(spec_ctx* c, const Pass& P) {
   aa.split = P.split;
   aa.max_splits = P.max_splits;
   aa.qtiles_per_wg = P.tpw;
+  aa.one_part = P.one_part ? 1 : 0;
   aa.stream = P.attn_stream ? 1 : 0;
   aa.out = c->attn_o;
   aa.out_lo = lo_off(c, nq * hd);
@@ -1285,7 +1298,9 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
     for (int i = 0; i <= K; ++i) max_depth = std::max(max_depth, dep[i]);
     rm[r] = ReqMeta{row, K + 1, rq.n, req[r], row * words, words, chain ? 1 : 0,
                     c->table_only ? -1 : rq.page0};
-    keys[r] = rq.n + K + 1;
+    // the attention plan (key ranges) from the committed length and the
+    // largest tree, so that a pass's key ranges do not depend on its K
+    keys[r] = rq.n + cfg.max_nodes;
     nrows[r] = K + 1;
     lv.req.push_back(req[r]);
     lv.row0.push_back(row);

@@ -153,11 +153,13 @@ int32_t spec_prefill(spec_ctx* ctx, int32_t req, const int32_t* prompt,
  * each request's rows being its root then its drafts in order.
  * The committed state is not modified.  Returns after the single
  * device-to-host copy of the results.
- * Row-count invariance: with one request and at most 40 rows, a row's
- * logits (hence its argmax) are bit-identical to those of a pass with
- * K_r = 0 at that row's position and prefix (an AR step), as long as the
- * committed length plus max_nodes stays within one 256-key bucket; larger
- * or multi-request passes agree with AR steps to rounding only. */
+ * Row-count invariance: with one request and at most 40 rows, the rows of
+ * the root and of the first-child chain from it (children in index order:
+ * a best-first tree's first branch) get logits (hence argmaxes)
+ * bit-identical to those of a pass with K_r = 0 at that row's position and
+ * prefix (an AR step), as long as the committed length plus max_nodes
+ * stays within one 256-key bucket; other rows, and larger or multi-request
+ * passes, agree with AR steps to rounding only. */
 int32_t spec_verify(spec_ctx* ctx, int32_t n_req, const int32_t* req,
                     const int32_t* n_nodes, const int32_t* draft_tokens,
                     const int32_t* parent_idx, int32_t* path,

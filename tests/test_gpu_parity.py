@@ -461,13 +461,24 @@ def test_full_width_trees(name, budget):
 # ------------------------------------------------ row-count invariance
 
 def _main_path_tree(K, main_len, rng):
-    """Parents of K draft nodes: nodes 0..main_len-1 a chain from the root
-    (the main path), every other node a child of a random earlier node or
-    of the root."""
-    par = np.empty(K, np.int32)
-    for i in range(K):
-        par[i] = i - 1 if i < main_len else rng.integers(-1, i)
-    return par, list(range(main_len))
+    """Parents of K draft nodes laid out like a best-first tree: the main
+    path (a chain from the root) is interleaved in index order with other
+    nodes hung off random earlier nodes, each main node being the first
+    child of its parent (so the main path is the depth-first walk's first
+    branch, not the lowest indices)."""
+    par, main = [], []
+    per = (K - main_len) // main_len
+    for d in range(main_len):
+        main.append(len(par))
+        par.append(main[-2] if d else -1)
+        for _ in range(per if d < main_len - 1 else K - len(par)):
+            if len(par) >= K:
+                break
+            cand = [-1] + [i for i in range(len(par)) if i != main[-1]]
+            par.append(int(rng.choice(cand)))
+    while len(par) < K:
+        par.append(int(rng.choice([-1] + list(range(len(par))))))
+    return np.array(par, np.int32), main
 
 
 @pytest.mark.parametrize("name,plen,K,kind", [

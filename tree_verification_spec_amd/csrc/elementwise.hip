@@ -600,7 +600,7 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(
   const int n = q.plen * hd;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int j = e / hd, dim = e % hd;
-    const int t = q.nctx + q.nodes[j];
+    const int t = q.nctx + q.slots[j];
     const int page = kv_page(-1, bt, t), off = t & 15;
     buf[0][e] = kc[kv_k_index(page, nkv, kvh, off, hd, dim)];
     buf[1][e] = vc[kv_v_index(page, nkv, kvh, off, hd, dim)];
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(
   __syncthreads();
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int j = e / hd, dim = e % hd;
-    if (q.nodes[j] == j + 1) continue;  // already in place
+    if (q.slots[j] == j + 1) continue;  // already in place
     const int t = q.nctx + j + 1;
     const int page = kv_page(-1, bt, t), off = t & 15;
     kc[kv_k_index(page, nkv, kvh, off, hd, dim)] = buf[0][e];

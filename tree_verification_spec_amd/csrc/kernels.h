@@ -219,9 +219,10 @@ struct CommitReq {
   int32_t row0;      // first row of the request in the verified pass
   int32_t plen;      // accepted drafts
   int32_t nodes[64]; // accepted node indices (root excluded), root-to-leaf
+  int32_t slots[64]; // their KV slots past nctx (the nodes' depth-first ranks)
 };
 
-// Move the accepted branch's K/V from slot (n + node) to position
+// Move the accepted branch's K/V from slot (n + rank) to position
 // (n + depth) for every attention layer.
 hipError_t launch_kv_compact(bool bf16, const CommitReq* cr, int n_req,
                              const int32_t* btab, int max_pages, void* kbase,

@@ -126,6 +126,7 @@ struct LastVerify {
   bool valid = false;
   std::vector<int> req, row0, nrows, nctx;
   std::vector<std::vector<int>> parent;  // node-local parents
+  std::vector<std::vector<int>> rank;    // node -> depth-first rank (its KV slot past n)
 };
 
 }  // namespace
@@ -1257,27 +1258,20 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
   for (int r = 0; r < n_req; ++r) {
     const Req& rq = c->reqs[req[r]];
     const int K = n_nodes[r];
-    std::vector<int> par(K + 1), dep(K + 1);
+    std::vector<int> par(K + 1), dep(K + 1), rank(K + 1);
     bool chain = true;
     for (int i = 0; i <= K; ++i) {
       const int p = i == 0 ? -1 : parent_idx[off + i - 1] + 1;
       par[i] = p;
       dep[i] = p < 0 ? 0 : dep[p] + 1;
       if (p != i - 1) chain = false;
-      RowMeta& m = rows[row + i];
-      m.token = i == 0 ? rq.root : draft_tokens[off + i - 1];
-      m.pos = rq.n + dep[i];
-      m.slot = slot_of(c, rq, rq.n + i);
-      m.req = r;
-      m.node = i;
-      m.parent = p;
-      m.keys = rq.n + K + 1;
-      uint64_t* a = anc + (size_t)(row + i) * words;
-      for (int w = 0; w < words; ++w) a[w] = p < 0 ? 0 : anc[(size_t)(row + p) * words + w];
-      a[i >> 6] |= 1ull << (i & 63);
     }
     // depth-first (pre-order) walk of the tree, children in index order:
-    // the recurrent layers visit the nodes in this order
+    // the recurrent layers visit the nodes in this order, and a node's KV
+    // slot is n + its rank in it, so the first-child chain from the root
+    // (in a best-first tree, the most probable branch) has its keys at its
+    // own positions, contiguous after the committed ones: its rows see the
+    // keys an AR step sees, in the same places, and its commit moves no KV
     {
       std::vector<int> kids_start(K + 2, 0), kids;
       for (int i = 1; i <= K; ++i) ++kids_start[par[i] + 1];
@@ -1290,9 +1284,25 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
       while (!stack.empty()) {
         const int v = stack.back();
         stack.pop_back();
+        rank[v] = k;
         rows[row + k++].order = v;
         for (int e = kids_start[v + 1] - 1; e >= kids_start[v]; --e) stack.push_back(kids[e]);
       }
+    }
+    for (int i = 0; i <= K; ++i) {
+      const int p = par[i];
+      RowMeta& m = rows[row + i];
+      m.token = i == 0 ? rq.root : draft_tokens[off + i - 1];
+      m.pos = rq.n + dep[i];
+      m.slot = slot_of(c, rq, rq.n + rank[i]);
+      m.req = r;
+      m.node = i;
+      m.parent = p;
+      m.keys = rq.n + K + 1;
+      // ancestors (and the node itself) by KV slot: bit rank(a)
+      uint64_t* a = anc + (size_t)(row + i) * words;
+      for (int w = 0; w < words; ++w) a[w] = p < 0 ? 0 : anc[(size_t)(row + p) * words + w];
+      a[rank[i] >> 6] |= 1ull << (rank[i] & 63);
     }
     if (!chain) any_tree = true;
     for (int i = 0; i <= K; ++i) max_depth = std::max(max_depth, dep[i]);
@@ -1307,6 +1317,7 @@ int verify_impl(spec_ctx* c, int32_t n_req, const int32_t* req, const int32_t* n
     lv.nrows.push_back(K + 1);
     lv.nctx.push_back(rq.n);
     lv.parent.push_back(par);
+    lv.rank.push_back(rank);
     row += K + 1;
     off += K;
   }
@@ -1376,7 +1387,7 @@ extern "C" int32_t spec_commit(spec_ctx* c, int32_t n_req, const int32_t* req,
       const int node = path[(size_t)r * slots + k] + 1;
       if (node < 1 || node > K || par[node] != prev)
         return fail(c, SPEC_E_STATE, "request %d: path is not a root path", req[r]);
-      if (node != k + 1) need_compact = true;
+      if (c->last.rank[r][node] != k + 1) need_compact = true;
       prev = node;
     }
   }
@@ -1386,7 +1397,10 @@ extern "C" int32_t spec_commit(spec_ctx* c, int32_t n_req, const int32_t* req,
     q.nctx = c->last.nctx[r];
     q.row0 = c->last.row0[r];
     q.plen = path_len[r];
-    for (int k = 0; k < path_len[r]; ++k) q.nodes[k] = path[(size_t)r * slots + k] + 1;
+    for (int k = 0; k < path_len[r]; ++k) {
+      q.nodes[k] = path[(size_t)r * slots + k] + 1;
+      q.slots[k] = c->last.rank[r][q.nodes[k]];
+    }
   }
   if (need_compact || c->n_lr) {
     HIP_TRY(hipMemcpyAsync(c->d_commit, c->h_commit, sizeof(CommitReq) * n_req,

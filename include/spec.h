@@ -153,7 +153,7 @@ int32_t spec_prefill(spec_ctx* ctx, int32_t req, const int32_t* prompt,
  * each request's rows being its root then its drafts in order.
  * The committed state is not modified.  Returns after the single
  * device-to-host copy of the results.
- * Row-count invariance: with one request and at most 40 rows, the rows of
+ * Row-count invariance: with one request and at most 128 rows, the rows of
  * the root and of the first-child chain from it (children in index order:
  * a best-first tree's first branch) get logits (hence argmaxes)
  * bit-identical to those of a pass with K_r = 0 at that row's position and

@@ -484,15 +484,17 @@ def _main_path_tree(K, main_len, rng):
 @pytest.mark.parametrize("name,plen,K,kind", [
     ("tiny_gqa_bf16", 100, 16, "chain"), ("tiny_gqa_bf16", 236, 16, "chain"),
     ("tiny_hybrid_bf16", 100, 20, "tree"), ("tiny_gqa", 100, 16, "chain"),
-    ("dense8b_l2", 120, 16, "chain"), ("hybrid27b_l4", 120, 32, "tree")])
+    ("dense8b_l2", 120, 16, "chain"), ("hybrid27b_l4", 120, 32, "tree"),
+    ("tiny_gqa_bf16", 100, 64, "tree"), ("dense8b_l2", 120, 64, "tree")])
 @pytest.mark.parametrize("stream", [True, False])
 def test_row_count_invariance(name, plen, K, kind, stream):
-    """A verify pass of one request with at most 40 rows computes each row's
+    """A verify pass of one request with at most 128 rows computes each row's
     logits with the same bits as a one-row pass (an AR step) at that row's
     position: the root row against the AR step at the committed length, and
     each main-path node against the AR step after committing the path up to
-    it (token forcing).  Chains of 17 rows and trees of 21 and 33 rows (the
-    full-width 27B shape with two query groups), attention streamed (the
+    it (token forcing).  Chains of 17 rows and trees of 21, 33 (the
+    full-width 27B shape with two query groups) and 65 rows (the 8B tree:
+    the GEMMs' two-tile shape, three query groups), attention streamed (the
     planner's choice) or one key split per workgroup (the debug flag); the
     236-token prompt crosses a 256-key boundary of the attention plan between
     the verify and the last AR step."""

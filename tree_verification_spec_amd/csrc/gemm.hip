@@ -134,11 +134,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
   // W12: the overflow blocks of crowded tiles (w12.h)
   const uint32_t* ovf = W12 ? w12_overflow(a.W, (size_t)a.ntiles * (a.K / 32)) : nullptr;
 
-  floatx4_t acc[NTW][MT];
+  // bf16 planes staged side by side: the hi and lo products accumulate
+  // apart and are added once at the end, as the stacked rows are (so a
+  // row's outputs are the same bits whatever the pass's row count)
+  constexpr bool kSepLo = NPL == 2;
+  floatx4_t acc[NTW][MT], acl[kSepLo ? NTW : 1][kSepLo ? MT : 1];
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kSepLo) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acl[t][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- activation chunk prefetch (registers) and store (LDS)
   // one unit = 16 bytes of one row: 8 consecutive K values of a bf16 plane,
@@ -298,7 +308,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
-          for (int p = 0; p < XF; ++p) mma32(acc[t][mt], wf[t], xc[mt][p]);
+          for (int p = 0; p < XF; ++p) {
+            if (kSepLo && p == 1) mma32(acl[t][mt], wf[t], xc[mt][1]);
+            else mma32(acc[t][mt], wf[t], xc[mt][p]);
+          }
       load_step(w[u], kw + u + WIN);
       // ordered: each step's refill is issued right after its MFMAs (the
       // scheduler would otherwise sink all refills to the end of the
@@ -414,6 +427,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs a) {
         });
       }
     }
+  }
+
+  if constexpr (kSepLo) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][mt][r] = acc[t][mt][r] + acl[t][mt][r];
   }
 
   // ---- results
@@ -538,7 +560,7 @@ hipError_t launch_one(const GemmArgs& a, const LaunchCtx& s) {
 }
 
 // ---------------------------------------------------------------- tall GEMM
-// More than 40 rows (bf16 activation planes; fused multi-request verify
+// More than 128 rows (bf16 activation planes; fused multi-request verify
 // passes and prefill chunks): the skinny kernel above gives each wave one
 // column tile and every row, so each staged activation fragment feeds one
 // MFMA and the LDS reads grow with the rows.  Here a wave owns a block of

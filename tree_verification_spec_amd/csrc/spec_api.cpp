@@ -34,7 +34,9 @@ constexpr int kMaxSplits = 128;  // attention key splits per request (verify pas
 constexpr int kMaxSplitsPrefill = 64;  // prefill chunks: splits of 128 keys up to 8192
 constexpr int kAttnSlots = 512;  // attention workgroups resident at once (2 per CU)
 constexpr int kAttnStreamSlots = 256;  // streamed attention workgroups resident at once (1 per CU)
-constexpr int kInvariantRows = 40;     // rows of the GEMMs' one shape (stacked hi / lo rows)
+constexpr int kInvariantRows = 128;    // rows whose GEMM outputs do not depend on the row count
+                                       // (the skinny kernel's shapes: one split count and K
+                                       // order per matrix, hi and lo products summed apart)
 constexpr int kMaxPath = 64;     // accepted-path slots per request in the walk result
 constexpr size_t kMaxGraphs = 8; // captured verify-pass graphs kept per context
 // tile order of the input projections (QKV, in_proj) and of the matrices
@@ -682,7 +684,7 @@ int plan_pass(spec_ctx* c, Pass& P, int R, int n_req, const std::vector<int>& ke
     // (multiples of 64 keys) for about one workgroup per CU
     // (forced by the debug flag: two ranges, so each range has several stages)
     // One request, at most kInvariantRows rows: the GEMMs of such passes
-    // share one launch shape (split counts, K order), so with one wave per
+    // give each output the same sums (split counts, K order), so with one wave per
     // query tile and a plan that does not depend on the pass's rows (query
     // groups sized for the largest tree, keys counted to the largest tree
     // by the caller) a row's logits are the same bits whatever the pass's
